@@ -1,0 +1,250 @@
+/*
+ * lssar_ref.c -- fp64 CPU oracle for LSSAR causal attention (forward).
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and the CPU
+ * baseline of the bench; never by the HIP library, and it shares no code
+ * with it.
+ *
+ * Source: paper note "Softplus Attention with Re-weighting Boosts Length
+ * Extrapolation in Large Language Models" (papernotes.org, ICML 2026),
+ * section Method details.  The steps below follow that section's order:
+ *
+ *   Overall framework + Key design 1 (LSSA, the normalisation stage):
+ *     Q_i <- Q_i/|Q_i|_2,  K_j <- K_j/|K_j|_2
+ *     A   = Softplus((log d . log N) (.) Q K^T) (.) M'
+ *           N: L x L, every element of row i equals i; M': lower triangle 1
+ *     A_i <- A_i / |A_i|_1
+ *   Key design 2 (re-weighting, the sharpening stage):
+ *     A   <- ReLU^p(A (.) N - O),  O = ones except its first 3 rows = 0
+ *     A_i <- A_i / |A_i|_1
+ *   Key design 3 (integration): the result replaces Softmax(.), so the
+ *     attention output is A V; the mask multiplies (0/1) instead of adding
+ *     -inf because Softplus is non-negative.
+ *
+ * Readings where the note is silent or loose (each one is a choice):
+ *   R1  "log" is the natural logarithm; d is the head dimension.
+ *   R2  Row index i of N is 1-based (row i attends to i tokens), so row 1
+ *       has scale log 1 = 0.
+ *   R3  No 1/sqrt(d) temperature: log d . log i replaces it.
+ *   R4  Softplus(x) = log(1 + e^x), beta = 1, no linear cut-over.
+ *   R5  M' multiplies AFTER Softplus: a masked entry is exactly 0 and adds
+ *       nothing to the row's L1 norm.
+ *   R6  A zero row of Q or K is normalised with its norm clamped to 1e-12.
+ *   R7  o_i = 0 for rows i = 1, 2, 3 and 1 for i >= 4, at every length.
+ *   R8  Stage 2 acts on the stage-1 L1-normalised A.
+ *   R9  p is an integer >= 1; ReLU(0)^p = 0.
+ *   R10 Degenerate rows: when m_i = max_j (i A_ij - o_i) <= eps, every
+ *       ReLU^p entry is (numerically) zero and the stage-2 L1 normalisation
+ *       has no meaningful value; the output row is then 0.  This is the
+ *       scale-invariant form of clamping the stage-2 denominator (the page
+ *       "Softmax alternatives and the attention-sink problem", Practical
+ *       advice, asks that the denominator never be zero).
+ *   R11 Square causal self-attention, one K/V head per Q head; q, k are the
+ *       post-RoPE vectors.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC lssar_ref.c -lm (no -ffast-math).
+ */
+#include "lssar_ref.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Softplus(x) = log(1 + e^x)  (R4), evaluated without overflow:
+ * for x > 0, log(1 + e^x) = x + log(1 + e^-x). */
+static double softplus(double x)
+{
+    if (x > 0.0)
+        return x + log1p(exp(-x));
+    return log1p(exp(x));
+}
+
+/* x^p by repeated multiplication (R9: integer p >= 1). */
+static double ipow(double x, int p)
+{
+    double r = 1.0;
+    for (int e = 0; e < p; ++e)
+        r *= x;
+    return r;
+}
+
+/* Row L2 normalisation (Key design 1): y = x / max(|x|_2, 1e-12)  (R6). */
+static void l2_normalise(const double* x, double* y, int d)
+{
+    double ss = 0.0;
+    for (int e = 0; e < d; ++e)
+        ss += x[e] * x[e];
+    double nrm = sqrt(ss);
+    if (nrm < 1e-12)
+        nrm = 1e-12;
+    for (int e = 0; e < d; ++e)
+        y[e] = x[e] / nrm;
+}
+
+/* One output row.  qh: the normalised query row i (0-based row = i-1);
+ * kh: all L normalised key rows of the head; v: the head's V; a: scratch of
+ * L doubles.  Every j in 1..L is computed and then multiplied by the mask
+ * M'_ij, as the matrix form on the page does. */
+static void lssar_row(const double* qh, const double* kh, const double* v,
+                      int L, int d, int p, double eps, int row,
+                      double* a, double* out)
+{
+    const int i = row + 1;                       /* R2: 1-based row index */
+    const double scale = log((double)d) * log((double)i);   /* log d . log N_ij, R1 */
+
+    /* Stage 1 (Key design 1): A_ij = Softplus(scale * q^_i . k^_j) * M'_ij */
+    double l1 = 0.0;
+    for (int j = 1; j <= L; ++j) {
+        const double* kj = kh + (size_t)(j - 1) * d;
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e)
+            dot += qh[e] * kj[e];
+        double mask = (j <= i) ? 1.0 : 0.0;     /* M': lower triangle = 1 (R5) */
+        a[j - 1] = softplus(scale * dot) * mask;
+        l1 += a[j - 1];
+    }
+    for (int j = 0; j < L; ++j)                  /* A_i <- A_i / |A_i|_1 */
+        a[j] /= l1;
+
+    /* Stage 2 (Key design 2): A <- ReLU^p(A * N - O), then L1 again */
+    const double o = (i <= 3) ? 0.0 : 1.0;       /* O: first 3 rows zero (R7) */
+    double m = -INFINITY;
+    for (int j = 0; j < L; ++j) {
+        a[j] = a[j] * (double)i - o;             /* A (.) N - O */
+        if (a[j] > m)
+            m = a[j];
+    }
+    if (!(m > eps)) {                            /* degenerate row (R10) */
+        memset(out, 0, sizeof(double) * (size_t)d);
+        return;
+    }
+    double l1b = 0.0;
+    for (int j = 0; j < L; ++j) {
+        double r = a[j] > 0.0 ? a[j] : 0.0;      /* ReLU */
+        a[j] = ipow(r, p);                       /* ^p */
+        l1b += a[j];
+    }
+    for (int j = 0; j < L; ++j)                  /* A_i <- A_i / |A_i|_1 */
+        a[j] /= l1b;
+
+    /* Attention output (Key design 3): out_i = sum_j A_ij v_j */
+    for (int e = 0; e < d; ++e)
+        out[e] = 0.0;
+    for (int j = 0; j < L; ++j) {
+        const double* vj = v + (size_t)j * d;
+        for (int e = 0; e < d; ++e)
+            out[e] += a[j] * vj[e];
+    }
+}
+
+static int bad_args(const void* q, const void* k, const void* v, const void* out,
+                    int L, int d, int p, double eps)
+{
+    return !q || !k || !v || !out || L < 1 || d < 1 || p < 1 || !(eps >= 0.0);
+}
+
+int lssar_ref_threads(int nthreads)
+{
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/* Normalise the rows of one head's Q and K (Key design 1). */
+static void normalise_head(const double* q, const double* k, double* qh,
+                           double* kh, int L, int d)
+{
+    for (int r = 0; r < L; ++r) {
+        l2_normalise(q + (size_t)r * d, qh + (size_t)r * d, d);
+        l2_normalise(k + (size_t)r * d, kh + (size_t)r * d, d);
+    }
+}
+
+int lssar_ref_head_rows_f64(const double* q, const double* k, const double* v,
+                            int L, int d, int p, double eps,
+                            const int* rows, int nrows, double* out,
+                            int nthreads)
+{
+    if (bad_args(q, k, v, out, L, d, p, eps) || nrows < 0 || (nrows && !rows))
+        return -1;
+    for (int r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= L)
+            return -1;
+    double* qh = malloc(sizeof(double) * (size_t)L * d);
+    double* kh = malloc(sizeof(double) * (size_t)L * d);
+    if (!qh || !kh) {
+        free(qh);
+        free(kh);
+        return -2;
+    }
+    normalise_head(q, k, qh, kh, L, d);
+    int fail = 0;
+#pragma omp parallel num_threads(lssar_ref_threads(nthreads))
+    {
+        double* a = malloc(sizeof(double) * (size_t)L);
+        if (!a) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int r = 0; r < nrows; ++r)
+                lssar_row(qh + (size_t)rows[r] * d, kh, v, L, d, p, eps, rows[r],
+                          a, out + (size_t)r * d);
+        }
+        free(a);
+    }
+    free(qh);
+    free(kh);
+    return fail ? -2 : 0;
+}
+
+int lssar_ref_fwd_f64(const double* q, const double* k, const double* v,
+                      double* out, int B, int H, int L, int d, int p,
+                      double eps, int nthreads)
+{
+    if (bad_args(q, k, v, out, L, d, p, eps) || B < 1 || H < 1)
+        return -1;
+    const size_t head = (size_t)L * d;
+    const long nheads = (long)B * H;
+    double* qh = malloc(sizeof(double) * head * (size_t)nheads);
+    double* kh = malloc(sizeof(double) * head * (size_t)nheads);
+    if (!qh || !kh) {
+        free(qh);
+        free(kh);
+        return -2;
+    }
+    const int nt = lssar_ref_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (long bh = 0; bh < nheads; ++bh)
+        normalise_head(q + bh * head, k + bh * head, qh + bh * head,
+                       kh + bh * head, L, d);
+    int fail = 0;
+#pragma omp parallel num_threads(nt)
+    {
+        double* a = malloc(sizeof(double) * (size_t)L);
+        if (!a) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+            /* rows are independent; row i costs O(L d), schedule dynamically */
+#pragma omp for schedule(dynamic, 4)
+            for (long t = 0; t < nheads * L; ++t) {
+                long bh = t / L;
+                int row = (int)(t % L);
+                lssar_row(qh + bh * head + (size_t)row * d, kh + bh * head,
+                          v + bh * head, L, d, p, eps, row, a,
+                          out + bh * head + (size_t)row * d);
+            }
+        }
+        free(a);
+    }
+    free(qh);
+    free(kh);
+    return fail ? -2 : 0;
+}

@@ -1,0 +1,46 @@
+/*
+ * lssar_ref.h -- fp64 CPU oracle for LSSAR causal attention (forward).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the bench may load this library.  It shares no code,
+ * header, table or helper with the HIP library, and the HIP library never
+ * calls it.
+ *
+ * What it computes is the definition in the paper note "Softplus Attention
+ * with Re-weighting Boosts Length Extrapolation in Large Language Models"
+ * (papernotes.org), section Method details: Overall framework, Key design 1
+ * (LSSA) and Key design 2 (re-weighting), written out as a plain loop in
+ * fp64.  Readings where the note is silent are listed in lssar_ref.c.
+ *
+ * Layout: every tensor is a contiguous row-major [B, H, L, d] array of
+ * doubles (the exact values of the dtype-rounded inputs).  Rows are queries
+ * (1-based position i = row index + 1); the output has the same layout.
+ */
+#ifndef LSSAR_REF_H
+#define LSSAR_REF_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Full forward over all B*H heads and L rows.  nthreads <= 0 uses the
+ * OpenMP default.  Returns 0, or -1 on invalid arguments (null pointer,
+ * B/H/L/d < 1, p < 1, eps < 0 or NaN), or -2 if scratch allocation fails. */
+int lssar_ref_fwd_f64(const double* q, const double* k, const double* v,
+                      double* out, int B, int H, int L, int d, int p,
+                      double eps, int nthreads);
+
+/* A chosen set of rows of ONE head: q, k, v are that head's [L, d] arrays,
+ * rows[r] is a 0-based query row, out is [nrows, d].  Same return codes. */
+int lssar_ref_head_rows_f64(const double* q, const double* k, const double* v,
+                            int L, int d, int p, double eps,
+                            const int* rows, int nrows, double* out,
+                            int nthreads);
+
+/* Number of OpenMP threads a call with this nthreads argument would use. */
+int lssar_ref_threads(int nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

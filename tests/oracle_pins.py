@@ -1,0 +1,371 @@
+"""Pins for the fp64 oracle: facts the pages and mathematics fix on their own.
+
+Every pin takes a loaded oracle library (``oracle.load()`` or a deliberately
+broken copy built by ``test_oracle_mutants.py``) and raises AssertionError
+when the oracle disagrees.  Only ``brute_force_matrix_form`` restates the
+definition; every other pin is a closed form of a constructed special case,
+an invariant or a limit, so it does not share the oracle's structure.
+
+Source of the definition: paper note "Softplus Attention with Re-weighting
+Boosts Length Extrapolation in Large Language Models", Method details,
+Key design 1 (LSSA), Key design 2 (re-weighting), Key design 3 (mask).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import mpmath as mp
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _fwd(lib, q, k, v, p, eps=oracle.DEFAULT_EPS):
+    return oracle.lssar_fwd(q, k, v, p, eps, nthreads=2, lib=lib)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------
+# Brute force: the literal matrix form at 50 digits, tiny L
+# --------------------------------------------------------------------------
+
+def brute_lssar(Q, K, V, p, eps=oracle.DEFAULT_EPS, dps=50):
+    """Matrix form with explicit N, M' and O (Key designs 1-2) in mpmath."""
+    with mp.workdps(dps):
+        L, d = Q.shape
+        Qm = mp.matrix(Q.tolist())
+        Km = mp.matrix(K.tolist())
+
+        def rownorm(M):
+            R = mp.matrix(M.rows, M.cols)
+            for r in range(M.rows):
+                n = mp.sqrt(mp.fsum(M[r, c] ** 2 for c in range(M.cols)))
+                n = max(n, mp.mpf("1e-12"))
+                for c in range(M.cols):
+                    R[r, c] = M[r, c] / n
+            return R
+
+        Qn, Kn = rownorm(Qm), rownorm(Km)
+        S = Qn * Kn.T
+        N = mp.matrix(L, L)
+        Mp = mp.matrix(L, L)
+        O = mp.matrix(L, L)
+        for i in range(L):
+            for j in range(L):
+                N[i, j] = i + 1
+                Mp[i, j] = 1 if j <= i else 0
+                O[i, j] = 0 if i < 3 else 1
+        A = mp.matrix(L, L)
+        for i in range(L):
+            for j in range(L):
+                A[i, j] = mp.log(1 + mp.exp(mp.log(d) * mp.log(N[i, j]) * S[i, j])) * Mp[i, j]
+        for i in range(L):
+            s = mp.fsum(abs(A[i, j]) for j in range(L))
+            for j in range(L):
+                A[i, j] = A[i, j] / s
+        X = mp.matrix(L, L)
+        for i in range(L):
+            for j in range(L):
+                X[i, j] = A[i, j] * N[i, j] - O[i, j]
+        W = mp.matrix(L, L)
+        for i in range(L):
+            m = max(X[i, j] for j in range(L))
+            if m <= eps:
+                continue            # degenerate row -> zero output
+            for j in range(L):
+                W[i, j] = max(X[i, j], 0) ** p
+            s = mp.fsum(abs(W[i, j]) for j in range(L))
+            for j in range(L):
+                W[i, j] = W[i, j] / s
+        Vm = mp.matrix(V.tolist())
+        out = W * Vm
+        return np.array([[float(out[i, c]) for c in range(d)] for i in range(L)])
+
+
+def brute_force_matrix_form(lib):
+    for seed, (L, d, p) in enumerate([(1, 4, 3), (5, 4, 1), (7, 8, 2), (9, 6, 3),
+                                      (12, 8, 15), (10, 3, 5)]):
+        r = _rng(100 + seed)
+        Q, K, V = (r.standard_normal((L, d)) for _ in range(3))
+        got = _fwd(lib, Q, K, V, p)
+        want = brute_lssar(Q, K, V, p)
+        err = np.max(np.abs(got - want))
+        assert err < 1e-12, f"brute force L={L} d={d} p={p}: max err {err:.3e}"
+
+
+# --------------------------------------------------------------------------
+# Closed forms of constructed special cases
+# --------------------------------------------------------------------------
+
+def _ortho(d, seed):
+    r = _rng(seed)
+    Qm, R = np.linalg.qr(r.standard_normal((d, d)))
+    return Qm.T * np.sign(np.diag(R))[:, None]      # rows orthonormal
+
+
+def row1_is_v1(lib):
+    """Row 1: log 1 = 0 makes its single stage-1 entry 1; o_1 = 0 keeps it."""
+    for seed, (L, d, p) in enumerate([(6, 8, 3), (33, 16, 15), (3, 64, 1)]):
+        r = _rng(200 + seed)
+        Q, K, V = (r.standard_normal((L, d)) for _ in range(3))
+        out = _fwd(lib, Q, K, V, p)
+        assert np.array_equal(out[0], V[0]) or np.max(np.abs(out[0] - V[0])) < 1e-15, \
+            "row 1 must reproduce v_1"
+
+
+def _closed_form_row(i, d, cos, p, V):
+    """Expected output of row i (1-based) whose cosines to keys 1..i are
+    ``cos`` (orthonormal keys): sp_j = softplus(ln d ln i c_j); A = sp/sum;
+    w_j = ReLU(i A_j - o_i)^p; out = sum w v / sum w (0 if max <= eps)."""
+    with mp.workdps(40):
+        lam = mp.log(d) * mp.log(i)
+        sp = [mp.log(1 + mp.exp(lam * mp.mpf(c))) for c in cos]
+        s1 = mp.fsum(sp)
+        o = 0 if i <= 3 else 1
+        x = [i * s / s1 - o for s in sp]
+        if max(x) <= oracle.DEFAULT_EPS:
+            return np.zeros(V.shape[1])
+        w = [max(t, 0) ** p for t in x]
+        den = mp.fsum(w)
+        return np.array([float(mp.fsum(w[j] * V[j, c] for j in range(len(w))) / den)
+                         for c in range(V.shape[1])])
+
+
+def _build_rows(L, d, cos_rows, seed):
+    """Keys: orthonormal directions with random positive lengths.  Query i:
+    unit vector with the given cosines to keys 1..len(c), completed with a
+    direction orthogonal to every key, then a random positive length."""
+    assert L < d
+    E = _ortho(d, seed)
+    r = _rng(seed + 1)
+    K = E[:L] * r.uniform(0.25, 4.0, size=(L, 1))
+    Q = np.zeros((L, d))
+    for i in range(L):
+        c = np.zeros(L)
+        c[:len(cos_rows[i])] = cos_rows[i]
+        rest = 1.0 - float(np.dot(c, c))
+        assert rest >= -1e-15
+        qv = c @ E[:L] + math.sqrt(max(rest, 0.0)) * E[L]
+        Q[i] = qv * r.uniform(0.25, 4.0)
+    V = r.standard_normal((L, d))
+    return Q, K, V
+
+
+def closed_form_rows(lib):
+    """Rows 2..L with hand-chosen cosines, including rows 2-3 (o = 0), row 4
+    (first row with o = 1) and rows where some entries fall below the mean."""
+    L, d = 12, 16
+    cos_rows = [[0.3], [1.0, 0.0], [0.2, 0.9, -0.1], [0.6, 0.5, 0.1, -0.3],
+                [0.0, 0.7, 0.7, 0.0, 0.1], [0.5] * 3 + [0.1] * 3,
+                [0.9, -0.4, 0.1], [0.2, 0.3, 0.4, 0.5, 0.6],
+                [-0.5, 0.8], [0.1] * 10, [0.95], [0.4, 0.4, 0.4, 0.41]]
+    for p in (1, 3, 15):
+        Q, K, V = _build_rows(L, d, cos_rows, seed=300 + p)
+        out = _fwd(lib, Q, K, V, p)
+        for i in range(2, L + 1):
+            cos = list(cos_rows[i - 1]) + [0.0] * (i - len(cos_rows[i - 1]))
+            cos = cos[:i]
+            want = _closed_form_row(i, d, cos, p, V[:i])
+            err = np.max(np.abs(out[i - 1] - want))
+            assert err < 1e-11, f"closed form row {i} p={p}: err {err:.3e}"
+
+
+def golden_row2_value(lib):
+    """Hand-derived value from the fixture (d=64, p=3, q_2 parallel to k_1,
+    orthogonal to k_2): w_1 = sp(ln64 ln2)^3 / (sp(ln64 ln2)^3 + (ln 2)^3)."""
+    with open(os.path.join(GOLDEN, "closed_forms.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        d, p, w1 = case["d"], case["p"], case["w1"]
+        E = _ortho(d, 7)
+        K = np.stack([E[0] * 2.5, E[1] * 0.75])
+        Q = np.stack([E[3] * 1.5, E[0] * 3.0])
+        V = np.stack([np.full(d, 1.0), np.zeros(d)])      # out_2 = w_1 * 1 + w_2 * 0
+        out = _fwd(lib, Q, K, V, p)
+        assert abs(out[1, 0] - w1) < 5e-7, f"row-2 golden d={d} p={p}: {out[1, 0]} vs {w1}"
+
+
+def onehot_orthonormal(lib):
+    """Rows i >= 4, orthonormal keys, q_i along key m(i): out_i = v_m(i)
+    exactly (every other entry has softplus(0) = ln 2, below the row mean)."""
+    for seed, (L, d, p) in enumerate([(16, 32, 3), (31, 32, 15), (40, 64, 1), (20, 64, 2)]):
+        r = _rng(400 + seed)
+        E = _ortho(d, 410 + seed)
+        perm = r.permutation(d)[:L]
+        K = E[perm] * r.uniform(0.5, 3.0, size=(L, 1))
+        mi = [int(r.integers(0, i + 1)) for i in range(L)]
+        Q = np.stack([K[mi[i]] * r.uniform(0.1, 5.0) for i in range(L)])
+        V = r.standard_normal((L, d))
+        out = _fwd(lib, Q, K, V, p)
+        for i in range(3, L):
+            err = np.max(np.abs(out[i] - V[mi[i]]))
+            assert err < 1e-12, f"one-hot row {i + 1} p={p}: err {err:.3e}"
+
+
+def two_way_tie(lib):
+    """q_i = (e_a + e_b)/sqrt2 over orthonormal keys: out_i = (v_a + v_b)/2."""
+    L, d = 24, 32
+    r = _rng(500)
+    E = _ortho(d, 501)
+    K = E[:L] * r.uniform(0.5, 2.0, size=(L, 1))
+    V = r.standard_normal((L, d))
+    Q = np.zeros((L, d))
+    pairs = {}
+    for i in range(L):
+        a, b = sorted(r.choice(i + 1, size=2, replace=False)) if i >= 1 else (0, 0)
+        pairs[i] = (a, b)
+        Q[i] = (E[a] + E[b]) * r.uniform(0.5, 2.0)
+    for p in (1, 3, 15):
+        out = _fwd(lib, Q, K, V, p)
+        for i in range(3, L):
+            a, b = pairs[i]
+            err = np.max(np.abs(out[i] - 0.5 * (V[a] + V[b])))
+            assert err < 1e-12, f"tie row {i + 1} p={p}: err {err:.3e}"
+
+
+def degenerate_rows(lib):
+    """All scores of a row equal: rows >= 4 are degenerate (output 0);
+    rows 1-3 have o = 0 and give the mean of v_1..v_i."""
+    L, d = 10, 8
+    r = _rng(600)
+    V = r.standard_normal((L, d))
+    # (a) zero query rows
+    K = r.standard_normal((L, d))
+    Q = np.zeros((L, d))
+    # (b) every key identical, queries random
+    K2 = np.tile(r.standard_normal((1, d)), (L, 1))
+    Q2 = r.standard_normal((L, d))
+    for (QQ, KK) in ((Q, K), (Q2, K2)):
+        for p in (1, 3, 15):
+            out = _fwd(lib, QQ, KK, V, p)
+            for i in range(L):
+                want = V[:i + 1].mean(axis=0) if i < 3 else np.zeros(d)
+                err = np.max(np.abs(out[i] - want))
+                assert err < 1e-12, f"degenerate row {i + 1} p={p}: err {err:.3e}"
+
+
+# --------------------------------------------------------------------------
+# Invariants
+# --------------------------------------------------------------------------
+
+def v_identity_probe(lib):
+    """V = I turns the output into the weight matrix: non-negative, exactly 0
+    above the diagonal (M' multiplies), rows sum to 1."""
+    for seed, (L, d, p) in enumerate([(16, 16, 3), (24, 32, 15), (9, 9, 2), (12, 12, 1)]):
+        r = _rng(700 + seed)
+        Q, K = r.standard_normal((L, d)), r.standard_normal((L, d))
+        V = np.eye(L, d)
+        W = _fwd(lib, Q, K, V, p)[:, :L]
+        assert np.all(W >= 0.0), "weights must be non-negative"
+        assert np.all(W[np.triu_indices(L, 1)] == 0.0), "masked weights must be exactly 0"
+        err = np.max(np.abs(W.sum(axis=1) - 1.0))
+        assert err < 1e-13, f"row sums: err {err:.3e}"
+
+
+def v_ones(lib):
+    r = _rng(800)
+    L, d = 40, 16
+    Q, K = r.standard_normal((L, d)), r.standard_normal((L, d))
+    for p in (1, 3, 15):
+        out = _fwd(lib, Q, K, np.ones((L, d)), p)
+        err = np.max(np.abs(out - 1.0))
+        assert err < 1e-13, f"V = ones: err {err:.3e}"
+
+
+def scale_invariance(lib):
+    """Rows of Q and K are L2-normalised, so rescaling them changes nothing."""
+    r = _rng(900)
+    L, d = 30, 16
+    Q, K, V = (r.standard_normal((L, d)) for _ in range(3))
+    for p in (3, 15):
+        base = _fwd(lib, Q, K, V, p)
+        s2 = _fwd(lib, Q * 8.0, K * 0.25, V, p)
+        assert np.max(np.abs(s2 - base)) < 1e-13, "power-of-two rescale changed output"
+        sq = r.uniform(0.1, 10.0, size=(L, 1))
+        sk = r.uniform(0.1, 10.0, size=(L, 1))
+        s3 = _fwd(lib, Q * sq, K * sk, V, p)
+        err = np.max(np.abs(s3 - base))
+        assert err < 1e-11, f"row rescale changed output by {err:.3e}"
+
+
+def linearity_in_v(lib):
+    r = _rng(1000)
+    L, d = 25, 8
+    Q, K, V1, V2 = (r.standard_normal((L, d)) for _ in range(4))
+    for p in (2, 15):
+        a = _fwd(lib, Q, K, V1, p)
+        b = _fwd(lib, Q, K, V2, p)
+        c = _fwd(lib, Q, K, 2.0 * V1 - 3.0 * V2, p)
+        assert np.max(np.abs(c - (2.0 * a - 3.0 * b))) < 1e-12, "output not linear in V"
+
+
+def causality(lib):
+    """out_i depends on keys/values 1..i only (bitwise)."""
+    r = _rng(1100)
+    L, d = 20, 8
+    Q, K, V = (r.standard_normal((L, d)) for _ in range(3))
+    for p in (1, 3, 15):
+        base = _fwd(lib, Q, K, V, p)
+        for cut in (0, 3, 10, 18):
+            K2, V2 = K.copy(), V.copy()
+            K2[cut + 1:] = r.standard_normal(K2[cut + 1:].shape)
+            V2[cut + 1:] = r.standard_normal(V2[cut + 1:].shape) * 100.0
+            o2 = _fwd(lib, Q, K2, V2, p)
+            assert np.array_equal(o2[:cut + 1], base[:cut + 1]), f"row <= {cut + 1} saw the future"
+
+
+def permutation_invariance(lib):
+    """Permuting (k_j, v_j) pairs among j <= i leaves out_i unchanged."""
+    r = _rng(1200)
+    L, d = 18, 8
+    Q, K, V = (r.standard_normal((L, d)) for _ in range(3))
+    i = L - 1
+    perm = r.permutation(L)
+    for p in (3, 15):
+        a = _fwd(lib, Q, K, V, p)[i]
+        b = _fwd(lib, Q, K[perm], V[perm], p)[i]
+        assert np.max(np.abs(a - b)) < 1e-12, "last row depends on key order"
+
+
+def hard_argmax_limit(lib):
+    """Key design 2: as p grows the weights approach the one-hot argmax.
+    For the normalised weights w(p) with ratios r_k = x_k/x_max < 1 of the
+    positive entries: |w(p) - e_max|_1 = 2 sum_k r_k^p / (1 + sum_k r_k^p)
+    exactly, which is at most 2 (n - 1) r_2^p; the max weight never drops.
+    The ratios come from the p = 1 weights, which are proportional to x."""
+    r = _rng(1300)
+    L, d = 14, 14
+    Q, K = r.standard_normal((L, d)), r.standard_normal((L, d))
+    V = np.eye(L, d)
+    W1 = _fwd(lib, Q, K, V, 1)[:, :L]
+    prev = np.zeros(L)
+    for p in range(1, 65):
+        W = _fwd(lib, Q, K, V, p)[:, :L]
+        for i in range(3, L):
+            w = W[i, :i + 1]
+            wmax = w.max()
+            assert wmax >= prev[i] - 1e-14, f"row {i + 1}: max weight fell at p={p}"
+            prev[i] = wmax
+            m = int(np.argmax(W1[i, :i + 1]))
+            ratios = np.delete(W1[i, :i + 1], m) / W1[i, m]
+            ratios = ratios[ratios > 0]
+            exact = 2.0 * np.sum(ratios ** p) / (1.0 + np.sum(ratios ** p))
+            dist = np.abs(w - np.eye(i + 1)[m]).sum()
+            assert abs(dist - exact) < 1e-9, f"row {i + 1} p={p}: {dist} vs {exact}"
+            if len(ratios):
+                assert dist <= 2.0 * len(ratios) * ratios.max() ** p + 1e-12
+    # at p = 64 every row's leader holds almost all the weight
+    assert np.median(prev[3:]) > 0.99
+
+
+PINS = [brute_force_matrix_form, row1_is_v1, closed_form_rows, golden_row2_value,
+        onehot_orthonormal, two_way_tie, degenerate_rows, v_identity_probe, v_ones,
+        scale_invariance, linearity_in_v, causality, permutation_invariance,
+        hard_argmax_limit]

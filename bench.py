@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Throughput of the LSSAR causal attention forward on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+the key-row L2-norm prep kernel, then the fused two-pass attention kernel
+(what lssar_attn_fwd_ws launches), with inputs already resident in HBM.
+
+Metric: algorithmic TFLOP/s, counting 4*d flops per unmasked (query, key)
+pair (QK^T once plus P.V once; the pass-2 score recompute and all
+elementwise work are not counted), i.e. 4*d*B*H*L(L+1)/2 per step.
+
+Default workload: 8x length extrapolation, B=1 H=12 L=8192 d=64 bf16 p=15
+with 16 planted keys per head (cosine 0.9 to one query), seed 0.
+
+Prints ONE JSON line.  Extra objects: "roofline" for the attention kernel
+(its mean duration from HIP events recorded on the launch stream inside the
+timed region), "cpu_baseline" (the fp64 oracle on a bounded row sample, on
+the host's cores), and "sweep" (the same path at L = 1K..16K, H=12, d=64,
+p=15, B = 16384/L, on device-generated N(0,1) inputs).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LSSAR causal attn fwd TFLOP/s (% bf16 MFMA peak) at L=1K..16K, 1 GPU"
+# MI355X published dense peaks (256 CUs, 2.4 GHz)
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+# HBM traffic of the attention kernel measured with rocprofv3 --pmc
+# (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration factor),
+# valid only for the kernel source whose hash is recorded with it.
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_record.json")
+KERNEL_SRC = os.path.join(ROOT, "softmax_free_attention_amd", "csrc", "lssar_device.hpp")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or ent.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def upload(inp):
+    import numpy as np
+    import torch
+    import lssar_inputs as gen
+    out = []
+    for a in (inp.q, inp.k, inp.v):
+        if inp.wl.dtype == "f32":
+            out.append(torch.from_numpy(np.ascontiguousarray(a)).cuda())
+        else:
+            out.append(torch.from_numpy(gen.bf16_bits(a).view(np.int16)).cuda().view(torch.bfloat16))
+    return out
+
+
+def time_path(q, k, v, p, steps, warmup, eps=1e-4):
+    """Run warmup + timed steps; returns (wall_s, fwd_ms_mean, prep_ms_mean)."""
+    import torch
+    import softmax_free_attention_amd as sfa
+    B, H, L, d = q.shape
+    fk = torch.empty(B * H * L, dtype=torch.float32, device=q.device)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        sfa.lssar_key_inv_norms(k, fk, stream=stream)
+        sfa.lssar_attn_fwd_prenormed(q, k, v, fk, out, p=p, eps=eps, stream=stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        sfa.lssar_key_inv_norms(k, fk, stream=stream)
+        ev[s][1].record(stream)
+        sfa.lssar_attn_fwd_prenormed(q, k, v, fk, out, p=p, eps=eps, stream=stream)
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    prep = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    return wall, fwd, prep
+
+
+def cpu_baseline(inp, seconds: float):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload's
+    rows (strided over all heads and positions), on all host cores."""
+    import numpy as np
+    import oracle
+    wl = inp.wl
+    total_rows = wl.B * wl.H * wl.L
+    nthreads = oracle.threads(0)
+
+    def run(rows_per_head, heads):
+        flops = 0
+        t0 = time.perf_counter()
+        for (b, h) in heads:
+            stride = max(1, wl.L // rows_per_head)
+            rows = np.arange(stride // 2, wl.L, stride)[:rows_per_head]
+            oracle.lssar_rows(inp.q[b, h], inp.k[b, h], inp.v[b, h], rows, wl.p, nthreads=nthreads)
+            flops += int(4 * wl.d * (rows + 1).sum())
+        return time.perf_counter() - t0, flops
+
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    cal_t, _ = run(max(1, 4 * nthreads), heads[:1])
+    per_row = cal_t / max(1, 4 * nthreads)
+    n = int(seconds / per_row / len(heads))
+    n = max(nthreads, min(wl.L, n))
+    dt, flops = run(n, heads)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{n * len(heads)} of {total_rows} query rows ({n} evenly strided rows in "
+                      f"each of {len(heads)} heads), fp64 literal oracle, {dt:.1f} s",
+            "seconds": dt}
+
+
+def sweep(steps, warmup):
+    import torch
+    res = {}
+    g = torch.Generator(device="cuda")
+    for L in (1024, 2048, 4096, 8192, 16384):
+        B = 16384 // L
+        g.manual_seed(L)
+        shape = (B, 12, L, 64)
+        q, k, v = (torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+                   .to(torch.bfloat16) for _ in range(3))
+        wall, fwd, prep = time_path(q, k, v, 15, steps, warmup)
+        flops = 4 * 64 * B * 12 * L * (L + 1) // 2
+        res[str(L)] = {"B": B, "tflops": round(flops * steps / wall / 1e12, 2),
+                       "kernel_tflops": round(flops / (fwd * 1e-3) / 1e12, 2),
+                       "pct_bf16_peak": round(100 * flops * steps / wall / 1e12 / PEAK_TFLOPS["bf16"], 2)}
+        del q, k, v
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="x8_planted")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the LSSAR forward is sharded over (batch, head) "
+              f"units with no communication, and this build runs and reports the single-GPU "
+              f"share (got --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lssar_inputs as gen
+    import softmax_free_attention_amd as sfa
+    sfa.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    wl = gen.WORKLOADS[args.workload]
+    log(f"bench: generating {wl.name} inputs")
+    inp = gen.make_inputs(wl)
+    q, k, v = upload(inp)
+    log(f"bench: timing {args.steps} steps after {args.warmup} warmup")
+    wall, fwd_ms, prep_ms = time_path(q, k, v, wl.p, args.steps, args.warmup)
+    flops = wl.flops
+    value = flops * args.steps / wall / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    achieved = flops / (fwd_ms * 1e-3) / 1e12
+    traffic = recorded_traffic(wl.name)
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "L": wl.L, "d": wl.d, "p": wl.p,
+                   "structure": wl.structure, "seed": wl.seed, "eps": 1e-4},
+        "pct_of_bf16_mfma_peak": round(100 * value / PEAK_TFLOPS["bf16"], 3),
+        "tokens_per_s": round(wl.B * wl.L * args.steps / wall, 1),
+        "kernel_ms": {"lssar_fwd": round(fwd_ms, 5), "lssar_prep": round(prep_ms, 5)},
+        "roofline": {"bound": "mfma", "kernel": "lssar_fwd_bf16_kernel" if wl.dtype == "bf16"
+                     else "lssar_fwd_f32_kernel",
+                     "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 5), "traffic": traffic},
+    }
+    if not args.no_sweep:
+        log("bench: L sweep")
+        line["sweep"] = sweep(steps=10, warmup=3)
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        cb = cpu_baseline(inp, args.cpu_seconds)
+        cb.pop("seconds", None)
+        line["cpu_baseline"] = cb
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

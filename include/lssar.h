@@ -1,0 +1,112 @@
+/*
+ * lssar.h -- C ABI of the MI355X (gfx950) LSSAR causal attention forward.
+ *
+ * LSSAR = Length Scaled Softplus Attention with Re-weighting, defined in the
+ * paper note "Softplus Attention with Re-weighting Boosts Length
+ * Extrapolation in Large Language Models" (papernotes.org, ICML 2026),
+ * section Method details:
+ *   Key design 1 (LSSA): L2-normalise every row of Q and K; for j <= i take
+ *     A_ij = Softplus(ln d * ln i * q^_i . k^_j); entries above the diagonal
+ *     are multiplied by 0 (the mask multiplies because Softplus >= 0, Key
+ *     design 3); divide each row by its L1 norm.
+ *   Key design 2 (re-weighting): A_ij <- ReLU(i * A_ij - o_i)^p with o_i = 0
+ *     for rows 1-3 and 1 otherwise; divide each row by its L1 norm again.
+ *   Key design 3: the weights replace Softmax, so out = A V.
+ * Rows are 1-based positions i; d is the head dimension; log is natural.
+ *
+ * Degenerate rows.  When m_i = max_j (i A_ij - o_i) <= eps every re-weighted
+ * entry is (numerically) zero and the second L1 normalisation has no value;
+ * such a row's output is all zeros.  The page "Softmax alternatives and the
+ * attention-sink problem" (Practical advice, implementation notes) asks that
+ * this denominator never be zero; this is its scale-invariant form.
+ *
+ * Conventions for every entry point:
+ *  - q, k, v, out: DEVICE pointers to contiguous row-major [B, H, L, d]
+ *    tensors of one dtype (fp32 or bf16), each 16-byte aligned.  out must
+ *    not overlap q, k or v.  The caller owns all buffers and the stream; the
+ *    library keeps no pointer after a call returns and holds no mutable
+ *    global state (calls on different streams may run concurrently).
+ *  - stream: a hipStream_t (NULL = the legacy default stream).  Calls are
+ *    asynchronous with respect to the host and ordered on the stream.
+ *  - Square causal self-attention: query i sees keys 1..i; one K/V head per
+ *    Q head; q and k are the vectors after any positional rotation.
+ *  - Arithmetic: scores contract the raw inputs with fp32 accumulation (bf16
+ *    MFMA for bf16, fp32 MFMA for fp32); norms, Softplus, row sums and the
+ *    re-weighting run in fp32; bf16 weights feed the P.V contraction for
+ *    bf16 inputs; the output is rounded to the input dtype (nearest-even).
+ *  - Every argument is validated on the host before any HIP call; invalid
+ *    input returns an error code and launches nothing.
+ */
+#ifndef LSSAR_H
+#define LSSAR_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+typedef enum { LSSAR_F32 = 0, LSSAR_BF16 = 1 } lssar_dtype;
+
+/* Status codes. */
+enum {
+    LSSAR_OK = 0,
+    LSSAR_EINVAL = -1,       /* null/misaligned/overlapping pointer, B,H,L < 1,
+                                p < 1, eps < 0 or not finite, sizes overflow */
+    LSSAR_EUNSUPPORTED = -2, /* d not in {64, 128}, unknown dtype, p > 1024,
+                                L > 2^24 */
+    LSSAR_EWORKSPACE = -3,   /* workspace null, misaligned or too small */
+    LSSAR_EHIP = -4          /* a HIP call or kernel launch failed; see
+                                lssar_last_hip_error() */
+};
+
+/* Workspace for lssar_attn_fwd_ws, in bytes: one fp32 inverse key norm per
+ * key row (4*B*H*L), rounded up to 256.  Returns 0 for invalid sizes. */
+size_t lssar_workspace_bytes(int B, int H, int L, int d, int dtype);
+
+/* LSSAR causal attention forward (Key designs 1-3 above) with a
+ * caller-provided device workspace of at least lssar_workspace_bytes()
+ * bytes, 256-byte aligned.  Allocates nothing.  Launches two kernels on
+ * `stream`: the key-row L2-norm prep kernel, then the fused two-pass
+ * attention kernel.  p: integer exponent >= 1 (the note reports 3 and 15).
+ * eps: degenerate-row threshold >= 0 (1e-4 is the reference choice). */
+int lssar_attn_fwd_ws(const void* q, const void* k, const void* v, void* out,
+                      int B, int H, int L, int d, int p, float eps, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* As lssar_attn_fwd_ws, but takes its workspace stream-ordered from the
+ * device's default memory pool (hipMallocAsync / hipFreeAsync on `stream`). */
+int lssar_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                   int B, int H, int L, int d, int p, float eps, int dtype,
+                   void* stream);
+
+/* Stage 1 alone: the key-row L2-norm prep kernel (Key design 1's
+ * K_j <- K_j / |K_j|_2, kept as a factor).  Writes fk[bh*L + j] =
+ * 1 / max(|k_j|_2, 1e-12) in fp32 for every key row; fk is a device buffer of
+ * at least 4*B*H*L bytes, 16-byte aligned, not overlapping k.  Same status
+ * codes as lssar_attn_fwd_ws (a bad fk is LSSAR_EWORKSPACE). */
+int lssar_key_inv_norms(const void* k, float* fk, int B, int H, int L, int d,
+                        int dtype, void* stream);
+
+/* Stage 2 alone: the fused two-pass attention kernel, given the fk array
+ * that lssar_key_inv_norms wrote for these keys.  lssar_attn_fwd_ws is this
+ * call preceded by lssar_key_inv_norms on the same stream. */
+int lssar_attn_fwd_prenormed(const void* q, const void* k, const void* v,
+                             const float* fk, void* out, int B, int H, int L,
+                             int d, int p, float eps, int dtype, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* lssar_status_str(int status);
+
+/* The hipError_t of the last LSSAR_EHIP returned on this host thread
+ * (0 if none). */
+int lssar_last_hip_error(void);
+
+/* ABI version: 10000 * major + 100 * minor + patch. */
+int lssar_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSSAR_H */

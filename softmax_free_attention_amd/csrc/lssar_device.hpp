@@ -1,0 +1,746 @@
+// lssar_device.hpp -- gfx950 (CDNA4) kernels of the LSSAR causal attention
+// forward.
+//
+// Method: paper note "Softplus Attention with Re-weighting Boosts Length
+// Extrapolation in Large Language Models" (papernotes.org), Method details.
+//   Key design 1 (LSSA): rows of Q and K L2-normalised; for j <= i,
+//     A_ij = Softplus(ln d * ln i * q^_i . k^_j), masked entries multiplied
+//     by 0 (Key design 3); each row divided by its L1 norm S1_i.
+//   Key design 2 (re-weighting): A_ij <- ReLU(i A_ij - o_i)^p, o_i = 0 for
+//     rows 1-3 else 1; each row divided by its L1 norm again; out = A V.
+//
+// How the kernels compute it (exact rearrangements of the definition):
+//   * The norms are applied to the fp32 accumulator of the raw contraction:
+//       s_ij = (ln d ln i / |q_i|) * (1/|k_j|) * (q_i . k_j).
+//     The prep kernel stores 1/|k_j| per key row; the attention kernel
+//     computes the query factor while loading its query block.
+//   * Softplus runs in base 2: with t = s log2(e), log2(1 + 2^t) =
+//     Softplus(s)/ln 2.  Every later quantity is a ratio of Softplus values,
+//     so the constant factor cancels; log2(e) is folded into the query factor.
+//   * With tau_i = o_i S1_i / i and sp_max the row's largest Softplus value,
+//       i A_ij - o_i = (i / S1_i) (sp_ij - tau_i),
+//     so the re-weighted row, after its L1 normalisation, equals the row of
+//       y_ij = clamp((sp_ij - tau_i) / (sp_max,i - tau_i), 0, 1)^p
+//     divided by its sum.  y stays in [0, 1], so y^p cannot overflow at any p
+//     (the note lists ReLU^p overflow at large p as a limitation).
+//   * m_i = max_j (i A_ij - o_i) = i (sp_max,i - tau_i) / S1_i decides the
+//     degenerate rows (m_i <= eps: output 0).
+//   * S1_i must be complete before any weight is known, so each workgroup
+//     makes two passes over its keys: pass 1 accumulates S1 and the row max
+//     of the scores; pass 2 recomputes the scores, re-weights and
+//     accumulates P.V and the weight sum with MFMA, then divides.
+//
+// Tiling (bf16): a workgroup of 4 waves owns 128 consecutive query rows of
+// one (batch, head); each wave owns 32 rows.  Keys stream through LDS in
+// tiles of 64, double-buffered.  Scores are computed transposed,
+// S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: each lane then holds 4 keys of
+// ONE query row, so row sums stay per lane until one cross-lane reduction
+// per pass, and the lane's weights are already the B operand of
+// O^T = V^T P^T.  V tiles are transposed into LDS when staged.  The weight
+// sum rides the same MFMA as one extra 16-row block of ones under V^T.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace lssar {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;   // 4 waves of 64
+constexpr int kWaves = 4;
+constexpr int kMQ = 32;         // query rows per wave
+constexpr int kBQ = kWaves * kMQ;
+constexpr int kBK = 64;         // keys per tile
+
+// ---------------------------------------------------------------------------
+// Elementwise pieces shared by both dtypes
+// ---------------------------------------------------------------------------
+
+// log2(1 + 2^t) = Softplus(t ln 2) / ln 2 (Key design 1's Softplus, base 2).
+// |t| <= log2(e) ln(d) ln(L) stays far below the exp2 overflow at 128 for
+// every supported size.  For t < -24 the result rounds to 0, an absolute
+// error below 2^-24 on values that are summed with O(1) terms.
+__device__ __forceinline__ float softplus2(float t)
+{
+    return __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(t));
+}
+
+// y^P for y in [0, 1] by a fixed multiplication chain (P = 0: runtime p).
+template <int P, typename F>
+__device__ __forceinline__ F pow_chain(F y, int p)
+{
+    if constexpr (P == 1) {
+        return y;
+    } else if constexpr (P == 2) {
+        return y * y;
+    } else if constexpr (P == 3) {
+        return y * y * y;
+    } else if constexpr (P == 15) {
+        F y2 = y * y, y3 = y2 * y, y6 = y3 * y3, y12 = y6 * y6;
+        return y12 * y3;
+    } else {
+        F r = 1, b = y;
+        while (p) {
+            if (p & 1)
+                r *= b;
+            b *= b;
+            p >>= 1;
+        }
+        return r;
+    }
+}
+
+// clamp(sp * c - tc, 0, 1): the rescaled ReLU argument; the clamp folds
+// into the FMA's output modifier.
+__device__ __forceinline__ float reweight_arg(float sp, float c, float tc)
+{
+    return __builtin_amdgcn_fmed3f(__builtin_fmaf(sp, c, -tc), 0.0f, 1.0f);
+}
+
+// Row constants after pass 1 (Key design 2).  i: 1-based row; s1: sum of
+// base-2 Softplus values; tmax: the row's largest scaled score.
+struct RowConst {
+    float c;      // 1 / (sp_max - tau), or 0 for a degenerate row
+    float tc;     // tau * c
+    bool degen;
+};
+
+__device__ __forceinline__ RowConst row_constants(int i, float s1, float tmax, float eps)
+{
+    const float spmax = softplus2(tmax);
+    const float o = (i <= 3) ? 0.0f : 1.0f;
+    const float tau = o * s1 / (float)i;
+    const float gap = spmax - tau;
+    const float m = (float)i * gap / s1;       // max_j (i A_ij - o_i)
+    RowConst rc;
+    rc.degen = !(m > eps);
+    rc.c = rc.degen ? 0.0f : 1.0f / gap;
+    rc.tc = tau * rc.c;
+    return rc;
+}
+
+// fp64 versions for the fp32-input kernel.  With fp32 inputs the parity bar
+// is 1e-5 absolute, and the re-weighting multiplies the absolute error of a
+// Softplus value by about p / (sp_ij - tau_i): at p = 15 the fp32 spacing of
+// scores and Softplus values near 30-70 (2^-19..2^-17) alone would use the
+// whole budget.  The score -> Softplus -> re-weighting chain therefore runs
+// in fp64 there; the contractions' inputs stay exact fp32 values.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ double softplus2_f64(double t)
+{
+    // log2(1 + 2^t), kept accurate for large |t| of either sign
+    constexpr double kLog2e = 1.4426950408889634074;
+    return t > 0.0 ? t + log1p(exp2(-t)) * kLog2e : log1p(exp2(t)) * kLog2e;
+}
+
+struct RowConstD {
+    double c, tc;
+    bool degen;
+};
+
+__device__ __forceinline__ RowConstD row_constants_f64(int i, double s1, double tmax, float eps)
+{
+    const double spmax = softplus2_f64(tmax);
+    const double o = (i <= 3) ? 0.0 : 1.0;
+    const double tau = o * s1 / (double)i;
+    const double gap = spmax - tau;
+    const double m = (double)i * gap / s1;
+    RowConstD rc;
+    rc.degen = !(m > (double)eps);
+    rc.c = rc.degen ? 0.0 : 1.0 / gap;
+    rc.tc = tau * rc.c;
+    return rc;
+}
+
+// log2(e) ln(d) ln(i) / max(|q_i|, 1e-12) from the squared norm, in fp64
+__device__ __forceinline__ double query_factor(double lam_scale, int i, double ss)
+{
+    return lam_scale * log((double)i) / fmax(sqrt(ss), 1e-12);
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------
+// Prep kernel: fk[row] = 1 / max(|k_row|_2, 1e-12) for every key row
+// (Key design 1's K_j <- K_j / |K_j|_2, kept as a factor).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void lssar_prep_kernel(const T* __restrict__ K,
+                                                              float* __restrict__ fk,
+                                                              long nrows)
+{
+    constexpr int EPL = 16 / (int)sizeof(T);   // elements per 16-byte load
+    constexpr int LPR = D / EPL;               // lanes per row
+    constexpr int RPB = kThreads / LPR;        // rows per block
+    const long row = (long)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int sub = threadIdx.x % LPR;
+    // squared norm accumulated in fp64, so fk carries one rounding only
+    double ss = 0.0;
+    if (row < nrows) {
+        if constexpr (sizeof(T) == 2) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(K + row * D + sub * EPL);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const double a = bf16lo(w[e]), b = bf16hi(w[e]);
+                ss = fma(a, a, ss);
+                ss = fma(b, b, ss);
+            }
+        } else {
+            // loaded as a float vector: a bit-cast of an element of a u32x4
+            // was lowered as element 0 for every index by this compiler
+            const f32x4 x = *reinterpret_cast<const f32x4*>(K + row * D + sub * EPL);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ss = fma((double)x[e], (double)x[e], ss);
+        }
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1)
+        ss += __shfl_xor(ss, m, LPR);
+    if (row < nrows && sub == 0)
+        fk[row] = (float)(1.0 / fmax(sqrt(ss), 1e-12));
+}
+
+// ---------------------------------------------------------------------------
+// bf16 attention kernel
+// ---------------------------------------------------------------------------
+
+// Position of key `key` (0..63 of a tile) inside a V^T row in LDS.  With
+// key = 32 c + 16 h + 4 g + r the position is 32 c + 8 g + 4 h + r, so the 8
+// keys that lane group g feeds to one 32-key MFMA step (from two 16-key
+// score blocks) sit in one 16-byte LDS word.
+__device__ __forceinline__ int vt_pos(int key)
+{
+    return (key & 32) + (((key >> 2) & 3) << 3) + (((key >> 4) & 1) << 2) + (key & 3);
+}
+
+template <int D, int P>
+__global__ __launch_bounds__(kThreads, 2) void lssar_fwd_bf16_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+    const __bf16* __restrict__ V, __bf16* __restrict__ O,
+    const float* __restrict__ FK, int BH, int L, int nqb, double lam_scale,
+    float eps, int p_rt)
+{
+    static_assert(D == 64 || D == 128, "head dim");
+    constexpr int DC = D / 32;                 // MFMA k-steps over d
+    constexpr int DS = D / 16;                 // 16-row blocks of O^T
+    constexpr int KS = D + 8;                  // K tile row stride (elements)
+    constexpr int VS = kBK + 8;                // V^T tile row stride
+    constexpr int KCH = kBK * D / 8 / kThreads;  // 16-byte K chunks per thread
+    constexpr int VCH = D / 64;                // V column groups per thread
+
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][kBK * KS];
+    __shared__ __attribute__((aligned(16))) __bf16 Vt[2][D * VS];
+    __shared__ __attribute__((aligned(16))) float Fs[2][kBK];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int row16 = lane & 15, grp = lane >> 4;
+
+    // heaviest query blocks (most keys) first
+    const int qb = nqb - 1 - (int)(blockIdx.x / BH);
+    const int bh = (int)(blockIdx.x % BH);
+    const int q0 = qb * kBQ;
+    const size_t hoff = (size_t)bh * L * D;
+    const __bf16* Qh = Q + hoff;
+    const __bf16* Kh = K + hoff;
+    const __bf16* Vh = V + hoff;
+    __bf16* Oh = O + hoff;
+    const float* Fh = FK + (size_t)bh * L;
+
+    const int qw0 = q0 + wave * kMQ;           // first query row of this wave
+    const int qwl = min(qw0 + kMQ - 1, L - 1); // last valid query row
+    const bool wave_active = qw0 < L;
+    const int kend = min(q0 + kBQ, L);
+    const int ntiles = (kend + kBK - 1) / kBK;
+
+    // ---- query block: B operand of S^T = K Q^T, and the row factors ----
+    bf16x8 qf[2][DC];
+    int qi[2];
+    float lam[2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+        qi[qs] = qw0 + 16 * qs + row16;
+        float ss = 0.0f;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (qi[qs] < L)
+                w = *reinterpret_cast<const u32x4*>(Qh + (size_t)qi[qs] * D + 32 * dc + 8 * grp);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float a = bf16lo(w[e]), b = bf16hi(w[e]);
+                ss = __builtin_fmaf(a, a, ss);
+                ss = __builtin_fmaf(b, b, ss);
+            }
+            qf[qs][dc] = __builtin_bit_cast(bf16x8, w);
+        }
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        // log2(e) ln d ln i / max(|q_i|, 1e-12)  (Key design 1: log d . log N)
+        lam[qs] = (float)query_factor(lam_scale, qi[qs] + 1, (double)ss);
+    }
+
+    // ---- staging: global -> registers -> LDS ----
+    u32x4 kreg[KCH];
+    u32x4 vreg[VCH][2];
+    float freg = 0.0f;
+
+    auto gload_k = [&](int kt) {
+#pragma unroll
+        for (int n = 0; n < KCH; ++n) {
+            const int c = tid + n * kThreads;
+            const int key = c / (D / 8), col8 = c % (D / 8);
+            const int kg = kt * kBK + key;
+            kreg[n] = kg < L ? *reinterpret_cast<const u32x4*>(Kh + (size_t)kg * D + col8 * 8)
+                             : u32x4{0u, 0u, 0u, 0u};
+        }
+        const int kg = kt * kBK + (tid & 63);
+        freg = (tid < 64 && kg < L) ? Fh[kg] : 0.0f;
+    };
+    auto swrite_k = [&](int buf) {
+#pragma unroll
+        for (int n = 0; n < KCH; ++n) {
+            const int c = tid + n * kThreads;
+            const int key = c / (D / 8), col8 = c % (D / 8);
+            *reinterpret_cast<u32x4*>(&Ks[buf][key * KS + col8 * 8]) = kreg[n];
+        }
+        if (tid < 64)
+            Fs[buf][tid] = freg;
+    };
+    auto gload_v = [&](int kt) {
+        const int kp = tid & 31, dcn = tid >> 5;
+        const int k0 = kt * kBK + 2 * kp;
+#pragma unroll
+        for (int n = 0; n < VCH; ++n) {
+            const int col8 = dcn + 8 * n;
+            vreg[n][0] = k0 < L ? *reinterpret_cast<const u32x4*>(Vh + (size_t)k0 * D + col8 * 8)
+                                : u32x4{0u, 0u, 0u, 0u};
+            vreg[n][1] = k0 + 1 < L
+                             ? *reinterpret_cast<const u32x4*>(Vh + (size_t)(k0 + 1) * D + col8 * 8)
+                             : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto swrite_v = [&](int buf) {
+        const int kp = tid & 31, dcn = tid >> 5;
+        const int pos = vt_pos(2 * kp);        // pos(2kp + 1) = pos + 1
+#pragma unroll
+        for (int n = 0; n < VCH; ++n) {
+            const int col8 = dcn + 8 * n;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t a = vreg[n][0][w], b = vreg[n][1][w];
+                const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x05040100u);
+                const uint32_t hi = __builtin_amdgcn_perm(b, a, 0x07060302u);
+                *reinterpret_cast<uint32_t*>(&Vt[buf][(col8 * 8 + 2 * w) * VS + pos]) = lo;
+                *reinterpret_cast<uint32_t*>(&Vt[buf][(col8 * 8 + 2 * w + 1) * VS + pos]) = hi;
+            }
+        }
+    };
+
+    // S^T block for the wave: acc[ks][qs][r] = k_(16ks+4grp+r) . q_(16qs+row16)
+    auto qk_tile = [&](int buf, f32x4 (&acc)[4][2]) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int qs = 0; qs < 2; ++qs)
+                acc[ks][qs] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    &Ks[buf][(16 * ks + row16) * KS + 32 * dc + 8 * grp]);
+#pragma unroll
+                for (int qs = 0; qs < 2; ++qs)
+                    acc[ks][qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qs][dc],
+                                                                          acc[ks][qs], 0, 0, 0);
+            }
+        }
+    };
+
+    // ---------------- pass 1: S1 and the row max of the scores ----------------
+    float s1[2] = {0.0f, 0.0f};
+    float tmax[2] = {-INFINITY, -INFINITY};
+
+    auto pass1_tile = [&](int kt, int buf, auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
+        f32x4 acc[4][2];
+        qk_tile(buf, acc);
+        float part[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const f32x4 f4 = *reinterpret_cast<const f32x4*>(&Fs[buf][16 * ks + 4 * grp]);
+#pragma unroll
+            for (int qs = 0; qs < 2; ++qs) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float t = acc[ks][qs][r] * (lam[qs] * f4[r]);
+                    float sp = softplus2(t);
+                    if constexpr (DIAG) {
+                        const bool ok = kt * kBK + 16 * ks + 4 * grp + r <= qi[qs];
+                        sp = ok ? sp : 0.0f;
+                        t = ok ? t : -INFINITY;
+                    }
+                    part[qs] += sp;
+                    tmax[qs] = fmaxf(tmax[qs], t);
+                }
+            }
+        }
+        s1[0] += part[0];
+        s1[1] += part[1];
+    };
+
+    gload_k(0);
+    swrite_k(0);
+    __syncthreads();
+    for (int kt = 0; kt < ntiles; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < ntiles)
+            gload_k(kt + 1);
+        if (wave_active && kt * kBK <= qwl) {
+            if (kt * kBK + kBK - 1 > qw0)
+                pass1_tile(kt, buf, std::true_type{});
+            else
+                pass1_tile(kt, buf, std::false_type{});
+        }
+        if (kt + 1 < ntiles)
+            swrite_k(buf ^ 1);
+        __syncthreads();
+    }
+
+    RowConst rc[2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+        float s = s1[qs];
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        float t = tmax[qs];
+        t = fmaxf(t, __shfl_xor(t, 16));
+        t = fmaxf(t, __shfl_xor(t, 32));
+        rc[qs] = row_constants(qi[qs] + 1, s, t, eps);
+    }
+
+    // ---------------- pass 2: re-weight, P.V and the weight sum ----------------
+    f32x4 oacc[DS][2];
+    f32x4 dacc[2];
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+            oacc[ds][qs] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    dacc[0] = dacc[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const __bf16 one = (__bf16)1.0f;
+    const bf16x8 ones = {one, one, one, one, one, one, one, one};
+
+    auto pass2_tile = [&](int kt, int buf, auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
+        f32x4 acc[4][2];
+        qk_tile(buf, acc);
+        f32x4 w[4][2];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const f32x4 f4 = *reinterpret_cast<const f32x4*>(&Fs[buf][16 * ks + 4 * grp]);
+#pragma unroll
+            for (int qs = 0; qs < 2; ++qs) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float t = acc[ks][qs][r] * (lam[qs] * f4[r]);
+                    const float y = reweight_arg(softplus2(t), rc[qs].c, rc[qs].tc);
+                    float wv = pow_chain<P>(y, p_rt);
+                    if constexpr (DIAG) {
+                        const bool ok = kt * kBK + 16 * ks + 4 * grp + r <= qi[qs];
+                        wv = ok ? wv : 0.0f;
+                    }
+                    w[ks][qs][r] = wv;
+                }
+            }
+        }
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+            bf16x8 bfr[2];
+#pragma unroll
+            for (int qs = 0; qs < 2; ++qs) {
+                const bf16x4 lo = __builtin_convertvector(w[2 * c2][qs], bf16x4);
+                const bf16x4 hi = __builtin_convertvector(w[2 * c2 + 1][qs], bf16x4);
+                bfr[qs] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    &Vt[buf][(16 * ds + row16) * VS + 32 * c2 + 8 * grp]);
+#pragma unroll
+                for (int qs = 0; qs < 2; ++qs)
+                    oacc[ds][qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfr[qs], oacc[ds][qs],
+                                                                           0, 0, 0);
+            }
+#pragma unroll
+            for (int qs = 0; qs < 2; ++qs)
+                dacc[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bfr[qs], dacc[qs], 0, 0, 0);
+        }
+    };
+
+    gload_k(0);
+    gload_v(0);
+    swrite_k(0);
+    swrite_v(0);
+    __syncthreads();
+    for (int kt = 0; kt < ntiles; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < ntiles) {
+            gload_k(kt + 1);
+            gload_v(kt + 1);
+        }
+        if (wave_active && kt * kBK <= qwl) {
+            if (kt * kBK + kBK - 1 > qw0)
+                pass2_tile(kt, buf, std::true_type{});
+            else
+                pass2_tile(kt, buf, std::false_type{});
+        }
+        if (kt + 1 < ntiles) {
+            swrite_k(buf ^ 1);
+            swrite_v(buf ^ 1);
+        }
+        __syncthreads();
+    }
+
+    // ---------------- finalize: out_i = U_i / D_i (0 if degenerate) ----------------
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+        if (qi[qs] >= L)
+            continue;
+        const float inv = rc[qs].degen ? 0.0f : 1.0f / dacc[qs][0];
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+            const f32x4 o = oacc[ds][qs] * inv;
+            const bf16x4 ob = __builtin_convertvector(o, bf16x4);
+            *reinterpret_cast<bf16x4*>(Oh + (size_t)qi[qs] * D + 16 * ds + 4 * grp) = ob;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 attention kernel: the same two passes.  Scores come from
+// v_mfma_f64_16x16x4_f64 on the exact fp32 inputs widened to fp64, and the
+// score -> Softplus -> row sums -> re-weighting chain runs in fp64 (see
+// softplus2_f64); the weights are rounded to fp32 once and P.V runs on
+// v_mfma_f32_16x16x4_f32.  K and V stay row-major in LDS (one element per
+// lane per MFMA operand); tiles are single-buffered.
+// ---------------------------------------------------------------------------
+template <int D, int P>
+__global__ __launch_bounds__(kThreads, 1) void lssar_fwd_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K,
+    const float* __restrict__ V, float* __restrict__ O,
+    const float* __restrict__ FK, int BH, int L, int nqb, double lam_scale,
+    float eps, int p_rt)
+{
+    static_assert(D == 64 || D == 128, "head dim");
+    constexpr int DK = D / 4;                  // MFMA k-steps over d
+    constexpr int DS = D / 16;
+    constexpr int KS = D + 4;                  // row stride (floats) for K and V tiles
+    constexpr int CH = kBK * D / 4 / kThreads; // 16-byte chunks per thread per tile
+
+    __shared__ __attribute__((aligned(16))) float Ks[kBK * KS];
+    __shared__ __attribute__((aligned(16))) float Vs[kBK * KS];
+    __shared__ __attribute__((aligned(16))) float Fs[kBK];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int row16 = lane & 15, grp = lane >> 4;
+    const int qb = nqb - 1 - (int)(blockIdx.x / BH);
+    const int bh = (int)(blockIdx.x % BH);
+    const int q0 = qb * kBQ;
+    const size_t hoff = (size_t)bh * L * D;
+    const float* Qh = Q + hoff;
+    const float* Kh = K + hoff;
+    const float* Vh = V + hoff;
+    float* Oh = O + hoff;
+    const float* Fh = FK + (size_t)bh * L;
+
+    const int qw0 = q0 + wave * kMQ;
+    const int qwl = min(qw0 + kMQ - 1, L - 1);
+    const bool wave_active = qw0 < L;
+    const int kend = min(q0 + kBQ, L);
+    const int ntiles = (kend + kBK - 1) / kBK;
+
+    float qf[2][DK];
+    int qi[2];
+    double lam[2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+        qi[qs] = qw0 + 16 * qs + row16;
+        double ss = 0.0;
+#pragma unroll
+        for (int kk = 0; kk < DK; ++kk) {
+            const float x = qi[qs] < L ? Qh[(size_t)qi[qs] * D + 4 * kk + grp] : 0.0f;
+            qf[qs][kk] = x;
+            ss = fma((double)x, (double)x, ss);
+        }
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        lam[qs] = query_factor(lam_scale, qi[qs] + 1, ss);
+    }
+
+    auto stage = [&](int kt, bool with_v) {
+#pragma unroll
+        for (int n = 0; n < CH; ++n) {
+            const int c = tid + n * kThreads;
+            const int key = c / (D / 4), col4 = c % (D / 4);
+            const int kg = kt * kBK + key;
+            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            *reinterpret_cast<f32x4*>(&Ks[key * KS + col4 * 4]) =
+                kg < L ? *reinterpret_cast<const f32x4*>(Kh + (size_t)kg * D + col4 * 4) : z;
+            if (with_v)
+                *reinterpret_cast<f32x4*>(&Vs[key * KS + col4 * 4]) =
+                    kg < L ? *reinterpret_cast<const f32x4*>(Vh + (size_t)kg * D + col4 * 4) : z;
+        }
+        if (tid < kBK) {
+            const int kg = kt * kBK + tid;
+            Fs[tid] = kg < L ? Fh[kg] : 0.0f;
+        }
+    };
+
+    // S^T block in fp64.  v_mfma_f64_16x16x4_f64 returns output row
+    // 4 r + grp in register r (measured; the fp32/bf16 16x16 forms return
+    // row 4 grp + r), so acc[ks][qs][r] = k_(16ks+grp+4r) . q_(16qs+row16).
+    auto key_of = [&](int ks, int r) { return 16 * ks + grp + 4 * r; };
+    auto qk_tile = [&](f64x4 (&acc)[4][2]) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int qs = 0; qs < 2; ++qs)
+                acc[ks][qs] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int kk = 0; kk < DK; ++kk) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const double a = Ks[(16 * ks + row16) * KS + 4 * kk + grp];
+#pragma unroll
+                for (int qs = 0; qs < 2; ++qs)
+                    acc[ks][qs] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)qf[qs][kk],
+                                                                       acc[ks][qs], 0, 0, 0);
+            }
+        }
+    };
+
+    // pass 1
+    double s1[2] = {0.0, 0.0};
+    double tmax[2] = {-INFINITY, -INFINITY};
+    for (int kt = 0; kt < ntiles; ++kt) {
+        __syncthreads();
+        stage(kt, false);
+        __syncthreads();
+        if (!(wave_active && kt * kBK <= qwl))
+            continue;
+        f64x4 acc[4][2];
+        qk_tile(acc);
+        double part[2] = {0.0, 0.0};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int qs = 0; qs < 2; ++qs) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = key_of(ks, r);
+                    const bool ok = kt * kBK + key <= qi[qs];
+                    if (ok) {
+                        const double t = acc[ks][qs][r] * (lam[qs] * (double)Fs[key]);
+                        part[qs] += softplus2_f64(t);
+                        tmax[qs] = fmax(tmax[qs], t);
+                    }
+                }
+            }
+        }
+        s1[0] += part[0];
+        s1[1] += part[1];
+    }
+    RowConstD rc[2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+        double s = s1[qs];
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        double t = tmax[qs];
+        t = fmax(t, __shfl_xor(t, 16));
+        t = fmax(t, __shfl_xor(t, 32));
+        rc[qs] = row_constants_f64(qi[qs] + 1, s, t, eps);
+    }
+
+    // pass 2
+    f32x4 oacc[DS][2];
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+            oacc[ds][qs] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float dsum[2] = {0.0f, 0.0f};
+    for (int kt = 0; kt < ntiles; ++kt) {
+        __syncthreads();
+        stage(kt, true);
+        __syncthreads();
+        if (!(wave_active && kt * kBK <= qwl))
+            continue;
+        f64x4 acc[4][2];
+        qk_tile(acc);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            float w[2][4];
+#pragma unroll
+            for (int qs = 0; qs < 2; ++qs) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = key_of(ks, r);
+                    const bool ok = kt * kBK + key <= qi[qs];
+                    float wv = 0.0f;
+                    if (ok) {
+                        const double t = acc[ks][qs][r] * (lam[qs] * (double)Fs[key]);
+                        double y = softplus2_f64(t) * rc[qs].c - rc[qs].tc;
+                        y = fmin(fmax(y, 0.0), 1.0);
+                        wv = (float)pow_chain<P>(y, p_rt);
+                    }
+                    w[qs][r] = wv;
+                    dsum[qs] += wv;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                for (int ds = 0; ds < DS; ++ds) {
+                    // P.V step r: k-slot grp carries key key_of(ks, r)
+                    const float a = Vs[key_of(ks, r) * KS + 16 * ds + row16];
+#pragma unroll
+                    for (int qs = 0; qs < 2; ++qs)
+                        oacc[ds][qs] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, w[qs][r],
+                                                                            oacc[ds][qs], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+        float s = dsum[qs];
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        if (qi[qs] >= L)
+            continue;
+        const float inv = rc[qs].degen ? 0.0f : 1.0f / s;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+            const f32x4 o = oacc[ds][qs] * inv;
+            *reinterpret_cast<f32x4*>(Oh + (size_t)qi[qs] * D + 16 * ds + 4 * grp) = o;
+        }
+    }
+}
+
+}  // namespace lssar

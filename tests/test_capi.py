@@ -1,0 +1,139 @@
+"""The C ABI library on the CPU: it loads, exports every declared symbol, and
+rejects invalid arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import softmax_free_attention_amd as sfa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lssar.h")
+
+# Fake device addresses: validation never dereferences them.
+A = 0x7F0000000000
+STEP = 1 << 30
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lssar_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(sfa.lib_path):
+        from softmax_free_attention_amd import build
+        build.build()
+    return sfa.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("lssar_attn_fwd", "lssar_attn_fwd_ws", "lssar_workspace_bytes",
+              "lssar_status_str", "lssar_key_inv_norms", "lssar_attn_fwd_prenormed"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    raw = ctypes.CDLL(sfa.lib_path)
+    for n in declared_functions():
+        assert hasattr(raw, n), f"{n} declared in include/lssar.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", sfa.lib_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (lssar_[a-z0-9_]+)$", out, flags=re.M))
+    assert exported == set(declared_functions()), "exported lssar_* symbols differ from the header"
+
+
+def test_library_has_no_oracle_dependency(L):
+    out = subprocess.run(["readelf", "-d", sfa.lib_path], capture_output=True, text=True,
+                         check=True).stdout
+    assert "lssar_ref" not in out
+    assert "libamdhip64" in out
+    for dirpath, _, files in os.walk(os.path.join(ROOT, "softmax_free_attention_amd")):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", src, flags=re.M), f
+                assert "lssar_ref" not in src, f
+
+
+def test_version_and_status_strings(L):
+    assert sfa.lssar_version() == 100
+    assert sfa.lssar_status_str(0) == "ok"
+    for st in (-1, -2, -3, -4, 7):
+        s = sfa.lssar_status_str(st)
+        assert isinstance(s, str) and s
+    assert sfa.lssar_last_hip_error() == 0
+
+
+def test_workspace_bytes(L):
+    assert sfa.lssar_workspace_bytes(1, 12, 8192, 64, sfa.LSSAR_BF16) == 4 * 12 * 8192
+    assert sfa.lssar_workspace_bytes(1, 1, 1, 64, sfa.LSSAR_F32) == 256
+    assert sfa.lssar_workspace_bytes(2, 3, 5, 128, sfa.LSSAR_F32) == 256
+    assert sfa.lssar_workspace_bytes(1, 1, 100, 64, sfa.LSSAR_F32) == 512
+    assert sfa.lssar_workspace_bytes(0, 1, 1, 64, 0) == 0
+    assert sfa.lssar_workspace_bytes(1, 1, 1, 96, 0) == 0
+    assert sfa.lssar_workspace_bytes(1, 1, 1, 64, 5) == 0
+
+
+def _fwd_ws(L, q=A, k=A + STEP, v=A + 2 * STEP, o=A + 3 * STEP, B=1, H=2, Ln=64, d=64, p=3,
+            eps=1e-4, dt=1, ws=A + 4 * STEP, wsb=1 << 20):
+    return L.lssar_attn_fwd_ws(q, k, v, o, B, H, Ln, d, p, eps, dt, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=0), sfa.LSSAR_EINVAL),
+    (dict(k=0), sfa.LSSAR_EINVAL),
+    (dict(v=0), sfa.LSSAR_EINVAL),
+    (dict(o=0), sfa.LSSAR_EINVAL),
+    (dict(B=0), sfa.LSSAR_EINVAL),
+    (dict(H=-1), sfa.LSSAR_EINVAL),
+    (dict(Ln=0), sfa.LSSAR_EINVAL),
+    (dict(p=0), sfa.LSSAR_EINVAL),
+    (dict(eps=-1.0), sfa.LSSAR_EINVAL),
+    (dict(eps=float("nan")), sfa.LSSAR_EINVAL),
+    (dict(eps=float("inf")), sfa.LSSAR_EINVAL),
+    (dict(d=96), sfa.LSSAR_EUNSUPPORTED),
+    (dict(d=32), sfa.LSSAR_EUNSUPPORTED),
+    (dict(dt=2), sfa.LSSAR_EUNSUPPORTED),
+    (dict(p=1025), sfa.LSSAR_EUNSUPPORTED),
+    (dict(Ln=(1 << 24) + 1), sfa.LSSAR_EUNSUPPORTED),
+    (dict(q=A + 8), sfa.LSSAR_EINVAL),                        # misaligned
+    (dict(o=A + 64), sfa.LSSAR_EINVAL),                       # out overlaps q
+    (dict(o=A + STEP + 2 * 64 * 64), sfa.LSSAR_EINVAL),       # out overlaps k
+    (dict(B=1 << 16, H=1 << 16), sfa.LSSAR_EINVAL),           # B*H overflows
+    (dict(ws=0), sfa.LSSAR_EWORKSPACE),
+    (dict(ws=A + 4 * STEP + 16), sfa.LSSAR_EWORKSPACE),       # not 256-aligned
+    (dict(wsb=100), sfa.LSSAR_EWORKSPACE),                    # too small
+    (dict(ws=A + STEP + 256), sfa.LSSAR_EWORKSPACE),          # overlaps k
+])
+def test_validation_before_any_hip_call(L, kw, want):
+    assert _fwd_ws(L, **kw) == want
+    assert sfa.lssar_last_hip_error() == 0
+
+
+def test_allocating_entry_validates(L):
+    assert L.lssar_attn_fwd(0, A, A + STEP, A + 2 * STEP, 1, 1, 8, 64, 3, 1e-4, 1, None) == -1
+    assert L.lssar_attn_fwd(A, A + STEP, A + 2 * STEP, A + 3 * STEP, 1, 1, 8, 80, 3, 1e-4, 1,
+                            None) == -2
+
+
+def test_stage_entries_validate(L):
+    # key norms: null k, bad d, fk null / misaligned / overlapping k
+    assert L.lssar_key_inv_norms(0, A, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EINVAL
+    assert L.lssar_key_inv_norms(A, A + STEP, 1, 1, 8, 72, 1, None) == sfa.LSSAR_EUNSUPPORTED
+    assert L.lssar_key_inv_norms(A, 0, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
+    assert L.lssar_key_inv_norms(A, A + STEP + 4, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
+    assert L.lssar_key_inv_norms(A, A + 16, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
+    # prenormed: same checks as the fused call plus fk
+    args = [A, A + STEP, A + 2 * STEP]
+    assert L.lssar_attn_fwd_prenormed(*args, 0, A + 3 * STEP, 1, 1, 8, 64, 3, 1e-4, 1,
+                                      None) == sfa.LSSAR_EWORKSPACE
+    assert L.lssar_attn_fwd_prenormed(*args, A + 4 * STEP, A + 3 * STEP, 1, 1, 8, 64, 0, 1e-4, 1,
+                                      None) == sfa.LSSAR_EINVAL
+    assert L.lssar_attn_fwd_prenormed(*args, A + 3 * STEP + 64, A + 3 * STEP, 1, 1, 8, 64, 3,
+                                      1e-4, 1, None) == sfa.LSSAR_EWORKSPACE

@@ -76,24 +76,25 @@ def upload(inp):
 
 
 def time_path(q, k, v, p, steps, warmup, eps=1e-4):
-    """Run warmup + timed steps; returns (wall_s, fwd_ms_mean, prep_ms_mean)."""
+    """Run warmup + timed steps; returns (wall_s, fwd_ms_mean, prep_ms_mean).
+    A step is lssar_prep then lssar_attn_fwd_prepped (what lssar_attn_fwd_ws
+    launches), with HIP events recorded between them on the launch stream."""
     import torch
     import softmax_free_attention_amd as sfa
-    B, H, L, d = q.shape
-    fk = torch.empty(B * H * L, dtype=torch.float32, device=q.device)
+    ws = sfa.workspace_for(q)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        sfa.lssar_key_inv_norms(k, fk, stream=stream)
-        sfa.lssar_attn_fwd_prenormed(q, k, v, fk, out, p=p, eps=eps, stream=stream)
+        sfa.lssar_prep(k, v, ws, stream=stream)
+        sfa.lssar_attn_fwd_prepped(q, k, v, ws, out, p=p, eps=eps, stream=stream)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
         ev[s][0].record(stream)
-        sfa.lssar_key_inv_norms(k, fk, stream=stream)
+        sfa.lssar_prep(k, v, ws, stream=stream)
         ev[s][1].record(stream)
-        sfa.lssar_attn_fwd_prenormed(q, k, v, fk, out, p=p, eps=eps, stream=stream)
+        sfa.lssar_attn_fwd_prepped(q, k, v, ws, out, p=p, eps=eps, stream=stream)
         ev[s][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

@@ -55,21 +55,24 @@ enum {
     LSSAR_EINVAL = -1,       /* null/misaligned/overlapping pointer, B,H,L < 1,
                                 p < 1, eps < 0 or not finite, sizes overflow */
     LSSAR_EUNSUPPORTED = -2, /* d not in {64, 128}, unknown dtype, p > 1024,
-                                L > 2^24 */
-    LSSAR_EWORKSPACE = -3,   /* workspace null, misaligned or too small */
+                                L > 2^22 */
+    LSSAR_EWORKSPACE = -3,   /* workspace null, misaligned, too small or
+                                overlapping a tensor */
     LSSAR_EHIP = -4          /* a HIP call or kernel launch failed; see
                                 lssar_last_hip_error() */
 };
 
-/* Workspace for lssar_attn_fwd_ws, in bytes: one fp32 inverse key norm per
- * key row (4*B*H*L), rounded up to 256.  Returns 0 for invalid sizes. */
+/* Workspace for lssar_attn_fwd_ws / lssar_prep / lssar_attn_fwd_prepped, in
+ * bytes: one fp32 inverse key norm per key row (4*B*H*L, rounded up to 256),
+ * plus for bf16 inputs a transposed copy of V (B*H*d*Lp bf16, Lp = L rounded
+ * up to 64, rounded up to 256).  Returns 0 for invalid sizes. */
 size_t lssar_workspace_bytes(int B, int H, int L, int d, int dtype);
 
 /* LSSAR causal attention forward (Key designs 1-3 above) with a
  * caller-provided device workspace of at least lssar_workspace_bytes()
- * bytes, 256-byte aligned.  Allocates nothing.  Launches two kernels on
- * `stream`: the key-row L2-norm prep kernel, then the fused two-pass
- * attention kernel.  p: integer exponent >= 1 (the note reports 3 and 15).
+ * bytes, 256-byte aligned, overlapping no tensor.  Allocates nothing.
+ * Equivalent to lssar_prep followed by lssar_attn_fwd_prepped on `stream`.
+ * p: integer exponent >= 1 (the note reports 3 and 15).
  * eps: degenerate-row threshold >= 0 (1e-4 is the reference choice). */
 int lssar_attn_fwd_ws(const void* q, const void* k, const void* v, void* out,
                       int B, int H, int L, int d, int p, float eps, int dtype,
@@ -81,20 +84,21 @@ int lssar_attn_fwd(const void* q, const void* k, const void* v, void* out,
                    int B, int H, int L, int d, int p, float eps, int dtype,
                    void* stream);
 
-/* Stage 1 alone: the key-row L2-norm prep kernel (Key design 1's
- * K_j <- K_j / |K_j|_2, kept as a factor).  Writes fk[bh*L + j] =
- * 1 / max(|k_j|_2, 1e-12) in fp32 for every key row; fk is a device buffer of
- * at least 4*B*H*L bytes, 16-byte aligned, not overlapping k.  Same status
- * codes as lssar_attn_fwd_ws (a bad fk is LSSAR_EWORKSPACE). */
-int lssar_key_inv_norms(const void* k, float* fk, int B, int H, int L, int d,
-                        int dtype, void* stream);
+/* Stage 1 alone: the prep kernels.  Writes into the workspace the fp32
+ * factors fk[bh*L + j] = 1 / max(|k_j|_2, 1e-12) (Key design 1's
+ * K_j <- K_j / |K_j|_2, kept as a factor of the score) and, for bf16 inputs,
+ * V transposed per head for the attention kernel.  Workspace rules as for
+ * lssar_attn_fwd_ws; a bad workspace is LSSAR_EWORKSPACE. */
+int lssar_prep(const void* k, const void* v, void* workspace,
+               size_t workspace_bytes, int B, int H, int L, int d, int dtype,
+               void* stream);
 
-/* Stage 2 alone: the fused two-pass attention kernel, given the fk array
- * that lssar_key_inv_norms wrote for these keys.  lssar_attn_fwd_ws is this
- * call preceded by lssar_key_inv_norms on the same stream. */
-int lssar_attn_fwd_prenormed(const void* q, const void* k, const void* v,
-                             const float* fk, void* out, int B, int H, int L,
-                             int d, int p, float eps, int dtype, void* stream);
+/* Stage 2 alone: the fused two-pass attention kernel, reading the workspace
+ * that lssar_prep filled for these k and v (stream-ordered after it). */
+int lssar_attn_fwd_prepped(const void* q, const void* k, const void* v,
+                           void* workspace, size_t workspace_bytes, void* out,
+                           int B, int H, int L, int d, int p, float eps,
+                           int dtype, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* lssar_status_str(int status);

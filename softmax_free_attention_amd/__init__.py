@@ -19,7 +19,7 @@ __all__ = [
     "LSSAR_F32", "LSSAR_BF16", "LSSAR_OK", "LSSAR_EINVAL", "LSSAR_EUNSUPPORTED",
     "LSSAR_EWORKSPACE", "LSSAR_EHIP", "LssarError", "lib", "lib_path",
     "lssar_workspace_bytes", "lssar_attn_fwd_ws", "lssar_attn_fwd",
-    "lssar_key_inv_norms", "lssar_attn_fwd_prenormed", "lssar_status_str",
+    "lssar_prep", "lssar_attn_fwd_prepped", "lssar_status_str", "workspace_for",
     "lssar_last_hip_error", "lssar_version", "DEFAULT_EPS",
 ]
 
@@ -56,10 +56,10 @@ def lib():
         L.lssar_attn_fwd_ws.restype = i
         L.lssar_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
         L.lssar_attn_fwd.restype = i
-        L.lssar_key_inv_norms.argtypes = [vp, vp, i, i, i, i, i, vp]
-        L.lssar_key_inv_norms.restype = i
-        L.lssar_attn_fwd_prenormed.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
-        L.lssar_attn_fwd_prenormed.restype = i
+        L.lssar_prep.argtypes = [vp, vp, vp, sz, i, i, i, i, i, vp]
+        L.lssar_prep.restype = i
+        L.lssar_attn_fwd_prepped.argtypes = [vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, i, vp]
+        L.lssar_attn_fwd_prepped.restype = i
         L.lssar_status_str.argtypes = [i]
         L.lssar_status_str.restype = ctypes.c_char_p
         L.lssar_last_hip_error.argtypes = []
@@ -153,28 +153,39 @@ def lssar_attn_fwd(q, k, v, out=None, *, p: int, eps: float = DEFAULT_EPS, strea
     return out
 
 
-def lssar_key_inv_norms(k, fk, *, stream=None):
-    """fk[b, h, j] <- 1 / max(|k[b, h, j]|_2, 1e-12); fk is a float32 device
-    tensor with B*H*L elements."""
+def workspace_for(q):
+    """A device byte tensor of lssar_workspace_bytes for tensors shaped like q."""
     import torch
-    if not k.is_cuda or not k.is_contiguous() or k.dim() != 4:
-        raise ValueError("k must be a contiguous [B, H, L, d] device tensor")
-    B, H, L, d = k.shape
-    if fk.dtype != torch.float32 or fk.numel() < B * H * L or not fk.is_cuda:
-        raise ValueError("fk must be a float32 device tensor of B*H*L elements")
-    st = lib().lssar_key_inv_norms(_ptr(k), _ptr(fk), B, H, L, d, _dtype_code(k),
-                                   _stream_ptr(stream))
-    _raise(st, "lssar_key_inv_norms")
-    return fk
+    B, H, L, d = q.shape
+    n = lssar_workspace_bytes(B, H, L, d, _dtype_code(q))
+    if n == 0:
+        raise ValueError(f"unsupported shape {tuple(q.shape)} / dtype {q.dtype}")
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
 
 
-def lssar_attn_fwd_prenormed(q, k, v, fk, out, *, p: int, eps: float = DEFAULT_EPS, stream=None):
-    """The fused attention kernel alone, given fk from lssar_key_inv_norms."""
-    import torch
+def _ws_args(workspace):
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def lssar_prep(k, v, workspace, *, stream=None):
+    """Stage 1 (prep kernels): key-row inverse norms and, for bf16, V^T, into
+    the workspace."""
+    B, H, L, d, dt = _check_qkv(k, k, v)
+    wp, wn = _ws_args(workspace)
+    st = lib().lssar_prep(_ptr(k), _ptr(v), wp, wn, B, H, L, d, dt, _stream_ptr(stream))
+    _raise(st, "lssar_prep")
+    return workspace
+
+
+def lssar_attn_fwd_prepped(q, k, v, workspace, out, *, p: int, eps: float = DEFAULT_EPS,
+                           stream=None):
+    """Stage 2 (the fused attention kernel), given a workspace filled by
+    lssar_prep for these k and v."""
     B, H, L, d, dt = _check_qkv(q, k, v, out)
-    if fk.dtype != torch.float32 or fk.numel() < B * H * L or not fk.is_cuda:
-        raise ValueError("fk must be a float32 device tensor of B*H*L elements")
-    st = lib().lssar_attn_fwd_prenormed(_ptr(q), _ptr(k), _ptr(v), _ptr(fk), _ptr(out), B, H,
-                                        L, d, int(p), float(eps), dt, _stream_ptr(stream))
-    _raise(st, "lssar_attn_fwd_prenormed")
+    wp, wn = _ws_args(workspace)
+    st = lib().lssar_attn_fwd_prepped(_ptr(q), _ptr(k), _ptr(v), wp, wn, _ptr(out), B, H, L, d,
+                                      int(p), float(eps), dt, _stream_ptr(stream))
+    _raise(st, "lssar_attn_fwd_prepped")
     return out

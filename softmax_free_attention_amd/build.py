@@ -19,6 +19,8 @@ ARCH = "gfx950"
 
 # Packed fp32 VALU ops are turned off for all device code.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+               # MFMA results stay in ordinary VGPRs (no AGPR round trips)
+               "-mllvm", "-amdgpu-mfma-vgpr-form",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

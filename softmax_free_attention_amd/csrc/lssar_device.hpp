@@ -56,9 +56,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;   // 4 waves of 64
 constexpr int kWaves = 4;
-constexpr int kMQ = 32;         // query rows per wave
-constexpr int kBQ = kWaves * kMQ;
 constexpr int kBK = 64;         // keys per tile
+// bf16 kernel: 16 query rows per wave, 64 per workgroup
+constexpr int kMQ16 = 16;
+constexpr int kBQ16 = kWaves * kMQ16;
+// fp32 kernel: 32 query rows per wave, 128 per workgroup
+constexpr int kMQ32 = 32;
+constexpr int kBQ32 = kWaves * kMQ32;
 
 // ---------------------------------------------------------------------------
 // Elementwise pieces shared by both dtypes
@@ -171,13 +175,15 @@ __device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
 // ---------------------------------------------------------------------------
-// Prep kernel: fk[row] = 1 / max(|k_row|_2, 1e-12) for every key row
-// (Key design 1's K_j <- K_j / |K_j|_2, kept as a factor).
+// Prep kernels
 // ---------------------------------------------------------------------------
+
+// fk[row] = 1 / max(|k_row|_2, 1e-12) for every key row (Key design 1's
+// K_j <- K_j / |K_j|_2, kept as a factor of the score).
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void lssar_prep_kernel(const T* __restrict__ K,
-                                                              float* __restrict__ fk,
-                                                              long nrows)
+__global__ __launch_bounds__(kThreads) void lssar_knorm_kernel(const T* __restrict__ K,
+                                                               float* __restrict__ fk,
+                                                               long nrows)
 {
     constexpr int EPL = 16 / (int)sizeof(T);   // elements per 16-byte load
     constexpr int LPR = D / EPL;               // lanes per row
@@ -211,320 +217,390 @@ __global__ __launch_bounds__(kThreads) void lssar_prep_kernel(const T* __restric
         fk[row] = (float)(1.0 / fmax(sqrt(ss), 1e-12));
 }
 
-// ---------------------------------------------------------------------------
-// bf16 attention kernel
-// ---------------------------------------------------------------------------
-
-// Position of key `key` (0..63 of a tile) inside a V^T row in LDS.  With
+// Position of key `key` (0..63 of a 64-key block) inside a row of V^T.  With
 // key = 32 c + 16 h + 4 g + r the position is 32 c + 8 g + 4 h + r, so the 8
-// keys that lane group g feeds to one 32-key MFMA step (from two 16-key
-// score blocks) sit in one 16-byte LDS word.
+// keys that lane group g feeds to one 32-key MFMA step (taken from two
+// 16-key score blocks) sit in one 16-byte word.
 __device__ __forceinline__ int vt_pos(int key)
 {
     return (key & 32) + (((key >> 2) & 3) << 3) + (((key >> 4) & 1) << 2) + (key & 3);
 }
+__device__ __forceinline__ int vt_key(int pos)
+{
+    return (pos & 32) + (((pos >> 2) & 1) << 4) + (((pos >> 3) & 3) << 2) + (pos & 3);
+}
+
+// V^T for the bf16 kernel: Vt[bh][e][kb*64 + vt_pos(j)] = V[bh][kb*64 + j][e]
+// for each 64-key block kb, zero for keys >= L; rows of Vt have Lp (L rounded
+// up to 64) entries.  One workgroup per (64-key block, head).
+template <int D>
+__global__ __launch_bounds__(kThreads) void lssar_vt_kernel(const __bf16* __restrict__ V,
+                                                            __bf16* __restrict__ Vt, int L,
+                                                            int Lp)
+{
+    constexpr int RS = D + 8;                  // LDS row stride (elements)
+    __shared__ __attribute__((aligned(16))) __bf16 tile[64 * RS];
+    const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+    const __bf16* Vh = V + (size_t)bh * L * D;
+#pragma unroll
+    for (int n = 0; n < 64 * D / 8 / kThreads; ++n) {
+        const int c = tid + n * kThreads;
+        const int key = c / (D / 8), col8 = c % (D / 8);
+        const int kg = kb * 64 + key;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (kg < L)
+            w = *reinterpret_cast<const u32x4*>(Vh + (size_t)kg * D + col8 * 8);
+        *reinterpret_cast<u32x4*>(&tile[key * RS + col8 * 8]) = w;
+    }
+    __syncthreads();
+    const unsigned short* t16 = reinterpret_cast<const unsigned short*>(tile);
+    __bf16* Vth = Vt + (size_t)bh * D * Lp;
+#pragma unroll
+    for (int n = 0; n < D * 8 / kThreads; ++n) {
+        const int c = tid + n * kThreads;
+        const int e = c / 8, p8 = c % 8;       // V^T row e, positions 8 p8 .. 8 p8 + 7
+        u32x4 w;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const uint32_t lo = t16[vt_key(8 * p8 + 2 * h) * RS + e];
+            const uint32_t hi = t16[vt_key(8 * p8 + 2 * h + 1) * RS + e];
+            w[h] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x4*>(Vth + (size_t)e * Lp + kb * 64 + 8 * p8) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 attention kernel
+// ---------------------------------------------------------------------------
+//
+// A workgroup of 4 waves owns query blocks of 64 rows of one (batch, head);
+// each wave owns 16 rows (lane & 15).  The causal work of block qb grows
+// with qb, so a workgroup takes the pair {nqb-1-pi, pi}: every workgroup does
+// the same number of key tiles.  Keys stream through LDS in tiles of 64 with
+// buffer loads that write LDS directly (16 bytes per lane, zero past the end
+// of the tensor), double-buffered.  LDS tiles are arrays of 16-byte slots,
+// XOR-swizzled so that the 16 lanes reading one MFMA operand hit distinct
+// banks.  Lane group grp = lane >> 4 holds keys 16 ks + 4 grp + r (r = 0..3)
+// of every 16-key block ks of a tile.
+//
+// Pass 1 keeps, per lane and query row, the partial sums of
+//   Softplus2(t) = max(t, 0) + log2(1 + 2^-|t|)
+// as sum_j max(t_j, 0) plus log2 of the product of the factors
+// (1 + 2^-|t_j|), each in (1, 2]: one exp2 per pair and one log2 per tile for
+// its 16 factors (their product stays below 2^16).  Masked pairs get
+// t = -inf, which adds exactly 0 to every sum in both passes (2^-inf = 0,
+// max(-inf, 0) = 0; in pass 2 Softplus2 = 0 gives y = clamp(-tau c) = 0).
+
+template <int D>
+struct Bf16Tile {
+    static constexpr int R = D / 8;                       // 16-byte slots per K row
+    static constexpr int KBYTES = kBK * D * 2;            // K tile
+    static constexpr int VBYTES = D * kBK * 2;            // V^T tile
+    static constexpr int FBYTES = kBK * 4;                // key factors
+    static constexpr int BYTES = KBYTES + VBYTES + FBYTES;
+    static constexpr int KLOADS = KBYTES / 1024 / kWaves; // 1 KB wave-loads per wave
+    static constexpr int VLOADS = VBYTES / 1024 / kWaves;
+    // XOR swizzle of a K row's slots (key & 15 is all that matters)
+    __device__ static int kswz(int key) { return R == 8 ? ((key >> 1) & 7) : (key & 15); }
+    // XOR swizzle of a V^T row's 8 slots
+    __device__ static int vswz(int e) { return (e >> 1) & 7; }
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer loads of base[voffset + soffset] written straight to LDS at
+// lds + size * lane, 16 or 4 bytes per lane (reads at or past `nbytes`
+// return zeros).  Kept out of kernel bodies: the host pass of a kernel that
+// names the buffer-resource type drops the kernel's launch stub.
+__device__ __forceinline__ void load16_to_lds(const void* base, unsigned nbytes, void* lds,
+                                              unsigned voffset, unsigned soffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                          0x00020000),
+        (lds_void*)lds, 16, (int)voffset, (int)soffset, 0, 0);
+}
+__device__ __forceinline__ void load4_to_lds(const void* base, unsigned nbytes, void* lds,
+                                             unsigned voffset, unsigned soffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                          0x00020000),
+        (lds_void*)lds, 4, (int)voffset, (int)soffset, 0, 0);
+}
 
 template <int D, int P>
-__global__ __launch_bounds__(kThreads, 2) void lssar_fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-    const __bf16* __restrict__ V, __bf16* __restrict__ O,
-    const float* __restrict__ FK, int BH, int L, int nqb, double lam_scale,
-    float eps, int p_rt)
+    const __bf16* __restrict__ VT, __bf16* __restrict__ O,
+    const float* __restrict__ FK, int BH, int L, int Lp, int nqb, int npair,
+    double lam_scale, float eps, int p_rt)
 {
     static_assert(D == 64 || D == 128, "head dim");
+    using T = Bf16Tile<D>;
     constexpr int DC = D / 32;                 // MFMA k-steps over d
     constexpr int DS = D / 16;                 // 16-row blocks of O^T
-    constexpr int KS = D + 8;                  // K tile row stride (elements)
-    constexpr int VS = kBK + 8;                // V^T tile row stride
-    constexpr int KCH = kBK * D / 8 / kThreads;  // 16-byte K chunks per thread
-    constexpr int VCH = D / 64;                // V column groups per thread
 
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][kBK * KS];
-    __shared__ __attribute__((aligned(16))) __bf16 Vt[2][D * VS];
-    __shared__ __attribute__((aligned(16))) float Fs[2][kBK];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2][T::BYTES];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    // wave index in a scalar register, so per-wave decisions are uniform branches
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int row16 = lane & 15, grp = lane >> 4;
-
-    // heaviest query blocks (most keys) first
-    const int qb = nqb - 1 - (int)(blockIdx.x / BH);
+    const int pi = (int)(blockIdx.x / BH);
     const int bh = (int)(blockIdx.x % BH);
-    const int q0 = qb * kBQ;
     const size_t hoff = (size_t)bh * L * D;
     const __bf16* Qh = Q + hoff;
-    const __bf16* Kh = K + hoff;
-    const __bf16* Vh = V + hoff;
     __bf16* Oh = O + hoff;
-    const float* Fh = FK + (size_t)bh * L;
 
-    const int qw0 = q0 + wave * kMQ;           // first query row of this wave
-    const int qwl = min(qw0 + kMQ - 1, L - 1); // last valid query row
-    const bool wave_active = qw0 < L;
-    const int kend = min(q0 + kBQ, L);
-    const int ntiles = (kend + kBK - 1) / kBK;
+    // this head's K, V^T and key factors; buffer reads past them return zeros
+    const void* kbase = K + hoff;
+    const unsigned kbytes = (unsigned)L * D * 2u;
+    const void* vbase = VT + (size_t)bh * D * Lp;
+    const unsigned vbytes = (unsigned)D * Lp * 2u;
+    const void* fbase = FK + (size_t)bh * L;
+    const unsigned fbytes = (unsigned)L * 4u;
 
-    // ---- query block: B operand of S^T = K Q^T, and the row factors ----
-    bf16x8 qf[2][DC];
-    int qi[2];
-    float lam[2];
+    // per-lane byte offsets (within a tile) of the 16-byte slots this lane loads
+    int kld[T::KLOADS], vld[T::VLOADS];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-        qi[qs] = qw0 + 16 * qs + row16;
-        float ss = 0.0f;
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (qi[qs] < L)
-                w = *reinterpret_cast<const u32x4*>(Qh + (size_t)qi[qs] * D + 32 * dc + 8 * grp);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float a = bf16lo(w[e]), b = bf16hi(w[e]);
-                ss = __builtin_fmaf(a, a, ss);
-                ss = __builtin_fmaf(b, b, ss);
-            }
-            qf[qs][dc] = __builtin_bit_cast(bf16x8, w);
-        }
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
-        // log2(e) ln d ln i / max(|q_i|, 1e-12)  (Key design 1: log d . log N)
-        lam[qs] = (float)query_factor(lam_scale, qi[qs] + 1, (double)ss);
+    for (int n = 0; n < T::KLOADS; ++n) {
+        const int slot = (wave * T::KLOADS + n) * 64 + lane;
+        const int key = slot / T::R, c = (slot % T::R) ^ T::kswz(key);
+        kld[n] = (key * D + c * 8) * 2;
     }
-
-    // ---- staging: global -> registers -> LDS ----
-    u32x4 kreg[KCH];
-    u32x4 vreg[VCH][2];
-    float freg = 0.0f;
-
-    auto gload_k = [&](int kt) {
 #pragma unroll
-        for (int n = 0; n < KCH; ++n) {
-            const int c = tid + n * kThreads;
-            const int key = c / (D / 8), col8 = c % (D / 8);
-            const int kg = kt * kBK + key;
-            kreg[n] = kg < L ? *reinterpret_cast<const u32x4*>(Kh + (size_t)kg * D + col8 * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
-        }
-        const int kg = kt * kBK + (tid & 63);
-        freg = (tid < 64 && kg < L) ? Fh[kg] : 0.0f;
-    };
-    auto swrite_k = [&](int buf) {
-#pragma unroll
-        for (int n = 0; n < KCH; ++n) {
-            const int c = tid + n * kThreads;
-            const int key = c / (D / 8), col8 = c % (D / 8);
-            *reinterpret_cast<u32x4*>(&Ks[buf][key * KS + col8 * 8]) = kreg[n];
-        }
-        if (tid < 64)
-            Fs[buf][tid] = freg;
-    };
-    auto gload_v = [&](int kt) {
-        const int kp = tid & 31, dcn = tid >> 5;
-        const int k0 = kt * kBK + 2 * kp;
-#pragma unroll
-        for (int n = 0; n < VCH; ++n) {
-            const int col8 = dcn + 8 * n;
-            vreg[n][0] = k0 < L ? *reinterpret_cast<const u32x4*>(Vh + (size_t)k0 * D + col8 * 8)
-                                : u32x4{0u, 0u, 0u, 0u};
-            vreg[n][1] = k0 + 1 < L
-                             ? *reinterpret_cast<const u32x4*>(Vh + (size_t)(k0 + 1) * D + col8 * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto swrite_v = [&](int buf) {
-        const int kp = tid & 31, dcn = tid >> 5;
-        const int pos = vt_pos(2 * kp);        // pos(2kp + 1) = pos + 1
-#pragma unroll
-        for (int n = 0; n < VCH; ++n) {
-            const int col8 = dcn + 8 * n;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t a = vreg[n][0][w], b = vreg[n][1][w];
-                const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x05040100u);
-                const uint32_t hi = __builtin_amdgcn_perm(b, a, 0x07060302u);
-                *reinterpret_cast<uint32_t*>(&Vt[buf][(col8 * 8 + 2 * w) * VS + pos]) = lo;
-                *reinterpret_cast<uint32_t*>(&Vt[buf][(col8 * 8 + 2 * w + 1) * VS + pos]) = hi;
-            }
-        }
-    };
-
-    // S^T block for the wave: acc[ks][qs][r] = k_(16ks+4grp+r) . q_(16qs+row16)
-    auto qk_tile = [&](int buf, f32x4 (&acc)[4][2]) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int qs = 0; qs < 2; ++qs)
-                acc[ks][qs] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    &Ks[buf][(16 * ks + row16) * KS + 32 * dc + 8 * grp]);
-#pragma unroll
-                for (int qs = 0; qs < 2; ++qs)
-                    acc[ks][qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qs][dc],
-                                                                          acc[ks][qs], 0, 0, 0);
-            }
-        }
-    };
-
-    // ---------------- pass 1: S1 and the row max of the scores ----------------
-    float s1[2] = {0.0f, 0.0f};
-    float tmax[2] = {-INFINITY, -INFINITY};
-
-    auto pass1_tile = [&](int kt, int buf, auto diag_tag) {
-        constexpr bool DIAG = decltype(diag_tag)::value;
-        f32x4 acc[4][2];
-        qk_tile(buf, acc);
-        float part[2] = {0.0f, 0.0f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const f32x4 f4 = *reinterpret_cast<const f32x4*>(&Fs[buf][16 * ks + 4 * grp]);
-#pragma unroll
-            for (int qs = 0; qs < 2; ++qs) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float t = acc[ks][qs][r] * (lam[qs] * f4[r]);
-                    float sp = softplus2(t);
-                    if constexpr (DIAG) {
-                        const bool ok = kt * kBK + 16 * ks + 4 * grp + r <= qi[qs];
-                        sp = ok ? sp : 0.0f;
-                        t = ok ? t : -INFINITY;
-                    }
-                    part[qs] += sp;
-                    tmax[qs] = fmaxf(tmax[qs], t);
-                }
-            }
-        }
-        s1[0] += part[0];
-        s1[1] += part[1];
-    };
-
-    gload_k(0);
-    swrite_k(0);
-    __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < ntiles)
-            gload_k(kt + 1);
-        if (wave_active && kt * kBK <= qwl) {
-            if (kt * kBK + kBK - 1 > qw0)
-                pass1_tile(kt, buf, std::true_type{});
-            else
-                pass1_tile(kt, buf, std::false_type{});
-        }
-        if (kt + 1 < ntiles)
-            swrite_k(buf ^ 1);
-        __syncthreads();
+    for (int n = 0; n < T::VLOADS; ++n) {
+        const int slot = (wave * T::VLOADS + n) * 64 + lane;
+        const int e = slot / 8, c = (slot % 8) ^ T::vswz(e);
+        vld[n] = (e * Lp + c * 8) * 2;
     }
+    // per-lane LDS byte offsets of the MFMA operand slots (16 ks / 16 ds rows
+    // further on are constant offsets)
+    int krd[DC], vrd[2];
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+        krd[dc] = (row16 * T::R + ((4 * dc + grp) ^ T::kswz(row16))) * 16;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+        vrd[c2] = T::KBYTES + (row16 * 8 + ((4 * c2 + grp) ^ T::vswz(row16))) * 16;
 
-    RowConst rc[2];
+    auto issue = [&](int kt, int buf, bool with_v) {
+        unsigned char* base = smem[buf];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-        float s = s1[qs];
-        s += __shfl_xor(s, 16);
-        s += __shfl_xor(s, 32);
-        float t = tmax[qs];
-        t = fmaxf(t, __shfl_xor(t, 16));
-        t = fmaxf(t, __shfl_xor(t, 32));
-        rc[qs] = row_constants(qi[qs] + 1, s, t, eps);
-    }
+        for (int n = 0; n < T::KLOADS; ++n)
+            load16_to_lds(kbase, kbytes, base + (wave * T::KLOADS + n) * 1024, kld[n],
+                            kt * kBK * D * 2);
+        if (with_v) {
+#pragma unroll
+            for (int n = 0; n < T::VLOADS; ++n)
+                load16_to_lds(vbase, vbytes, base + T::KBYTES + (wave * T::VLOADS + n) * 1024,
+                                vld[n], kt * kBK * 2);
+        }
+        if (wave == 0)
+            load4_to_lds(fbase, fbytes, base + T::KBYTES + T::VBYTES, lane * 4, kt * kBK * 4);
+    };
 
-    // ---------------- pass 2: re-weight, P.V and the weight sum ----------------
-    f32x4 oacc[DS][2];
-    f32x4 dacc[2];
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs)
-            oacc[ds][qs] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    dacc[0] = dacc[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const __bf16 one = (__bf16)1.0f;
     const bf16x8 ones = {one, one, one, one, one, one, one, one};
+    const int nblk = (pi == nqb - 1 - pi) ? 1 : 2;
 
-    auto pass2_tile = [&](int kt, int buf, auto diag_tag) {
-        constexpr bool DIAG = decltype(diag_tag)::value;
-        f32x4 acc[4][2];
-        qk_tile(buf, acc);
-        f32x4 w[4][2];
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int qb = blk == 0 ? nqb - 1 - pi : pi;
+        const int q0 = qb * kBQ16;
+        const int qw0 = q0 + wave * kMQ16;         // first query row of this wave
+        const int qwl = min(qw0 + kMQ16 - 1, L - 1);  // last valid query row
+        const bool wave_active = qw0 < L;
+        const int ntiles = qb + 1;
+        const int qi = qw0 + row16;                // this lane's query row (0-based)
+
+        // ---- query rows: B operand of S^T = K Q^T, and the row factor ----
+        bf16x8 qf[DC];
+        float lam;
+        {
+            float ss = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const f32x4 f4 = *reinterpret_cast<const f32x4*>(&Fs[buf][16 * ks + 4 * grp]);
+            for (int dc = 0; dc < DC; ++dc) {
+                u32x4 w = {0u, 0u, 0u, 0u};
+                if (qi < L)
+                    w = *reinterpret_cast<const u32x4*>(Qh + (size_t)qi * D + 32 * dc + 8 * grp);
 #pragma unroll
-            for (int qs = 0; qs < 2; ++qs) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float t = acc[ks][qs][r] * (lam[qs] * f4[r]);
-                    const float y = reweight_arg(softplus2(t), rc[qs].c, rc[qs].tc);
-                    float wv = pow_chain<P>(y, p_rt);
-                    if constexpr (DIAG) {
-                        const bool ok = kt * kBK + 16 * ks + 4 * grp + r <= qi[qs];
-                        wv = ok ? wv : 0.0f;
-                    }
-                    w[ks][qs][r] = wv;
+                for (int e = 0; e < 4; ++e) {
+                    float a = bf16lo(w[e]), b = bf16hi(w[e]);
+                    ss = __builtin_fmaf(a, a, ss);
+                    ss = __builtin_fmaf(b, b, ss);
                 }
+                qf[dc] = __builtin_bit_cast(bf16x8, w);
             }
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            // log2(e) ln d ln i / max(|q_i|, 1e-12)  (Key design 1: log d . log N)
+            lam = (float)query_factor(lam_scale, qi + 1, (double)ss);
         }
+
+        // scores of 16-key block ks: acc[r] = k_(16ks+4grp+r) . q_(row16)
+        auto qk_block = [&](const unsigned char* base, int ks) {
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-            bf16x8 bfr[2];
-#pragma unroll
-            for (int qs = 0; qs < 2; ++qs) {
-                const bf16x4 lo = __builtin_convertvector(w[2 * c2][qs], bf16x4);
-                const bf16x4 hi = __builtin_convertvector(w[2 * c2 + 1][qs], bf16x4);
-                bfr[qs] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            for (int dc = 0; dc < DC; ++dc) {
+                const bf16x8 a =
+                    *reinterpret_cast<const bf16x8*>(base + krd[dc] + ks * 16 * T::R * 16);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[dc], acc, 0, 0, 0);
             }
+            return acc;
+        };
+        // t = acc * lam * f_key; masked (t = -inf) on diagonal tiles
+        auto scale_block = [&](int kt, const unsigned char* base, int ks, f32x4 acc, bool diag) {
+            const f32x4 f4 = *reinterpret_cast<const f32x4*>(
+                base + T::KBYTES + T::VBYTES + (16 * ks + 4 * grp) * 4);
+            f32x4 t = acc * (f4 * lam);
+            if (diag) {
+                const int k0 = kt * kBK + 16 * ks + 4 * grp;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    t[r] = (k0 + r <= qi) ? t[r] : -INFINITY;
+            }
+            return t;
+        };
+
+        // ---------------- pass 1: S1 and the row max of the scores ----------------
+        float s1 = 0.0f;
+        float tmax = -INFINITY;
+        auto pass1_tile = [&](int kt, const unsigned char* base, auto diag_tag) {
+            constexpr bool DIAG = decltype(diag_tag)::value;
+            // 16-key blocks with at least one key <= the wave's last row
+            const int nks = DIAG ? min(4, (qwl - kt * kBK) / 16 + 1) : 4;
+            f32x4 acc[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                if (!DIAG || ks < nks)
+                    acc[ks] = qk_block(base, ks);
+            float pos_sum = 0.0f, prod = 1.0f;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                if (DIAG && ks >= nks)
+                    continue;
+                const f32x4 t = scale_block(kt, base, ks, acc[ks], DIAG);
+                f32x4 u;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    u[r] = __builtin_amdgcn_exp2f(-fabsf(t[r]));
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    pos_sum += fmaxf(t[r], 0.0f);
+                tmax = fmaxf(tmax, fmaxf(t[0], t[1]));
+                tmax = fmaxf(tmax, fmaxf(t[2], t[3]));
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    prod = __builtin_fmaf(prod, u[r], prod);
+            }
+            s1 += pos_sum + __builtin_amdgcn_logf(prod);
+        };
+        __syncthreads();                           // LDS buffers free
+        issue(0, 0, false);
+        for (int kt = 0; kt < ntiles; ++kt) {
+            const int buf = kt & 1;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();                       // tile kt landed; buf^1 free
+            if (kt + 1 < ntiles)
+                issue(kt + 1, buf ^ 1, false);
+            if (!(wave_active && kt * kBK <= qwl))
+                continue;
+            if (kt * kBK + kBK - 1 > qw0)
+                pass1_tile(kt, smem[buf], std::true_type{});
+            else
+                pass1_tile(kt, smem[buf], std::false_type{});
+        }
+
+        RowConst rc;
+        {
+            float sum = s1;
+            sum += __shfl_xor(sum, 16);
+            sum += __shfl_xor(sum, 32);
+            float t = tmax;
+            t = fmaxf(t, __shfl_xor(t, 16));
+            t = fmaxf(t, __shfl_xor(t, 32));
+            rc = row_constants(qi + 1, sum, t, eps);
+        }
+
+        // ---------------- pass 2: re-weight, P.V and the weight sum ----------------
+        f32x4 oacc[DS];
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+            oacc[ds] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 dacc = {0.0f, 0.0f, 0.0f, 0.0f};
+
+        auto weights = [&](f32x4 t) {
+            f32x4 e, w;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                e[r] = __builtin_amdgcn_exp2f(t[r]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                e[r] = __builtin_amdgcn_logf(1.0f + e[r]);       // Softplus2
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                w[r] = pow_chain<P>(reweight_arg(e[r], rc.c, rc.tc), p_rt);
+            return w;
+        };
+
+        auto pass2_tile = [&](int kt, const unsigned char* base, auto diag_tag) {
+            constexpr bool DIAG = decltype(diag_tag)::value;
+            const int nks = DIAG ? min(4, (qwl - kt * kBK) / 16 + 1) : 4;
+            f32x4 acc[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                if (!DIAG || ks < nks)
+                    acc[ks] = qk_block(base, ks);
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                if (DIAG && 2 * c2 >= nks)
+                    continue;
+                const f32x4 w0 = weights(scale_block(kt, base, 2 * c2, acc[2 * c2], DIAG));
+                const f32x4 w1 =
+                    (!DIAG || 2 * c2 + 1 < nks)
+                        ? weights(scale_block(kt, base, 2 * c2 + 1, acc[2 * c2 + 1], DIAG))
+                        : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                const bf16x4 lo = __builtin_convertvector(w0, bf16x4);
+                const bf16x4 hi = __builtin_convertvector(w1, bf16x4);
+                const bf16x8 bfr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+                for (int ds = 0; ds < DS; ++ds) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + vrd[c2] +
+                                                                      ds * 16 * 8 * 16);
+                    oacc[ds] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfr, oacc[ds], 0, 0, 0);
+                }
+                dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bfr, dacc, 0, 0, 0);
+            }
+        };
+
+        __syncthreads();                           // pass-1 readers done with the buffers
+        issue(0, 0, true);
+        for (int kt = 0; kt < ntiles; ++kt) {
+            const int buf = kt & 1;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (kt + 1 < ntiles)
+                issue(kt + 1, buf ^ 1, true);
+            if (!(wave_active && kt * kBK <= qwl))
+                continue;
+            if (kt * kBK + kBK - 1 > qw0)
+                pass2_tile(kt, smem[buf], std::true_type{});
+            else
+                pass2_tile(kt, smem[buf], std::false_type{});
+        }
+
+        // ---------------- finalize: out_i = U_i / D_i (0 if degenerate) ----------------
+        if (qi < L) {
+            const float inv = rc.degen ? 0.0f : 1.0f / dacc[0];
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    &Vt[buf][(16 * ds + row16) * VS + 32 * c2 + 8 * grp]);
-#pragma unroll
-                for (int qs = 0; qs < 2; ++qs)
-                    oacc[ds][qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfr[qs], oacc[ds][qs],
-                                                                           0, 0, 0);
+                const f32x4 o = oacc[ds] * inv;
+                const bf16x4 ob = __builtin_convertvector(o, bf16x4);
+                *reinterpret_cast<bf16x4*>(Oh + (size_t)qi * D + 16 * ds + 4 * grp) = ob;
             }
-#pragma unroll
-            for (int qs = 0; qs < 2; ++qs)
-                dacc[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bfr[qs], dacc[qs], 0, 0, 0);
-        }
-    };
-
-    gload_k(0);
-    gload_v(0);
-    swrite_k(0);
-    swrite_v(0);
-    __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < ntiles) {
-            gload_k(kt + 1);
-            gload_v(kt + 1);
-        }
-        if (wave_active && kt * kBK <= qwl) {
-            if (kt * kBK + kBK - 1 > qw0)
-                pass2_tile(kt, buf, std::true_type{});
-            else
-                pass2_tile(kt, buf, std::false_type{});
-        }
-        if (kt + 1 < ntiles) {
-            swrite_k(buf ^ 1);
-            swrite_v(buf ^ 1);
-        }
-        __syncthreads();
-    }
-
-    // ---------------- finalize: out_i = U_i / D_i (0 if degenerate) ----------------
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-        if (qi[qs] >= L)
-            continue;
-        const float inv = rc[qs].degen ? 0.0f : 1.0f / dacc[qs][0];
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-            const f32x4 o = oacc[ds][qs] * inv;
-            const bf16x4 ob = __builtin_convertvector(o, bf16x4);
-            *reinterpret_cast<bf16x4*>(Oh + (size_t)qi[qs] * D + 16 * ds + 4 * grp) = ob;
         }
     }
 }
@@ -559,7 +635,7 @@ __global__ __launch_bounds__(kThreads, 1) void lssar_fwd_f32_kernel(
     const int row16 = lane & 15, grp = lane >> 4;
     const int qb = nqb - 1 - (int)(blockIdx.x / BH);
     const int bh = (int)(blockIdx.x % BH);
-    const int q0 = qb * kBQ;
+    const int q0 = qb * kBQ32;
     const size_t hoff = (size_t)bh * L * D;
     const float* Qh = Q + hoff;
     const float* Kh = K + hoff;
@@ -567,10 +643,10 @@ __global__ __launch_bounds__(kThreads, 1) void lssar_fwd_f32_kernel(
     float* Oh = O + hoff;
     const float* Fh = FK + (size_t)bh * L;
 
-    const int qw0 = q0 + wave * kMQ;
-    const int qwl = min(qw0 + kMQ - 1, L - 1);
+    const int qw0 = q0 + wave * kMQ32;
+    const int qwl = min(qw0 + kMQ32 - 1, L - 1);
     const bool wave_active = qw0 < L;
-    const int kend = min(q0 + kBQ, L);
+    const int kend = min(q0 + kBQ32, L);
     const int ntiles = (kend + kBK - 1) / kBK;
 
     float qf[2][DK];

@@ -31,9 +31,7 @@ def run_ws(q, k, v, p, eps=1e-4, stream=None):
     """One call of lssar_attn_fwd_ws (the bench's launch configuration)."""
     import torch
     import softmax_free_attention_amd as sfa
-    B, H, L, d = q.shape
-    dt = sfa.LSSAR_BF16 if q.dtype == torch.bfloat16 else sfa.LSSAR_F32
-    ws = torch.empty(sfa.lssar_workspace_bytes(B, H, L, d, dt), dtype=torch.uint8, device=q.device)
+    ws = sfa.workspace_for(q)
     out = torch.empty_like(q)
     sfa.lssar_attn_fwd_ws(q, k, v, out, ws, p=p, eps=eps, stream=stream)
     return out

@@ -34,7 +34,7 @@ def L():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("lssar_attn_fwd", "lssar_attn_fwd_ws", "lssar_workspace_bytes",
-              "lssar_status_str", "lssar_key_inv_norms", "lssar_attn_fwd_prenormed"):
+              "lssar_status_str", "lssar_prep", "lssar_attn_fwd_prepped"):
         assert n in names
 
 
@@ -62,7 +62,7 @@ def test_library_has_no_oracle_dependency(L):
 
 
 def test_version_and_status_strings(L):
-    assert sfa.lssar_version() == 100
+    assert sfa.lssar_version() == 200
     assert sfa.lssar_status_str(0) == "ok"
     for st in (-1, -2, -3, -4, 7):
         s = sfa.lssar_status_str(st)
@@ -71,13 +71,17 @@ def test_version_and_status_strings(L):
 
 
 def test_workspace_bytes(L):
-    assert sfa.lssar_workspace_bytes(1, 12, 8192, 64, sfa.LSSAR_BF16) == 4 * 12 * 8192
+    # fp32: one fp32 factor per key row, rounded up to 256 bytes
     assert sfa.lssar_workspace_bytes(1, 1, 1, 64, sfa.LSSAR_F32) == 256
     assert sfa.lssar_workspace_bytes(2, 3, 5, 128, sfa.LSSAR_F32) == 256
     assert sfa.lssar_workspace_bytes(1, 1, 100, 64, sfa.LSSAR_F32) == 512
+    # bf16: plus V^T with rows padded to a multiple of 64 keys
+    assert sfa.lssar_workspace_bytes(1, 12, 8192, 64, sfa.LSSAR_BF16) == 4 * 12 * 8192 + 12 * 64 * 8192 * 2
+    assert sfa.lssar_workspace_bytes(2, 3, 77, 128, sfa.LSSAR_BF16) == 2048 + 6 * 128 * 128 * 2
     assert sfa.lssar_workspace_bytes(0, 1, 1, 64, 0) == 0
     assert sfa.lssar_workspace_bytes(1, 1, 1, 96, 0) == 0
     assert sfa.lssar_workspace_bytes(1, 1, 1, 64, 5) == 0
+    assert sfa.lssar_workspace_bytes(1, 1, (1 << 22) + 1, 64, 1) == 0
 
 
 def _fwd_ws(L, q=A, k=A + STEP, v=A + 2 * STEP, o=A + 3 * STEP, B=1, H=2, Ln=64, d=64, p=3,
@@ -101,7 +105,7 @@ def _fwd_ws(L, q=A, k=A + STEP, v=A + 2 * STEP, o=A + 3 * STEP, B=1, H=2, Ln=64,
     (dict(d=32), sfa.LSSAR_EUNSUPPORTED),
     (dict(dt=2), sfa.LSSAR_EUNSUPPORTED),
     (dict(p=1025), sfa.LSSAR_EUNSUPPORTED),
-    (dict(Ln=(1 << 24) + 1), sfa.LSSAR_EUNSUPPORTED),
+    (dict(Ln=(1 << 22) + 1), sfa.LSSAR_EUNSUPPORTED),
     (dict(q=A + 8), sfa.LSSAR_EINVAL),                        # misaligned
     (dict(o=A + 64), sfa.LSSAR_EINVAL),                       # out overlaps q
     (dict(o=A + STEP + 2 * 64 * 64), sfa.LSSAR_EINVAL),       # out overlaps k
@@ -109,6 +113,7 @@ def _fwd_ws(L, q=A, k=A + STEP, v=A + 2 * STEP, o=A + 3 * STEP, B=1, H=2, Ln=64,
     (dict(ws=0), sfa.LSSAR_EWORKSPACE),
     (dict(ws=A + 4 * STEP + 16), sfa.LSSAR_EWORKSPACE),       # not 256-aligned
     (dict(wsb=100), sfa.LSSAR_EWORKSPACE),                    # too small
+    (dict(ws=A + 3 * STEP - 256), sfa.LSSAR_EWORKSPACE),      # overlaps out
     (dict(ws=A + STEP + 256), sfa.LSSAR_EWORKSPACE),          # overlaps k
 ])
 def test_validation_before_any_hip_call(L, kw, want):
@@ -123,17 +128,21 @@ def test_allocating_entry_validates(L):
 
 
 def test_stage_entries_validate(L):
-    # key norms: null k, bad d, fk null / misaligned / overlapping k
-    assert L.lssar_key_inv_norms(0, A, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EINVAL
-    assert L.lssar_key_inv_norms(A, A + STEP, 1, 1, 8, 72, 1, None) == sfa.LSSAR_EUNSUPPORTED
-    assert L.lssar_key_inv_norms(A, 0, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
-    assert L.lssar_key_inv_norms(A, A + STEP + 4, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
-    assert L.lssar_key_inv_norms(A, A + 16, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
-    # prenormed: same checks as the fused call plus fk
-    args = [A, A + STEP, A + 2 * STEP]
-    assert L.lssar_attn_fwd_prenormed(*args, 0, A + 3 * STEP, 1, 1, 8, 64, 3, 1e-4, 1,
-                                      None) == sfa.LSSAR_EWORKSPACE
-    assert L.lssar_attn_fwd_prenormed(*args, A + 4 * STEP, A + 3 * STEP, 1, 1, 8, 64, 0, 1e-4, 1,
-                                      None) == sfa.LSSAR_EINVAL
-    assert L.lssar_attn_fwd_prenormed(*args, A + 3 * STEP + 64, A + 3 * STEP, 1, 1, 8, 64, 3,
-                                      1e-4, 1, None) == sfa.LSSAR_EWORKSPACE
+    k, v, ws = A, A + STEP, A + 4 * STEP
+    # prep: null k/v, bad d, bad workspace (null, misaligned, small, overlapping)
+    assert L.lssar_prep(0, v, ws, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EINVAL
+    assert L.lssar_prep(k, 0, ws, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EINVAL
+    assert L.lssar_prep(k, v, ws, 1 << 20, 1, 1, 8, 72, 1, None) == sfa.LSSAR_EUNSUPPORTED
+    assert L.lssar_prep(k, v, 0, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
+    assert L.lssar_prep(k, v, ws + 16, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
+    assert L.lssar_prep(k, v, ws, 64, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
+    assert L.lssar_prep(k, v, v - 256, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
+    # prepped: the fused-call checks plus the workspace
+    q, o = A + 2 * STEP, A + 3 * STEP
+    assert L.lssar_attn_fwd_prepped(q, k, v, 0, 1 << 20, o, 1, 1, 8, 64, 3, 1e-4, 1,
+                                    None) == sfa.LSSAR_EWORKSPACE
+    assert L.lssar_attn_fwd_prepped(q, k, v, ws, 1 << 20, o, 1, 1, 8, 64, 0, 1e-4, 1,
+                                    None) == sfa.LSSAR_EINVAL
+    assert L.lssar_attn_fwd_prepped(q, k, v, o, 1 << 20, o, 1, 1, 8, 64, 3, 1e-4, 1,
+                                    None) == sfa.LSSAR_EWORKSPACE
+    assert sfa.lssar_last_hip_error() == 0

@@ -164,10 +164,10 @@ def test_bitwise_determinism_and_entry_points_agree():
     a = run_ws(q, k, v, 15)
     b = run_ws(q, k, v, 15)
     c = sfa.lssar_attn_fwd(q, k, v, p=15)
-    fk = torch.empty(4 * 1500, dtype=torch.float32, device=q.device)
-    sfa.lssar_key_inv_norms(k, fk)
+    ws = sfa.workspace_for(q)
+    sfa.lssar_prep(k, v, ws)
     d = torch.empty_like(q)
-    sfa.lssar_attn_fwd_prenormed(q, k, v, fk, d, p=15)
+    sfa.lssar_attn_fwd_prepped(q, k, v, ws, d, p=15)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         e = run_ws(q, k, v, 15, stream=s)
@@ -177,18 +177,36 @@ def test_bitwise_determinism_and_entry_points_agree():
         assert torch.equal(a.view(torch.int16), t.view(torch.int16))
 
 
-def test_key_inv_norms():
+def test_prep_workspace_contents():
+    """Stage 1 writes 1/max(|k_j|, 1e-12) per key row and, for bf16, V^T with
+    every 64-key block permuted for the attention kernel, zero past L."""
     import softmax_free_attention_amd as sfa
     for dtype, d in (("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)):
-        inp = gen.make_inputs("gpt2s", B=2, H=3, L=77, d=d, dtype=dtype, seed=9)
+        L = 77
+        inp = gen.make_inputs("gpt2s", B=2, H=3, L=L, d=d, dtype=dtype, seed=9)
         k = inp.k.copy()
         k[0, 0, 5] = 0.0
-        kt = to_device(k, dtype)
-        fk = torch.empty(2 * 3 * 77, dtype=torch.float32, device=kt.device)
-        sfa.lssar_key_inv_norms(kt, fk)
+        kt, vt = to_device(k, dtype), to_device(inp.v, dtype)
+        ws = sfa.workspace_for(kt)
+        sfa.lssar_prep(kt, vt, ws)
+        torch.cuda.synchronize()
+        raw = ws.cpu().numpy()
+        nrow = 2 * 3 * L
+        fk = raw[:4 * nrow].view(np.float32).reshape(2, 3, L)
         want = 1.0 / np.maximum(np.linalg.norm(k.astype(np.float64), axis=-1), 1e-12)
-        got = fk.cpu().numpy().reshape(2, 3, 77)
-        assert np.max(np.abs(got / want - 1.0)) < 1e-6
+        assert np.max(np.abs(fk / want - 1.0)) < 1e-6
+        if dtype == "bf16":
+            Lp = 128
+            off = (4 * nrow + 255) // 256 * 256
+            vtt = raw[off:off + 2 * 3 * d * Lp * 2].view(np.uint16).reshape(2, 3, d, Lp)
+            vtt = (vtt.astype(np.uint32) << 16).view(np.float32)
+            # position pos of block kb holds key 32c + 16h + 4g + r for
+            # pos = 32c + 8g + 4h + r
+            pos = np.arange(Lp)
+            key = (pos & ~63) + (pos & 32) + ((pos >> 2) & 1) * 16 + ((pos >> 3) & 3) * 4 + (pos & 3)
+            vp = np.zeros((2, 3, Lp, d), np.float32)
+            vp[:, :, :L] = inp.v
+            assert np.array_equal(vtt, np.swapaxes(vp[:, :, key], -1, -2))
 
 
 def test_causality_and_scale_invariance():

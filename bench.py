@@ -75,15 +75,24 @@ def upload(inp):
     return out
 
 
-def time_path(q, k, v, p, steps, warmup, eps=1e-4):
+def time_path(q, k, v, p, steps, warmup, eps=1e-4, settle_s=0.0):
     """Run warmup + timed steps; returns (wall_s, fwd_ms_mean, prep_ms_mean).
     A step is lssar_prep then lssar_attn_fwd_prepped (what lssar_attn_fwd_ws
-    launches), with HIP events recorded between them on the launch stream."""
+    launches), with HIP events recorded between them on the launch stream.
+    Before the warmup steps the same step runs untimed for settle_s seconds:
+    the GPU clock needs a couple of seconds of load to reach its steady
+    state, and a few milliseconds of warmup alone would time the ramp."""
     import torch
     import softmax_free_attention_amd as sfa
     ws = sfa.workspace_for(q)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            sfa.lssar_prep(k, v, ws, stream=stream)
+            sfa.lssar_attn_fwd_prepped(q, k, v, ws, out, p=p, eps=eps, stream=stream)
+        torch.cuda.synchronize()
     for _ in range(warmup):
         sfa.lssar_prep(k, v, ws, stream=stream)
         sfa.lssar_attn_fwd_prepped(q, k, v, ws, out, p=p, eps=eps, stream=stream)
@@ -144,7 +153,7 @@ def sweep(steps, warmup):
         shape = (B, 12, L, 64)
         q, k, v = (torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
                    .to(torch.bfloat16) for _ in range(3))
-        wall, fwd, prep = time_path(q, k, v, 15, steps, warmup)
+        wall, fwd, prep = time_path(q, k, v, 15, steps, warmup, settle_s=0.3)
         flops = 4 * 64 * B * 12 * L * (L + 1) // 2
         res[str(L)] = {"B": B, "tflops": round(flops * steps / wall / 1e12, 2),
                        "kernel_tflops": round(flops / (fwd * 1e-3) / 1e12, 2),
@@ -162,6 +171,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--calib-mib", type=int, default=0,
+                    help="after timing, run a plain elementwise copy of this many MiB (read N, "
+                         "write N), the reference kernel for scaling rocprofv3 FETCH/WRITE_SIZE")
+    ap.add_argument("--settle-seconds", type=float, default=3.0,
+                    help="untimed load before the warmup steps, for the GPU clock to settle")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -184,7 +198,8 @@ def main():
     inp = gen.make_inputs(wl)
     q, k, v = upload(inp)
     log(f"bench: timing {args.steps} steps after {args.warmup} warmup")
-    wall, fwd_ms, prep_ms = time_path(q, k, v, wl.p, args.steps, args.warmup)
+    wall, fwd_ms, prep_ms = time_path(q, k, v, wl.p, args.steps, args.warmup,
+                                      settle_s=args.settle_seconds)
     flops = wl.flops
     value = flops * args.steps / wall / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
@@ -205,6 +220,13 @@ def main():
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 5), "traffic": traffic},
     }
+    if args.calib_mib > 0:
+        n = args.calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.add(src, 0.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_sweep:
         log("bench: L sweep")
         line["sweep"] = sweep(steps=10, warmup=3)

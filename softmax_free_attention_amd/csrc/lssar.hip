@@ -122,11 +122,12 @@ void launch_knorm(const void* k, float* fk, long nrows, hipStream_t s)
 }
 
 template <int D>
-void launch_vt(const void* v, void* vt, int BH, int L, int Lp, hipStream_t s)
+void launch_prep_bf16(const void* k, const void* v, float* fk, void* vt, int BH, int L, int Lp,
+                      hipStream_t s)
 {
-    hipLaunchKernelGGL((lssar::lssar_vt_kernel<D>), dim3(Lp / lssar::kBK, BH),
-                       dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(v),
-                       static_cast<__bf16*>(vt), L, Lp);
+    hipLaunchKernelGGL((lssar::lssar_prep_bf16_kernel<D>), dim3(Lp / lssar::kBK, BH),
+                       dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(k),
+                       static_cast<const __bf16*>(v), fk, static_cast<__bf16*>(vt), L, Lp);
 }
 
 int run_prep(const void* k, const void* v, void* ws, int B, int H, int L, int d, int dtype,
@@ -137,13 +138,10 @@ int run_prep(const void* k, const void* v, void* ws, int B, int H, int L, int d,
     const long nrows = (long)B * H * L;
     if (dtype == LSSAR_BF16) {
         void* vt = static_cast<unsigned char*>(ws) + w.fk_bytes;
-        if (d == 64) {
-            launch_knorm<__bf16, 64>(k, fk, nrows, s);
-            launch_vt<64>(v, vt, B * H, L, w.Lp, s);
-        } else {
-            launch_knorm<__bf16, 128>(k, fk, nrows, s);
-            launch_vt<128>(v, vt, B * H, L, w.Lp, s);
-        }
+        if (d == 64)
+            launch_prep_bf16<64>(k, v, fk, vt, B * H, L, w.Lp, s);
+        else
+            launch_prep_bf16<128>(k, v, fk, vt, B * H, L, w.Lp, s);
     } else {
         if (d == 64)
             launch_knorm<float, 64>(k, fk, nrows, s);

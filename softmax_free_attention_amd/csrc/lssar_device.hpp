@@ -171,6 +171,18 @@ __device__ __forceinline__ double query_factor(double lam_scale, int i, double s
     return lam_scale * log((double)i) / fmax(sqrt(ss), 1e-12);
 }
 
+// Workgroup -> work-item map that keeps each XCD on a contiguous slice of the
+// work.  Workgroups are dispatched round-robin over the 8 XCDs (workgroup w
+// runs on XCD w % 8), and each XCD has its own L2; item order is head-major,
+// so the heads whose K and V an XCD reads stay few and stay in its L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_item(int w, int n)
+{
+    const int x = w % kXcds, local = w / kXcds;
+    const int per = n / kXcds, rem = n % kXcds;
+    return x * per + min(x, rem) + local;
+}
+
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
@@ -230,18 +242,47 @@ __device__ __forceinline__ int vt_key(int pos)
     return (pos & 32) + (((pos >> 2) & 1) << 4) + (((pos >> 3) & 3) << 2) + (pos & 3);
 }
 
-// V^T for the bf16 kernel: Vt[bh][e][kb*64 + vt_pos(j)] = V[bh][kb*64 + j][e]
-// for each 64-key block kb, zero for keys >= L; rows of Vt have Lp (L rounded
-// up to 64) entries.  One workgroup per (64-key block, head).
+// Prep for the bf16 kernel, one workgroup per (64-key block kb, head bh):
+//  * fk[bh*L + j] = 1 / max(|k_j|_2, 1e-12) for the block's keys (fp64 sum);
+//  * Vt[bh][e][kb*64 + vt_pos(j)] = V[bh][kb*64 + j][e], zero for keys >= L;
+//    rows of Vt hold Lp (L rounded up to 64) entries.
+// V goes through LDS: each thread then gathers two adjacent dims of 8 keys
+// with 4-byte LDS reads and writes two 16-byte pieces of V^T.
 template <int D>
-__global__ __launch_bounds__(kThreads) void lssar_vt_kernel(const __bf16* __restrict__ V,
-                                                            __bf16* __restrict__ Vt, int L,
-                                                            int Lp)
+__global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
+    const __bf16* __restrict__ K, const __bf16* __restrict__ V, float* __restrict__ fk,
+    __bf16* __restrict__ Vt, int L, int Lp)
 {
-    constexpr int RS = D + 8;                  // LDS row stride (elements)
-    __shared__ __attribute__((aligned(16))) __bf16 tile[64 * RS];
+    constexpr int RS = D + 2;                  // LDS row stride (elements), odd word count
+    constexpr int LPR = D / 8;                 // lanes per key row for the norms
+    __shared__ __attribute__((aligned(16))) uint32_t tile[64 * RS / 2];
     const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-    const __bf16* Vh = V + (size_t)bh * L * D;
+    const size_t hoff = (size_t)bh * L * D;
+
+    // key norms: 64 rows x LPR lanes, 16 bytes per lane per step
+#pragma unroll
+    for (int n = 0; n < 64 * LPR / kThreads; ++n) {
+        const int c = tid + n * kThreads;
+        const int key = c / LPR, sub = c % LPR;
+        const int kg = kb * 64 + key;
+        double ss = 0.0;
+        if (kg < L) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(K + hoff + (size_t)kg * D + sub * 8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const double x = bf16lo(w[e]), y = bf16hi(w[e]);
+                ss = fma(x, x, ss);
+                ss = fma(y, y, ss);
+            }
+        }
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1)
+            ss += __shfl_xor(ss, m, LPR);
+        if (kg < L && sub == 0)
+            fk[(size_t)bh * L + kg] = (float)(1.0 / fmax(sqrt(ss), 1e-12));
+    }
+
+    // V block -> LDS (row stride RS elements: 4-byte aligned rows)
 #pragma unroll
     for (int n = 0; n < 64 * D / 8 / kThreads; ++n) {
         const int c = tid + n * kThreads;
@@ -249,24 +290,30 @@ __global__ __launch_bounds__(kThreads) void lssar_vt_kernel(const __bf16* __rest
         const int kg = kb * 64 + key;
         u32x4 w = {0u, 0u, 0u, 0u};
         if (kg < L)
-            w = *reinterpret_cast<const u32x4*>(Vh + (size_t)kg * D + col8 * 8);
-        *reinterpret_cast<u32x4*>(&tile[key * RS + col8 * 8]) = w;
+            w = *reinterpret_cast<const u32x4*>(V + hoff + (size_t)kg * D + col8 * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            tile[(key * RS + col8 * 8) / 2 + e] = w[e];
     }
     __syncthreads();
-    const unsigned short* t16 = reinterpret_cast<const unsigned short*>(tile);
+    // V^T: thread -> dims (2m, 2m+1), positions 8 p8 .. 8 p8 + 7
     __bf16* Vth = Vt + (size_t)bh * D * Lp;
 #pragma unroll
-    for (int n = 0; n < D * 8 / kThreads; ++n) {
+    for (int n = 0; n < (D / 2) * 8 / kThreads; ++n) {
         const int c = tid + n * kThreads;
-        const int e = c / 8, p8 = c % 8;       // V^T row e, positions 8 p8 .. 8 p8 + 7
-        u32x4 w;
+        const int m = c / 8, p8 = c % 8;
+        uint32_t wv[8];
+#pragma unroll
+        for (int h = 0; h < 8; ++h)
+            wv[h] = tile[(vt_key(8 * p8 + h) * RS) / 2 + m];     // (v[key][2m], v[key][2m+1])
+        u32x4 lo, hi;
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-            const uint32_t lo = t16[vt_key(8 * p8 + 2 * h) * RS + e];
-            const uint32_t hi = t16[vt_key(8 * p8 + 2 * h + 1) * RS + e];
-            w[h] = lo | (hi << 16);
+            lo[h] = __builtin_amdgcn_perm(wv[2 * h + 1], wv[2 * h], 0x05040100u);
+            hi[h] = __builtin_amdgcn_perm(wv[2 * h + 1], wv[2 * h], 0x07060302u);
         }
-        *reinterpret_cast<u32x4*>(Vth + (size_t)e * Lp + kb * 64 + 8 * p8) = w;
+        *reinterpret_cast<u32x4*>(Vth + (size_t)(2 * m) * Lp + kb * 64 + 8 * p8) = lo;
+        *reinterpret_cast<u32x4*>(Vth + (size_t)(2 * m + 1) * Lp + kb * 64 + 8 * p8) = hi;
     }
 }
 
@@ -349,8 +396,9 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int row16 = lane & 15, grp = lane >> 4;
-    const int pi = (int)(blockIdx.x / BH);
-    const int bh = (int)(blockIdx.x % BH);
+    const int item = xcd_item((int)blockIdx.x, npair * BH);
+    const int bh = item / npair;
+    const int pi = item % npair;
     const size_t hoff = (size_t)bh * L * D;
     const __bf16* Qh = Q + hoff;
     __bf16* Oh = O + hoff;
@@ -490,8 +538,8 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     pos_sum += fmaxf(t[r], 0.0f);
-                tmax = fmaxf(tmax, fmaxf(t[0], t[1]));
-                tmax = fmaxf(tmax, fmaxf(t[2], t[3]));
+                tmax = fmaxf(fmaxf(tmax, t[0]), t[1]);
+                tmax = fmaxf(fmaxf(tmax, t[2]), t[3]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     prod = __builtin_fmaf(prod, u[r], prod);

@@ -20,13 +20,15 @@ SRC = os.path.join(HERE, "lssar_ref.c")
 LIB = os.path.join(HERE, "liblssar_ref.so")
 
 DEFAULT_EPS = 1e-4
+PHI_SOFTPLUS = 0
+PHI_SIGMOID = 1
 
 _lib = None
 
 
 def build(src: str = SRC, out: str = LIB) -> str:
     """Compile the oracle with gcc (fp64, OpenMP, no fast-math)."""
-    tmp = out + ".tmp"
+    tmp = f"{out}.{os.getpid()}.tmp"
     subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
                     "-o", tmp, src, "-lm"], check=True)
     os.replace(tmp, out)
@@ -55,6 +57,14 @@ def _bind(lib):
                                             ctypes.c_int, ctypes.c_double, ip,
                                             ctypes.c_int, dp, ctypes.c_int]
     lib.lssar_ref_head_rows_f64.restype = ctypes.c_int
+    lib.lssar_ref_fwd_ex_f64.argtypes = [dp, dp, dp, dp] + [ctypes.c_int] * 5 + [
+        ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.lssar_ref_fwd_ex_f64.restype = ctypes.c_int
+    lib.lssar_ref_head_rows_ex_f64.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_double, ctypes.c_int,
+                                               ctypes.c_int, ip, ctypes.c_int, dp,
+                                               ctypes.c_int]
+    lib.lssar_ref_head_rows_ex_f64.restype = ctypes.c_int
     lib.lssar_ref_threads.argtypes = [ctypes.c_int]
     lib.lssar_ref_threads.restype = ctypes.c_int
     return lib
@@ -69,8 +79,10 @@ def _ptr(a: np.ndarray, t=ctypes.c_double):
 
 
 def lssar_fwd(q, k, v, p: int, eps: float = DEFAULT_EPS, nthreads: int = 0,
-              lib=None) -> np.ndarray:
-    """Oracle forward on [B,H,L,d] (or [L,d]) inputs; returns fp64 output."""
+              lib=None, phi: int = PHI_SOFTPLUS, reweight: bool = True) -> np.ndarray:
+    """Oracle forward on [B,H,L,d] (or [L,d]) inputs; returns fp64 output.
+    ``phi`` picks the stage-1 map (Softplus, or the ablation's Sigmoid);
+    ``reweight=False`` stops after stage 1 (the ablation's LSSA only)."""
     lib = lib or load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     squeeze = q.ndim == 2
@@ -79,26 +91,28 @@ def lssar_fwd(q, k, v, p: int, eps: float = DEFAULT_EPS, nthreads: int = 0,
     B, H, L, d = q.shape
     assert k.shape == q.shape and v.shape == q.shape
     out = np.empty_like(q)
-    rc = lib.lssar_ref_fwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, L, d,
-                               int(p), float(eps), int(nthreads))
+    rc = lib.lssar_ref_fwd_ex_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, L, d,
+                                  int(p), float(eps), int(phi), int(bool(reweight)),
+                                  int(nthreads))
     if rc != 0:
-        raise ValueError(f"lssar_ref_fwd_f64 failed with status {rc}")
+        raise ValueError(f"lssar_ref_fwd_ex_f64 failed with status {rc}")
     return out[0, 0] if squeeze else out
 
 
 def lssar_rows(q, k, v, rows, p: int, eps: float = DEFAULT_EPS, nthreads: int = 0,
-               lib=None) -> np.ndarray:
+               lib=None, phi: int = PHI_SOFTPLUS, reweight: bool = True) -> np.ndarray:
     """Oracle output for chosen 0-based query rows of ONE head ([L,d] inputs)."""
     lib = lib or load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     L, d = q.shape
     r = np.ascontiguousarray(rows, dtype=np.int32)
     out = np.empty((len(r), d), dtype=np.float64)
-    rc = lib.lssar_ref_head_rows_f64(_ptr(q), _ptr(k), _ptr(v), L, d, int(p),
-                                     float(eps), _ptr(r, ctypes.c_int), len(r),
-                                     _ptr(out), int(nthreads))
+    rc = lib.lssar_ref_head_rows_ex_f64(_ptr(q), _ptr(k), _ptr(v), L, d, int(p),
+                                        float(eps), int(phi), int(bool(reweight)),
+                                        _ptr(r, ctypes.c_int), len(r), _ptr(out),
+                                        int(nthreads))
     if rc != 0:
-        raise ValueError(f"lssar_ref_head_rows_f64 failed with status {rc}")
+        raise ValueError(f"lssar_ref_head_rows_ex_f64 failed with status {rc}")
     return out
 
 

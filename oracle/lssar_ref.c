@@ -42,6 +42,16 @@
  *   R11 Square causal self-attention, one K/V head per Q head; q, k are the
  *       post-RoPE vectors.
  *
+ * Two variants from the note's ablation table (section Key experimental
+ * data, ablation), selected by arguments of the _ex entry points:
+ *   R12 phi = Sigmoid ("Sigmoid + L1 + re-weighting"): the non-negative map
+ *       of Key design 1 becomes the logistic sigmoid 1/(1 + e^-x); the
+ *       scores, mask, both L1 normalisations, N, O and ReLU^p stay as above.
+ *   R13 LSSA only ("LSSA only, no re-weighting"; also the main-results row
+ *       "LSSA, normalisation stage only"): stage 1, then out = A V; p and
+ *       eps play no part and no row is degenerate (every A_ij with j <= i
+ *       is positive).
+ *
  * Build: gcc -O2 -fopenmp -shared -fPIC lssar_ref.c -lm (no -ffast-math).
  */
 #include "lssar_ref.h"
@@ -60,6 +70,21 @@ static double softplus(double x)
     if (x > 0.0)
         return x + log1p(exp(-x));
     return log1p(exp(x));
+}
+
+/* Logistic sigmoid 1/(1 + e^-x) (R12), evaluated without overflow. */
+static double sigmoid(double x)
+{
+    if (x >= 0.0)
+        return 1.0 / (1.0 + exp(-x));
+    const double e = exp(x);
+    return e / (1.0 + e);
+}
+
+/* The non-negative map of stage 1: Softplus (R4) or Sigmoid (R12). */
+static double phi_fn(int phi, double x)
+{
+    return phi == LSSAR_REF_PHI_SIGMOID ? sigmoid(x) : softplus(x);
 }
 
 /* x^p by repeated multiplication (R9: integer p >= 1). */
@@ -87,15 +112,16 @@ static void l2_normalise(const double* x, double* y, int d)
 /* One output row.  qh: the normalised query row i (0-based row = i-1);
  * kh: all L normalised key rows of the head; v: the head's V; a: scratch of
  * L doubles.  Every j in 1..L is computed and then multiplied by the mask
- * M'_ij, as the matrix form on the page does. */
+ * M'_ij, as the matrix form on the page does.  phi picks the stage-1 map
+ * (R4/R12); reweight = 0 skips stage 2 (R13). */
 static void lssar_row(const double* qh, const double* kh, const double* v,
-                      int L, int d, int p, double eps, int row,
-                      double* a, double* out)
+                      int L, int d, int p, double eps, int phi, int reweight,
+                      int row, double* a, double* out)
 {
     const int i = row + 1;                       /* R2: 1-based row index */
     const double scale = log((double)d) * log((double)i);   /* log d . log N_ij, R1 */
 
-    /* Stage 1 (Key design 1): A_ij = Softplus(scale * q^_i . k^_j) * M'_ij */
+    /* Stage 1 (Key design 1): A_ij = phi(scale * q^_i . k^_j) * M'_ij */
     double l1 = 0.0;
     for (int j = 1; j <= L; ++j) {
         const double* kj = kh + (size_t)(j - 1) * d;
@@ -103,32 +129,34 @@ static void lssar_row(const double* qh, const double* kh, const double* v,
         for (int e = 0; e < d; ++e)
             dot += qh[e] * kj[e];
         double mask = (j <= i) ? 1.0 : 0.0;     /* M': lower triangle = 1 (R5) */
-        a[j - 1] = softplus(scale * dot) * mask;
+        a[j - 1] = phi_fn(phi, scale * dot) * mask;
         l1 += a[j - 1];
     }
     for (int j = 0; j < L; ++j)                  /* A_i <- A_i / |A_i|_1 */
         a[j] /= l1;
 
-    /* Stage 2 (Key design 2): A <- ReLU^p(A * N - O), then L1 again */
-    const double o = (i <= 3) ? 0.0 : 1.0;       /* O: first 3 rows zero (R7) */
-    double m = -INFINITY;
-    for (int j = 0; j < L; ++j) {
-        a[j] = a[j] * (double)i - o;             /* A (.) N - O */
-        if (a[j] > m)
-            m = a[j];
+    if (reweight) {
+        /* Stage 2 (Key design 2): A <- ReLU^p(A * N - O), then L1 again */
+        const double o = (i <= 3) ? 0.0 : 1.0;       /* O: first 3 rows zero (R7) */
+        double m = -INFINITY;
+        for (int j = 0; j < L; ++j) {
+            a[j] = a[j] * (double)i - o;             /* A (.) N - O */
+            if (a[j] > m)
+                m = a[j];
+        }
+        if (!(m > eps)) {                            /* degenerate row (R10) */
+            memset(out, 0, sizeof(double) * (size_t)d);
+            return;
+        }
+        double l1b = 0.0;
+        for (int j = 0; j < L; ++j) {
+            double r = a[j] > 0.0 ? a[j] : 0.0;      /* ReLU */
+            a[j] = ipow(r, p);                       /* ^p */
+            l1b += a[j];
+        }
+        for (int j = 0; j < L; ++j)                  /* A_i <- A_i / |A_i|_1 */
+            a[j] /= l1b;
     }
-    if (!(m > eps)) {                            /* degenerate row (R10) */
-        memset(out, 0, sizeof(double) * (size_t)d);
-        return;
-    }
-    double l1b = 0.0;
-    for (int j = 0; j < L; ++j) {
-        double r = a[j] > 0.0 ? a[j] : 0.0;      /* ReLU */
-        a[j] = ipow(r, p);                       /* ^p */
-        l1b += a[j];
-    }
-    for (int j = 0; j < L; ++j)                  /* A_i <- A_i / |A_i|_1 */
-        a[j] /= l1b;
 
     /* Attention output (Key design 3): out_i = sum_j A_ij v_j */
     for (int e = 0; e < d; ++e)
@@ -141,9 +169,11 @@ static void lssar_row(const double* qh, const double* kh, const double* v,
 }
 
 static int bad_args(const void* q, const void* k, const void* v, const void* out,
-                    int L, int d, int p, double eps)
+                    int L, int d, int p, double eps, int phi, int reweight)
 {
-    return !q || !k || !v || !out || L < 1 || d < 1 || p < 1 || !(eps >= 0.0);
+    return !q || !k || !v || !out || L < 1 || d < 1 || p < 1 || !(eps >= 0.0) ||
+           (phi != LSSAR_REF_PHI_SOFTPLUS && phi != LSSAR_REF_PHI_SIGMOID) ||
+           (reweight != 0 && reweight != 1);
 }
 
 int lssar_ref_threads(int nthreads)
@@ -166,12 +196,13 @@ static void normalise_head(const double* q, const double* k, double* qh,
     }
 }
 
-int lssar_ref_head_rows_f64(const double* q, const double* k, const double* v,
-                            int L, int d, int p, double eps,
-                            const int* rows, int nrows, double* out,
-                            int nthreads)
+int lssar_ref_head_rows_ex_f64(const double* q, const double* k, const double* v,
+                               int L, int d, int p, double eps, int phi,
+                               int reweight, const int* rows, int nrows,
+                               double* out, int nthreads)
 {
-    if (bad_args(q, k, v, out, L, d, p, eps) || nrows < 0 || (nrows && !rows))
+    if (bad_args(q, k, v, out, L, d, p, eps, phi, reweight) || nrows < 0 ||
+        (nrows && !rows))
         return -1;
     for (int r = 0; r < nrows; ++r)
         if (rows[r] < 0 || rows[r] >= L)
@@ -194,8 +225,8 @@ int lssar_ref_head_rows_f64(const double* q, const double* k, const double* v,
         } else {
 #pragma omp for schedule(dynamic, 1)
             for (int r = 0; r < nrows; ++r)
-                lssar_row(qh + (size_t)rows[r] * d, kh, v, L, d, p, eps, rows[r],
-                          a, out + (size_t)r * d);
+                lssar_row(qh + (size_t)rows[r] * d, kh, v, L, d, p, eps, phi,
+                          reweight, rows[r], a, out + (size_t)r * d);
         }
         free(a);
     }
@@ -204,11 +235,11 @@ int lssar_ref_head_rows_f64(const double* q, const double* k, const double* v,
     return fail ? -2 : 0;
 }
 
-int lssar_ref_fwd_f64(const double* q, const double* k, const double* v,
-                      double* out, int B, int H, int L, int d, int p,
-                      double eps, int nthreads)
+int lssar_ref_fwd_ex_f64(const double* q, const double* k, const double* v,
+                         double* out, int B, int H, int L, int d, int p,
+                         double eps, int phi, int reweight, int nthreads)
 {
-    if (bad_args(q, k, v, out, L, d, p, eps) || B < 1 || H < 1)
+    if (bad_args(q, k, v, out, L, d, p, eps, phi, reweight) || B < 1 || H < 1)
         return -1;
     const size_t head = (size_t)L * d;
     const long nheads = (long)B * H;
@@ -238,7 +269,7 @@ int lssar_ref_fwd_f64(const double* q, const double* k, const double* v,
                 long bh = t / L;
                 int row = (int)(t % L);
                 lssar_row(qh + bh * head + (size_t)row * d, kh + bh * head,
-                          v + bh * head, L, d, p, eps, row, a,
+                          v + bh * head, L, d, p, eps, phi, reweight, row, a,
                           out + bh * head + (size_t)row * d);
             }
         }
@@ -247,4 +278,21 @@ int lssar_ref_fwd_f64(const double* q, const double* k, const double* v,
     free(qh);
     free(kh);
     return fail ? -2 : 0;
+}
+
+int lssar_ref_head_rows_f64(const double* q, const double* k, const double* v,
+                            int L, int d, int p, double eps,
+                            const int* rows, int nrows, double* out,
+                            int nthreads)
+{
+    return lssar_ref_head_rows_ex_f64(q, k, v, L, d, p, eps, LSSAR_REF_PHI_SOFTPLUS,
+                                      1, rows, nrows, out, nthreads);
+}
+
+int lssar_ref_fwd_f64(const double* q, const double* k, const double* v,
+                      double* out, int B, int H, int L, int d, int p,
+                      double eps, int nthreads)
+{
+    return lssar_ref_fwd_ex_f64(q, k, v, out, B, H, L, d, p, eps,
+                                LSSAR_REF_PHI_SOFTPLUS, 1, nthreads);
 }

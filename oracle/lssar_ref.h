@@ -37,6 +37,23 @@ int lssar_ref_head_rows_f64(const double* q, const double* k, const double* v,
                             const int* rows, int nrows, double* out,
                             int nthreads);
 
+/* Stage-1 map for the _ex entry points: Softplus (the method) or the
+ * logistic Sigmoid of the note's ablation ("Sigmoid + L1 + re-weighting"). */
+enum { LSSAR_REF_PHI_SOFTPLUS = 0, LSSAR_REF_PHI_SIGMOID = 1 };
+
+/* As lssar_ref_fwd_f64 with the stage-1 map phi and reweight = 1 (both
+ * stages) or 0 (stage 1 only, then A V: the ablation's "LSSA only"; p and
+ * eps are then checked but unused).  -1 also for an unknown phi/reweight. */
+int lssar_ref_fwd_ex_f64(const double* q, const double* k, const double* v,
+                         double* out, int B, int H, int L, int d, int p,
+                         double eps, int phi, int reweight, int nthreads);
+
+/* As lssar_ref_head_rows_f64 with phi and reweight as above. */
+int lssar_ref_head_rows_ex_f64(const double* q, const double* k, const double* v,
+                               int L, int d, int p, double eps, int phi,
+                               int reweight, const int* rows, int nrows,
+                               double* out, int nthreads);
+
 /* Number of OpenMP threads a call with this nthreads argument would use. */
 int lssar_ref_threads(int nthreads);
 

@@ -8,7 +8,10 @@ an invariant or a limit, so it does not share the oracle's structure.
 
 Source of the definition: paper note "Softplus Attention with Re-weighting
 Boosts Length Extrapolation in Large Language Models", Method details,
-Key design 1 (LSSA), Key design 2 (re-weighting), Key design 3 (mask).
+Key design 1 (LSSA), Key design 2 (re-weighting), Key design 3 (mask).  The
+two variants of the note's ablation table (Key experimental data, ablation)
+are pinned alongside: the stage-1 map swapped for the logistic Sigmoid, and
+stage 1 alone ("LSSA only").  A pin that holds for a variant runs it too.
 """
 from __future__ import annotations
 
@@ -24,8 +27,22 @@ import oracle
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
-def _fwd(lib, q, k, v, p, eps=oracle.DEFAULT_EPS):
-    return oracle.lssar_fwd(q, k, v, p, eps, nthreads=2, lib=lib)
+SP, SIG = oracle.PHI_SOFTPLUS, oracle.PHI_SIGMOID
+# (phi, reweight): the method, the Sigmoid swap, and stage 1 alone
+MODES = [(SP, True), (SIG, True), (SP, False)]
+RW_MODES = [m for m in MODES if m[1]]
+
+
+def _fwd(lib, q, k, v, p, eps=oracle.DEFAULT_EPS, mode=(SP, True)):
+    return oracle.lssar_fwd(q, k, v, p, eps, nthreads=2, lib=lib, phi=mode[0],
+                            reweight=mode[1])
+
+
+def _phi_mp(phi, x):
+    """Softplus log(1 + e^x), or the logistic sigmoid 1/(1 + e^-x)."""
+    if phi == SIG:
+        return 1 / (1 + mp.exp(-x))
+    return mp.log(1 + mp.exp(x))
 
 
 def _rng(seed):
@@ -36,8 +53,9 @@ def _rng(seed):
 # Brute force: the literal matrix form at 50 digits, tiny L
 # --------------------------------------------------------------------------
 
-def brute_lssar(Q, K, V, p, eps=oracle.DEFAULT_EPS, dps=50):
+def brute_lssar(Q, K, V, p, eps=oracle.DEFAULT_EPS, dps=50, mode=(SP, True)):
     """Matrix form with explicit N, M' and O (Key designs 1-2) in mpmath."""
+    phi, reweight = mode
     with mp.workdps(dps):
         L, d = Q.shape
         Qm = mp.matrix(Q.tolist())
@@ -65,11 +83,15 @@ def brute_lssar(Q, K, V, p, eps=oracle.DEFAULT_EPS, dps=50):
         A = mp.matrix(L, L)
         for i in range(L):
             for j in range(L):
-                A[i, j] = mp.log(1 + mp.exp(mp.log(d) * mp.log(N[i, j]) * S[i, j])) * Mp[i, j]
+                A[i, j] = _phi_mp(phi, mp.log(d) * mp.log(N[i, j]) * S[i, j]) * Mp[i, j]
         for i in range(L):
             s = mp.fsum(abs(A[i, j]) for j in range(L))
             for j in range(L):
                 A[i, j] = A[i, j] / s
+        Vm = mp.matrix(V.tolist())
+        if not reweight:
+            out = A * Vm
+            return np.array([[float(out[i, c]) for c in range(d)] for i in range(L)])
         X = mp.matrix(L, L)
         for i in range(L):
             for j in range(L):
@@ -84,20 +106,20 @@ def brute_lssar(Q, K, V, p, eps=oracle.DEFAULT_EPS, dps=50):
             s = mp.fsum(abs(W[i, j]) for j in range(L))
             for j in range(L):
                 W[i, j] = W[i, j] / s
-        Vm = mp.matrix(V.tolist())
         out = W * Vm
         return np.array([[float(out[i, c]) for c in range(d)] for i in range(L)])
 
 
 def brute_force_matrix_form(lib):
-    for seed, (L, d, p) in enumerate([(1, 4, 3), (5, 4, 1), (7, 8, 2), (9, 6, 3),
-                                      (12, 8, 15), (10, 3, 5)]):
-        r = _rng(100 + seed)
-        Q, K, V = (r.standard_normal((L, d)) for _ in range(3))
-        got = _fwd(lib, Q, K, V, p)
-        want = brute_lssar(Q, K, V, p)
-        err = np.max(np.abs(got - want))
-        assert err < 1e-12, f"brute force L={L} d={d} p={p}: max err {err:.3e}"
+    for mode in MODES:
+        cases = [(1, 4, 3), (5, 4, 1), (7, 8, 2), (9, 6, 3), (12, 8, 15), (10, 3, 5)]
+        for seed, (L, d, p) in enumerate(cases if mode == (SP, True) else cases[1::2]):
+            r = _rng(100 + seed)
+            Q, K, V = (r.standard_normal((L, d)) for _ in range(3))
+            got = _fwd(lib, Q, K, V, p, mode=mode)
+            want = brute_lssar(Q, K, V, p, mode=mode)
+            err = np.max(np.abs(got - want))
+            assert err < 1e-12, f"brute force {mode} L={L} d={d} p={p}: max err {err:.3e}"
 
 
 # --------------------------------------------------------------------------
@@ -112,22 +134,27 @@ def _ortho(d, seed):
 
 def row1_is_v1(lib):
     """Row 1: log 1 = 0 makes its single stage-1 entry 1; o_1 = 0 keeps it."""
-    for seed, (L, d, p) in enumerate([(6, 8, 3), (33, 16, 15), (3, 64, 1)]):
-        r = _rng(200 + seed)
-        Q, K, V = (r.standard_normal((L, d)) for _ in range(3))
-        out = _fwd(lib, Q, K, V, p)
-        assert np.array_equal(out[0], V[0]) or np.max(np.abs(out[0] - V[0])) < 1e-15, \
-            "row 1 must reproduce v_1"
+    for mode in MODES:
+        for seed, (L, d, p) in enumerate([(6, 8, 3), (33, 16, 15), (3, 64, 1)]):
+            r = _rng(200 + seed)
+            Q, K, V = (r.standard_normal((L, d)) for _ in range(3))
+            out = _fwd(lib, Q, K, V, p, mode=mode)
+            assert np.array_equal(out[0], V[0]) or np.max(np.abs(out[0] - V[0])) < 1e-15, \
+                f"row 1 must reproduce v_1 ({mode})"
 
 
-def _closed_form_row(i, d, cos, p, V):
+def _closed_form_row(i, d, cos, p, V, mode=(SP, True)):
     """Expected output of row i (1-based) whose cosines to keys 1..i are
-    ``cos`` (orthonormal keys): sp_j = softplus(ln d ln i c_j); A = sp/sum;
-    w_j = ReLU(i A_j - o_i)^p; out = sum w v / sum w (0 if max <= eps)."""
+    ``cos`` (orthonormal keys): sp_j = phi(ln d ln i c_j); A = sp/sum;
+    w_j = ReLU(i A_j - o_i)^p; out = sum w v / sum w (0 if max <= eps).
+    Stage 1 alone: out = sum A v."""
     with mp.workdps(40):
         lam = mp.log(d) * mp.log(i)
-        sp = [mp.log(1 + mp.exp(lam * mp.mpf(c))) for c in cos]
+        sp = [_phi_mp(mode[0], lam * mp.mpf(c)) for c in cos]
         s1 = mp.fsum(sp)
+        if not mode[1]:
+            return np.array([float(mp.fsum(sp[j] * V[j, c] for j in range(len(sp))) / s1)
+                             for c in range(V.shape[1])])
         o = 0 if i <= 3 else 1
         x = [i * s / s1 - o for s in sp]
         if max(x) <= oracle.DEFAULT_EPS:
@@ -166,15 +193,16 @@ def closed_form_rows(lib):
                 [0.0, 0.7, 0.7, 0.0, 0.1], [0.5] * 3 + [0.1] * 3,
                 [0.9, -0.4, 0.1], [0.2, 0.3, 0.4, 0.5, 0.6],
                 [-0.5, 0.8], [0.1] * 10, [0.95], [0.4, 0.4, 0.4, 0.41]]
-    for p in (1, 3, 15):
-        Q, K, V = _build_rows(L, d, cos_rows, seed=300 + p)
-        out = _fwd(lib, Q, K, V, p)
-        for i in range(2, L + 1):
-            cos = list(cos_rows[i - 1]) + [0.0] * (i - len(cos_rows[i - 1]))
-            cos = cos[:i]
-            want = _closed_form_row(i, d, cos, p, V[:i])
-            err = np.max(np.abs(out[i - 1] - want))
-            assert err < 1e-11, f"closed form row {i} p={p}: err {err:.3e}"
+    for mode in MODES:
+        for p in ((1, 3, 15) if mode[1] else (3,)):
+            Q, K, V = _build_rows(L, d, cos_rows, seed=300 + p)
+            out = _fwd(lib, Q, K, V, p, mode=mode)
+            for i in range(2, L + 1):
+                cos = list(cos_rows[i - 1]) + [0.0] * (i - len(cos_rows[i - 1]))
+                cos = cos[:i]
+                want = _closed_form_row(i, d, cos, p, V[:i], mode)
+                err = np.max(np.abs(out[i - 1] - want))
+                assert err < 1e-11, f"closed form row {i} p={p} {mode}: err {err:.3e}"
 
 
 def golden_row2_value(lib):
@@ -192,21 +220,48 @@ def golden_row2_value(lib):
         assert abs(out[1, 0] - w1) < 5e-7, f"row-2 golden d={d} p={p}: {out[1, 0]} vs {w1}"
 
 
+def sigmoid_antisymmetric_pair(lib):
+    """Sigmoid map, row 2 (o_2 = 0) with cosines +c and -c to two
+    orthonormal keys: sigma(-x) = 1 - sigma(x) makes the re-weighted weight
+    of key 1 exactly sigma(x)^p / (sigma(x)^p + sigma(-x)^p) = 1/(1 + e^(-p x)),
+    x = ln d ln 2 c, so out_2 = w v_1 + (1 - w) v_2."""
+    for d, p, c in [(8, 1, 0.7), (16, 3, 0.3), (64, 15, 0.05), (32, 2, -0.6), (4, 5, 0.7071)]:
+        E = _ortho(d, 1400 + p)
+        K = np.stack([E[0] * 1.7, E[1] * 0.6])
+        u = c * E[0] - c * E[1] + math.sqrt(1.0 - 2.0 * c * c) * E[2]
+        Q = np.stack([E[2], u * 2.5])
+        V = np.stack([np.arange(d, dtype=float), np.full(d, -1.0)])
+        out = _fwd(lib, Q, K, V, p, mode=(SIG, True))
+        x = math.log(d) * math.log(2.0) * c
+        w = 1.0 / (1.0 + math.exp(-p * x))
+        err = np.max(np.abs(out[1] - (w * V[0] + (1.0 - w) * V[1])))
+        assert err < 1e-13, f"sigmoid pair d={d} p={p} c={c}: err {err:.3e}"
+
+
 def onehot_orthonormal(lib):
     """Rows i >= 4, orthonormal keys, q_i along key m(i): out_i = v_m(i)
-    exactly (every other entry has softplus(0) = ln 2, below the row mean)."""
-    for seed, (L, d, p) in enumerate([(16, 32, 3), (31, 32, 15), (40, 64, 1), (20, 64, 2)]):
-        r = _rng(400 + seed)
-        E = _ortho(d, 410 + seed)
-        perm = r.permutation(d)[:L]
-        K = E[perm] * r.uniform(0.5, 3.0, size=(L, 1))
-        mi = [int(r.integers(0, i + 1)) for i in range(L)]
-        Q = np.stack([K[mi[i]] * r.uniform(0.1, 5.0) for i in range(L)])
-        V = r.standard_normal((L, d))
-        out = _fwd(lib, Q, K, V, p)
-        for i in range(3, L):
-            err = np.max(np.abs(out[i] - V[mi[i]]))
-            assert err < 1e-12, f"one-hot row {i + 1} p={p}: err {err:.3e}"
+    exactly (every other entry has phi(0) -- ln 2 for Softplus, 1/2 for
+    Sigmoid -- below the row mean).  Stage 1 alone gives
+    (phi(ln d ln i) v_m + phi(0) sum_(j != m) v_j) / (phi(ln d ln i) + (i-1) phi(0))."""
+    for mode in MODES:
+        for seed, (L, d, p) in enumerate([(16, 32, 3), (31, 32, 15), (40, 64, 1), (20, 64, 2)]):
+            r = _rng(400 + seed)
+            E = _ortho(d, 410 + seed)
+            perm = r.permutation(d)[:L]
+            K = E[perm] * r.uniform(0.5, 3.0, size=(L, 1))
+            mi = [int(r.integers(0, i + 1)) for i in range(L)]
+            Q = np.stack([K[mi[i]] * r.uniform(0.1, 5.0) for i in range(L)])
+            V = r.standard_normal((L, d))
+            out = _fwd(lib, Q, K, V, p, mode=mode)
+            for i in range(3, L):
+                if mode[1]:
+                    want = V[mi[i]]
+                else:
+                    big = math.log1p(math.exp(math.log(d) * math.log(i + 1)))
+                    rest = V[:i + 1].sum(axis=0) - V[mi[i]]
+                    want = (big * V[mi[i]] + math.log(2.0) * rest) / (big + i * math.log(2.0))
+                err = np.max(np.abs(out[i] - want))
+                assert err < 1e-12, f"one-hot row {i + 1} p={p} {mode}: err {err:.3e}"
 
 
 def two_way_tie(lib):
@@ -222,17 +277,19 @@ def two_way_tie(lib):
         a, b = sorted(r.choice(i + 1, size=2, replace=False)) if i >= 1 else (0, 0)
         pairs[i] = (a, b)
         Q[i] = (E[a] + E[b]) * r.uniform(0.5, 2.0)
-    for p in (1, 3, 15):
-        out = _fwd(lib, Q, K, V, p)
-        for i in range(3, L):
-            a, b = pairs[i]
-            err = np.max(np.abs(out[i] - 0.5 * (V[a] + V[b])))
-            assert err < 1e-12, f"tie row {i + 1} p={p}: err {err:.3e}"
+    for mode in RW_MODES:
+        for p in (1, 3, 15):
+            out = _fwd(lib, Q, K, V, p, mode=mode)
+            for i in range(3, L):
+                a, b = pairs[i]
+                err = np.max(np.abs(out[i] - 0.5 * (V[a] + V[b])))
+                assert err < 1e-12, f"tie row {i + 1} p={p} {mode}: err {err:.3e}"
 
 
 def degenerate_rows(lib):
     """All scores of a row equal: rows >= 4 are degenerate (output 0);
-    rows 1-3 have o = 0 and give the mean of v_1..v_i."""
+    rows 1-3 have o = 0 and give the mean of v_1..v_i.  Stage 1 alone has
+    no degenerate rows: every row gives the mean of v_1..v_i."""
     L, d = 10, 8
     r = _rng(600)
     V = r.standard_normal((L, d))
@@ -242,13 +299,14 @@ def degenerate_rows(lib):
     # (b) every key identical, queries random
     K2 = np.tile(r.standard_normal((1, d)), (L, 1))
     Q2 = r.standard_normal((L, d))
-    for (QQ, KK) in ((Q, K), (Q2, K2)):
-        for p in (1, 3, 15):
-            out = _fwd(lib, QQ, KK, V, p)
-            for i in range(L):
-                want = V[:i + 1].mean(axis=0) if i < 3 else np.zeros(d)
-                err = np.max(np.abs(out[i] - want))
-                assert err < 1e-12, f"degenerate row {i + 1} p={p}: err {err:.3e}"
+    for mode in MODES:
+        for (QQ, KK) in ((Q, K), (Q2, K2)):
+            for p in (1, 3, 15):
+                out = _fwd(lib, QQ, KK, V, p, mode=mode)
+                for i in range(L):
+                    want = V[:i + 1].mean(axis=0) if (i < 3 or not mode[1]) else np.zeros(d)
+                    err = np.max(np.abs(out[i] - want))
+                    assert err < 1e-12, f"degenerate row {i + 1} p={p} {mode}: err {err:.3e}"
 
 
 # --------------------------------------------------------------------------
@@ -257,26 +315,31 @@ def degenerate_rows(lib):
 
 def v_identity_probe(lib):
     """V = I turns the output into the weight matrix: non-negative, exactly 0
-    above the diagonal (M' multiplies), rows sum to 1."""
-    for seed, (L, d, p) in enumerate([(16, 16, 3), (24, 32, 15), (9, 9, 2), (12, 12, 1)]):
-        r = _rng(700 + seed)
-        Q, K = r.standard_normal((L, d)), r.standard_normal((L, d))
-        V = np.eye(L, d)
-        W = _fwd(lib, Q, K, V, p)[:, :L]
-        assert np.all(W >= 0.0), "weights must be non-negative"
-        assert np.all(W[np.triu_indices(L, 1)] == 0.0), "masked weights must be exactly 0"
-        err = np.max(np.abs(W.sum(axis=1) - 1.0))
-        assert err < 1e-13, f"row sums: err {err:.3e}"
+    above the diagonal (M' multiplies), rows sum to 1.  Stage 1 alone keeps
+    every unmasked weight strictly positive."""
+    for mode in MODES:
+        for seed, (L, d, p) in enumerate([(16, 16, 3), (24, 32, 15), (9, 9, 2), (12, 12, 1)]):
+            r = _rng(700 + seed)
+            Q, K = r.standard_normal((L, d)), r.standard_normal((L, d))
+            V = np.eye(L, d)
+            W = _fwd(lib, Q, K, V, p, mode=mode)[:, :L]
+            assert np.all(W >= 0.0), "weights must be non-negative"
+            assert np.all(W[np.triu_indices(L, 1)] == 0.0), "masked weights must be exactly 0"
+            if not mode[1]:
+                assert np.all(W[np.tril_indices(L)] > 0.0), "stage-1 weights must be positive"
+            err = np.max(np.abs(W.sum(axis=1) - 1.0))
+            assert err < 1e-13, f"row sums {mode}: err {err:.3e}"
 
 
 def v_ones(lib):
     r = _rng(800)
     L, d = 40, 16
     Q, K = r.standard_normal((L, d)), r.standard_normal((L, d))
-    for p in (1, 3, 15):
-        out = _fwd(lib, Q, K, np.ones((L, d)), p)
-        err = np.max(np.abs(out - 1.0))
-        assert err < 1e-13, f"V = ones: err {err:.3e}"
+    for mode in MODES:
+        for p in (1, 3, 15):
+            out = _fwd(lib, Q, K, np.ones((L, d)), p, mode=mode)
+            err = np.max(np.abs(out - 1.0))
+            assert err < 1e-13, f"V = ones {mode}: err {err:.3e}"
 
 
 def scale_invariance(lib):
@@ -284,26 +347,28 @@ def scale_invariance(lib):
     r = _rng(900)
     L, d = 30, 16
     Q, K, V = (r.standard_normal((L, d)) for _ in range(3))
-    for p in (3, 15):
-        base = _fwd(lib, Q, K, V, p)
-        s2 = _fwd(lib, Q * 8.0, K * 0.25, V, p)
-        assert np.max(np.abs(s2 - base)) < 1e-13, "power-of-two rescale changed output"
-        sq = r.uniform(0.1, 10.0, size=(L, 1))
-        sk = r.uniform(0.1, 10.0, size=(L, 1))
-        s3 = _fwd(lib, Q * sq, K * sk, V, p)
-        err = np.max(np.abs(s3 - base))
-        assert err < 1e-11, f"row rescale changed output by {err:.3e}"
+    sq = r.uniform(0.1, 10.0, size=(L, 1))
+    sk = r.uniform(0.1, 10.0, size=(L, 1))
+    for mode in MODES:
+        for p in (3, 15):
+            base = _fwd(lib, Q, K, V, p, mode=mode)
+            s2 = _fwd(lib, Q * 8.0, K * 0.25, V, p, mode=mode)
+            assert np.max(np.abs(s2 - base)) < 1e-13, "power-of-two rescale changed output"
+            s3 = _fwd(lib, Q * sq, K * sk, V, p, mode=mode)
+            err = np.max(np.abs(s3 - base))
+            assert err < 1e-11, f"row rescale changed output by {err:.3e} ({mode})"
 
 
 def linearity_in_v(lib):
     r = _rng(1000)
     L, d = 25, 8
     Q, K, V1, V2 = (r.standard_normal((L, d)) for _ in range(4))
-    for p in (2, 15):
-        a = _fwd(lib, Q, K, V1, p)
-        b = _fwd(lib, Q, K, V2, p)
-        c = _fwd(lib, Q, K, 2.0 * V1 - 3.0 * V2, p)
-        assert np.max(np.abs(c - (2.0 * a - 3.0 * b))) < 1e-12, "output not linear in V"
+    for mode in MODES:
+        for p in (2, 15):
+            a = _fwd(lib, Q, K, V1, p, mode=mode)
+            b = _fwd(lib, Q, K, V2, p, mode=mode)
+            c = _fwd(lib, Q, K, 2.0 * V1 - 3.0 * V2, p, mode=mode)
+            assert np.max(np.abs(c - (2.0 * a - 3.0 * b))) < 1e-12, "output not linear in V"
 
 
 def causality(lib):
@@ -311,14 +376,16 @@ def causality(lib):
     r = _rng(1100)
     L, d = 20, 8
     Q, K, V = (r.standard_normal((L, d)) for _ in range(3))
-    for p in (1, 3, 15):
-        base = _fwd(lib, Q, K, V, p)
-        for cut in (0, 3, 10, 18):
-            K2, V2 = K.copy(), V.copy()
-            K2[cut + 1:] = r.standard_normal(K2[cut + 1:].shape)
-            V2[cut + 1:] = r.standard_normal(V2[cut + 1:].shape) * 100.0
-            o2 = _fwd(lib, Q, K2, V2, p)
-            assert np.array_equal(o2[:cut + 1], base[:cut + 1]), f"row <= {cut + 1} saw the future"
+    for mode in MODES:
+        for p in (1, 3, 15):
+            base = _fwd(lib, Q, K, V, p, mode=mode)
+            for cut in (0, 3, 10, 18):
+                K2, V2 = K.copy(), V.copy()
+                K2[cut + 1:] = r.standard_normal(K2[cut + 1:].shape)
+                V2[cut + 1:] = r.standard_normal(V2[cut + 1:].shape) * 100.0
+                o2 = _fwd(lib, Q, K2, V2, p, mode=mode)
+                assert np.array_equal(o2[:cut + 1], base[:cut + 1]), \
+                    f"row <= {cut + 1} saw the future ({mode})"
 
 
 def permutation_invariance(lib):
@@ -328,10 +395,11 @@ def permutation_invariance(lib):
     Q, K, V = (r.standard_normal((L, d)) for _ in range(3))
     i = L - 1
     perm = r.permutation(L)
-    for p in (3, 15):
-        a = _fwd(lib, Q, K, V, p)[i]
-        b = _fwd(lib, Q, K[perm], V[perm], p)[i]
-        assert np.max(np.abs(a - b)) < 1e-12, "last row depends on key order"
+    for mode in MODES:
+        for p in (3, 15):
+            a = _fwd(lib, Q, K, V, p, mode=mode)[i]
+            b = _fwd(lib, Q, K[perm], V[perm], p, mode=mode)[i]
+            assert np.max(np.abs(a - b)) < 1e-12, f"last row depends on key order ({mode})"
 
 
 def hard_argmax_limit(lib):
@@ -340,14 +408,19 @@ def hard_argmax_limit(lib):
     positive entries: |w(p) - e_max|_1 = 2 sum_k r_k^p / (1 + sum_k r_k^p)
     exactly, which is at most 2 (n - 1) r_2^p; the max weight never drops.
     The ratios come from the p = 1 weights, which are proportional to x."""
+    for mode in RW_MODES:
+        _hard_argmax_limit(lib, mode)
+
+
+def _hard_argmax_limit(lib, mode):
     r = _rng(1300)
     L, d = 14, 14
     Q, K = r.standard_normal((L, d)), r.standard_normal((L, d))
     V = np.eye(L, d)
-    W1 = _fwd(lib, Q, K, V, 1)[:, :L]
+    W1 = _fwd(lib, Q, K, V, 1, mode=mode)[:, :L]
     prev = np.zeros(L)
     for p in range(1, 65):
-        W = _fwd(lib, Q, K, V, p)[:, :L]
+        W = _fwd(lib, Q, K, V, p, mode=mode)[:, :L]
         for i in range(3, L):
             w = W[i, :i + 1]
             wmax = w.max()
@@ -366,6 +439,6 @@ def hard_argmax_limit(lib):
 
 
 PINS = [brute_force_matrix_form, row1_is_v1, closed_form_rows, golden_row2_value,
-        onehot_orthonormal, two_way_tie, degenerate_rows, v_identity_probe, v_ones,
-        scale_invariance, linearity_in_v, causality, permutation_invariance,
+        sigmoid_antisymmetric_pair, onehot_orthonormal, two_way_tie, degenerate_rows,
+        v_identity_probe, v_ones, scale_invariance, linearity_in_v, causality, permutation_invariance,
         hard_argmax_limit]

@@ -18,9 +18,10 @@ SRC = open(oracle.SRC).read()
 MUTANTS = [
     ("log2-base", "log((double)d) * log((double)i)", "log2((double)d) * log2((double)i)"),
     ("no-log-d", "log((double)d) * log((double)i)", "log((double)i)"),
-    ("sqrt-d-temperature", "softplus(scale * dot) * mask", "softplus(scale * dot / sqrt((double)d)) * mask"),
+    ("sqrt-d-temperature", "phi_fn(phi, scale * dot) * mask",
+     "phi_fn(phi, scale * dot / sqrt((double)d)) * mask"),
     ("zero-based-i", "const int i = row + 1;", "const int i = row + 2;"),
-    ("mask-before-softplus", "softplus(scale * dot) * mask", "softplus(scale * dot * mask)"),
+    ("mask-before-softplus", "phi_fn(phi, scale * dot) * mask", "phi_fn(phi, scale * dot * mask)"),
     ("mask-excludes-diagonal", "(j <= i) ? 1.0 : 0.0", "(j < i) ? 1.0 : 0.0"),
     ("softplus-sign", "return x + log1p(exp(-x));", "return x + log1p(exp(x));"),
     ("softplus-neg-branch", "return log1p(exp(x));", "return log1p(exp(-x));"),
@@ -39,6 +40,15 @@ MUTANTS = [
     ("no-l2-normalise", "y[e] = x[e] / nrm;", "y[e] = x[e];"),
     ("dot-wrong-index", "dot += qh[e] * kj[e];", "dot += qh[e] * kj[0];"),
     ("norm-not-sqrt", "double nrm = sqrt(ss);", "double nrm = ss;"),
+    # the ablation variants: Sigmoid as the stage-1 map, and stage 1 alone
+    ("sigmoid-sign", "return 1.0 / (1.0 + exp(-x));", "return 1.0 / (1.0 + exp(x));"),
+    ("sigmoid-neg-branch", "return e / (1.0 + e);", "return 1.0 / (1.0 + e);"),
+    ("sigmoid-ignored", "return phi == LSSAR_REF_PHI_SIGMOID ? sigmoid(x) : softplus(x);",
+     "return softplus(x);"),
+    ("sigmoid-everywhere", "return phi == LSSAR_REF_PHI_SIGMOID ? sigmoid(x) : softplus(x);",
+     "return sigmoid(x);"),
+    ("lssa-only-reweights", "    if (reweight) {", "    if (1) {"),
+    ("never-reweights", "    if (reweight) {", "    if (0) {"),
 ]
 
 INDEPENDENT_PINS = [p for p in oracle_pins.PINS if p is not oracle_pins.brute_force_matrix_form]

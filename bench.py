@@ -15,8 +15,11 @@ with 16 planted keys per head (cosine 0.9 to one query), seed 0.
 Prints ONE JSON line.  Extra objects: "roofline" for the attention kernel
 (its mean duration from HIP events recorded on the launch stream inside the
 timed region), "cpu_baseline" (the fp64 oracle on a bounded row sample, on
-the host's cores), and "sweep" (the same path at L = 1K..16K, H=12, d=64,
-p=15, B = 16384/L, on device-generated N(0,1) inputs).
+the host's cores), "sweep" (the same path at L = 1K..16K, H=12, d=64,
+p=15, B = 16384/L, on device-generated N(0,1) inputs) and "variants" (the
+note's two ablation variants on the same resident inputs: the Sigmoid
+stage-1 map with re-weighting, and stage 1 alone, each timed as its whole
+entry point, prep included).
 """
 from __future__ import annotations
 
@@ -112,6 +115,34 @@ def time_path(q, k, v, p, steps, warmup, eps=1e-4, settle_s=0.0):
     return wall, fwd, prep
 
 
+def time_variants(q, k, v, p, steps, warmup, eps=1e-4):
+    """Mean ms per call of the ablation variants' entry points (prep plus
+    attention kernel), HIP events on the launch stream."""
+    import torch
+    import softmax_free_attention_amd as sfa
+    ws = sfa.workspace_for(q)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    calls = {
+        "sigmoid_reweight": lambda: sfa.lssar_attn_fwd_phi_ws(
+            q, k, v, out, ws, p=p, eps=eps, phi=sfa.LSSAR_PHI_SIGMOID, stream=stream),
+        "lssa_only": lambda: sfa.lssar_lssa_fwd_ws(q, k, v, out, ws, stream=stream),
+    }
+    res = {}
+    for name, fn in calls.items():
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    return res
+
+
 def cpu_baseline(inp, seconds: float):
     """The fp64 oracle, as it stands, on a bounded sample of the workload's
     rows (strided over all heads and positions), on all host cores."""
@@ -171,6 +202,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--calib-mib", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB (read N, "
                          "write N), the reference kernel for scaling rocprofv3 FETCH/WRITE_SIZE")
@@ -227,6 +259,11 @@ def main():
         torch.add(src, 0.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if not args.no_variants:
+        log("bench: ablation variants")
+        vt = time_variants(q, k, v, wl.p, args.steps, args.warmup)
+        line["variants"] = {n: {"ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+                            for n, ms in vt.items()}
     if not args.no_sweep:
         log("bench: L sweep")
         line["sweep"] = sweep(steps=10, warmup=3)

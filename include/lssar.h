@@ -49,13 +49,19 @@ extern "C" {
 /* Element types. */
 typedef enum { LSSAR_F32 = 0, LSSAR_BF16 = 1 } lssar_dtype;
 
+/* Stage-1 maps for lssar_attn_fwd_phi_ws: Softplus (the method) or the
+ * logistic Sigmoid 1/(1 + e^-x) that the note's ablation table (section Key
+ * experimental data, ablation, row "Sigmoid + L1 + re-weighting") puts in
+ * its place. */
+typedef enum { LSSAR_PHI_SOFTPLUS = 0, LSSAR_PHI_SIGMOID = 1 } lssar_phi;
+
 /* Status codes. */
 enum {
     LSSAR_OK = 0,
     LSSAR_EINVAL = -1,       /* null/misaligned/overlapping pointer, B,H,L < 1,
                                 p < 1, eps < 0 or not finite, sizes overflow */
-    LSSAR_EUNSUPPORTED = -2, /* d not in {64, 128}, unknown dtype, p > 1024,
-                                L > 2^22 */
+    LSSAR_EUNSUPPORTED = -2, /* d not in {64, 128}, unknown dtype or phi,
+                                p > 1024, L > 2^22 */
     LSSAR_EWORKSPACE = -3,   /* workspace null, misaligned, too small or
                                 overlapping a tensor */
     LSSAR_EHIP = -4          /* a HIP call or kernel launch failed; see
@@ -84,7 +90,7 @@ int lssar_attn_fwd(const void* q, const void* k, const void* v, void* out,
                    int B, int H, int L, int d, int p, float eps, int dtype,
                    void* stream);
 
-/* Stage 1 alone: the prep kernels.  Writes into the workspace the fp32
+/* The prep step alone (the prep kernels).  Writes into the workspace the fp32
  * factors fk[bh*L + j] = 1 / max(|k_j|_2, 1e-12) (Key design 1's
  * K_j <- K_j / |K_j|_2, kept as a factor of the score) and, for bf16 inputs,
  * V transposed per head for the attention kernel.  Workspace rules as for
@@ -93,12 +99,34 @@ int lssar_prep(const void* k, const void* v, void* workspace,
                size_t workspace_bytes, int B, int H, int L, int d, int dtype,
                void* stream);
 
-/* Stage 2 alone: the fused two-pass attention kernel, reading the workspace
+/* The attention kernel alone (fused, two passes), reading the workspace
  * that lssar_prep filled for these k and v (stream-ordered after it). */
 int lssar_attn_fwd_prepped(const void* q, const void* k, const void* v,
                            void* workspace, size_t workspace_bytes, void* out,
                            int B, int H, int L, int d, int p, float eps,
                            int dtype, void* stream);
+
+/* Ablation variant (Key experimental data, ablation, "Sigmoid + L1 +
+ * re-weighting"): as lssar_attn_fwd_ws with the stage-1 map chosen by phi.
+ * With LSSAR_PHI_SOFTPLUS it computes exactly what lssar_attn_fwd_ws does;
+ * with LSSAR_PHI_SIGMOID, A_ij = Sigmoid(ln d * ln i * q^_i . k^_j) for
+ * j <= i, and every later step (mask, both L1 normalisations, N, O, ReLU^p,
+ * the degenerate-row rule) is unchanged.  Same arguments, workspace and
+ * errors; an unknown phi is LSSAR_EUNSUPPORTED. */
+int lssar_attn_fwd_phi_ws(const void* q, const void* k, const void* v, void* out,
+                          int B, int H, int L, int d, int p, float eps, int phi,
+                          int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Stage 1 alone, then A V: the note's "LSSA only" (Key experimental data,
+ * main results row "LSSA, normalisation stage only", and the ablation row
+ * "LSSA only, no re-weighting").  out_i = sum_(j<=i) A_ij v_j with A the
+ * L1-normalised Softplus row of Key design 1; no row is degenerate.  One
+ * pass over the keys.  Arguments, workspace (lssar_workspace_bytes) and
+ * errors as for lssar_attn_fwd_ws, without p and eps. */
+int lssar_lssa_fwd_ws(const void* q, const void* k, const void* v, void* out,
+                      int B, int H, int L, int d, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* lssar_status_str(int status);

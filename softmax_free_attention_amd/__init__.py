@@ -8,7 +8,9 @@ supplies device memory and streams.  There is no fallback: if the library is
 missing or fails to load, every call raises.
 
 Method: paper note "Softplus Attention with Re-weighting Boosts Length
-Extrapolation in Large Language Models", Method details, Key designs 1-3.
+Extrapolation in Large Language Models", Method details, Key designs 1-3;
+the two variants of its ablation table (Key experimental data, ablation):
+the Sigmoid stage-1 map and stage 1 alone ("LSSA only").
 """
 from __future__ import annotations
 
@@ -20,10 +22,12 @@ __all__ = [
     "LSSAR_EWORKSPACE", "LSSAR_EHIP", "LssarError", "lib", "lib_path",
     "lssar_workspace_bytes", "lssar_attn_fwd_ws", "lssar_attn_fwd",
     "lssar_prep", "lssar_attn_fwd_prepped", "lssar_status_str", "workspace_for",
-    "lssar_last_hip_error", "lssar_version", "DEFAULT_EPS",
+    "lssar_last_hip_error", "lssar_version", "DEFAULT_EPS", "LSSAR_PHI_SOFTPLUS",
+    "LSSAR_PHI_SIGMOID", "lssar_attn_fwd_phi_ws", "lssar_lssa_fwd_ws",
 ]
 
 LSSAR_F32, LSSAR_BF16 = 0, 1
+LSSAR_PHI_SOFTPLUS, LSSAR_PHI_SIGMOID = 0, 1
 LSSAR_OK, LSSAR_EINVAL, LSSAR_EUNSUPPORTED, LSSAR_EWORKSPACE, LSSAR_EHIP = 0, -1, -2, -3, -4
 DEFAULT_EPS = 1e-4
 
@@ -60,6 +64,10 @@ def lib():
         L.lssar_prep.restype = i
         L.lssar_attn_fwd_prepped.argtypes = [vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, i, vp]
         L.lssar_attn_fwd_prepped.restype = i
+        L.lssar_attn_fwd_phi_ws.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+        L.lssar_attn_fwd_phi_ws.restype = i
+        L.lssar_lssa_fwd_ws.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, sz, vp]
+        L.lssar_lssa_fwd_ws.restype = i
         L.lssar_status_str.argtypes = [i]
         L.lssar_status_str.restype = ctypes.c_char_p
         L.lssar_last_hip_error.argtypes = []
@@ -170,7 +178,7 @@ def _ws_args(workspace):
 
 
 def lssar_prep(k, v, workspace, *, stream=None):
-    """Stage 1 (prep kernels): key-row inverse norms and, for bf16, V^T, into
+    """The prep step (prep kernels): key-row inverse norms and, for bf16, V^T, into
     the workspace."""
     B, H, L, d, dt = _check_qkv(k, k, v)
     wp, wn = _ws_args(workspace)
@@ -181,11 +189,34 @@ def lssar_prep(k, v, workspace, *, stream=None):
 
 def lssar_attn_fwd_prepped(q, k, v, workspace, out, *, p: int, eps: float = DEFAULT_EPS,
                            stream=None):
-    """Stage 2 (the fused attention kernel), given a workspace filled by
+    """The attention kernel alone (fused), given a workspace filled by
     lssar_prep for these k and v."""
     B, H, L, d, dt = _check_qkv(q, k, v, out)
     wp, wn = _ws_args(workspace)
     st = lib().lssar_attn_fwd_prepped(_ptr(q), _ptr(k), _ptr(v), wp, wn, _ptr(out), B, H, L, d,
                                       int(p), float(eps), dt, _stream_ptr(stream))
     _raise(st, "lssar_attn_fwd_prepped")
+    return out
+
+
+def lssar_attn_fwd_phi_ws(q, k, v, out, workspace, *, p: int, eps: float = DEFAULT_EPS,
+                          phi: int = LSSAR_PHI_SOFTPLUS, stream=None):
+    """As lssar_attn_fwd_ws with the stage-1 map chosen by ``phi``
+    (LSSAR_PHI_SOFTPLUS or the ablation's LSSAR_PHI_SIGMOID)."""
+    B, H, L, d, dt = _check_qkv(q, k, v, out)
+    wp, wn = _ws_args(workspace)
+    st = lib().lssar_attn_fwd_phi_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, L, d, int(p),
+                                     float(eps), int(phi), dt, wp, wn, _stream_ptr(stream))
+    _raise(st, "lssar_attn_fwd_phi_ws")
+    return out
+
+
+def lssar_lssa_fwd_ws(q, k, v, out, workspace, *, stream=None):
+    """Stage 1 alone, then A V (the ablation's "LSSA only"), with a
+    caller-owned workspace of lssar_workspace_bytes."""
+    B, H, L, d, dt = _check_qkv(q, k, v, out)
+    wp, wn = _ws_args(workspace)
+    st = lib().lssar_lssa_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, L, d, dt, wp, wn,
+                                 _stream_ptr(stream))
+    _raise(st, "lssar_lssa_fwd_ws")
     return out

@@ -154,7 +154,7 @@ int run_prep(const void* k, const void* v, void* ws, int B, int H, int L, int d,
     return LSSAR_OK;
 }
 
-template <int D, int P>
+template <int D, int P, int PHI, bool RW>
 void launch_fwd(const void* q, const void* k, const void* v, void* ws, void* out, int BH, int L,
                 int dtype, double lam_scale, float eps, int p, hipStream_t s)
 {
@@ -165,45 +165,99 @@ void launch_fwd(const void* q, const void* k, const void* v, void* ws, void* out
         const int npair = (nqb + 1) / 2;
         const __bf16* vt =
             reinterpret_cast<const __bf16*>(static_cast<unsigned char*>(ws) + w.fk_bytes);
-        hipLaunchKernelGGL((lssar::lssar_fwd_bf16_kernel<D, P>), dim3((unsigned)(npair * BH)),
+        hipLaunchKernelGGL((lssar::lssar_fwd_bf16_kernel<D, P, PHI, RW>),
+                           dim3((unsigned)(npair * BH)),
                            dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(q),
                            static_cast<const __bf16*>(k), vt, static_cast<__bf16*>(out), fk, BH,
                            L, w.Lp, nqb, npair, lam_scale, eps, p);
     } else {
         const int nqb = (L + lssar::kBQ32 - 1) / lssar::kBQ32;
-        hipLaunchKernelGGL((lssar::lssar_fwd_f32_kernel<D, P>), dim3((unsigned)(nqb * BH)),
+        hipLaunchKernelGGL((lssar::lssar_fwd_f32_kernel<D, P, PHI, RW>),
+                           dim3((unsigned)(nqb * BH)),
                            dim3(lssar::kThreads), 0, s, static_cast<const float*>(q),
                            static_cast<const float*>(k), static_cast<const float*>(v),
                            static_cast<float*>(out), fk, BH, L, nqb, lam_scale, eps, p);
     }
 }
 
-template <int D>
+// What the attention kernel computes: the stage-1 map and whether stage 2
+// (re-weighting) runs.
+struct Variant {
+    int phi;        // LSSAR_PHI_SOFTPLUS or LSSAR_PHI_SIGMOID
+    bool reweight;  // false: stage 1 only, p and eps unused
+};
+constexpr Variant kLssar = {LSSAR_PHI_SOFTPLUS, true};
+
+template <int D, int PHI>
 void dispatch_p(const void* q, const void* k, const void* v, void* ws, void* out, int BH, int L,
                 int dtype, double lam_scale, float eps, int p, hipStream_t s)
 {
-    switch (p) {
-    case 1: launch_fwd<D, 1>(q, k, v, ws, out, BH, L, dtype, lam_scale, eps, p, s); break;
-    case 2: launch_fwd<D, 2>(q, k, v, ws, out, BH, L, dtype, lam_scale, eps, p, s); break;
-    case 3: launch_fwd<D, 3>(q, k, v, ws, out, BH, L, dtype, lam_scale, eps, p, s); break;
-    case 15: launch_fwd<D, 15>(q, k, v, ws, out, BH, L, dtype, lam_scale, eps, p, s); break;
-    default: launch_fwd<D, 0>(q, k, v, ws, out, BH, L, dtype, lam_scale, eps, p, s); break;
+#define LSSAR_LAUNCH(PV) \
+    launch_fwd<D, PV, PHI, true>(q, k, v, ws, out, BH, L, dtype, lam_scale, eps, p, s)
+    if constexpr (PHI == lssar::kPhiSoftplus) {
+        switch (p) {
+        case 1: LSSAR_LAUNCH(1); break;
+        case 2: LSSAR_LAUNCH(2); break;
+        case 3: LSSAR_LAUNCH(3); break;
+        case 15: LSSAR_LAUNCH(15); break;
+        default: LSSAR_LAUNCH(0); break;
+        }
+    } else {
+        switch (p) {
+        case 3: LSSAR_LAUNCH(3); break;
+        case 15: LSSAR_LAUNCH(15); break;
+        default: LSSAR_LAUNCH(0); break;
+        }
     }
+#undef LSSAR_LAUNCH
+}
+
+template <int D>
+void dispatch_variant(const void* q, const void* k, const void* v, void* ws, void* out, int BH,
+                      int L, int dtype, double lam_scale, float eps, int p, Variant var,
+                      hipStream_t s)
+{
+    if (!var.reweight)
+        launch_fwd<D, 1, lssar::kPhiSoftplus, false>(q, k, v, ws, out, BH, L, dtype, lam_scale,
+                                                     eps, p, s);
+    else if (var.phi == LSSAR_PHI_SIGMOID)
+        dispatch_p<D, lssar::kPhiSigmoid>(q, k, v, ws, out, BH, L, dtype, lam_scale, eps, p, s);
+    else
+        dispatch_p<D, lssar::kPhiSoftplus>(q, k, v, ws, out, BH, L, dtype, lam_scale, eps, p, s);
 }
 
 int run_fwd(const void* q, const void* k, const void* v, void* ws, void* out, int B, int H, int L,
-            int d, int p, float eps, int dtype, hipStream_t s)
+            int d, int p, float eps, int dtype, hipStream_t s, Variant var = kLssar)
 {
     // log2(e) * ln(d): the per-row factor is this times ln(i) / |q_i|
     const double lam_scale = std::log((double)d) / std::log(2.0);
     if (d == 64)
-        dispatch_p<64>(q, k, v, ws, out, B * H, L, dtype, lam_scale, eps, p, s);
+        dispatch_variant<64>(q, k, v, ws, out, B * H, L, dtype, lam_scale, eps, p, var, s);
     else
-        dispatch_p<128>(q, k, v, ws, out, B * H, L, dtype, lam_scale, eps, p, s);
+        dispatch_variant<128>(q, k, v, ws, out, B * H, L, dtype, lam_scale, eps, p, var, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return hip_fail(e);
     return LSSAR_OK;
+}
+
+// Validation, prep and attention kernel on a caller-owned workspace.
+int fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H, int L, int d,
+           int p, float eps, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+           Variant var)
+{
+    int st = validate(q, k, v, out, B, H, L, d, p, eps, dtype);
+    if (st != LSSAR_OK)
+        return st;
+    const size_t tbytes = (size_t)B * H * L * d * elem_bytes(dtype);
+    st = validate_ws(workspace, workspace_bytes, layout(B, H, L, d, dtype), tbytes, q, k, v, out);
+    if (st != LSSAR_OK)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_prep(k, v, workspace, B, H, L, d, dtype, s);
+    if (st != LSSAR_OK)
+        return st;
+    return run_fwd(q, k, v, workspace, out, B, H, L, d, p, eps, dtype, s, var);
 }
 
 }  // namespace
@@ -221,18 +275,26 @@ int lssar_attn_fwd_ws(const void* q, const void* k, const void* v, void* out, in
                       int d, int p, float eps, int dtype, void* workspace, size_t workspace_bytes,
                       void* stream)
 {
-    int st = validate(q, k, v, out, B, H, L, d, p, eps, dtype);
-    if (st != LSSAR_OK)
-        return st;
-    const size_t tbytes = (size_t)B * H * L * d * elem_bytes(dtype);
-    st = validate_ws(workspace, workspace_bytes, layout(B, H, L, d, dtype), tbytes, q, k, v, out);
-    if (st != LSSAR_OK)
-        return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    st = run_prep(k, v, workspace, B, H, L, d, dtype, s);
-    if (st != LSSAR_OK)
-        return st;
-    return run_fwd(q, k, v, workspace, out, B, H, L, d, p, eps, dtype, s);
+    return fwd_ws(q, k, v, out, B, H, L, d, p, eps, dtype, workspace, workspace_bytes, stream,
+                  kLssar);
+}
+
+int lssar_attn_fwd_phi_ws(const void* q, const void* k, const void* v, void* out, int B, int H,
+                          int L, int d, int p, float eps, int phi, int dtype, void* workspace,
+                          size_t workspace_bytes, void* stream)
+{
+    if (phi != LSSAR_PHI_SOFTPLUS && phi != LSSAR_PHI_SIGMOID)
+        return LSSAR_EUNSUPPORTED;
+    return fwd_ws(q, k, v, out, B, H, L, d, p, eps, dtype, workspace, workspace_bytes, stream,
+                  Variant{phi, true});
+}
+
+int lssar_lssa_fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H, int L,
+                      int d, int dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    // p and eps take no part in stage 1; valid placeholders pass validation
+    return fwd_ws(q, k, v, out, B, H, L, d, 1, 0.0f, dtype, workspace, workspace_bytes, stream,
+                  Variant{LSSAR_PHI_SOFTPLUS, false});
 }
 
 int lssar_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int L,
@@ -303,6 +365,6 @@ const char* lssar_status_str(int status)
 
 int lssar_last_hip_error(void) { return g_last_hip_error; }
 
-int lssar_version(void) { return 200; }
+int lssar_version(void) { return 300; }
 
 }  // extern "C"

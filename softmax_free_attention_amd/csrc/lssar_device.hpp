@@ -30,6 +30,12 @@
 //     of the scores; pass 2 recomputes the scores, re-weights and
 //     accumulates P.V and the weight sum with MFMA, then divides.
 //
+// Variants (the note's ablation table, Key experimental data): the stage-1
+// map phi may be the logistic Sigmoid instead of Softplus ("Sigmoid + L1 +
+// re-weighting"; the same rearrangement holds with phi in place of
+// Softplus), and stage 2 may be left out ("LSSA only": out = A V, one pass
+// over the keys with weights phi(s_ij) normalised by their sum).
+//
 // Tiling (bf16): a workgroup of 4 waves owns 128 consecutive query rows of
 // one (batch, head); each wave owns 32 rows.  Keys stream through LDS in
 // tiles of 64, double-buffered.  Scores are computed transposed,
@@ -77,6 +83,25 @@ __device__ __forceinline__ float softplus2(float t)
     return __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
+// Stage-1 maps.  Sigmoid(t ln 2) = 1 / (1 + 2^-t) needs no constant factor;
+// a masked t = -inf gives 1 / inf = 0.
+constexpr int kPhiSoftplus = 0;
+constexpr int kPhiSigmoid = 1;
+
+__device__ __forceinline__ float sigmoid2(float t)
+{
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t));
+}
+
+template <int PHI>
+__device__ __forceinline__ float phi2(float t)
+{
+    if constexpr (PHI == kPhiSigmoid)
+        return sigmoid2(t);
+    else
+        return softplus2(t);
+}
+
 // y^P for y in [0, 1] by a fixed multiplication chain (P = 0: runtime p).
 template <int P, typename F>
 __device__ __forceinline__ F pow_chain(F y, int p)
@@ -110,16 +135,18 @@ __device__ __forceinline__ float reweight_arg(float sp, float c, float tc)
 }
 
 // Row constants after pass 1 (Key design 2).  i: 1-based row; s1: sum of
-// base-2 Softplus values; tmax: the row's largest scaled score.
+// the row's phi values (base-2 Softplus or Sigmoid); tmax: the row's largest
+// scaled score (phi is increasing, so phi(tmax) is the row's largest value).
 struct RowConst {
     float c;      // 1 / (sp_max - tau), or 0 for a degenerate row
     float tc;     // tau * c
     bool degen;
 };
 
+template <int PHI>
 __device__ __forceinline__ RowConst row_constants(int i, float s1, float tmax, float eps)
 {
-    const float spmax = softplus2(tmax);
+    const float spmax = phi2<PHI>(tmax);
     const float o = (i <= 3) ? 0.0f : 1.0f;
     const float tau = o * s1 / (float)i;
     const float gap = spmax - tau;
@@ -146,14 +173,29 @@ __device__ __forceinline__ double softplus2_f64(double t)
     return t > 0.0 ? t + log1p(exp2(-t)) * kLog2e : log1p(exp2(t)) * kLog2e;
 }
 
+__device__ __forceinline__ double sigmoid2_f64(double t)
+{
+    return 1.0 / (1.0 + exp2(-t));
+}
+
+template <int PHI>
+__device__ __forceinline__ double phi2_f64(double t)
+{
+    if constexpr (PHI == kPhiSigmoid)
+        return sigmoid2_f64(t);
+    else
+        return softplus2_f64(t);
+}
+
 struct RowConstD {
     double c, tc;
     bool degen;
 };
 
+template <int PHI>
 __device__ __forceinline__ RowConstD row_constants_f64(int i, double s1, double tmax, float eps)
 {
-    const double spmax = softplus2_f64(tmax);
+    const double spmax = phi2_f64<PHI>(tmax);
     const double o = (i <= 3) ? 0.0 : 1.0;
     const double tau = o * s1 / (double)i;
     const double gap = spmax - tau;
@@ -377,7 +419,8 @@ __device__ __forceinline__ void load4_to_lds(const void* base, unsigned nbytes, 
         (lds_void*)lds, 4, (int)voffset, (int)soffset, 0, 0);
 }
 
-template <int D, int P>
+// PHI: stage-1 map; RW: false = stage 1 only (no pass 1, weights phi(t)).
+template <int D, int P, int PHI, bool RW>
 __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ VT, __bf16* __restrict__ O,
@@ -531,46 +574,57 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
                 if (DIAG && ks >= nks)
                     continue;
                 const f32x4 t = scale_block(kt, base, ks, acc[ks], DIAG);
-                f32x4 u;
+                if constexpr (PHI == kPhiSoftplus) {
+                    f32x4 u;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    u[r] = __builtin_amdgcn_exp2f(-fabsf(t[r]));
+                    for (int r = 0; r < 4; ++r)
+                        u[r] = __builtin_amdgcn_exp2f(-fabsf(t[r]));
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    pos_sum += fmaxf(t[r], 0.0f);
-                tmax = fmaxf(fmaxf(tmax, t[0]), t[1]);
-                tmax = fmaxf(fmaxf(tmax, t[2]), t[3]);
+                    for (int r = 0; r < 4; ++r)
+                        pos_sum += fmaxf(t[r], 0.0f);
+                    tmax = fmaxf(fmaxf(tmax, t[0]), t[1]);
+                    tmax = fmaxf(fmaxf(tmax, t[2]), t[3]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    prod = __builtin_fmaf(prod, u[r], prod);
+                    for (int r = 0; r < 4; ++r)
+                        prod = __builtin_fmaf(prod, u[r], prod);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        pos_sum += sigmoid2(t[r]);
+                    tmax = fmaxf(fmaxf(tmax, t[0]), t[1]);
+                    tmax = fmaxf(fmaxf(tmax, t[2]), t[3]);
+                }
             }
-            s1 += pos_sum + __builtin_amdgcn_logf(prod);
-        };
-        __syncthreads();                           // LDS buffers free
-        issue(0, 0, false);
-        for (int kt = 0; kt < ntiles; ++kt) {
-            const int buf = kt & 1;
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();                       // tile kt landed; buf^1 free
-            if (kt + 1 < ntiles)
-                issue(kt + 1, buf ^ 1, false);
-            if (!(wave_active && kt * kBK <= qwl))
-                continue;
-            if (kt * kBK + kBK - 1 > qw0)
-                pass1_tile(kt, smem[buf], std::true_type{});
+            if constexpr (PHI == kPhiSoftplus)
+                s1 += pos_sum + __builtin_amdgcn_logf(prod);
             else
-                pass1_tile(kt, smem[buf], std::false_type{});
-        }
+                s1 += pos_sum;
+        };
+        RowConst rc = {0.0f, 0.0f, false};
+        if constexpr (RW) {
+            __syncthreads();                       // LDS buffers free
+            issue(0, 0, false);
+            for (int kt = 0; kt < ntiles; ++kt) {
+                const int buf = kt & 1;
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();                   // tile kt landed; buf^1 free
+                if (kt + 1 < ntiles)
+                    issue(kt + 1, buf ^ 1, false);
+                if (!(wave_active && kt * kBK <= qwl))
+                    continue;
+                if (kt * kBK + kBK - 1 > qw0)
+                    pass1_tile(kt, smem[buf], std::true_type{});
+                else
+                    pass1_tile(kt, smem[buf], std::false_type{});
+            }
 
-        RowConst rc;
-        {
             float sum = s1;
             sum += __shfl_xor(sum, 16);
             sum += __shfl_xor(sum, 32);
             float t = tmax;
             t = fmaxf(t, __shfl_xor(t, 16));
             t = fmaxf(t, __shfl_xor(t, 32));
-            rc = row_constants(qi + 1, sum, t, eps);
+            rc = row_constants<PHI>(qi + 1, sum, t, eps);
         }
 
         // ---------------- pass 2: re-weight, P.V and the weight sum ----------------
@@ -582,12 +636,20 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
 
         auto weights = [&](f32x4 t) {
             f32x4 e, w;
+            if constexpr (PHI == kPhiSoftplus) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                e[r] = __builtin_amdgcn_exp2f(t[r]);
+                for (int r = 0; r < 4; ++r)
+                    e[r] = __builtin_amdgcn_exp2f(t[r]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                e[r] = __builtin_amdgcn_logf(1.0f + e[r]);       // Softplus2
+                for (int r = 0; r < 4; ++r)
+                    e[r] = __builtin_amdgcn_logf(1.0f + e[r]);   // Softplus2
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    e[r] = sigmoid2(t[r]);
+            }
+            if constexpr (!RW)
+                return e;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 w[r] = pow_chain<P>(reweight_arg(e[r], rc.c, rc.tc), p_rt);
@@ -624,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
             }
         };
 
-        __syncthreads();                           // pass-1 readers done with the buffers
+        __syncthreads();                           // earlier readers done with the buffers
         issue(0, 0, true);
         for (int kt = 0; kt < ntiles; ++kt) {
             const int buf = kt & 1;
@@ -661,7 +723,7 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
 // v_mfma_f32_16x16x4_f32.  K and V stay row-major in LDS (one element per
 // lane per MFMA operand); tiles are single-buffered.
 // ---------------------------------------------------------------------------
-template <int D, int P>
+template <int D, int P, int PHI, bool RW>
 __global__ __launch_bounds__(kThreads, 1) void lssar_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K,
     const float* __restrict__ V, float* __restrict__ O,
@@ -757,47 +819,49 @@ __global__ __launch_bounds__(kThreads, 1) void lssar_fwd_f32_kernel(
         }
     };
 
-    // pass 1
-    double s1[2] = {0.0, 0.0};
-    double tmax[2] = {-INFINITY, -INFINITY};
-    for (int kt = 0; kt < ntiles; ++kt) {
-        __syncthreads();
-        stage(kt, false);
-        __syncthreads();
-        if (!(wave_active && kt * kBK <= qwl))
-            continue;
-        f64x4 acc[4][2];
-        qk_tile(acc);
-        double part[2] = {0.0, 0.0};
+    // pass 1 (both stages only)
+    RowConstD rc[2] = {{0.0, 0.0, false}, {0.0, 0.0, false}};
+    if constexpr (RW) {
+        double s1[2] = {0.0, 0.0};
+        double tmax[2] = {-INFINITY, -INFINITY};
+        for (int kt = 0; kt < ntiles; ++kt) {
+            __syncthreads();
+            stage(kt, false);
+            __syncthreads();
+            if (!(wave_active && kt * kBK <= qwl))
+                continue;
+            f64x4 acc[4][2];
+            qk_tile(acc);
+            double part[2] = {0.0, 0.0};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-            for (int qs = 0; qs < 2; ++qs) {
+                for (int qs = 0; qs < 2; ++qs) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = key_of(ks, r);
-                    const bool ok = kt * kBK + key <= qi[qs];
-                    if (ok) {
-                        const double t = acc[ks][qs][r] * (lam[qs] * (double)Fs[key]);
-                        part[qs] += softplus2_f64(t);
-                        tmax[qs] = fmax(tmax[qs], t);
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = key_of(ks, r);
+                        const bool ok = kt * kBK + key <= qi[qs];
+                        if (ok) {
+                            const double t = acc[ks][qs][r] * (lam[qs] * (double)Fs[key]);
+                            part[qs] += phi2_f64<PHI>(t);
+                            tmax[qs] = fmax(tmax[qs], t);
+                        }
                     }
                 }
             }
+            s1[0] += part[0];
+            s1[1] += part[1];
         }
-        s1[0] += part[0];
-        s1[1] += part[1];
-    }
-    RowConstD rc[2];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-        double s = s1[qs];
-        s += __shfl_xor(s, 16);
-        s += __shfl_xor(s, 32);
-        double t = tmax[qs];
-        t = fmax(t, __shfl_xor(t, 16));
-        t = fmax(t, __shfl_xor(t, 32));
-        rc[qs] = row_constants_f64(qi[qs] + 1, s, t, eps);
+        for (int qs = 0; qs < 2; ++qs) {
+            double s = s1[qs];
+            s += __shfl_xor(s, 16);
+            s += __shfl_xor(s, 32);
+            double t = tmax[qs];
+            t = fmax(t, __shfl_xor(t, 16));
+            t = fmax(t, __shfl_xor(t, 32));
+            rc[qs] = row_constants_f64<PHI>(qi[qs] + 1, s, t, eps);
+        }
     }
 
     // pass 2
@@ -828,9 +892,13 @@ __global__ __launch_bounds__(kThreads, 1) void lssar_fwd_f32_kernel(
                     float wv = 0.0f;
                     if (ok) {
                         const double t = acc[ks][qs][r] * (lam[qs] * (double)Fs[key]);
-                        double y = softplus2_f64(t) * rc[qs].c - rc[qs].tc;
-                        y = fmin(fmax(y, 0.0), 1.0);
-                        wv = (float)pow_chain<P>(y, p_rt);
+                        if constexpr (RW) {
+                            double y = phi2_f64<PHI>(t) * rc[qs].c - rc[qs].tc;
+                            y = fmin(fmax(y, 0.0), 1.0);
+                            wv = (float)pow_chain<P>(y, p_rt);
+                        } else {
+                            wv = (float)phi2_f64<PHI>(t);
+                        }
                     }
                     w[qs][r] = wv;
                     dsum[qs] += wv;

@@ -34,7 +34,8 @@ def L():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("lssar_attn_fwd", "lssar_attn_fwd_ws", "lssar_workspace_bytes",
-              "lssar_status_str", "lssar_prep", "lssar_attn_fwd_prepped"):
+              "lssar_status_str", "lssar_prep", "lssar_attn_fwd_prepped",
+              "lssar_attn_fwd_phi_ws", "lssar_lssa_fwd_ws"):
         assert n in names
 
 
@@ -62,7 +63,7 @@ def test_library_has_no_oracle_dependency(L):
 
 
 def test_version_and_status_strings(L):
-    assert sfa.lssar_version() == 200
+    assert sfa.lssar_version() == 300
     assert sfa.lssar_status_str(0) == "ok"
     for st in (-1, -2, -3, -4, 7):
         s = sfa.lssar_status_str(st)
@@ -145,4 +146,23 @@ def test_stage_entries_validate(L):
                                     None) == sfa.LSSAR_EINVAL
     assert L.lssar_attn_fwd_prepped(q, k, v, o, 1 << 20, o, 1, 1, 8, 64, 3, 1e-4, 1,
                                     None) == sfa.LSSAR_EWORKSPACE
+    assert sfa.lssar_last_hip_error() == 0
+
+
+def test_variant_entries_validate(L):
+    q, k, v, o, ws = A, A + STEP, A + 2 * STEP, A + 3 * STEP, A + 4 * STEP
+    phi = L.lssar_attn_fwd_phi_ws
+    assert phi(q, k, v, o, 1, 2, 64, 64, 3, 1e-4, 2, 1, ws, 1 << 20, None) == sfa.LSSAR_EUNSUPPORTED
+    assert phi(q, k, v, o, 1, 2, 64, 64, 3, 1e-4, -1, 1, ws, 1 << 20, None) == sfa.LSSAR_EUNSUPPORTED
+    assert phi(0, k, v, o, 1, 2, 64, 64, 3, 1e-4, 1, 1, ws, 1 << 20, None) == sfa.LSSAR_EINVAL
+    assert phi(q, k, v, o, 1, 2, 64, 64, 0, 1e-4, 1, 1, ws, 1 << 20, None) == sfa.LSSAR_EINVAL
+    assert phi(q, k, v, o, 1, 2, 64, 96, 3, 1e-4, 1, 1, ws, 1 << 20, None) == sfa.LSSAR_EUNSUPPORTED
+    assert phi(q, k, v, o, 1, 2, 64, 64, 3, 1e-4, 1, 1, ws, 64, None) == sfa.LSSAR_EWORKSPACE
+    lssa = L.lssar_lssa_fwd_ws
+    assert lssa(q, k, v, 0, 1, 2, 64, 64, 1, ws, 1 << 20, None) == sfa.LSSAR_EINVAL
+    assert lssa(q, k, v, o, 1, 2, 0, 64, 1, ws, 1 << 20, None) == sfa.LSSAR_EINVAL
+    assert lssa(q, k, v, o, 1, 2, 64, 80, 1, ws, 1 << 20, None) == sfa.LSSAR_EUNSUPPORTED
+    assert lssa(q, k, v, o, 1, 2, 64, 64, 3, ws, 1 << 20, None) == sfa.LSSAR_EUNSUPPORTED
+    assert lssa(q, k, v, o, 1, 2, 64, 64, 1, 0, 1 << 20, None) == sfa.LSSAR_EWORKSPACE
+    assert lssa(q, k, v, o, 1, 2, 64, 64, 1, o + 256, 1 << 20, None) == sfa.LSSAR_EWORKSPACE
     assert sfa.lssar_last_hip_error() == 0

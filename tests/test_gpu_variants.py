@@ -1,0 +1,186 @@
+"""The ablation variants on the HIP path vs the fp64 oracle, through the C ABI.
+
+Variants (paper note "Softplus Attention with Re-weighting Boosts Length
+Extrapolation in Large Language Models", Key experimental data, ablation):
+the Sigmoid stage-1 map with re-weighting (lssar_attn_fwd_phi_ws) and stage 1
+alone, "LSSA only" (lssar_lssa_fwd_ws).  Same bars as the method: max-abs
+1e-5 for fp32 inputs, 3e-2 for bf16 inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import lssar_inputs as gen
+import oracle
+from gpu_util import BF16_TOL, run_ws, to_device, to_host, tol_for
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+SIG = oracle.PHI_SIGMOID
+SMALL_L = [1, 2, 3, 4, 5, 17, 63, 64, 65, 127, 128, 129, 255, 300, 513]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import softmax_free_attention_amd as sfa
+    sfa.lib()
+
+
+def run_variant(q, k, v, variant, p=3, eps=1e-4):
+    """variant: "sigmoid" (re-weighted) or "lssa" (stage 1 only)."""
+    import softmax_free_attention_amd as sfa
+    ws = sfa.workspace_for(q)
+    out = torch.empty_like(q)
+    if variant == "lssa":
+        sfa.lssar_lssa_fwd_ws(q, k, v, out, ws)
+    else:
+        sfa.lssar_attn_fwd_phi_ws(q, k, v, out, ws, p=p, eps=eps, phi=sfa.LSSAR_PHI_SIGMOID)
+    return out
+
+
+def oracle_variant(q, k, v, variant, p=3):
+    if variant == "lssa":
+        return oracle.lssar_fwd(q, k, v, p, reweight=False)
+    return oracle.lssar_fwd(q, k, v, p, phi=SIG)
+
+
+def _gpu(inp, variant, p):
+    q, k, v = (to_device(a, inp.wl.dtype) for a in (inp.q, inp.k, inp.v))
+    out = run_variant(q, k, v, variant, p)
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+CASES = [("sigmoid", 3), ("sigmoid", 15), ("sigmoid", 7), ("lssa", 1)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("variant,p", CASES, ids=[f"{v}-p{p}" for v, p in CASES])
+def test_small_shapes_full_parity(dtype, d, variant, p):
+    tol = tol_for(dtype)
+    for L in SMALL_L:
+        inp = gen.make_inputs("gpt2s", B=1, H=2, L=L, d=d, dtype=dtype, p=p, seed=L + 1000)
+        got = _gpu(inp, variant, p)
+        want = oracle_variant(inp.q, inp.k, inp.v, variant, p)
+        err = float(np.max(np.abs(got - want)))
+        print(f"{variant} {dtype} d={d} p={p} L={L}: max-abs {err:.3e}", flush=True)
+        assert err <= tol, f"{variant} {dtype} d={d} p={p} L={L}: max-abs {err:.3e} > {tol}"
+
+
+def _sample_rows(wl, rng, planted):
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    if len(heads) > 8:
+        idx = rng.choice(len(heads), size=8, replace=False)
+        heads = [heads[i] for i in sorted(idx)]
+    out = []
+    for b, h in heads:
+        rows = {0, 1, 2, 3, 4, wl.L - 1}
+        rows.update(int(x) for x in rng.integers(0, wl.L, size=8))
+        if (b, h) in planted:
+            rows.add(planted[(b, h)])
+        out.append((b, h, sorted(rows)))
+    return out
+
+
+@pytest.mark.parametrize("name", ["x8_planted", "wide"])
+@pytest.mark.parametrize("variant", ["sigmoid", "lssa"])
+def test_full_workload_sampled_parity(name, variant):
+    """The full-size workloads, in the launch configuration the bench times,
+    on sampled rows the oracle computes one by one."""
+    inp = gen.make_inputs(name)
+    wl = inp.wl
+    print(f"{variant} {name}: B{wl.B} H{wl.H} L{wl.L} d{wl.d} p{wl.p}", flush=True)
+    got = _gpu(inp, variant, wl.p)
+    rng = np.random.default_rng(17)
+    planted = {(b, h): r for b, h, r, _ in inp.meta.get("planted", [])}
+    worst = 0.0
+    for b, h, rows in _sample_rows(wl, rng, planted):
+        want = oracle.lssar_rows(inp.q[b, h], inp.k[b, h], inp.v[b, h], rows, wl.p,
+                                 phi=oracle.PHI_SOFTPLUS if variant == "lssa" else SIG,
+                                 reweight=variant != "lssa")
+        err = float(np.max(np.abs(got[b, h, rows] - want)))
+        worst = max(worst, err)
+        assert err <= BF16_TOL, f"{variant} {name} b={b} h={h}: max-abs {err:.3e}"
+    assert np.array_equal(got[:, :, 0], inp.v[:, :, 0].astype(np.float64))
+    assert np.all(np.isfinite(got))
+    print(f"{variant} {name}: sampled max-abs {worst:.3e}", flush=True)
+
+
+def test_softplus_phi_entry_matches_method_bitwise():
+    import softmax_free_attention_amd as sfa
+    for dtype, d, p in (("bf16", 64, 15), ("bf16", 128, 3), ("f32", 64, 3)):
+        inp = gen.make_inputs("gpt2s", B=1, H=3, L=333, d=d, dtype=dtype, p=p, seed=41)
+        q, k, v = (to_device(a, dtype) for a in (inp.q, inp.k, inp.v))
+        a = run_ws(q, k, v, p)
+        ws = sfa.workspace_for(q)
+        b = torch.empty_like(q)
+        sfa.lssar_attn_fwd_phi_ws(q, k, v, b, ws, p=p, phi=sfa.LSSAR_PHI_SOFTPLUS)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_v_ones_and_identity():
+    """V = ones gives 1 exactly (bf16) for both variants.  V = I gives the
+    weights: non-negative, 0 above the diagonal, rows summing to 1; stage 1
+    alone keeps every unmasked weight positive."""
+    for variant in ("sigmoid", "lssa"):
+        inp = gen.make_inputs("gpt2s", B=1, H=2, L=64, d=64, dtype="bf16", p=15, seed=51)
+        q, k = to_device(inp.q, "bf16"), to_device(inp.k, "bf16")
+        ones = torch.ones_like(q)
+        assert bool((run_variant(q, k, ones, variant, 15) == 1.0).all())
+        eye = to_device(np.broadcast_to(np.eye(64, dtype=np.float32), (1, 2, 64, 64)).copy(),
+                        "bf16")
+        W = to_host(run_variant(q, k, eye, variant, 15))
+        iu = np.triu_indices(64, 1)
+        assert np.all(W >= 0.0)
+        assert np.all(W[:, :, iu[0], iu[1]] == 0.0)
+        assert np.max(np.abs(W.sum(axis=-1) - 1.0)) <= 2e-2
+        if variant == "lssa":
+            il = np.tril_indices(64)
+            assert np.all(W[:, :, il[0], il[1]] > 0.0)
+
+
+def test_zero_queries():
+    """Zero query rows make every score 0: with re-weighting rows >= 4 are
+    degenerate (output 0); stage 1 alone gives the mean of v_1..v_i."""
+    for dtype in ("f32", "bf16"):
+        inp = gen.make_inputs("gpt2s", B=1, H=2, L=150, d=64, dtype=dtype, p=3, seed=61)
+        q = inp.q.copy()
+        zero_rows = [0, 1, 2, 3, 4, 63, 64, 149]
+        q[:, :, zero_rows] = 0.0
+        for variant in ("sigmoid", "lssa"):
+            qd, kd, vd = (to_device(a, dtype) for a in (q, inp.k, inp.v))
+            got = to_host(run_variant(qd, kd, vd, variant, 3))
+            want = oracle_variant(q, inp.k, inp.v, variant, 3)
+            assert np.max(np.abs(got - want)) <= tol_for(dtype)
+            if variant == "sigmoid":
+                assert np.all(got[:, :, [3, 4, 63, 64, 149]] == 0.0)
+
+
+def test_causality_bitwise():
+    inp = gen.make_inputs("gpt2s", B=1, H=2, L=300, d=64, p=15, seed=71)
+    q, k, v = (to_device(a, "bf16") for a in (inp.q, inp.k, inp.v))
+    for variant in ("sigmoid", "lssa"):
+        base = run_variant(q, k, v, variant, 15)
+        for cut in (0, 4, 64, 200):
+            k2, v2 = k.clone(), v.clone()
+            k2[:, :, cut + 1:] = torch.randn_like(k2[:, :, cut + 1:])
+            v2[:, :, cut + 1:] = torch.randn_like(v2[:, :, cut + 1:]) * 100
+            o2 = run_variant(q, k2, v2, variant, 15)
+            assert torch.equal(o2[:, :, :cut + 1].view(torch.int16),
+                               base[:, :, :cut + 1].view(torch.int16))
+
+
+def test_binding_rejects_unknown_phi():
+    import softmax_free_attention_amd as sfa
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device="cuda")
+    ws = sfa.workspace_for(q)
+    with pytest.raises(sfa.LssarError) as e:
+        sfa.lssar_attn_fwd_phi_ws(q, q.clone(), q.clone(), torch.empty_like(q), ws, p=3, phi=2)
+    assert e.value.status == sfa.LSSAR_EUNSUPPORTED

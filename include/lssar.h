@@ -30,10 +30,12 @@
  *    asynchronous with respect to the host and ordered on the stream.
  *  - Square causal self-attention: query i sees keys 1..i; one K/V head per
  *    Q head; q and k are the vectors after any positional rotation.
- *  - Arithmetic: scores contract the raw inputs with fp32 accumulation (bf16
- *    MFMA for bf16, fp32 MFMA for fp32); norms, Softplus, row sums and the
- *    re-weighting run in fp32; bf16 weights feed the P.V contraction for
- *    bf16 inputs; the output is rounded to the input dtype (nearest-even).
+ *  - Arithmetic, bf16 inputs: scores contract the raw inputs on bf16 MFMA
+ *    with fp32 accumulation; norms, Softplus, row sums and the re-weighting
+ *    run in fp32; bf16 weights feed the P.V contraction (fp32 accumulation).
+ *    fp32 inputs: scores on fp64 MFMA, norms and the score -> Softplus ->
+ *    re-weighting chain in fp64, fp32 weights and P.V on fp32 MFMA.  The
+ *    output is rounded to the input dtype (nearest-even).
  *  - Every argument is validated on the host before any HIP call; invalid
  *    input returns an error code and launches nothing.
  */
@@ -68,10 +70,11 @@ enum {
                                 lssar_last_hip_error() */
 };
 
-/* Workspace for lssar_attn_fwd_ws / lssar_prep / lssar_attn_fwd_prepped, in
- * bytes: one fp32 inverse key norm per key row (4*B*H*L, rounded up to 256),
- * plus for bf16 inputs a transposed copy of V (B*H*d*Lp bf16, Lp = L rounded
- * up to 64, rounded up to 256).  Returns 0 for invalid sizes. */
+/* Workspace for every entry point that takes one, in bytes: one inverse key
+ * norm per key row (fp32 for bf16 inputs: 4*B*H*L; fp64 for fp32 inputs:
+ * 8*B*H*L; rounded up to 256), plus for bf16 inputs a transposed copy of V
+ * (B*H*d*Lp bf16, Lp = L rounded up to 64, rounded up to 256).  Returns 0
+ * for invalid sizes. */
 size_t lssar_workspace_bytes(int B, int H, int L, int d, int dtype);
 
 /* LSSAR causal attention forward (Key designs 1-3 above) with a
@@ -90,10 +93,11 @@ int lssar_attn_fwd(const void* q, const void* k, const void* v, void* out,
                    int B, int H, int L, int d, int p, float eps, int dtype,
                    void* stream);
 
-/* The prep step alone (the prep kernels).  Writes into the workspace the fp32
+/* The prep step alone (the prep kernels).  Writes into the workspace the
  * factors fk[bh*L + j] = 1 / max(|k_j|_2, 1e-12) (Key design 1's
- * K_j <- K_j / |K_j|_2, kept as a factor of the score) and, for bf16 inputs,
- * V transposed per head for the attention kernel.  Workspace rules as for
+ * K_j <- K_j / |K_j|_2, kept as a factor of the score; fp32 for bf16
+ * inputs, fp64 for fp32 inputs) and, for bf16 inputs, V transposed per head
+ * for the attention kernel.  Workspace rules as for
  * lssar_attn_fwd_ws; a bad workspace is LSSAR_EWORKSPACE. */
 int lssar_prep(const void* k, const void* v, void* workspace,
                size_t workspace_bytes, int B, int H, int L, int d, int dtype,

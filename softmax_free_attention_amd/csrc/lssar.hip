@@ -41,7 +41,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace layout: [fk: fp32 per key row][Vt: bf16 V^T, bf16 inputs only]
+// Workspace layout: [fk: inverse key norm per key row, fp32 for bf16 inputs
+// and fp64 for fp32 inputs][Vt: bf16 V^T, bf16 inputs only]
 struct Layout {
     size_t fk_bytes, vt_bytes;
     int Lp;
@@ -52,7 +53,7 @@ Layout layout(long long B, long long H, long long L, int d, int dtype)
 {
     Layout w;
     w.Lp = (int)((L + lssar::kBK - 1) / lssar::kBK * lssar::kBK);
-    w.fk_bytes = round256((size_t)(4 * B * H * L));
+    w.fk_bytes = round256((size_t)((dtype == LSSAR_F32 ? 8 : 4) * B * H * L));
     w.vt_bytes = dtype == LSSAR_BF16 ? round256((size_t)(B * H * d) * (size_t)w.Lp * 2) : 0;
     return w;
 }
@@ -111,14 +112,13 @@ int validate_ws(const void* ws, size_t ws_bytes, const Layout& w, size_t tbytes,
     return LSSAR_OK;
 }
 
-template <typename T, int D>
-void launch_knorm(const void* k, float* fk, long nrows, hipStream_t s)
+template <int D>
+void launch_knorm_f32(const void* k, double* fk, long nrows, hipStream_t s)
 {
-    constexpr int lpr = D / (16 / (int)sizeof(T));
-    constexpr int rpb = lssar::kThreads / lpr;
+    constexpr int rpb = lssar::kThreads / (D / 4);
     const unsigned grid = (unsigned)((nrows + rpb - 1) / rpb);
-    hipLaunchKernelGGL((lssar::lssar_knorm_kernel<T, D>), dim3(grid), dim3(lssar::kThreads), 0,
-                       s, static_cast<const T*>(k), fk, nrows);
+    hipLaunchKernelGGL((lssar::lssar_knorm_f32_kernel<D>), dim3(grid), dim3(lssar::kThreads), 0,
+                       s, static_cast<const float*>(k), fk, nrows);
 }
 
 template <int D>
@@ -134,19 +134,20 @@ int run_prep(const void* k, const void* v, void* ws, int B, int H, int L, int d,
              hipStream_t s)
 {
     const Layout w = layout(B, H, L, d, dtype);
-    float* fk = static_cast<float*>(ws);
     const long nrows = (long)B * H * L;
     if (dtype == LSSAR_BF16) {
+        float* fk = static_cast<float*>(ws);
         void* vt = static_cast<unsigned char*>(ws) + w.fk_bytes;
         if (d == 64)
             launch_prep_bf16<64>(k, v, fk, vt, B * H, L, w.Lp, s);
         else
             launch_prep_bf16<128>(k, v, fk, vt, B * H, L, w.Lp, s);
     } else {
+        double* fk = static_cast<double*>(ws);
         if (d == 64)
-            launch_knorm<float, 64>(k, fk, nrows, s);
+            launch_knorm_f32<64>(k, fk, nrows, s);
         else
-            launch_knorm<float, 128>(k, fk, nrows, s);
+            launch_knorm_f32<128>(k, fk, nrows, s);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -159,8 +160,8 @@ void launch_fwd(const void* q, const void* k, const void* v, void* ws, void* out
                 int dtype, double lam_scale, float eps, int p, hipStream_t s)
 {
     const Layout w = layout(1, BH, L, D, dtype);
-    const float* fk = static_cast<const float*>(ws);
     if (dtype == LSSAR_BF16) {
+        const float* fk = static_cast<const float*>(ws);
         const int nqb = (L + lssar::kBQ16 - 1) / lssar::kBQ16;
         const int npair = (nqb + 1) / 2;
         const __bf16* vt =
@@ -176,7 +177,8 @@ void launch_fwd(const void* q, const void* k, const void* v, void* ws, void* out
                            dim3((unsigned)(nqb * BH)),
                            dim3(lssar::kThreads), 0, s, static_cast<const float*>(q),
                            static_cast<const float*>(k), static_cast<const float*>(v),
-                           static_cast<float*>(out), fk, BH, L, nqb, lam_scale, eps, p);
+                           static_cast<float*>(out), static_cast<const double*>(ws), BH, L, nqb,
+                           lam_scale, eps, p);
     }
 }
 

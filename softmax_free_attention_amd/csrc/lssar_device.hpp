@@ -102,6 +102,33 @@ __device__ __forceinline__ float phi2(float t)
         return softplus2(t);
 }
 
+// Deep rows.  fp32 evaluates log2(1 + 2^t) through the rounding of 1 + 2^t,
+// whose absolute error 2^-24 is a relative error 2^-24 / 2^t of the result:
+// for t below about -8 the value loses digits, and below -24 it is 0.  A row
+// whose largest score is below kDeep (every Softplus2 value below
+// log2(1 + 2^kDeep)) is only as good as these digits, so its block is
+// computed again with softplus2_acc, which takes the series
+// ln(1 + e) = e - e^2 / 2 + ... for e = 2^t < 2^-8 (dropped terms below
+// 2^-17.6 relative) and the logarithm otherwise.  Stage 1 alone flags a row
+// whose mean Softplus2 value is below kDeepMean instead (its largest score
+// is not tracked there).
+constexpr float kDeep = -4.0f;
+constexpr float kDeepMean = 1.0f / 1024.0f;
+
+__device__ __forceinline__ float softplus2_acc(float t)
+{
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float e = __builtin_amdgcn_exp2f(t);
+    const float series = kLog2e * e * __builtin_fmaf(-0.5f, e, 1.0f);
+    return e < (1.0f / 256.0f) ? series : __builtin_amdgcn_logf(1.0f + e);
+}
+
+// What a run of pass 1 accumulates: S1 (in product form) and the row max,
+// S1 from softplus2_acc and the row max (blocks computed again), or the row
+// max alone.
+constexpr int kPass1Sum = 0;
+constexpr int kPass1Acc = 1;
+
 // y^P for y in [0, 1] by a fixed multiplication chain (P = 0: runtime p).
 template <int P, typename F>
 __device__ __forceinline__ F pow_chain(F y, int p)
@@ -135,18 +162,16 @@ __device__ __forceinline__ float reweight_arg(float sp, float c, float tc)
 }
 
 // Row constants after pass 1 (Key design 2).  i: 1-based row; s1: sum of
-// the row's phi values (base-2 Softplus or Sigmoid); tmax: the row's largest
-// scaled score (phi is increasing, so phi(tmax) is the row's largest value).
+// the row's phi values (base-2 Softplus or Sigmoid, or relative Softplus for
+// a deep row); spmax: the row's largest phi value.
 struct RowConst {
     float c;      // 1 / (sp_max - tau), or 0 for a degenerate row
     float tc;     // tau * c
     bool degen;
 };
 
-template <int PHI>
-__device__ __forceinline__ RowConst row_constants(int i, float s1, float tmax, float eps)
+__device__ __forceinline__ RowConst row_constants_sp(int i, float s1, float spmax, float eps)
 {
-    const float spmax = phi2<PHI>(tmax);
     const float o = (i <= 3) ? 0.0f : 1.0f;
     const float tau = o * s1 / (float)i;
     const float gap = spmax - tau;
@@ -156,6 +181,13 @@ __device__ __forceinline__ RowConst row_constants(int i, float s1, float tmax, f
     rc.c = rc.degen ? 0.0f : 1.0f / gap;
     rc.tc = tau * rc.c;
     return rc;
+}
+
+// ... from the row's largest scaled score tmax (phi is increasing)
+template <int PHI>
+__device__ __forceinline__ RowConst row_constants(int i, float s1, float tmax, float eps)
+{
+    return row_constants_sp(i, s1, phi2<PHI>(tmax), eps);
 }
 
 // fp64 versions for the fp32-input kernel.  With fp32 inputs the parity bar
@@ -232,43 +264,33 @@ __device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(
 // Prep kernels
 // ---------------------------------------------------------------------------
 
-// fk[row] = 1 / max(|k_row|_2, 1e-12) for every key row (Key design 1's
-// K_j <- K_j / |K_j|_2, kept as a factor of the score).
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void lssar_knorm_kernel(const T* __restrict__ K,
-                                                               float* __restrict__ fk,
-                                                               long nrows)
+// Prep for the fp32 kernel: fk[row] = 1 / max(|k_row|_2, 1e-12) in fp64 for
+// every key row (Key design 1's K_j <- K_j / |K_j|_2, kept as a factor of
+// the score).  fp64 because deep rows (every score far below 0) turn the
+// absolute error of a score into a relative error of its Softplus value.
+template <int D>
+__global__ __launch_bounds__(kThreads) void lssar_knorm_f32_kernel(const float* __restrict__ K,
+                                                                   double* __restrict__ fk,
+                                                                   long nrows)
 {
-    constexpr int EPL = 16 / (int)sizeof(T);   // elements per 16-byte load
-    constexpr int LPR = D / EPL;               // lanes per row
+    constexpr int LPR = D / 4;                 // lanes per row, 4 floats per lane
     constexpr int RPB = kThreads / LPR;        // rows per block
     const long row = (long)blockIdx.x * RPB + threadIdx.x / LPR;
     const int sub = threadIdx.x % LPR;
-    // squared norm accumulated in fp64, so fk carries one rounding only
     double ss = 0.0;
     if (row < nrows) {
-        if constexpr (sizeof(T) == 2) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(K + row * D + sub * EPL);
+        // loaded as a float vector: a bit-cast of an element of a u32x4 was
+        // lowered as element 0 for every index by this compiler
+        const f32x4 x = *reinterpret_cast<const f32x4*>(K + row * D + sub * 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const double a = bf16lo(w[e]), b = bf16hi(w[e]);
-                ss = fma(a, a, ss);
-                ss = fma(b, b, ss);
-            }
-        } else {
-            // loaded as a float vector: a bit-cast of an element of a u32x4
-            // was lowered as element 0 for every index by this compiler
-            const f32x4 x = *reinterpret_cast<const f32x4*>(K + row * D + sub * EPL);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                ss = fma((double)x[e], (double)x[e], ss);
-        }
+        for (int e = 0; e < 4; ++e)
+            ss = fma((double)x[e], (double)x[e], ss);
     }
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1)
         ss += __shfl_xor(ss, m, LPR);
     if (row < nrows && sub == 0)
-        fk[row] = (float)(1.0 / fmax(sqrt(ss), 1e-12));
+        fk[row] = 1.0 / fmax(sqrt(ss), 1e-12);
 }
 
 // Position of key `key` (0..63 of a 64-key block) inside a row of V^T.  With
@@ -432,7 +454,12 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
     constexpr int DC = D / 32;                 // MFMA k-steps over d
     constexpr int DS = D / 16;                 // 16-row blocks of O^T
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2][T::BYTES];
+    // One LDS object: the two tile buffers, then the deep-row flags.  (A
+    // second __shared__ object makes the compiler wait for the in-flight
+    // LDS-direct loads before every LDS read in the tile loops.)
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * T::BYTES + 16];
+    auto smem = [&](int buf) { return lds + buf * T::BYTES; };
+    int* const flags = reinterpret_cast<int*>(lds + 2 * T::BYTES);
 
     const int tid = threadIdx.x;
     // wave index in a scalar register, so per-wave decisions are uniform branches
@@ -479,7 +506,7 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
         vrd[c2] = T::KBYTES + (row16 * 8 + ((4 * c2 + grp) ^ T::vswz(row16))) * 16;
 
     auto issue = [&](int kt, int buf, bool with_v) {
-        unsigned char* base = smem[buf];
+        unsigned char* base = smem(buf);
 #pragma unroll
         for (int n = 0; n < T::KLOADS; ++n)
             load16_to_lds(kbase, kbytes, base + (wave * T::KLOADS + n) * 1024, kld[n],
@@ -498,7 +525,16 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
     const bf16x8 ones = {one, one, one, one, one, one, one, one};
     const int nblk = (pi == nqb - 1 - pi) ? 1 : 2;
 
-    for (int blk = 0; blk < nblk; ++blk) {
+    // deep-row flags of the workgroup's (up to) two query blocks; the first
+    // barrier of block 0 orders these stores before any flag is set.  The
+    // flags are read once, after a barrier that follows every block.
+    if (tid < 2)
+        flags[tid] = 0;
+
+    // One query block (blk 0: the pair's later block, blk 1: the earlier).
+    // REDO: the block computed again with softplus2_acc (deep rows).
+    auto block_body = [&](int blk, auto redo_tag) {
+        constexpr bool REDO = decltype(redo_tag)::value;
         const int qb = blk == 0 ? nqb - 1 - pi : pi;
         const int q0 = qb * kBQ16;
         const int qw0 = q0 + wave * kMQ16;         // first query row of this wave
@@ -556,11 +592,21 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
             return t;
         };
 
+        auto row_sum = [](float x) {
+            x += __shfl_xor(x, 16);
+            return x + __shfl_xor(x, 32);
+        };
+        auto row_max = [](float x) {
+            x = fmaxf(x, __shfl_xor(x, 16));
+            return fmaxf(x, __shfl_xor(x, 32));
+        };
+
         // ---------------- pass 1: S1 and the row max of the scores ----------------
         float s1 = 0.0f;
         float tmax = -INFINITY;
-        auto pass1_tile = [&](int kt, const unsigned char* base, auto diag_tag) {
+        auto pass1_tile = [&](int kt, const unsigned char* base, auto diag_tag, auto kind_tag) {
             constexpr bool DIAG = decltype(diag_tag)::value;
+            constexpr int KIND = decltype(kind_tag)::value;
             // 16-key blocks with at least one key <= the wave's last row
             const int nks = DIAG ? min(4, (qwl - kt * kBK) / 16 + 1) : 4;
             f32x4 acc[4];
@@ -574,7 +620,13 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
                 if (DIAG && ks >= nks)
                     continue;
                 const f32x4 t = scale_block(kt, base, ks, acc[ks], DIAG);
-                if constexpr (PHI == kPhiSoftplus) {
+                if constexpr (KIND == kPass1Acc) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        pos_sum += softplus2_acc(t[r]);
+                    tmax = fmaxf(fmaxf(tmax, t[0]), t[1]);
+                    tmax = fmaxf(fmaxf(tmax, t[2]), t[3]);
+                } else if constexpr (PHI == kPhiSoftplus) {
                     f32x4 u;
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
@@ -595,13 +647,12 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
                     tmax = fmaxf(fmaxf(tmax, t[2]), t[3]);
                 }
             }
-            if constexpr (PHI == kPhiSoftplus)
+            if constexpr (KIND == kPass1Sum && PHI == kPhiSoftplus)
                 s1 += pos_sum + __builtin_amdgcn_logf(prod);
             else
                 s1 += pos_sum;
         };
-        RowConst rc = {0.0f, 0.0f, false};
-        if constexpr (RW) {
+        auto run_pass1 = [&](auto kind_tag) {
             __syncthreads();                       // LDS buffers free
             issue(0, 0, false);
             for (int kt = 0; kt < ntiles; ++kt) {
@@ -613,18 +664,26 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
                 if (!(wave_active && kt * kBK <= qwl))
                     continue;
                 if (kt * kBK + kBK - 1 > qw0)
-                    pass1_tile(kt, smem[buf], std::true_type{});
+                    pass1_tile(kt, smem(buf), std::true_type{}, kind_tag);
                 else
-                    pass1_tile(kt, smem[buf], std::false_type{});
+                    pass1_tile(kt, smem(buf), std::false_type{}, kind_tag);
             }
+        };
 
-            float sum = s1;
-            sum += __shfl_xor(sum, 16);
-            sum += __shfl_xor(sum, 32);
-            float t = tmax;
-            t = fmaxf(t, __shfl_xor(t, 16));
-            t = fmaxf(t, __shfl_xor(t, 32));
-            rc = row_constants<PHI>(qi + 1, sum, t, eps);
+        RowConst rc = {0.0f, 0.0f, false};
+        if constexpr (RW) {
+            if constexpr (REDO) {
+                run_pass1(std::integral_constant<int, kPass1Acc>{});
+                const float trow = row_max(tmax);
+                rc = row_constants_sp(qi + 1, row_sum(s1), softplus2_acc(trow), eps);
+            } else {
+                run_pass1(std::integral_constant<int, kPass1Sum>{});
+                const float trow = row_max(tmax);
+                rc = row_constants<PHI>(qi + 1, row_sum(s1), trow, eps);
+                if constexpr (PHI == kPhiSoftplus)
+                    if (qi < L && trow < kDeep)
+                        flags[blk] = 1;
+            }
         }
 
         // ---------------- pass 2: re-weight, P.V and the weight sum ----------------
@@ -636,7 +695,11 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
 
         auto weights = [&](f32x4 t) {
             f32x4 e, w;
-            if constexpr (PHI == kPhiSoftplus) {
+            if constexpr (REDO) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    e[r] = softplus2_acc(t[r]);
+            } else if constexpr (PHI == kPhiSoftplus) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     e[r] = __builtin_amdgcn_exp2f(t[r]);
@@ -697,10 +760,13 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
             if (!(wave_active && kt * kBK <= qwl))
                 continue;
             if (kt * kBK + kBK - 1 > qw0)
-                pass2_tile(kt, smem[buf], std::true_type{});
+                pass2_tile(kt, smem(buf), std::true_type{});
             else
-                pass2_tile(kt, smem[buf], std::false_type{});
+                pass2_tile(kt, smem(buf), std::false_type{});
         }
+        if constexpr (!RW && PHI == kPhiSoftplus && !REDO)
+            if (qi < L && dacc[0] < (float)(qi + 1) * kDeepMean)
+                flags[blk] = 1;
 
         // ---------------- finalize: out_i = U_i / D_i (0 if degenerate) ----------------
         if (qi < L) {
@@ -712,6 +778,15 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
                 *reinterpret_cast<bf16x4*>(Oh + (size_t)qi * D + 16 * ds + 4 * grp) = ob;
             }
         }
+    };
+
+    for (int blk = 0; blk < nblk; ++blk)
+        block_body(blk, std::false_type{});
+    if constexpr (PHI == kPhiSoftplus) {
+        __syncthreads();                           // every block's flag is set
+        for (int blk = 0; blk < nblk; ++blk)
+            if (flags[blk])
+                block_body(blk, std::true_type{});
     }
 }
 
@@ -727,7 +802,7 @@ template <int D, int P, int PHI, bool RW>
 __global__ __launch_bounds__(kThreads, 1) void lssar_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K,
     const float* __restrict__ V, float* __restrict__ O,
-    const float* __restrict__ FK, int BH, int L, int nqb, double lam_scale,
+    const double* __restrict__ FK, int BH, int L, int nqb, double lam_scale,
     float eps, int p_rt)
 {
     static_assert(D == 64 || D == 128, "head dim");
@@ -738,7 +813,7 @@ __global__ __launch_bounds__(kThreads, 1) void lssar_fwd_f32_kernel(
 
     __shared__ __attribute__((aligned(16))) float Ks[kBK * KS];
     __shared__ __attribute__((aligned(16))) float Vs[kBK * KS];
-    __shared__ __attribute__((aligned(16))) float Fs[kBK];
+    __shared__ __attribute__((aligned(16))) double Fs[kBK];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -751,7 +826,7 @@ __global__ __launch_bounds__(kThreads, 1) void lssar_fwd_f32_kernel(
     const float* Kh = K + hoff;
     const float* Vh = V + hoff;
     float* Oh = O + hoff;
-    const float* Fh = FK + (size_t)bh * L;
+    const double* Fh = FK + (size_t)bh * L;
 
     const int qw0 = q0 + wave * kMQ32;
     const int qwl = min(qw0 + kMQ32 - 1, L - 1);
@@ -792,7 +867,7 @@ __global__ __launch_bounds__(kThreads, 1) void lssar_fwd_f32_kernel(
         }
         if (tid < kBK) {
             const int kg = kt * kBK + tid;
-            Fs[tid] = kg < L ? Fh[kg] : 0.0f;
+            Fs[tid] = kg < L ? Fh[kg] : 0.0;
         }
     };
 
@@ -842,7 +917,7 @@ __global__ __launch_bounds__(kThreads, 1) void lssar_fwd_f32_kernel(
                         const int key = key_of(ks, r);
                         const bool ok = kt * kBK + key <= qi[qs];
                         if (ok) {
-                            const double t = acc[ks][qs][r] * (lam[qs] * (double)Fs[key]);
+                            const double t = acc[ks][qs][r] * (lam[qs] * Fs[key]);
                             part[qs] += phi2_f64<PHI>(t);
                             tmax[qs] = fmax(tmax[qs], t);
                         }
@@ -891,7 +966,7 @@ __global__ __launch_bounds__(kThreads, 1) void lssar_fwd_f32_kernel(
                     const bool ok = kt * kBK + key <= qi[qs];
                     float wv = 0.0f;
                     if (ok) {
-                        const double t = acc[ks][qs][r] * (lam[qs] * (double)Fs[key]);
+                        const double t = acc[ks][qs][r] * (lam[qs] * Fs[key]);
                         if constexpr (RW) {
                             double y = phi2_f64<PHI>(t) * rc[qs].c - rc[qs].tc;
                             y = fmin(fmax(y, 0.0), 1.0);

@@ -72,10 +72,11 @@ def test_version_and_status_strings(L):
 
 
 def test_workspace_bytes(L):
-    # fp32: one fp32 factor per key row, rounded up to 256 bytes
+    # fp32: one fp64 factor per key row, rounded up to 256 bytes
     assert sfa.lssar_workspace_bytes(1, 1, 1, 64, sfa.LSSAR_F32) == 256
     assert sfa.lssar_workspace_bytes(2, 3, 5, 128, sfa.LSSAR_F32) == 256
-    assert sfa.lssar_workspace_bytes(1, 1, 100, 64, sfa.LSSAR_F32) == 512
+    assert sfa.lssar_workspace_bytes(1, 1, 100, 64, sfa.LSSAR_F32) == 1024
+    assert sfa.lssar_workspace_bytes(1, 1, 32, 64, sfa.LSSAR_F32) == 256
     # bf16: plus V^T with rows padded to a multiple of 64 keys
     assert sfa.lssar_workspace_bytes(1, 12, 8192, 64, sfa.LSSAR_BF16) == 4 * 12 * 8192 + 12 * 64 * 8192 * 2
     assert sfa.lssar_workspace_bytes(2, 3, 77, 128, sfa.LSSAR_BF16) == 2048 + 6 * 128 * 128 * 2

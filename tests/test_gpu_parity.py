@@ -178,7 +178,8 @@ def test_bitwise_determinism_and_entry_points_agree():
 
 
 def test_prep_workspace_contents():
-    """Stage 1 writes 1/max(|k_j|, 1e-12) per key row and, for bf16, V^T with
+    """The prep step writes 1/max(|k_j|, 1e-12) per key row (fp32 for bf16,
+    fp64 for fp32 inputs) and, for bf16, V^T with
     every 64-key block permuted for the attention kernel, zero past L."""
     import softmax_free_attention_amd as sfa
     for dtype, d in (("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)):
@@ -192,9 +193,10 @@ def test_prep_workspace_contents():
         torch.cuda.synchronize()
         raw = ws.cpu().numpy()
         nrow = 2 * 3 * L
-        fk = raw[:4 * nrow].view(np.float32).reshape(2, 3, L)
+        fdt = np.float32 if dtype == "bf16" else np.float64
+        fk = raw[:fdt().itemsize * nrow].view(fdt).reshape(2, 3, L)
         want = 1.0 / np.maximum(np.linalg.norm(k.astype(np.float64), axis=-1), 1e-12)
-        assert np.max(np.abs(fk / want - 1.0)) < 1e-6
+        assert np.max(np.abs(fk / want - 1.0)) < (1e-6 if dtype == "bf16" else 1e-14)
         if dtype == "bf16":
             Lp = 128
             off = (4 * nrow + 255) // 256 * 256

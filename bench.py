@@ -19,7 +19,11 @@ the host's cores), "sweep" (the same path at L = 1K..16K, H=12, d=64,
 p=15, B = 16384/L, on device-generated N(0,1) inputs) and "variants" (the
 note's two ablation variants on the same resident inputs: the Sigmoid
 stage-1 map with re-weighting, and stage 1 alone, each timed as its whole
-entry point, prep included).
+entry point, prep included) and "decode" (the decode step over a key/value
+cache: 16 sequences x 12 heads at 8192 cached tokens, the same with ragged
+lengths, and a wide-head case; HBM-bound, reported as GB/s of algorithmic
+bytes and tokens/s; caches drawn N(0,1) on the device, lengths from the
+input generator).
 """
 from __future__ import annotations
 
@@ -143,6 +147,48 @@ def time_variants(q, k, v, p, steps, warmup, eps=1e-4):
     return res
 
 
+def time_decode(name, steps, warmup):
+    """Mean time of one decode step (lssar_decode_ws: three kernels) on a
+    device-generated cache, HIP events on the launch stream."""
+    import numpy as np
+    import torch
+    import lssar_inputs as gen
+    import softmax_free_attention_amd as sfa
+    wl = gen.DECODE_WORKLOADS[name]
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed)
+    q = torch.randn((wl.B, wl.H, wl.d), generator=g, device="cuda").to(dt)
+    k = torch.randn((wl.B, wl.H, wl.Lmax, wl.d), generator=g, device="cuda").to(dt)
+    v = torch.randn((wl.B, wl.H, wl.Lmax, wl.d), generator=g, device="cuda").to(dt)
+    lens_np = gen.decode_lens(wl)
+    lens = torch.from_numpy(lens_np).cuda()
+    ws = sfa.decode_workspace_for(k)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        sfa.lssar_decode_ws(q, k, v, lens, out, ws, p=wl.p, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        sfa.lssar_decode_ws(q, k, v, lens, out, ws, p=wl.p, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    eb = 2 if wl.dtype == "bf16" else 4
+    # algorithmic bytes: K and V rows in use read once, q read, out written, lens
+    nbytes = 2 * wl.H * wl.d * eb * int(lens_np.sum()) + 2 * wl.B * wl.H * wl.d * eb + 4 * wl.B
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del q, k, v, ws, out
+    return {"B": wl.B, "H": wl.H, "Lmax": wl.Lmax, "d": wl.d, "p": wl.p, "lens": wl.lens,
+            "mean_len": round(float(lens_np.mean()), 1), "ms": round(ms, 5),
+            "tokens_per_s": round(wl.B / (ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "bytes": nbytes}}
+
+
 def cpu_baseline(inp, seconds: float):
     """The fp64 oracle, as it stands, on a bounded sample of the workload's
     rows (strided over all heads and positions), on all host cores."""
@@ -203,6 +249,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--calib-mib", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB (read N, "
                          "write N), the reference kernel for scaling rocprofv3 FETCH/WRITE_SIZE")
@@ -264,6 +311,10 @@ def main():
         vt = time_variants(q, k, v, wl.p, args.steps, args.warmup)
         line["variants"] = {n: {"ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
                             for n, ms in vt.items()}
+    if not args.no_decode:
+        log("bench: decode")
+        line["decode"] = {n: time_decode(n, 50, 10)
+                          for n in ("x8_decode", "x8_decode_ragged", "wide_decode")}
     if not args.no_sweep:
         log("bench: L sweep")
         line["sweep"] = sweep(steps=10, warmup=3)

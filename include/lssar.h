@@ -132,6 +132,33 @@ int lssar_lssa_fwd_ws(const void* q, const void* k, const void* v, void* out,
                       int B, int H, int L, int d, int dtype, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* Workspace of lssar_decode_ws, in bytes (0 for invalid sizes): per cache
+ * row one score, per 256-row chunk of every head 2 + (d + 1) partial sums;
+ * fp32 values for bf16 inputs, fp64 for fp32 inputs; each part rounded up
+ * to 256 bytes. */
+size_t lssar_decode_workspace_bytes(int B, int H, int Lmax, int d, int dtype);
+
+/* Decode step over a key/value cache: for every (b, h) one new query at
+ * 1-based position i = lens[b] attends to cache rows 1..i, and out[b, h] is
+ * row i of the causal forward (Key designs 1-3, same readings, same
+ * degenerate-row rule).  The note's Limitations and main results concern
+ * this use: extrapolation to 8-16x the training length at inference.
+ *  - q, out: DEVICE [B, H, d]; k_cache, v_cache: DEVICE [B, H, Lmax, d] with
+ *    the new token's key and value already written at row i - 1 (0-based);
+ *    rows at or past lens[b] are never read.  One dtype, 16-byte aligned;
+ *    out overlaps nothing.
+ *  - lens: DEVICE int32 [B] (4-byte aligned) or NULL (every sequence uses
+ *    all Lmax rows).  Read by the kernels, so it can change between calls
+ *    (and between replays of a captured graph) without host involvement.
+ *    Values are clamped to [0, Lmax]; a sequence of length 0 gets zeros.
+ *  - p, eps, dtype, errors: as for lssar_attn_fwd_ws.  d in {64, 128}.
+ *  - workspace: lssar_decode_workspace_bytes(), 256-byte aligned, overlapping
+ *    no argument.  Allocates nothing; three kernel launches on `stream`. */
+int lssar_decode_ws(const void* q, const void* k_cache, const void* v_cache,
+                    const int* lens, void* out, int B, int H, int Lmax, int d,
+                    int p, float eps, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* lssar_status_str(int status);
 

@@ -36,6 +36,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "workload", "normals", "uniforms", "words",
     "round_to_bf16", "bf16_bits", "make_inputs", "Inputs",
+    "DecodeWorkload", "DECODE_WORKLOADS", "DecodeInputs", "make_decode_inputs", "decode_lens",
 ]
 
 _GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -83,23 +84,42 @@ def uniforms(seed: int, stream: int, start: int, count: int) -> np.ndarray:
     return ((w >> np.uint64(11)).astype(np.float64) + 1.0) * (2.0 ** -53)
 
 
+def _normals_into(out: np.ndarray, seed: int, stream: int, start: int, p0: int, p1: int) -> None:
+    u = uniforms(seed, stream, start + 2 * p0, 2 * (p1 - p0))
+    r = np.sqrt(-2.0 * np.log(u[0::2]))
+    th = (2.0 * math.pi) * u[1::2]
+    out[2 * p0:2 * p1:2] = r * np.cos(th)
+    out[2 * p0 + 1:2 * p1:2] = r * np.sin(th)
+
+
 def normals(seed: int, stream: int, start: int, count: int) -> np.ndarray:
     """Standard normal fp64 draws by Box-Muller over consecutive word pairs.
 
     Normal ``2m`` and ``2m+1`` of a stream both come from words ``2m, 2m+1``;
     ``start`` must be even so that a slice reproduces the full sequence.
+    Large draws are split into chunks that threads fill independently (each
+    element depends on its counter only, so the values do not change).
     """
     assert start % 2 == 0
     npairs = (count + 1) // 2
     out = np.empty(2 * npairs, dtype=np.float64)
-    for p0 in range(0, npairs, _CHUNK // 2):
-        p1 = min(npairs, p0 + _CHUNK // 2)
-        u = uniforms(seed, stream, start + 2 * p0, 2 * (p1 - p0))
-        r = np.sqrt(-2.0 * np.log(u[0::2]))
-        th = (2.0 * math.pi) * u[1::2]
-        out[2 * p0:2 * p1:2] = r * np.cos(th)
-        out[2 * p0 + 1:2 * p1:2] = r * np.sin(th)
+    chunks = [(p0, min(npairs, p0 + _CHUNK // 2)) for p0 in range(0, npairs, _CHUNK // 2)]
+    if len(chunks) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(len(chunks), _threads())) as ex:
+            list(ex.map(lambda c: _normals_into(out, seed, stream, start, c[0], c[1]), chunks))
+    else:
+        for p0, p1 in chunks:
+            _normals_into(out, seed, stream, start, p0, p1)
     return out[:count]
+
+
+def _threads() -> int:
+    import os
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return max(1, min(16, os.cpu_count() or 1))
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -180,8 +200,25 @@ class Inputs:
 
 
 def _finish(x: np.ndarray, dtype: str) -> np.ndarray:
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    return round_to_bf16(x) if dtype == "bf16" else x
+    """fp64 draws -> fp32 (round to nearest) -> bf16 values for bf16 workloads;
+    large arrays are converted in chunks by threads."""
+    src = np.ascontiguousarray(x).reshape(-1)
+    out = np.empty(src.shape, dtype=np.float32)
+
+    def conv(c0):
+        c1 = min(src.size, c0 + _CHUNK)
+        y = src[c0:c1].astype(np.float32)
+        out[c0:c1] = round_to_bf16(y) if dtype == "bf16" else y
+
+    starts = range(0, src.size, _CHUNK)
+    if len(starts) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(len(starts), _threads())) as ex:
+            list(ex.map(conv, starts))
+    else:
+        for c0 in starts:
+            conv(c0)
+    return out.reshape(x.shape)
 
 
 def _iid(wl: Workload, stream: int) -> np.ndarray:
@@ -271,3 +308,75 @@ def make_inputs(wl: Workload | str, **overrides) -> Inputs:
         k = _finish(kk, wl.dtype)
     v = _finish(v, wl.dtype)
     return Inputs(wl, q, k, v, meta)
+
+
+# --------------------------------------------------------------------------
+# Decode step: one new query per (batch, head) against a key/value cache
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """A batch of B sequences, each with its own cache length lens[b] <= Lmax.
+    lens: "full" (every sequence at Lmax) or "ragged" (uniform in
+    [Lmax/2, Lmax] from the auxiliary stream)."""
+    name: str
+    B: int
+    H: int
+    Lmax: int
+    d: int
+    dtype: str
+    p: int
+    lens: str = "full"
+    seed: int = 0
+    note: str = ""
+
+    def with_(self, **kw) -> "DecodeWorkload":
+        f = {k: getattr(self, k) for k in self.__dataclass_fields__}
+        f.update(kw)
+        return DecodeWorkload(**f)
+
+
+DECODE_WORKLOADS = {
+    "x8_decode": DecodeWorkload("x8_decode", 16, 12, 8192, 64, "bf16", 15, "full",
+                                note="8x extrapolation at inference: 16 sequences of 8192 "
+                                     "cached tokens, GPT-2-small heads"),
+    "x8_decode_ragged": DecodeWorkload("x8_decode_ragged", 16, 12, 8192, 64, "bf16", 15,
+                                       "ragged", note="as x8_decode, lengths in [4096, 8192]"),
+    "wide_decode": DecodeWorkload("wide_decode", 4, 32, 4096, 128, "bf16", 15, "ragged",
+                                  note="wide heads, lengths in [2048, 4096]"),
+}
+
+
+@dataclass
+class DecodeInputs:
+    """q [B,H,d]; k, v [B,H,Lmax,d] (dtype-exact fp32 values); lens int32 [B]."""
+    wl: DecodeWorkload
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    lens: np.ndarray
+
+
+def make_decode_inputs(wl: DecodeWorkload | str, **overrides) -> DecodeInputs:
+    """Cache rows and queries i.i.d. N(0,1) from streams K, V and Q; lengths
+    from the auxiliary stream.  Rows past a sequence's length are drawn too
+    (they must never be read)."""
+    if isinstance(wl, str):
+        wl = DECODE_WORKLOADS[wl]
+    if overrides:
+        wl = wl.with_(**overrides)
+    B, H, L, d = wl.B, wl.H, wl.Lmax, wl.d
+    q = normals(wl.seed, STREAM_Q, 0, B * H * d).reshape(B, H, d)
+    k = normals(wl.seed, STREAM_K, 0, B * H * L * d).reshape(B, H, L, d)
+    v = normals(wl.seed, STREAM_V, 0, B * H * L * d).reshape(B, H, L, d)
+    return DecodeInputs(wl, _finish(q, wl.dtype), _finish(k, wl.dtype), _finish(v, wl.dtype),
+                        decode_lens(wl))
+
+
+def decode_lens(wl: DecodeWorkload) -> np.ndarray:
+    """Cache length of each sequence (int32 [B])."""
+    B, L = wl.B, wl.Lmax
+    if wl.lens == "full":
+        return np.full(B, L, dtype=np.int32)
+    u = uniforms(wl.seed, STREAM_AUX, 0, B)
+    return np.minimum(L // 2 + (u * (L - L // 2 + 1)).astype(np.int64), L).astype(np.int32)

@@ -24,6 +24,7 @@ __all__ = [
     "lssar_prep", "lssar_attn_fwd_prepped", "lssar_status_str", "workspace_for",
     "lssar_last_hip_error", "lssar_version", "DEFAULT_EPS", "LSSAR_PHI_SOFTPLUS",
     "LSSAR_PHI_SIGMOID", "lssar_attn_fwd_phi_ws", "lssar_lssa_fwd_ws",
+    "lssar_decode_workspace_bytes", "lssar_decode_ws", "decode_workspace_for",
 ]
 
 LSSAR_F32, LSSAR_BF16 = 0, 1
@@ -68,6 +69,10 @@ def lib():
         L.lssar_attn_fwd_phi_ws.restype = i
         L.lssar_lssa_fwd_ws.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, sz, vp]
         L.lssar_lssa_fwd_ws.restype = i
+        L.lssar_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.lssar_decode_workspace_bytes.restype = sz
+        L.lssar_decode_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+        L.lssar_decode_ws.restype = i
         L.lssar_status_str.argtypes = [i]
         L.lssar_status_str.restype = ctypes.c_char_p
         L.lssar_last_hip_error.argtypes = []
@@ -219,4 +224,47 @@ def lssar_lssa_fwd_ws(q, k, v, out, workspace, *, stream=None):
     st = lib().lssar_lssa_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, L, d, dt, wp, wn,
                                  _stream_ptr(stream))
     _raise(st, "lssar_lssa_fwd_ws")
+    return out
+
+
+def lssar_decode_workspace_bytes(B: int, H: int, Lmax: int, d: int, dtype: int) -> int:
+    return int(lib().lssar_decode_workspace_bytes(B, H, Lmax, d, dtype))
+
+
+def decode_workspace_for(k_cache):
+    """A device byte tensor of lssar_decode_workspace_bytes for a cache shaped
+    like k_cache ([B, H, Lmax, d])."""
+    import torch
+    B, H, Lmax, d = k_cache.shape
+    n = lssar_decode_workspace_bytes(B, H, Lmax, d, _dtype_code(k_cache))
+    if n == 0:
+        raise ValueError(f"unsupported cache shape {tuple(k_cache.shape)} / dtype {k_cache.dtype}")
+    return torch.empty(n, dtype=torch.uint8, device=k_cache.device)
+
+
+def lssar_decode_ws(q, k_cache, v_cache, lens, out, workspace, *, p: int,
+                    eps: float = DEFAULT_EPS, stream=None):
+    """Decode step: q and out [B, H, d], caches [B, H, Lmax, d], lens a device
+    int32 tensor [B] (1-based position of each sequence's query) or None (all
+    Lmax rows).  Returns out."""
+    import torch
+    for name, t in (("q", q), ("out", out)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 3 or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a contiguous device tensor [B, H, d] of q's dtype")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4 or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a contiguous device tensor [B, H, Lmax, d]")
+    B, H, Lmax, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or tuple(q.shape) != (B, H, d) or out.shape != q.shape:
+        raise ValueError("q/out [B, H, d] and caches [B, H, Lmax, d] must agree")
+    lp = None
+    if lens is not None:
+        if not lens.is_cuda or lens.dtype != torch.int32 or lens.numel() != B or \
+                not lens.is_contiguous():
+            raise ValueError("lens must be a contiguous device int32 tensor of B entries")
+        lp = _ptr(lens)
+    wp, wn = _ws_args(workspace)
+    st = lib().lssar_decode_ws(_ptr(q), _ptr(k_cache), _ptr(v_cache), lp, _ptr(out), B, H, Lmax,
+                               d, int(p), float(eps), _dtype_code(q), wp, wn, _stream_ptr(stream))
+    _raise(st, "lssar_decode_ws")
     return out

@@ -15,6 +15,7 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "lssar_decode.hpp"
 #include "lssar_device.hpp"
 
 namespace {
@@ -262,6 +263,79 @@ int fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H,
     return run_fwd(q, k, v, workspace, out, B, H, L, d, p, eps, dtype, s, var);
 }
 
+// ---------------------------------------------------------------------------
+// Decode step
+// ---------------------------------------------------------------------------
+
+// Workspace: [scores: C per cache row][part1: 2 C per chunk][part2: d+1 C per
+// chunk], C = fp32 for bf16 inputs and fp64 for fp32 inputs, each part
+// rounded up to 256 bytes.
+struct DecLayout {
+    size_t scores_bytes, part1_bytes, part2_bytes;
+    int nsplit;
+    size_t total() const { return scores_bytes + part1_bytes + part2_bytes; }
+};
+
+DecLayout dec_layout(long long B, long long H, long long Lmax, int d, int dtype)
+{
+    DecLayout w;
+    const size_t cb = dtype == LSSAR_F32 ? 8 : 4;
+    w.nsplit = (int)((Lmax + lssar::kDecChunk - 1) / lssar::kDecChunk);
+    const size_t bh = (size_t)(B * H);
+    w.scores_bytes = round256(cb * bh * (size_t)Lmax);
+    w.part1_bytes = round256(cb * bh * (size_t)w.nsplit * 2);
+    w.part2_bytes = round256(cb * bh * (size_t)w.nsplit * (size_t)(d + 1));
+    return w;
+}
+
+int validate_decode_shape(int B, int H, int Lmax, int d, int dtype)
+{
+    int st = validate_shape(B, H, Lmax, d, dtype);
+    if (st != LSSAR_OK)
+        return st;
+    const long long nsplit = (Lmax + lssar::kDecChunk - 1) / lssar::kDecChunk;
+    if ((long long)B * H * nsplit > (1LL << 31) - 1)
+        return LSSAR_EINVAL;
+    return LSSAR_OK;
+}
+
+template <typename T, int D, int P>
+void launch_decode(const void* q, const void* kc, const void* vc, const int* lens, void* out,
+                   void* ws, int B, int H, int Lmax, int p, float eps, double lam_scale,
+                   hipStream_t s)
+{
+    using C = typename lssar::DecTraits<T>::C;
+    const DecLayout w = dec_layout(B, H, Lmax, D, std::is_same<T, float>::value ? LSSAR_F32
+                                                                                 : LSSAR_BF16);
+    auto* base = static_cast<unsigned char*>(ws);
+    C* scores = reinterpret_cast<C*>(base);
+    C* part1 = reinterpret_cast<C*>(base + w.scores_bytes);
+    C* part2 = reinterpret_cast<C*>(base + w.scores_bytes + w.part1_bytes);
+    const int BH = B * H;
+    const unsigned grid = (unsigned)((long long)BH * w.nsplit);
+    hipLaunchKernelGGL((lssar::lssar_decode_scores_kernel<T, D>), dim3(grid),
+                       dim3(lssar::kDecThreads), 0, s, static_cast<const T*>(q),
+                       static_cast<const T*>(kc), lens, scores, part1, H, Lmax, w.nsplit,
+                       lam_scale);
+    hipLaunchKernelGGL((lssar::lssar_decode_pv_kernel<T, D, P>), dim3(grid),
+                       dim3(lssar::kDecThreads), 0, s, static_cast<const T*>(vc), lens,
+                       scores, part1, part2, H, Lmax, w.nsplit, eps, p);
+    hipLaunchKernelGGL((lssar::lssar_decode_combine_kernel<T, D>), dim3((unsigned)BH), dim3(D), 0,
+                       s, lens, part2, static_cast<T*>(out), H, Lmax, w.nsplit);
+}
+
+template <typename T, int D>
+void decode_dispatch_p(const void* q, const void* kc, const void* vc, const int* lens, void* out,
+                       void* ws, int B, int H, int Lmax, int p, float eps, double lam_scale,
+                       hipStream_t s)
+{
+    switch (p) {
+    case 3: launch_decode<T, D, 3>(q, kc, vc, lens, out, ws, B, H, Lmax, p, eps, lam_scale, s); break;
+    case 15: launch_decode<T, D, 15>(q, kc, vc, lens, out, ws, B, H, Lmax, p, eps, lam_scale, s); break;
+    default: launch_decode<T, D, 0>(q, kc, vc, lens, out, ws, B, H, Lmax, p, eps, lam_scale, s); break;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -353,6 +427,67 @@ int lssar_attn_fwd_prepped(const void* q, const void* k, const void* v, void* wo
                    static_cast<hipStream_t>(stream));
 }
 
+size_t lssar_decode_workspace_bytes(int B, int H, int Lmax, int d, int dtype)
+{
+    if (validate_decode_shape(B, H, Lmax, d, dtype) != LSSAR_OK)
+        return 0;
+    return dec_layout(B, H, Lmax, d, dtype).total();
+}
+
+int lssar_decode_ws(const void* q, const void* k_cache, const void* v_cache, const int* lens,
+                    void* out, int B, int H, int Lmax, int d, int p, float eps, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!q || !k_cache || !v_cache || !out)
+        return LSSAR_EINVAL;
+    if (p < 1 || !(eps >= 0.0f) || !std::isfinite(eps))
+        return LSSAR_EINVAL;
+    int st = validate_decode_shape(B, H, Lmax, d, dtype);
+    if (st != LSSAR_OK)
+        return st;
+    if (p > kMaxP)
+        return LSSAR_EUNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        (reinterpret_cast<uintptr_t>(lens) & 3u) != 0)
+        return LSSAR_EINVAL;
+    const size_t eb = elem_bytes(dtype);
+    const size_t qbytes = (size_t)B * H * d * eb;
+    const size_t cbytes = (size_t)B * H * Lmax * d * eb;
+    const size_t lbytes = lens ? (size_t)B * sizeof(int) : 0;
+    if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k_cache, cbytes) ||
+        overlaps(out, qbytes, v_cache, cbytes) || (lens && overlaps(out, qbytes, lens, lbytes)))
+        return LSSAR_EINVAL;
+    const DecLayout w = dec_layout(B, H, Lmax, d, dtype);
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+        workspace_bytes < w.total())
+        return LSSAR_EWORKSPACE;
+    if (overlaps(workspace, w.total(), q, qbytes) || overlaps(workspace, w.total(), k_cache, cbytes) ||
+        overlaps(workspace, w.total(), v_cache, cbytes) || overlaps(workspace, w.total(), out, qbytes) ||
+        (lens && overlaps(workspace, w.total(), lens, lbytes)))
+        return LSSAR_EWORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const double lam_scale = std::log((double)d) / std::log(2.0);
+    if (dtype == LSSAR_BF16) {
+        if (d == 64)
+            decode_dispatch_p<__bf16, 64>(q, k_cache, v_cache, lens, out, workspace, B, H, Lmax,
+                                          p, eps, lam_scale, s);
+        else
+            decode_dispatch_p<__bf16, 128>(q, k_cache, v_cache, lens, out, workspace, B, H, Lmax,
+                                           p, eps, lam_scale, s);
+    } else {
+        if (d == 64)
+            decode_dispatch_p<float, 64>(q, k_cache, v_cache, lens, out, workspace, B, H, Lmax,
+                                         p, eps, lam_scale, s);
+        else
+            decode_dispatch_p<float, 128>(q, k_cache, v_cache, lens, out, workspace, B, H, Lmax,
+                                          p, eps, lam_scale, s);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return hip_fail(e);
+    return LSSAR_OK;
+}
+
 const char* lssar_status_str(int status)
 {
     switch (status) {
@@ -367,6 +502,6 @@ const char* lssar_status_str(int status)
 
 int lssar_last_hip_error(void) { return g_last_hip_error; }
 
-int lssar_version(void) { return 300; }
+int lssar_version(void) { return 400; }
 
 }  // extern "C"

@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("lssar_attn_fwd", "lssar_attn_fwd_ws", "lssar_workspace_bytes",
               "lssar_status_str", "lssar_prep", "lssar_attn_fwd_prepped",
-              "lssar_attn_fwd_phi_ws", "lssar_lssa_fwd_ws"):
+              "lssar_attn_fwd_phi_ws", "lssar_lssa_fwd_ws", "lssar_decode_ws",
+              "lssar_decode_workspace_bytes"):
         assert n in names
 
 
@@ -63,7 +64,7 @@ def test_library_has_no_oracle_dependency(L):
 
 
 def test_version_and_status_strings(L):
-    assert sfa.lssar_version() == 300
+    assert sfa.lssar_version() == 400
     assert sfa.lssar_status_str(0) == "ok"
     for st in (-1, -2, -3, -4, 7):
         s = sfa.lssar_status_str(st)
@@ -166,4 +167,47 @@ def test_variant_entries_validate(L):
     assert lssa(q, k, v, o, 1, 2, 64, 64, 3, ws, 1 << 20, None) == sfa.LSSAR_EUNSUPPORTED
     assert lssa(q, k, v, o, 1, 2, 64, 64, 1, 0, 1 << 20, None) == sfa.LSSAR_EWORKSPACE
     assert lssa(q, k, v, o, 1, 2, 64, 64, 1, o + 256, 1 << 20, None) == sfa.LSSAR_EWORKSPACE
+    assert sfa.lssar_last_hip_error() == 0
+
+
+def test_decode_workspace_bytes(L):
+    # bf16: fp32 scores per cache row, 2 + (d + 1) fp32 partials per 256-row chunk
+    r = lambda x: (x + 255) // 256 * 256
+    assert sfa.lssar_decode_workspace_bytes(16, 12, 8192, 64, sfa.LSSAR_BF16) == \
+        r(4 * 192 * 8192) + r(4 * 192 * 32 * 2) + r(4 * 192 * 32 * 65)
+    assert sfa.lssar_decode_workspace_bytes(3, 2, 300, 128, sfa.LSSAR_F32) == \
+        r(8 * 6 * 300) + r(8 * 6 * 2 * 2) + r(8 * 6 * 2 * 129)
+    assert sfa.lssar_decode_workspace_bytes(1, 1, 1, 64, sfa.LSSAR_BF16) == 256 + 256 + 512
+    assert sfa.lssar_decode_workspace_bytes(1, 1, 1, 96, sfa.LSSAR_BF16) == 0
+    assert sfa.lssar_decode_workspace_bytes(0, 1, 1, 64, sfa.LSSAR_BF16) == 0
+
+
+def test_decode_validates_before_any_hip_call(L):
+    q, k, v, o, ws, ln = A, A + STEP, A + 2 * STEP, A + 3 * STEP, A + 4 * STEP, A + 5 * STEP
+    dec = L.lssar_decode_ws
+    big = 1 << 30
+
+    def call(q=q, k=k, v=v, ln=ln, o=o, B=2, H=2, Lm=100, d=64, p=3, eps=1e-4, dt=1, ws=ws,
+             wsb=big):
+        return dec(q, k, v, ln, o, B, H, Lm, d, p, eps, dt, ws, wsb, None)
+
+    assert call(q=0) == sfa.LSSAR_EINVAL
+    assert call(k=0) == sfa.LSSAR_EINVAL
+    assert call(o=0) == sfa.LSSAR_EINVAL
+    assert call(p=0) == sfa.LSSAR_EINVAL
+    assert call(eps=float("nan")) == sfa.LSSAR_EINVAL
+    assert call(Lm=0) == sfa.LSSAR_EINVAL
+    assert call(d=80) == sfa.LSSAR_EUNSUPPORTED
+    assert call(dt=3) == sfa.LSSAR_EUNSUPPORTED
+    assert call(p=2000) == sfa.LSSAR_EUNSUPPORTED
+    assert call(q=q + 8) == sfa.LSSAR_EINVAL                    # misaligned
+    assert call(ln=ln + 2) == sfa.LSSAR_EINVAL                  # lens misaligned
+    assert call(o=q + 64) == sfa.LSSAR_EINVAL                   # out overlaps q
+    assert call(o=k + 4096) == sfa.LSSAR_EINVAL                 # out inside the cache
+    assert call(o=ln - 64) == sfa.LSSAR_EINVAL                  # out overlaps lens
+    assert call(ws=0) == sfa.LSSAR_EWORKSPACE
+    assert call(ws=ws + 128) == sfa.LSSAR_EWORKSPACE
+    assert call(wsb=100) == sfa.LSSAR_EWORKSPACE
+    assert call(ws=v + 256) == sfa.LSSAR_EWORKSPACE             # overlaps the V cache
+    assert call(ws=ln - 256) == sfa.LSSAR_EWORKSPACE            # overlaps lens
     assert sfa.lssar_last_hip_error() == 0

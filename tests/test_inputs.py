@@ -76,3 +76,15 @@ def test_lowrank_structure_small():
     s = np.linalg.svd(q, compute_uv=False)
     # rank-8 signal plus std-0.1 noise: a clear gap after the 8th value
     assert s[7] > 5.0 * s[8]
+
+
+def test_decode_inputs():
+    a = gen.make_decode_inputs("x8_decode_ragged", B=8, Lmax=512, H=2)
+    b = gen.make_decode_inputs("x8_decode_ragged", B=8, Lmax=512, H=2)
+    assert a.q.shape == (8, 2, 64) and a.k.shape == (8, 2, 512, 64)
+    assert np.array_equal(a.k, b.k) and np.array_equal(a.lens, b.lens)
+    assert a.lens.dtype == np.int32 and np.all(a.lens >= 256) and np.all(a.lens <= 512)
+    assert len(set(a.lens.tolist())) > 1
+    assert np.array_equal(a.k, gen.round_to_bf16(a.k))
+    f = gen.make_decode_inputs("x8_decode", B=2, Lmax=64, H=1)
+    assert np.all(f.lens == 64)

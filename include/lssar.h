@@ -133,7 +133,8 @@ int lssar_lssa_fwd_ws(const void* q, const void* k, const void* v, void* out,
                       size_t workspace_bytes, void* stream);
 
 /* Workspace of lssar_decode_ws, in bytes (0 for invalid sizes): per cache
- * row one score, per 256-row chunk of every head 2 + (d + 1) partial sums;
+ * row one score, per chunk of 16384/d rows of every head 2 + (d + 1) partial
+ * sums;
  * fp32 values for bf16 inputs, fp64 for fp32 inputs; each part rounded up
  * to 256 bytes. */
 size_t lssar_decode_workspace_bytes(int B, int H, int Lmax, int d, int dtype);

@@ -269,7 +269,7 @@ int fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H,
 
 // Workspace: [scores: C per cache row][part1: 2 C per chunk][part2: d+1 C per
 // chunk], C = fp32 for bf16 inputs and fp64 for fp32 inputs, each part
-// rounded up to 256 bytes.
+// rounded up to 256 bytes.  Chunks: 16384 / d cache rows.
 struct DecLayout {
     size_t scores_bytes, part1_bytes, part2_bytes;
     int nsplit;
@@ -280,7 +280,8 @@ DecLayout dec_layout(long long B, long long H, long long Lmax, int d, int dtype)
 {
     DecLayout w;
     const size_t cb = dtype == LSSAR_F32 ? 8 : 4;
-    w.nsplit = (int)((Lmax + lssar::kDecChunk - 1) / lssar::kDecChunk);
+    const int chunk = lssar::dec_chunk(d);
+    w.nsplit = (int)((Lmax + chunk - 1) / chunk);
     const size_t bh = (size_t)(B * H);
     w.scores_bytes = round256(cb * bh * (size_t)Lmax);
     w.part1_bytes = round256(cb * bh * (size_t)w.nsplit * 2);
@@ -293,7 +294,7 @@ int validate_decode_shape(int B, int H, int Lmax, int d, int dtype)
     int st = validate_shape(B, H, Lmax, d, dtype);
     if (st != LSSAR_OK)
         return st;
-    const long long nsplit = (Lmax + lssar::kDecChunk - 1) / lssar::kDecChunk;
+    const long long nsplit = (Lmax + lssar::dec_chunk(d) - 1) / lssar::dec_chunk(d);
     if ((long long)B * H * nsplit > (1LL << 31) - 1)
         return LSSAR_EINVAL;
     return LSSAR_OK;
@@ -320,8 +321,9 @@ void launch_decode(const void* q, const void* kc, const void* vc, const int* len
     hipLaunchKernelGGL((lssar::lssar_decode_pv_kernel<T, D, P>), dim3(grid),
                        dim3(lssar::kDecThreads), 0, s, static_cast<const T*>(vc), lens,
                        scores, part1, part2, H, Lmax, w.nsplit, eps, p);
-    hipLaunchKernelGGL((lssar::lssar_decode_combine_kernel<T, D>), dim3((unsigned)BH), dim3(D), 0,
-                       s, lens, part2, static_cast<T*>(out), H, Lmax, w.nsplit);
+    hipLaunchKernelGGL((lssar::lssar_decode_combine_kernel<T, D>), dim3((unsigned)BH),
+                       dim3(lssar::kDecThreads), 0, s, lens, part2, static_cast<T*>(out), H, Lmax,
+                       w.nsplit);
 }
 
 template <typename T, int D>

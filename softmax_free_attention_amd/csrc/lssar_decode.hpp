@@ -26,15 +26,18 @@
 //
 // Lanes: a 16-byte load holds EPL elements of a row; LPK = d / EPL lanes
 // share one key, and a wave reads 64 / LPK consecutive keys (1 KB) per load,
-// so every load instruction reads whole cache lines.
+// so every load instruction reads whole cache lines.  Each wave owns a
+// quarter of its workgroup's chunk and issues all of its loads before using
+// any (range-checked buffer loads: no branch around the chunk's tail).
 #pragma once
 
 #include "lssar_device.hpp"
 
 namespace lssar {
 
-constexpr int kDecChunk = 256;     // keys per workgroup
 constexpr int kDecThreads = 256;
+// keys per workgroup: 32 KB of bf16 rows (256 keys at d = 64, 128 at d = 128)
+__host__ __device__ constexpr int dec_chunk(int d) { return 16384 / d; }
 
 // Compute type per input type: fp32 inputs run the whole step in fp64 (the
 // parity bar for fp32 inputs is 1e-5; see the fp32 forward kernel).
@@ -43,26 +46,65 @@ struct DecTraits;
 template <>
 struct DecTraits<__bf16> {
     using C = float;
+    using Raw = u32x4;                         // 16 bytes as loaded
     static constexpr int EPL = 8;
 };
 template <>
 struct DecTraits<float> {
     using C = double;
+    using Raw = f32x4;
     static constexpr int EPL = 4;
 };
 
-__device__ __forceinline__ void load_row16(const __bf16* p, float (&x)[8])
+// Buffer loads of base[voffset] with a range check: bytes at or past nbytes
+// read as zero, so a chunk's tail needs no branch around its loads (kept out
+// of kernel bodies, like the LDS-direct loads of the forward kernel).
+__device__ __forceinline__ u32x4 buf_load16(const void* base, unsigned nbytes, unsigned voffset)
 {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+    return __builtin_amdgcn_raw_buffer_load_b128(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                          0x00020000),
+        (int)voffset, 0, 0);
+}
+__device__ __forceinline__ float buf_load_c(const float* base, unsigned nbytes, unsigned voffset)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(
+                   __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0,
+                                                     (int)nbytes, 0x00020000),
+                   (int)voffset, 0, 0));
+}
+__device__ __forceinline__ double buf_load_c(const double* base, unsigned nbytes, unsigned voffset)
+{
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(
+        double, __builtin_amdgcn_raw_buffer_load_b64(
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<double*>(base), (short)0,
+                                                      (int)nbytes, 0x00020000),
+                    (int)voffset, 0, 0));
+}
+
+__device__ __forceinline__ u32x4 as_raw(u32x4 w, const __bf16*) { return w; }
+__device__ __forceinline__ f32x4 as_raw(u32x4 w, const float*) { return __builtin_bit_cast(f32x4, w); }
+
+__device__ __forceinline__ u32x4 load_raw(const __bf16* p)
+{
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ f32x4 load_raw(const float* p)
+{
+    return *reinterpret_cast<const f32x4*>(p);
+}
+__device__ __forceinline__ void unpack(const u32x4& w, float (&x)[8])
+{
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         x[2 * e] = bf16lo(w[e]);
         x[2 * e + 1] = bf16hi(w[e]);
     }
 }
-__device__ __forceinline__ void load_row16(const float* p, double (&x)[4])
+__device__ __forceinline__ void unpack(const f32x4& w, double (&x)[4])
 {
-    const f32x4 w = *reinterpret_cast<const f32x4*>(p);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         x[e] = (double)w[e];
@@ -76,6 +118,10 @@ __device__ __forceinline__ C dmax(C a, C b)
 {
     return a > b ? a : b;
 }
+
+// 1 / max(sqrt(ss), 1e-12) in the compute type
+__device__ __forceinline__ float inv_norm(float ss) { return 1.0f / fmaxf(sqrtf(ss), 1e-12f); }
+__device__ __forceinline__ double inv_norm(double ss) { return 1.0 / fmax(sqrt(ss), 1e-12); }
 
 // Cache rows in use for batch b: lens[b] clamped to [0, Lmax] (all Lmax
 // rows when lens is null).
@@ -121,6 +167,7 @@ __global__ __launch_bounds__(kDecThreads) void lssar_decode_scores_kernel(
 
     const int bh = (int)(blockIdx.x / nsplit), split = (int)(blockIdx.x % nsplit);
     const int len = dec_len(lens, bh / H, Lmax);
+    constexpr int kDecChunk = dec_chunk(D);
     const int k0 = split * kDecChunk;
     if (k0 >= len)
         return;                                // whole workgroup: uniform
@@ -128,8 +175,21 @@ __global__ __launch_bounds__(kDecThreads) void lssar_decode_scores_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % LPK, ksl = lane / LPK;
 
+    using Raw = typename DecTraits<T>::Raw;
+    constexpr int NLD = kDecChunk / 4 / KPW;   // loads per lane
+    constexpr unsigned RB = D * sizeof(T);     // bytes per cache row
+    // the chunk's rows; keys past kend read as zeros
+    const T* cbase = Kc + ((size_t)bh * Lmax + k0) * D;
+    const unsigned cbytes = (unsigned)(kend - k0) * RB;
+    const int kw = wave * (kDecChunk / 4);     // this wave's first key in the chunk
+    Raw raw[NLD];
+#pragma unroll
+    for (int n = 0; n < NLD; ++n)
+        raw[n] = as_raw(buf_load16(cbase, cbytes, (unsigned)(kw + n * KPW + ksl) * RB + sub * 16u),
+                        cbase);
+
     C qv[EPL];
-    load_row16(Q + (size_t)bh * D + sub * EPL, qv);
+    unpack(load_raw(Q + (size_t)bh * D + sub * EPL), qv);
     C qss = 0;
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
@@ -140,17 +200,13 @@ __global__ __launch_bounds__(kDecThreads) void lssar_decode_scores_kernel(
     // log2(e) ln d ln i / max(|q|, 1e-12), i = len (Key design 1: log d . log N)
     const C lam = (C)(lam_scale * log((double)len) / fmax(sqrt((double)qss), 1e-12));
 
-    const T* Kh = Kc + (size_t)bh * Lmax * D;
     C* sh = scores + (size_t)bh * Lmax;
     C s1 = 0, tmax = -INFINITY;
-    for (int kb = k0 + wave * KPW; kb < kend; kb += 4 * KPW) {
-        const int key = kb + ksl;
-        C kv[EPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e)
-            kv[e] = 0;
-        if (key < kend)
-            load_row16(Kh + (size_t)key * D + sub * EPL, kv);
+    for (int n = 0; n < NLD; ++n) {
+        const int key = k0 + kw + n * KPW + ksl;
+        C kv[EPL];
+        unpack(raw[n], kv);
         C dot = 0, ss = 0;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
@@ -163,7 +219,7 @@ __global__ __launch_bounds__(kDecThreads) void lssar_decode_scores_kernel(
             ss += __shfl_xor(ss, o);
         }
         if (key < kend && sub == 0) {
-            const C t = dot * lam / (C)fmax(sqrt((double)ss), 1e-12);
+            const C t = dot * lam * inv_norm(ss);
             sh[key] = t;
             s1 += softplus_dec(t);
             tmax = dmax(tmax, t);
@@ -185,14 +241,20 @@ struct DecRow {
 };
 
 template <typename C>
-__device__ __forceinline__ DecRow<C> dec_row(const C* p1, int nvalid, int len, float eps, C* red)
+__device__ __forceinline__ DecRow<C> dec_row(const C* p1, int nvalid, int len, float eps)
 {
+    // every wave reduces all partials itself, in the same order: no barrier
+    const int lane = threadIdx.x & 63;
     C s = 0, m = -INFINITY;
-    for (int sp = threadIdx.x; sp < nvalid; sp += kDecThreads) {
+    for (int sp = lane; sp < nvalid; sp += 64) {
         s += p1[2 * sp];
         m = dmax(m, p1[2 * sp + 1]);
     }
-    block_sum_max(s, m, red);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        s += __shfl_xor(s, o);
+        m = dmax(m, __shfl_xor(m, o));
+    }
     const C spmax = softplus_dec(m);
     const C o = len <= 3 ? (C)0 : (C)1;
     const C tau = o * s / (C)len;
@@ -217,11 +279,11 @@ __global__ __launch_bounds__(kDecThreads) void lssar_decode_pv_kernel(
     constexpr int EPL = DecTraits<T>::EPL;
     constexpr int LPK = D / EPL;
     constexpr int KPW = 64 / LPK;
-    __shared__ C red[8];
     __shared__ C accs[4][D + 1];
 
     const int bh = (int)(blockIdx.x / nsplit), split = (int)(blockIdx.x % nsplit);
     const int len = dec_len(lens, bh / H, Lmax);
+    constexpr int kDecChunk = dec_chunk(D);
     const int k0 = split * kDecChunk;
     if (k0 >= len)
         return;
@@ -230,7 +292,24 @@ __global__ __launch_bounds__(kDecThreads) void lssar_decode_pv_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % LPK, ksl = lane / LPK;
 
-    const DecRow<C> rc = dec_row<C>(part1 + (size_t)bh * nsplit * 2, nvalid, len, eps, red);
+    using Raw = typename DecTraits<T>::Raw;
+    constexpr int NLD = kDecChunk / 4 / KPW;
+    constexpr unsigned RB = D * sizeof(T);
+    const T* cbase = Vc + ((size_t)bh * Lmax + k0) * D;
+    const unsigned cbytes = (unsigned)(kend - k0) * RB;
+    const C* sbase = scores + (size_t)bh * Lmax + k0;
+    const unsigned sbytes = (unsigned)(kend - k0) * (unsigned)sizeof(C);
+    const int kw = wave * (kDecChunk / 4);
+    Raw raw[NLD];
+    C tk[NLD];
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) {
+        const unsigned lk = (unsigned)(kw + n * KPW + ksl);
+        raw[n] = as_raw(buf_load16(cbase, cbytes, lk * RB + sub * 16u), cbase);
+        tk[n] = buf_load_c(sbase, sbytes, lk * (unsigned)sizeof(C));
+    }
+
+    const DecRow<C> rc = dec_row<C>(part1 + (size_t)bh * nsplit * 2, nvalid, len, eps);
     C* out2 = part2 + ((size_t)bh * nsplit + split) * (D + 1);
     if (rc.degen) {                            // uniform: write zero sums
         for (int e = threadIdx.x; e <= D; e += kDecThreads)
@@ -238,27 +317,25 @@ __global__ __launch_bounds__(kDecThreads) void lssar_decode_pv_kernel(
         return;
     }
 
-    const T* Vh = Vc + (size_t)bh * Lmax * D;
-    const C* sh = scores + (size_t)bh * Lmax;
     C acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
         acc[e] = 0;
     C dsum = 0;
-    for (int kb = k0 + wave * KPW; kb < kend; kb += 4 * KPW) {
-        const int key = kb + ksl;
-        if (key < kend) {
-            C y = softplus_dec(sh[key]) * rc.c - rc.tc;
-            y = y < (C)0 ? (C)0 : (y > (C)1 ? (C)1 : y);
-            const C w = pow_chain<P>(y, p_rt);
-            C vv[EPL];
-            load_row16(Vh + (size_t)key * D + sub * EPL, vv);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e)
-                acc[e] += w * vv[e];
-            if (sub == 0)
-                dsum += w;
-        }
+    for (int n = 0; n < NLD; ++n) {
+        C y = softplus_dec(tk[n]) * rc.c - rc.tc;
+        y = y < (C)0 ? (C)0 : (y > (C)1 ? (C)1 : y);
+        // keys past the chunk (their rows read as zeros) get weight 0
+        const bool valid = kw + n * KPW + ksl < kend - k0;
+        const C w = valid ? pow_chain<P>(y, p_rt) : (C)0;
+        C vv[EPL];
+        unpack(raw[n], vv);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            acc[e] += w * vv[e];
+        if (sub == 0)
+            dsum += w;
     }
     // lanes with the same sub hold the same dims: sum over the key slots
 #pragma unroll
@@ -283,24 +360,48 @@ __global__ __launch_bounds__(kDecThreads) void lssar_decode_pv_kernel(
 }
 
 // out = U / D over the chunks of each head (0 when D = 0: degenerate rows
-// and empty caches).  One workgroup of D threads per head.
+// and empty caches).  One workgroup per head: thread (g, e) sums chunks
+// g, g + G, ... of element e (G = 256 / (D + 1) rounded down, the element D
+// being the weight sum), four loads in flight at a time; the G partial sums
+// are then added in a fixed order.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void lssar_decode_combine_kernel(
+__global__ __launch_bounds__(kDecThreads) void lssar_decode_combine_kernel(
     const int* __restrict__ lens, const typename DecTraits<T>::C* __restrict__ part2,
     T* __restrict__ out, int H, int Lmax, int nsplit)
 {
     using C = typename DecTraits<T>::C;
-    const int bh = blockIdx.x, e = threadIdx.x;
+    constexpr int E = D + 1;                   // elements per chunk record
+    constexpr int G = kDecThreads / E;         // chunk groups
+    __shared__ C red[G][E];
+    const int bh = blockIdx.x;
     const int len = dec_len(lens, bh / H, Lmax);
-    const int nvalid = (len + kDecChunk - 1) / kDecChunk;
-    const C* p2 = part2 + (size_t)bh * nsplit * (D + 1);
-    C u = 0, den = 0;
-    for (int sp = 0; sp < nvalid; ++sp) {
-        u += p2[(size_t)sp * (D + 1) + e];
-        den += p2[(size_t)sp * (D + 1) + D];
+    const int nvalid = (len + dec_chunk(D) - 1) / dec_chunk(D);
+    const C* p2 = part2 + (size_t)bh * nsplit * E;
+    const int g = threadIdx.x / E, e = threadIdx.x % E;
+    if (g < G) {
+        C a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+        int sp = g;
+        for (; sp + 3 * G < nvalid; sp += 4 * G) {
+            a0 += p2[(size_t)sp * E + e];
+            a1 += p2[(size_t)(sp + G) * E + e];
+            a2 += p2[(size_t)(sp + 2 * G) * E + e];
+            a3 += p2[(size_t)(sp + 3 * G) * E + e];
+        }
+        for (; sp < nvalid; sp += G)
+            a0 += p2[(size_t)sp * E + e];
+        red[g][e] = (a0 + a1) + (a2 + a3);
     }
-    const C o = den > (C)0 ? u / den : (C)0;
-    out[(size_t)bh * D + e] = (T)o;
+    __syncthreads();
+    if (threadIdx.x < D) {
+        C u = 0, den = 0;
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            u += red[k][threadIdx.x];
+            den += red[k][D];
+        }
+        const C o = den > (C)0 ? u / den : (C)0;
+        out[(size_t)bh * D + threadIdx.x] = (T)o;
+    }
 }
 
 }  // namespace lssar

@@ -171,12 +171,13 @@ def test_variant_entries_validate(L):
 
 
 def test_decode_workspace_bytes(L):
-    # bf16: fp32 scores per cache row, 2 + (d + 1) fp32 partials per 256-row chunk
+    # bf16: fp32 scores per cache row, 2 + (d + 1) fp32 partials per chunk of
+    # 16384 / d rows
     r = lambda x: (x + 255) // 256 * 256
     assert sfa.lssar_decode_workspace_bytes(16, 12, 8192, 64, sfa.LSSAR_BF16) == \
         r(4 * 192 * 8192) + r(4 * 192 * 32 * 2) + r(4 * 192 * 32 * 65)
     assert sfa.lssar_decode_workspace_bytes(3, 2, 300, 128, sfa.LSSAR_F32) == \
-        r(8 * 6 * 300) + r(8 * 6 * 2 * 2) + r(8 * 6 * 2 * 129)
+        r(8 * 6 * 300) + r(8 * 6 * 3 * 2) + r(8 * 6 * 3 * 129)
     assert sfa.lssar_decode_workspace_bytes(1, 1, 1, 64, sfa.LSSAR_BF16) == 256 + 256 + 512
     assert sfa.lssar_decode_workspace_bytes(1, 1, 1, 96, sfa.LSSAR_BF16) == 0
     assert sfa.lssar_decode_workspace_bytes(0, 1, 1, 64, sfa.LSSAR_BF16) == 0

@@ -65,6 +65,9 @@ def _bind(lib):
                                                ctypes.c_int, ip, ctypes.c_int, dp,
                                                ctypes.c_int]
     lib.lssar_ref_head_rows_ex_f64.restype = ctypes.c_int
+    lib.lssar_ref_bwd_f64.argtypes = [dp] * 7 + [ctypes.c_int] * 5 + [ctypes.c_double,
+                                                                      ctypes.c_int]
+    lib.lssar_ref_bwd_f64.restype = ctypes.c_int
     lib.lssar_ref_threads.argtypes = [ctypes.c_int]
     lib.lssar_ref_threads.restype = ctypes.c_int
     return lib
@@ -114,6 +117,27 @@ def lssar_rows(q, k, v, rows, p: int, eps: float = DEFAULT_EPS, nthreads: int = 
     if rc != 0:
         raise ValueError(f"lssar_ref_head_rows_ex_f64 failed with status {rc}")
     return out
+
+
+def lssar_bwd(q, k, v, dout, p: int, eps: float = DEFAULT_EPS, nthreads: int = 0,
+              lib=None):
+    """Oracle backward on [B,H,L,d] (or [L,d]) inputs for the loss
+    sum(dout * out); returns (dq, dk, dv) in fp64."""
+    lib = lib or load()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    squeeze = q.ndim == 2
+    if squeeze:
+        q, k, v, dout = q[None, None], k[None, None], v[None, None], dout[None, None]
+    B, H, L, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape and dout.shape == q.shape
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    rc = lib.lssar_ref_bwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+                               _ptr(dv), B, H, L, d, int(p), float(eps), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"lssar_ref_bwd_f64 failed with status {rc}")
+    if squeeze:
+        return dq[0, 0], dk[0, 0], dv[0, 0]
+    return dq, dk, dv
 
 
 def threads(nthreads: int = 0, lib=None) -> int:

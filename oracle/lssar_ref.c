@@ -52,6 +52,14 @@
  *       eps play no part and no row is degenerate (every A_ij with j <= i
  *       is positive).
  *
+ * Backward (lssar_ref_bwd_f64): the chain rule through the same steps in
+ * reverse, for the loss sum_i dout_i . out_i:
+ *   R16 A degenerate row (R10) has the constant output 0 and passes no
+ *       gradient to q, k or v.  ReLU'(0) = 0, so p = 1 entries exactly at
+ *       the threshold pass none either.
+ *   R17 The norm clamp of R6 is differentiated as written: for |x| > 1e-12
+ *       d(x/|x|) = (I - x^ x^T) / |x|; below it, I / 1e-12.
+ *
  * Build: gcc -O2 -fopenmp -shared -fPIC lssar_ref.c -lm (no -ffast-math).
  */
 #include "lssar_ref.h"
@@ -295,4 +303,153 @@ int lssar_ref_fwd_f64(const double* q, const double* k, const double* v,
 {
     return lssar_ref_fwd_ex_f64(q, k, v, out, B, H, L, d, p, eps,
                                 LSSAR_REF_PHI_SOFTPLUS, 1, nthreads);
+}
+
+/* ------------------------------------------------------------------------
+ * Backward
+ * ------------------------------------------------------------------------ */
+
+/* d(x / max(|x|, 1e-12)) applied to the gradient g of the normalised row
+ * (R17). */
+static void l2_normalise_bwd(const double* x, const double* g, double* out, int d)
+{
+    double ss = 0.0;
+    for (int e = 0; e < d; ++e)
+        ss += x[e] * x[e];
+    const double nrm = sqrt(ss);
+    if (!(nrm > 1e-12)) {
+        for (int e = 0; e < d; ++e)
+            out[e] = g[e] / 1e-12;
+        return;
+    }
+    double gx = 0.0;
+    for (int e = 0; e < d; ++e)
+        gx += g[e] * x[e] / nrm;
+    for (int e = 0; e < d; ++e)
+        out[e] = (g[e] - gx * x[e] / nrm) / nrm;
+}
+
+/* One head: accumulate the gradients of every row into dqh (per row, the
+ * gradient of the normalised query), dkh (normalised keys) and dv.
+ * Scratch: 6 * L doubles. */
+static void lssar_head_bwd(const double* qh, const double* kh, const double* v,
+                           const double* dout, int L, int d, int p, double eps,
+                           double* dqh, double* dkh, double* dv, double* scr)
+{
+    double* s = scr;            /* scores s_j           */
+    double* a = scr + L;        /* Softplus values a_j  */
+    double* x = scr + 2 * L;    /* i A_j - o            */
+    double* w = scr + 3 * L;    /* final weights W_j    */
+    double* g = scr + 4 * L;    /* gradients, reused    */
+    double* A = scr + 5 * L;    /* stage-1 weights A_j  */
+    for (int row = 0; row < L; ++row) {
+        const int i = 1 + row;                   /* R2 */
+        const double lam = log((double)d) * log((double)i);
+        const double* qi = qh + (size_t)row * d;
+        const double* gi = dout + (size_t)row * d;
+        /* forward of the row (Key designs 1-2), keys 1..i */
+        double S = 0.0;
+        for (int j = 0; j < i; ++j) {
+            double dot = 0.0;
+            for (int e = 0; e < d; ++e)
+                dot += qi[e] * kh[(size_t)j * d + e];
+            s[j] = lam * dot;
+            a[j] = softplus(s[j]);
+            S += a[j];
+        }
+        const double o = (i <= 3) ? 0.0 : 1.0;
+        double m = -INFINITY;
+        for (int j = 0; j < i; ++j) {
+            A[j] = a[j] / S;
+            x[j] = A[j] * (double)i - o;
+            if (x[j] > m)
+                m = x[j];
+        }
+        if (!(m > eps))
+            continue;                            /* R16: no gradient */
+        double R = 0.0;
+        for (int j = 0; j < i; ++j) {
+            w[j] = x[j] > 0.0 ? ipow(x[j], p) : 0.0;
+            R += w[j];
+        }
+        for (int j = 0; j < i; ++j)
+            w[j] /= R;
+        /* dW_j = dout_i . v_j; through W = r / R */
+        double delta = 0.0;
+        for (int j = 0; j < i; ++j) {
+            double dw = 0.0;
+            for (int e = 0; e < d; ++e)
+                dw += gi[e] * v[(size_t)j * d + e];
+            g[j] = dw;
+            delta += w[j] * dw;
+        }
+        /* dr_j = (dW_j - delta) / R; dx_j = dr_j p x^(p-1) for x > 0;
+           dA_j = i dx_j */
+        double eps1 = 0.0;
+        for (int j = 0; j < i; ++j) {
+            const double dr = (g[j] - delta) / R;
+            const double dx = x[j] > 0.0 ? dr * (double)p * ipow(x[j], p - 1) : 0.0;
+            g[j] = (double)i * dx;
+            eps1 += A[j] * g[j];
+        }
+        /* through A = a / S, a = Softplus(s) (derivative: the logistic
+           sigmoid), s = lam (q^ . k^) */
+        for (int j = 0; j < i; ++j) {
+            const double da = (g[j] - eps1) / S;
+            const double ds = da * sigmoid(s[j]);
+            const double dc = lam * ds;
+            for (int e = 0; e < d; ++e) {
+                dqh[(size_t)row * d + e] += dc * kh[(size_t)j * d + e];
+                dkh[(size_t)j * d + e] += dc * qi[e];
+                dv[(size_t)j * d + e] += w[j] * gi[e];
+            }
+        }
+    }
+}
+
+int lssar_ref_bwd_f64(const double* q, const double* k, const double* v,
+                      const double* dout, double* dq, double* dk, double* dv,
+                      int B, int H, int L, int d, int p, double eps, int nthreads)
+{
+    if (bad_args(q, k, v, dout, L, d, p, eps, LSSAR_REF_PHI_SOFTPLUS, 1) ||
+        !dq || !dk || !dv || B < 1 || H < 1)
+        return -1;
+    const size_t head = (size_t)L * d;
+    const long nheads = (long)B * H;
+    int fail = 0;
+#pragma omp parallel num_threads(lssar_ref_threads(nthreads))
+    {
+        double* qh = malloc(sizeof(double) * head);
+        double* kh = malloc(sizeof(double) * head);
+        double* dqh = malloc(sizeof(double) * head);
+        double* dkh = malloc(sizeof(double) * head);
+        double* scr = malloc(sizeof(double) * 6 * (size_t)L);
+        if (!qh || !kh || !dqh || !dkh || !scr) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long bh = 0; bh < nheads; ++bh) {
+                const size_t off = (size_t)bh * head;
+                normalise_head(q + off, k + off, qh, kh, L, d);
+                memset(dqh, 0, sizeof(double) * head);
+                memset(dkh, 0, sizeof(double) * head);
+                memset(dv + off, 0, sizeof(double) * head);
+                lssar_head_bwd(qh, kh, v + off, dout + off, L, d, p, eps, dqh, dkh,
+                               dv + off, scr);
+                for (int r = 0; r < L; ++r) {
+                    l2_normalise_bwd(q + off + (size_t)r * d, dqh + (size_t)r * d,
+                                     dq + off + (size_t)r * d, d);
+                    l2_normalise_bwd(k + off + (size_t)r * d, dkh + (size_t)r * d,
+                                     dk + off + (size_t)r * d, d);
+                }
+            }
+        }
+        free(qh);
+        free(kh);
+        free(dqh);
+        free(dkh);
+        free(scr);
+    }
+    return fail ? -2 : 0;
 }

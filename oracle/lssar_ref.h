@@ -54,6 +54,14 @@ int lssar_ref_head_rows_ex_f64(const double* q, const double* k, const double* v
                                int reweight, const int* rows, int nrows,
                                double* out, int nthreads);
 
+/* Backward of lssar_ref_fwd_f64 for the loss sum over rows of
+ * dout_i . out_i: writes dq, dk, dv ([B, H, L, d], same layout).  The
+ * chain rule through the same steps in reverse; a degenerate row passes no
+ * gradient.  Same return codes (dout and the outputs must be non-null). */
+int lssar_ref_bwd_f64(const double* q, const double* k, const double* v,
+                      const double* dout, double* dq, double* dk, double* dv,
+                      int B, int H, int L, int d, int p, double eps, int nthreads);
+
 /* Number of OpenMP threads a call with this nthreads argument would use. */
 int lssar_ref_threads(int nthreads);
 

@@ -438,7 +438,104 @@ def _hard_argmax_limit(lib, mode):
     assert np.median(prev[3:]) > 0.99
 
 
+# --------------------------------------------------------------------------
+# Backward (lssar_ref_bwd_f64): pinned by the forward oracle it differentiates
+# --------------------------------------------------------------------------
+
+def _bwd(lib, q, k, v, g, p, eps=oracle.DEFAULT_EPS):
+    return oracle.lssar_bwd(q, k, v, g, p, eps, nthreads=2, lib=lib)
+
+
+def bwd_finite_differences(lib):
+    """Central differences of sum(dout * forward) (the forward oracle, pinned
+    above) against the backward, every entry of dq, dk and dv."""
+    cases = [(6, 5, 3, 0), (7, 4, 1, 1), (5, 6, 2, 2), (8, 4, 15, 3), (3, 3, 3, 4), (9, 3, 5, 5)]
+    h = 1e-6
+    for L, d, p, seed in cases:
+        r = _rng(1500 + seed)
+        Q, K, V, G = (r.standard_normal((L, d)) for _ in range(4))
+        dq, dk, dv = _bwd(lib, Q, K, V, G, p)
+
+        def loss(Qx, Kx, Vx):
+            return float(np.sum(G * _fwd(lib, Qx, Kx, Vx, p)))
+
+        for name, X, D in (("q", Q, dq), ("k", K, dk), ("v", V, dv)):
+            num = np.zeros_like(X)
+            for idx in np.ndindex(X.shape):
+                Xp, Xm = X.copy(), X.copy()
+                Xp[idx] += h
+                Xm[idx] -= h
+                args = {"q": lambda Y: (Y, K, V), "k": lambda Y: (Q, Y, V),
+                        "v": lambda Y: (Q, K, Y)}[name]
+                num[idx] = (loss(*args(Xp)) - loss(*args(Xm))) / (2 * h)
+            err = np.max(np.abs(num - D))
+            assert err < 1e-6 * (1.0 + np.max(np.abs(D))), \
+                f"d{name} vs finite differences L={L} d={d} p={p}: {err:.3e}"
+
+
+def bwd_scale_invariance(lib):
+    """The output does not change when a row of Q or K is rescaled, so each
+    gradient row is orthogonal to its input row: q_i . dq_i = k_j . dk_j = 0."""
+    r = _rng(1600)
+    for L, d, p in ((20, 8, 3), (33, 16, 15)):
+        Q, K, V, G = (r.standard_normal((L, d)) for _ in range(4))
+        dq, dk, _ = _bwd(lib, Q, K, V, G, p)
+        scale = 1e-12 * (np.max(np.abs(dq)) + np.max(np.abs(dk))) * np.max(np.abs(Q))
+        assert np.max(np.abs((Q * dq).sum(axis=1))) < 100 * scale + 1e-13
+        assert np.max(np.abs((K * dk).sum(axis=1))) < 100 * scale + 1e-13
+        assert np.max(np.abs(dq)) > 1e-3                    # not trivially zero
+
+
+def bwd_dv_is_weights_transposed(lib):
+    """out = W V is linear in V, so dv = W^T dout; W comes from the forward
+    with V = I."""
+    r = _rng(1700)
+    for L, d, p in ((12, 12, 3), (16, 20, 15), (9, 9, 1)):
+        Q, K, V, G = (r.standard_normal((L, d)) for _ in range(4))
+        W = _fwd(lib, Q, K, np.eye(L, d), p)[:, :L]
+        _, _, dv = _bwd(lib, Q, K, V, G, p)
+        assert np.max(np.abs(dv - W.T @ G)) < 1e-12
+
+
+def bwd_causality_and_row1(lib):
+    """dk_j and dv_j see dout_i for i >= j only; dq_i sees keys and values
+    j <= i only (bitwise); row 1 (scale ln 1 = 0) passes no gradient to q."""
+    r = _rng(1800)
+    L, d, p = 14, 6, 3
+    Q, K, V, G = (r.standard_normal((L, d)) for _ in range(4))
+    dq, dk, dv = _bwd(lib, Q, K, V, G, p)
+    assert np.max(np.abs(dq[0])) == 0.0
+    cut = 6
+    G2 = G.copy()
+    G2[:cut] = r.standard_normal((cut, d))
+    _, dk2, dv2 = _bwd(lib, Q, K, V, G2, p)
+    assert np.array_equal(dk2[cut:], dk[cut:]) and np.array_equal(dv2[cut:], dv[cut:])
+    K3, V3 = K.copy(), V.copy()
+    K3[cut:] = r.standard_normal((L - cut, d))
+    V3[cut:] = r.standard_normal((L - cut, d))
+    dq3, _, _ = _bwd(lib, Q, K3, V3, G, p)
+    assert np.array_equal(dq3[:cut], dq[:cut])
+
+
+def bwd_degenerate_rows(lib):
+    """Identical keys make rows >= 4 degenerate (constant output 0): they pass
+    no gradient, so dq of those rows is 0 and dv gets rows 1-3 only."""
+    r = _rng(1900)
+    L, d = 10, 5
+    K = np.tile(r.standard_normal((1, d)), (L, 1))
+    Q, V, G = (r.standard_normal((L, d)) for _ in range(3))
+    for p in (1, 3):
+        dq, dk, dv = _bwd(lib, Q, K, V, G, p)
+        assert np.all(dq[3:] == 0.0)
+        G3 = G.copy()
+        G3[3:] = 0.0
+        _, _, dv3 = _bwd(lib, Q, K, V, G3, p)
+        assert np.array_equal(dv, dv3)
+
+
 PINS = [brute_force_matrix_form, row1_is_v1, closed_form_rows, golden_row2_value,
         sigmoid_antisymmetric_pair, onehot_orthonormal, two_way_tie, degenerate_rows,
-        v_identity_probe, v_ones, scale_invariance, linearity_in_v, causality, permutation_invariance,
-        hard_argmax_limit]
+        v_identity_probe, v_ones, scale_invariance, linearity_in_v, causality,
+        permutation_invariance, hard_argmax_limit, bwd_finite_differences,
+        bwd_scale_invariance, bwd_dv_is_weights_transposed, bwd_causality_and_row1,
+        bwd_degenerate_rows]

@@ -49,14 +49,30 @@ MUTANTS = [
      "return sigmoid(x);"),
     ("lssa-only-reweights", "    if (reweight) {", "    if (1) {"),
     ("never-reweights", "    if (reweight) {", "    if (0) {"),
+    # the backward
+    ("bwd-no-delta", "const double dr = (g[j] - delta) / R;", "const double dr = g[j] / R;"),
+    ("bwd-no-eps", "const double da = (g[j] - eps1) / S;", "const double da = g[j] / S;"),
+    ("bwd-no-sigmoid", "const double ds = da * sigmoid(s[j]);", "const double ds = da;"),
+    ("bwd-power", "dr * (double)p * ipow(x[j], p - 1)", "dr * (double)p * ipow(x[j], p)"),
+    ("bwd-no-N", "g[j] = (double)i * dx;", "g[j] = dx;"),
+    ("bwd-no-lambda", "const double dc = lam * ds;", "const double dc = ds;"),
+    ("bwd-no-projection", "out[e] = (g[e] - gx * x[e] / nrm) / nrm;", "out[e] = g[e] / nrm;"),
+    ("bwd-dv-stage1-weights", "dv[(size_t)j * d + e] += w[j] * gi[e];",
+     "dv[(size_t)j * d + e] += A[j] * gi[e];"),
+    ("bwd-dk-wrong-operand", "dkh[(size_t)j * d + e] += dc * qi[e];",
+     "dkh[(size_t)j * d + e] += dc * kh[(size_t)j * d + e];"),
+    ("bwd-degenerate-passes", "            continue;                            /* R16: no gradient */",
+     "            ;"),
 ]
 
 INDEPENDENT_PINS = [p for p in oracle_pins.PINS if p is not oracle_pins.brute_force_matrix_form]
 
 
 def test_mutant_texts_apply():
+    # a pattern may occur in the forward and in the backward (they share the
+    # definition); every occurrence is mutated
     for name, old, new in MUTANTS:
-        assert SRC.count(old) == 1, f"mutant {name}: pattern must occur exactly once"
+        assert SRC.count(old) >= 1, f"mutant {name}: pattern not found"
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])

@@ -1,5 +1,7 @@
 /*
- * lssar.h -- C ABI of the MI355X (gfx950) LSSAR causal attention forward.
+ * lssar.h -- C ABI of the MI355X (gfx950) LSSAR causal attention: forward,
+ * its ablation variants, the decode step over a key/value cache, and the
+ * backward.
  *
  * LSSAR = Length Scaled Softplus Attention with Re-weighting, defined in the
  * paper note "Softplus Attention with Re-weighting Boosts Length
@@ -159,6 +161,32 @@ int lssar_decode_ws(const void* q, const void* k_cache, const void* v_cache,
                     const int* lens, void* out, int B, int H, int Lmax, int d,
                     int p, float eps, int dtype, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* Workspace of lssar_attn_bwd_ws, in bytes (0 for invalid sizes): per row
+ * of Q and K one inverse norm, and 8 coefficients per query row; fp32 for
+ * bf16 inputs, fp64 for fp32 inputs; each part rounded up to 256 bytes. */
+size_t lssar_bwd_workspace_bytes(int B, int H, int L, int d, int dtype);
+
+/* Backward of lssar_attn_fwd_ws for the loss sum over rows of dout_i .
+ * out_i: the gradients dq, dk, dv of the causal forward (Key designs 1-3,
+ * the same readings and degenerate-row rule; a degenerate row passes no
+ * gradient), by the chain rule through its steps in reverse: the stage-2 L1
+ * normalisation, ReLU^p, N and O, the stage-1 L1 normalisation, Softplus
+ * (derivative: the logistic sigmoid), the scores and the L2 norms (clamped
+ * at 1e-12 as in the forward).  The forward's row statistics are
+ * recomputed; nothing from the forward call is needed.
+ *  - q, k, v, dout: DEVICE [B, H, L, d] inputs; dq, dk, dv: DEVICE
+ *    [B, H, L, d] outputs, same dtype, 16-byte aligned; no output overlaps
+ *    an input or another output.
+ *  - Arithmetic: fp32 for bf16 inputs (outputs rounded to bf16), fp64 for
+ *    fp32 inputs.
+ *  - p, eps, dtype, d, errors: as for lssar_attn_fwd_ws.  workspace:
+ *    lssar_bwd_workspace_bytes(), 256-byte aligned, overlapping no tensor.
+ *    Allocates nothing; four kernel launches on `stream`. */
+int lssar_attn_bwd_ws(const void* q, const void* k, const void* v,
+                      const void* dout, void* dq, void* dk, void* dv, int B,
+                      int H, int L, int d, int p, float eps, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* lssar_status_str(int status);

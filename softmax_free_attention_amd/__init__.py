@@ -25,6 +25,7 @@ __all__ = [
     "lssar_last_hip_error", "lssar_version", "DEFAULT_EPS", "LSSAR_PHI_SOFTPLUS",
     "LSSAR_PHI_SIGMOID", "lssar_attn_fwd_phi_ws", "lssar_lssa_fwd_ws",
     "lssar_decode_workspace_bytes", "lssar_decode_ws", "decode_workspace_for",
+    "lssar_bwd_workspace_bytes", "lssar_attn_bwd_ws", "bwd_workspace_for",
 ]
 
 LSSAR_F32, LSSAR_BF16 = 0, 1
@@ -73,6 +74,10 @@ def lib():
         L.lssar_decode_workspace_bytes.restype = sz
         L.lssar_decode_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
         L.lssar_decode_ws.restype = i
+        L.lssar_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.lssar_bwd_workspace_bytes.restype = sz
+        L.lssar_attn_bwd_ws.argtypes = [vp] * 7 + [i, i, i, i, i, f, i, vp, sz, vp]
+        L.lssar_attn_bwd_ws.restype = i
         L.lssar_status_str.argtypes = [i]
         L.lssar_status_str.restype = ctypes.c_char_p
         L.lssar_last_hip_error.argtypes = []
@@ -268,3 +273,33 @@ def lssar_decode_ws(q, k_cache, v_cache, lens, out, workspace, *, p: int,
                                d, int(p), float(eps), _dtype_code(q), wp, wn, _stream_ptr(stream))
     _raise(st, "lssar_decode_ws")
     return out
+
+
+def lssar_bwd_workspace_bytes(B: int, H: int, L: int, d: int, dtype: int) -> int:
+    return int(lib().lssar_bwd_workspace_bytes(B, H, L, d, dtype))
+
+
+def bwd_workspace_for(q):
+    """A device byte tensor of lssar_bwd_workspace_bytes for tensors shaped like q."""
+    import torch
+    B, H, L, d = q.shape
+    n = lssar_bwd_workspace_bytes(B, H, L, d, _dtype_code(q))
+    if n == 0:
+        raise ValueError(f"unsupported shape {tuple(q.shape)} / dtype {q.dtype}")
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def lssar_attn_bwd_ws(q, k, v, dout, dq, dk, dv, workspace, *, p: int,
+                      eps: float = DEFAULT_EPS, stream=None):
+    """Gradients (dq, dk, dv) of sum(dout * LSSAR(q, k, v)), written into the
+    given tensors.  Returns (dq, dk, dv)."""
+    B, H, L, d, dt = _check_qkv(q, k, v, dout)
+    _check_qkv(dq, dk, dv)
+    if dq.shape != q.shape or dq.dtype != q.dtype:
+        raise ValueError("gradients must match q in shape and dtype")
+    wp, wn = _ws_args(workspace)
+    st = lib().lssar_attn_bwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), B, H, L, d, int(p), float(eps), dt, wp, wn,
+                                 _stream_ptr(stream))
+    _raise(st, "lssar_attn_bwd_ws")
+    return dq, dk, dv

@@ -15,6 +15,7 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "lssar_bwd.hpp"
 #include "lssar_decode.hpp"
 #include "lssar_device.hpp"
 
@@ -338,6 +339,77 @@ void decode_dispatch_p(const void* q, const void* kc, const void* vc, const int*
     }
 }
 
+// ---------------------------------------------------------------------------
+// Backward
+// ---------------------------------------------------------------------------
+
+// Workspace: [rq: C per query row][fk: C per key row][stats: 8 C per query
+// row], C = fp32 for bf16 inputs and fp64 for fp32 inputs, each part rounded
+// up to 256 bytes.
+struct BwdLayout {
+    size_t rq_bytes, fk_bytes, st_bytes;
+    size_t total() const { return rq_bytes + fk_bytes + st_bytes; }
+};
+
+BwdLayout bwd_layout(long long B, long long H, long long L, int dtype)
+{
+    const size_t cb = dtype == LSSAR_F32 ? 8 : 4;
+    const size_t rows = (size_t)(B * H * L);
+    BwdLayout w;
+    w.rq_bytes = round256(cb * rows);
+    w.fk_bytes = round256(cb * rows);
+    w.st_bytes = round256(cb * rows * lssar::kBwdRowStats);
+    return w;
+}
+
+template <typename T, int D, int P>
+void launch_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                void* dv, void* ws, long nrows, int L, int p, float eps, double lam_scale,
+                hipStream_t s)
+{
+    using C = typename lssar::DecTraits<T>::C;
+    const BwdLayout w = bwd_layout(1, 1, nrows, std::is_same<T, float>::value ? LSSAR_F32
+                                                                             : LSSAR_BF16);
+    auto* base = static_cast<unsigned char*>(ws);
+    C* rq = reinterpret_cast<C*>(base);
+    C* fk = reinterpret_cast<C*>(base + w.rq_bytes);
+    C* st = reinterpret_cast<C*>(base + w.rq_bytes + w.fk_bytes);
+    const T* Q = static_cast<const T*>(q);
+    const T* K = static_cast<const T*>(k);
+    const T* V = static_cast<const T*>(v);
+    const T* G = static_cast<const T*>(dout);
+    constexpr int rpb = lssar::kBwdThreads / (D / lssar::DecTraits<T>::EPL);
+    hipLaunchKernelGGL((lssar::lssar_bwd_norms_kernel<T, D>),
+                       dim3((unsigned)((nrows + rpb - 1) / rpb)), dim3(lssar::kBwdThreads), 0, s,
+                       Q, K, rq, fk, nrows);
+    const unsigned g4 = (unsigned)((nrows + 3) / 4);
+    hipLaunchKernelGGL((lssar::lssar_bwd_rowstats_kernel<T, D, P>), dim3(g4),
+                       dim3(lssar::kBwdThreads), 0, s, Q, K, V, G, rq, fk, st, L, nrows,
+                       lam_scale, eps, p);
+    hipLaunchKernelGGL((lssar::lssar_bwd_dq_kernel<T, D, P>), dim3(g4), dim3(lssar::kBwdThreads),
+                       0, s, Q, K, V, G, fk, st, static_cast<T*>(dq), L, nrows, p);
+    hipLaunchKernelGGL((lssar::lssar_bwd_dkdv_kernel<T, D, P>), dim3(g4),
+                       dim3(lssar::kBwdThreads), 0, s, Q, K, V, G, fk, st, static_cast<T*>(dk),
+                       static_cast<T*>(dv), L, nrows, p);
+}
+
+template <typename T, int D>
+void bwd_dispatch_p(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                    void* dk, void* dv, void* ws, long nrows, int L, int p, float eps,
+                    double lam_scale, hipStream_t s)
+{
+#define LSSAR_BWD(PV) \
+    launch_bwd<T, D, PV>(q, k, v, dout, dq, dk, dv, ws, nrows, L, p, eps, lam_scale, s)
+    switch (p) {
+    case 1: LSSAR_BWD(1); break;
+    case 2: LSSAR_BWD(2); break;
+    case 3: LSSAR_BWD(3); break;
+    case 15: LSSAR_BWD(15); break;
+    default: LSSAR_BWD(0); break;
+    }
+#undef LSSAR_BWD
+}
+
 }  // namespace
 
 extern "C" {
@@ -490,6 +562,68 @@ int lssar_decode_ws(const void* q, const void* k_cache, const void* v_cache, con
     return LSSAR_OK;
 }
 
+size_t lssar_bwd_workspace_bytes(int B, int H, int L, int d, int dtype)
+{
+    if (validate_shape(B, H, L, d, dtype) != LSSAR_OK)
+        return 0;
+    return bwd_layout(B, H, L, dtype).total();
+}
+
+int lssar_attn_bwd_ws(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                      void* dk, void* dv, int B, int H, int L, int d, int p, float eps, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!dout || !dq || !dk || !dv)
+        return LSSAR_EINVAL;
+    // q, k, v, sizes, p, eps, dtype and alignment as for the forward, with dq
+    // standing in for out (it must not overlap q, k or v)
+    int st = validate(q, k, v, dq, B, H, L, d, p, eps, dtype);
+    if (st != LSSAR_OK)
+        return st;
+    if (!aligned16(dout) || !aligned16(dk) || !aligned16(dv))
+        return LSSAR_EINVAL;
+    const size_t tb = (size_t)B * H * L * d * elem_bytes(dtype);
+    const void* ins[4] = {q, k, v, dout};
+    const void* outs[3] = {dq, dk, dv};
+    for (const void* o : outs) {
+        for (const void* in : ins)
+            if (overlaps(o, tb, in, tb))
+                return LSSAR_EINVAL;
+    }
+    if (overlaps(dq, tb, dk, tb) || overlaps(dq, tb, dv, tb) || overlaps(dk, tb, dv, tb))
+        return LSSAR_EINVAL;
+    const BwdLayout w = bwd_layout(B, H, L, dtype);
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+        workspace_bytes < w.total())
+        return LSSAR_EWORKSPACE;
+    for (const void* t : {q, k, v, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
+                          static_cast<const void*>(dv)})
+        if (overlaps(workspace, w.total(), t, tb))
+            return LSSAR_EWORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const double lam_scale = std::log((double)d) / std::log(2.0);
+    const long nrows = (long)B * H * L;
+    if (dtype == LSSAR_BF16) {
+        if (d == 64)
+            bwd_dispatch_p<__bf16, 64>(q, k, v, dout, dq, dk, dv, workspace, nrows, L, p, eps,
+                                       lam_scale, s);
+        else
+            bwd_dispatch_p<__bf16, 128>(q, k, v, dout, dq, dk, dv, workspace, nrows, L, p, eps,
+                                        lam_scale, s);
+    } else {
+        if (d == 64)
+            bwd_dispatch_p<float, 64>(q, k, v, dout, dq, dk, dv, workspace, nrows, L, p, eps,
+                                      lam_scale, s);
+        else
+            bwd_dispatch_p<float, 128>(q, k, v, dout, dq, dk, dv, workspace, nrows, L, p, eps,
+                                       lam_scale, s);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return hip_fail(e);
+    return LSSAR_OK;
+}
+
 const char* lssar_status_str(int status)
 {
     switch (status) {
@@ -504,6 +638,6 @@ const char* lssar_status_str(int status)
 
 int lssar_last_hip_error(void) { return g_last_hip_error; }
 
-int lssar_version(void) { return 400; }
+int lssar_version(void) { return 500; }
 
 }  // extern "C"

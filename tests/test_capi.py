@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
     for n in ("lssar_attn_fwd", "lssar_attn_fwd_ws", "lssar_workspace_bytes",
               "lssar_status_str", "lssar_prep", "lssar_attn_fwd_prepped",
               "lssar_attn_fwd_phi_ws", "lssar_lssa_fwd_ws", "lssar_decode_ws",
-              "lssar_decode_workspace_bytes"):
+              "lssar_decode_workspace_bytes", "lssar_attn_bwd_ws", "lssar_bwd_workspace_bytes"):
         assert n in names
 
 
@@ -64,7 +64,7 @@ def test_library_has_no_oracle_dependency(L):
 
 
 def test_version_and_status_strings(L):
-    assert sfa.lssar_version() == 400
+    assert sfa.lssar_version() == 500
     assert sfa.lssar_status_str(0) == "ok"
     for st in (-1, -2, -3, -4, 7):
         s = sfa.lssar_status_str(st)
@@ -211,4 +211,38 @@ def test_decode_validates_before_any_hip_call(L):
     assert call(wsb=100) == sfa.LSSAR_EWORKSPACE
     assert call(ws=v + 256) == sfa.LSSAR_EWORKSPACE             # overlaps the V cache
     assert call(ws=ln - 256) == sfa.LSSAR_EWORKSPACE            # overlaps lens
+    assert sfa.lssar_last_hip_error() == 0
+
+
+def test_bwd_workspace_bytes(L):
+    r = lambda x: (x + 255) // 256 * 256
+    assert sfa.lssar_bwd_workspace_bytes(1, 12, 8192, 64, sfa.LSSAR_BF16) == \
+        2 * r(4 * 12 * 8192) + r(4 * 8 * 12 * 8192)
+    assert sfa.lssar_bwd_workspace_bytes(2, 3, 5, 128, sfa.LSSAR_F32) == 2 * r(8 * 30) + r(64 * 30)
+    assert sfa.lssar_bwd_workspace_bytes(1, 1, 1, 80, sfa.LSSAR_F32) == 0
+
+
+def test_bwd_validates_before_any_hip_call(L):
+    S = STEP
+    base = dict(q=A, k=A + S, v=A + 2 * S, g=A + 3 * S, dq=A + 4 * S, dk=A + 5 * S, dv=A + 6 * S,
+                B=1, H=2, Ln=64, d=64, p=3, eps=1e-4, dt=1, ws=A + 7 * S, wsb=1 << 24)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.lssar_attn_bwd_ws(a["q"], a["k"], a["v"], a["g"], a["dq"], a["dk"], a["dv"],
+                                   a["B"], a["H"], a["Ln"], a["d"], a["p"], a["eps"], a["dt"],
+                                   a["ws"], a["wsb"], None)
+
+    assert call(g=0) == sfa.LSSAR_EINVAL
+    assert call(dv=0) == sfa.LSSAR_EINVAL
+    assert call(q=0) == sfa.LSSAR_EINVAL
+    assert call(p=0) == sfa.LSSAR_EINVAL
+    assert call(d=96) == sfa.LSSAR_EUNSUPPORTED
+    assert call(dk=A + 5 * S + 8) == sfa.LSSAR_EINVAL           # misaligned
+    assert call(dq=A + 3 * S + 64) == sfa.LSSAR_EINVAL          # dq overlaps dout
+    assert call(dv=A + 4 * S + 64) == sfa.LSSAR_EINVAL          # dv overlaps dq
+    assert call(dk=A + 64) == sfa.LSSAR_EINVAL                  # dk overlaps q
+    assert call(ws=0) == sfa.LSSAR_EWORKSPACE
+    assert call(wsb=1000) == sfa.LSSAR_EWORKSPACE
+    assert call(ws=A + 6 * S + 256) == sfa.LSSAR_EWORKSPACE     # overlaps dv
     assert sfa.lssar_last_hip_error() == 0

@@ -16,6 +16,7 @@
 #include <type_traits>
 
 #include "lssar_bwd.hpp"
+#include "lssar_bwd_mfma.hpp"
 #include "lssar_decode.hpp"
 #include "lssar_device.hpp"
 
@@ -344,32 +345,37 @@ void decode_dispatch_p(const void* q, const void* kc, const void* vc, const int*
 // ---------------------------------------------------------------------------
 
 // Workspace: [rq: C per query row][fk: C per key row][stats: 8 C per query
-// row], C = fp32 for bf16 inputs and fp64 for fp32 inputs, each part rounded
-// up to 256 bytes.
+// row], C = fp32 for bf16 inputs and fp64 for fp32 inputs; for bf16 inputs
+// also [Q^T][K^T][dO^T] (bf16 [head][d][Lp], Lp = L rounded up to 64); each
+// part rounded up to 256 bytes.
 struct BwdLayout {
-    size_t rq_bytes, fk_bytes, st_bytes;
-    size_t total() const { return rq_bytes + fk_bytes + st_bytes; }
+    size_t rq_bytes, fk_bytes, st_bytes, tr_bytes;
+    int Lp;
+    size_t total() const { return rq_bytes + fk_bytes + st_bytes + 3 * tr_bytes; }
 };
 
-BwdLayout bwd_layout(long long B, long long H, long long L, int dtype)
+BwdLayout bwd_layout(long long B, long long H, long long L, int d, int dtype)
 {
     const size_t cb = dtype == LSSAR_F32 ? 8 : 4;
     const size_t rows = (size_t)(B * H * L);
     BwdLayout w;
+    w.Lp = (int)((L + 63) / 64 * 64);
     w.rq_bytes = round256(cb * rows);
     w.fk_bytes = round256(cb * rows);
     w.st_bytes = round256(cb * rows * lssar::kBwdRowStats);
+    w.tr_bytes = dtype == LSSAR_BF16 ? round256((size_t)(B * H * d) * (size_t)w.Lp * 2) : 0;
     return w;
 }
 
 template <typename T, int D, int P>
 void launch_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
-                void* dv, void* ws, long nrows, int L, int p, float eps, double lam_scale,
+                void* dv, void* ws, int BH, int L, int p, float eps, double lam_scale,
                 hipStream_t s)
 {
     using C = typename lssar::DecTraits<T>::C;
-    const BwdLayout w = bwd_layout(1, 1, nrows, std::is_same<T, float>::value ? LSSAR_F32
-                                                                             : LSSAR_BF16);
+    constexpr bool BF = std::is_same<T, __bf16>::value;
+    const BwdLayout w = bwd_layout(1, BH, L, D, BF ? LSSAR_BF16 : LSSAR_F32);
+    const long nrows = (long)BH * L;
     auto* base = static_cast<unsigned char*>(ws);
     C* rq = reinterpret_cast<C*>(base);
     C* fk = reinterpret_cast<C*>(base + w.rq_bytes);
@@ -378,16 +384,34 @@ void launch_bwd(const void* q, const void* k, const void* v, const void* dout, v
     const T* K = static_cast<const T*>(k);
     const T* V = static_cast<const T*>(v);
     const T* G = static_cast<const T*>(dout);
-    constexpr int rpb = lssar::kBwdThreads / (D / lssar::DecTraits<T>::EPL);
-    hipLaunchKernelGGL((lssar::lssar_bwd_norms_kernel<T, D>),
-                       dim3((unsigned)((nrows + rpb - 1) / rpb)), dim3(lssar::kBwdThreads), 0, s,
-                       Q, K, rq, fk, nrows);
     const unsigned g4 = (unsigned)((nrows + 3) / 4);
-    hipLaunchKernelGGL((lssar::lssar_bwd_rowstats_kernel<T, D, P>), dim3(g4),
-                       dim3(lssar::kBwdThreads), 0, s, Q, K, V, G, rq, fk, st, L, nrows,
-                       lam_scale, eps, p);
-    hipLaunchKernelGGL((lssar::lssar_bwd_dq_kernel<T, D, P>), dim3(g4), dim3(lssar::kBwdThreads),
-                       0, s, Q, K, V, G, fk, st, static_cast<T*>(dq), L, nrows, p);
+    if constexpr (BF) {
+        unsigned char* tb = base + w.rq_bytes + w.fk_bytes + w.st_bytes;
+        __bf16* QT = reinterpret_cast<__bf16*>(tb);
+        __bf16* KT = reinterpret_cast<__bf16*>(tb + w.tr_bytes);
+        __bf16* GT = reinterpret_cast<__bf16*>(tb + 2 * w.tr_bytes);
+        hipLaunchKernelGGL((lssar::lssar_bwd_prep_kernel<D>), dim3(w.Lp / 64, BH),
+                           dim3(lssar::kThreads), 0, s, Q, K, G, rq, fk, QT, KT, GT, L, w.Lp);
+        const int nqb = (L + 63) / 64, npair = (nqb + 1) / 2;
+        const dim3 grid((unsigned)(npair * BH));
+        hipLaunchKernelGGL((lssar::lssar_bwd_qside_kernel<D, P, 0>), grid, dim3(lssar::kThreads),
+                           0, s, Q, K, V, G, KT, rq, fk, st, static_cast<__bf16*>(dq), BH, L,
+                           w.Lp, nqb, npair, lam_scale, eps, p);
+        hipLaunchKernelGGL((lssar::lssar_bwd_qside_kernel<D, P, 1>), grid, dim3(lssar::kThreads),
+                           0, s, Q, K, V, G, KT, rq, fk, st, static_cast<__bf16*>(dq), BH, L,
+                           w.Lp, nqb, npair, lam_scale, eps, p);
+    } else {
+        constexpr int rpb = lssar::kBwdThreads / (D / lssar::DecTraits<T>::EPL);
+        hipLaunchKernelGGL((lssar::lssar_bwd_norms_kernel<T, D>),
+                           dim3((unsigned)((nrows + rpb - 1) / rpb)), dim3(lssar::kBwdThreads), 0,
+                           s, Q, K, rq, fk, nrows);
+        hipLaunchKernelGGL((lssar::lssar_bwd_rowstats_kernel<T, D, P>), dim3(g4),
+                           dim3(lssar::kBwdThreads), 0, s, Q, K, V, G, rq, fk, st, L, nrows,
+                           lam_scale, eps, p);
+        hipLaunchKernelGGL((lssar::lssar_bwd_dq_kernel<T, D, P>), dim3(g4),
+                           dim3(lssar::kBwdThreads), 0, s, Q, K, V, G, fk, st,
+                           static_cast<T*>(dq), L, nrows, p);
+    }
     hipLaunchKernelGGL((lssar::lssar_bwd_dkdv_kernel<T, D, P>), dim3(g4),
                        dim3(lssar::kBwdThreads), 0, s, Q, K, V, G, fk, st, static_cast<T*>(dk),
                        static_cast<T*>(dv), L, nrows, p);
@@ -395,11 +419,11 @@ void launch_bwd(const void* q, const void* k, const void* v, const void* dout, v
 
 template <typename T, int D>
 void bwd_dispatch_p(const void* q, const void* k, const void* v, const void* dout, void* dq,
-                    void* dk, void* dv, void* ws, long nrows, int L, int p, float eps,
+                    void* dk, void* dv, void* ws, int BH, int L, int p, float eps,
                     double lam_scale, hipStream_t s)
 {
 #define LSSAR_BWD(PV) \
-    launch_bwd<T, D, PV>(q, k, v, dout, dq, dk, dv, ws, nrows, L, p, eps, lam_scale, s)
+    launch_bwd<T, D, PV>(q, k, v, dout, dq, dk, dv, ws, BH, L, p, eps, lam_scale, s)
     switch (p) {
     case 1: LSSAR_BWD(1); break;
     case 2: LSSAR_BWD(2); break;
@@ -566,7 +590,7 @@ size_t lssar_bwd_workspace_bytes(int B, int H, int L, int d, int dtype)
 {
     if (validate_shape(B, H, L, d, dtype) != LSSAR_OK)
         return 0;
-    return bwd_layout(B, H, L, dtype).total();
+    return bwd_layout(B, H, L, d, dtype).total();
 }
 
 int lssar_attn_bwd_ws(const void* q, const void* k, const void* v, const void* dout, void* dq,
@@ -592,7 +616,7 @@ int lssar_attn_bwd_ws(const void* q, const void* k, const void* v, const void* d
     }
     if (overlaps(dq, tb, dk, tb) || overlaps(dq, tb, dv, tb) || overlaps(dk, tb, dv, tb))
         return LSSAR_EINVAL;
-    const BwdLayout w = bwd_layout(B, H, L, dtype);
+    const BwdLayout w = bwd_layout(B, H, L, d, dtype);
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
         workspace_bytes < w.total())
         return LSSAR_EWORKSPACE;
@@ -602,20 +626,20 @@ int lssar_attn_bwd_ws(const void* q, const void* k, const void* v, const void* d
             return LSSAR_EWORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const double lam_scale = std::log((double)d) / std::log(2.0);
-    const long nrows = (long)B * H * L;
+    const int BH = B * H;
     if (dtype == LSSAR_BF16) {
         if (d == 64)
-            bwd_dispatch_p<__bf16, 64>(q, k, v, dout, dq, dk, dv, workspace, nrows, L, p, eps,
+            bwd_dispatch_p<__bf16, 64>(q, k, v, dout, dq, dk, dv, workspace, BH, L, p, eps,
                                        lam_scale, s);
         else
-            bwd_dispatch_p<__bf16, 128>(q, k, v, dout, dq, dk, dv, workspace, nrows, L, p, eps,
+            bwd_dispatch_p<__bf16, 128>(q, k, v, dout, dq, dk, dv, workspace, BH, L, p, eps,
                                         lam_scale, s);
     } else {
         if (d == 64)
-            bwd_dispatch_p<float, 64>(q, k, v, dout, dq, dk, dv, workspace, nrows, L, p, eps,
+            bwd_dispatch_p<float, 64>(q, k, v, dout, dq, dk, dv, workspace, BH, L, p, eps,
                                       lam_scale, s);
         else
-            bwd_dispatch_p<float, 128>(q, k, v, dout, dq, dk, dv, workspace, nrows, L, p, eps,
+            bwd_dispatch_p<float, 128>(q, k, v, dout, dq, dk, dv, workspace, BH, L, p, eps,
                                        lam_scale, s);
     }
     hipError_t e = hipGetLastError();

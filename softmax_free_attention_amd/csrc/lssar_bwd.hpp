@@ -104,6 +104,9 @@ __device__ __forceinline__ C pow_m1(C y, int p)
 {
     if constexpr (P == 1) {
         return y > (C)0 ? (C)1 : (C)0;
+    } else if constexpr (P == 15) {
+        const C y2 = y * y, y3 = y2 * y, y6 = y3 * y3, y7 = y6 * y;
+        return y7 * y7;
     } else if constexpr (P == 0) {
         return p == 1 ? (y > (C)0 ? (C)1 : (C)0) : pow_chain<0>(y, p - 1);
     } else {

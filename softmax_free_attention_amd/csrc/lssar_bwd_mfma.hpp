@@ -1,0 +1,463 @@
+// lssar_bwd_mfma.hpp -- matrix-core kernels of the LSSAR backward for bf16
+// inputs on gfx950.
+//
+// The gradient formulas are those of lssar_bwd.hpp (the chain rule through
+// Key designs 1-3 of the paper note "Softplus Attention with Re-weighting
+// Boosts Length Extrapolation in Large Language Models", Method details);
+// these kernels evaluate them on the matrix cores:
+//   prep:     key factors f_j = 1/|k_j|, query factors 1/|q_i|, and the
+//             transposed copies Q^T, K^T, dO^T ([head][d][Lp], zero past L);
+//   rowstats: per query block, the scores S^T = K Q^T and dW^T = V dO^T on
+//             v_mfma_f32_16x16x32_bf16, pass 1 the row's S and max score,
+//             pass 2 the sums Y, P1, P2, Z; writes the row coefficients;
+//   dq:       per query block, S^T, dW^T, the pair gradients dc_ij f_j, and
+//             dQ^ = (dc f) K on v_mfma_f32_16x16x16_bf16, whose output
+//             layout (lane = one query, four keys) is exactly its A operand;
+//   dkdv:     per key block, S = Q K^T and dW = dO V^T (lane = one key, four
+//             queries), then dV = W^T dO and dK^ = (dc / |q|)^T Q on
+//             v_mfma_f32_16x16x16_bf16 with dO^T and Q^T as B operands.
+// A workgroup is 4 waves x 16 rows (queries, or keys in dkdv) of a 64-row
+// block; paired blocks {n-1-pi, pi} give every workgroup the same number of
+// 64-row tiles.  Tiles of the other side stream through LDS by LDS-direct
+// buffer loads, double-buffered, as in the forward kernel.  Softplus is
+// softplus2_acc (exact for every score) and its derivative is sigmoid2.
+#pragma once
+
+#include "lssar_bwd.hpp"
+#include "lssar_device.hpp"
+
+namespace lssar {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16k16(bf16x4 a, bf16x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// LDS layouts of one 64-row tile:
+//  * row-major: 64 rows x D bf16 as 16-byte slots, slot c of row r at
+//    r * R + (c ^ swz(r)), R = D / 8 (the forward's K tile layout);
+//  * transposed: D rows (dims) x 64 bf16 (the tile's rows), 8 slots per
+//    dim row, slot c of dim row e at e * 8 + (c ^ (e & 7)).
+template <int D>
+struct BwdTiles {
+    static constexpr int R = D / 8;
+    static constexpr int RM = 64 * D * 2;        // bytes of a row-major tile
+    static constexpr int TR = D * 64 * 2;        // bytes of a transposed tile
+    static constexpr int RM_LOADS = RM / 1024 / kWaves;   // wave-loads per wave
+    static constexpr int TR_LOADS = TR / 1024 / kWaves;
+    __device__ static int swz(int r) { return R == 8 ? ((r >> 1) & 7) : (r & 15); }
+};
+
+// Bytes of a 16-byte slot (slot index s of the tile) in the global tensor:
+// row-major source [rows][D] (row stride D*2) and transposed source
+// [D][Lp] (row stride Lp*2).
+template <int D>
+__device__ __forceinline__ unsigned rm_src(int s)
+{
+    using T = BwdTiles<D>;
+    const int r = s / T::R, c = (s % T::R) ^ T::swz(r);
+    return (unsigned)((r * D + c * 8) * 2);
+}
+__device__ __forceinline__ unsigned tr_src(int s, int Lp)
+{
+    const int e = s / 8, c = (s % 8) ^ (e & 7);
+    return (unsigned)(e * Lp * 2 + c * 16);
+}
+
+// ---------------------------------------------------------------------------
+// Prep: factors and transposes, one workgroup per (64-row block, head)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void lssar_bwd_prep_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ G,
+    float* __restrict__ rq, float* __restrict__ fk, __bf16* __restrict__ QT,
+    __bf16* __restrict__ KT, __bf16* __restrict__ GT, int L, int Lp)
+{
+    constexpr int RS = D + 2;                  // LDS row stride (elements), odd word count
+    constexpr int LPR = D / 8;
+    __shared__ __attribute__((aligned(16))) uint32_t tile[64 * RS / 2];
+    const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+    const size_t hoff = (size_t)bh * L * D;
+
+    // factors 1 / max(|x|, 1e-12) of the block's Q and K rows (fp64 sums)
+#pragma unroll
+    for (int n = 0; n < 64 * LPR / kThreads; ++n) {
+        const int c = tid + n * kThreads;
+        const int row = c / LPR, sub = c % LPR;
+        const int rg = kb * 64 + row;
+        double sq = 0.0, sk = 0.0;
+        if (rg < L) {
+            const u32x4 wq = *reinterpret_cast<const u32x4*>(Q + hoff + (size_t)rg * D + sub * 8);
+            const u32x4 wk = *reinterpret_cast<const u32x4*>(K + hoff + (size_t)rg * D + sub * 8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const double a = bf16lo(wq[e]), b = bf16hi(wq[e]);
+                const double x = bf16lo(wk[e]), y = bf16hi(wk[e]);
+                sq = fma(a, a, fma(b, b, sq));
+                sk = fma(x, x, fma(y, y, sk));
+            }
+        }
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) {
+            sq += __shfl_xor(sq, m, LPR);
+            sk += __shfl_xor(sk, m, LPR);
+        }
+        if (rg < L && sub == 0) {
+            rq[(size_t)bh * L + rg] = (float)(1.0 / fmax(sqrt(sq), 1e-12));
+            fk[(size_t)bh * L + rg] = (float)(1.0 / fmax(sqrt(sk), 1e-12));
+        }
+    }
+
+    // transposes of the block of Q, K and dO: [bh][e][kb*64 + r]
+    const __bf16* srcs[3] = {Q, K, G};
+    __bf16* dsts[3] = {QT, KT, GT};
+#pragma unroll
+    for (int m3 = 0; m3 < 3; ++m3) {
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < 64 * D / 8 / kThreads; ++n) {
+            const int c = tid + n * kThreads;
+            const int row = c / (D / 8), col8 = c % (D / 8);
+            const int rg = kb * 64 + row;
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (rg < L)
+                w = *reinterpret_cast<const u32x4*>(srcs[m3] + hoff + (size_t)rg * D + col8 * 8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                tile[(row * RS + col8 * 8) / 2 + e] = w[e];
+        }
+        __syncthreads();
+        __bf16* Th = dsts[m3] + (size_t)bh * D * Lp;
+#pragma unroll
+        for (int n = 0; n < (D / 2) * 8 / kThreads; ++n) {
+            const int c = tid + n * kThreads;
+            const int m = c / 8, p8 = c % 8;
+            uint32_t wv[8];
+#pragma unroll
+            for (int h = 0; h < 8; ++h)
+                wv[h] = tile[((8 * p8 + h) * RS) / 2 + m];     // (x[r][2m], x[r][2m+1])
+            u32x4 lo, hi;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                lo[h] = __builtin_amdgcn_perm(wv[2 * h + 1], wv[2 * h], 0x05040100u);
+                hi[h] = __builtin_amdgcn_perm(wv[2 * h + 1], wv[2 * h], 0x07060302u);
+            }
+            *reinterpret_cast<u32x4*>(Th + (size_t)(2 * m) * Lp + kb * 64 + 8 * p8) = lo;
+            *reinterpret_cast<u32x4*>(Th + (size_t)(2 * m + 1) * Lp + kb * 64 + 8 * p8) = hi;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Query-side kernels (rowstats, dq): lane (row16, grp) owns query row16 of its
+// wave and keys 16 ks + 4 grp + r of each 16-key block ks of a tile.
+// ---------------------------------------------------------------------------
+
+// MODE 0: rowstats (writes 8 coefficients per query row); MODE 1: dq.
+template <int D, int P, int MODE>
+__global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ G, const __bf16* __restrict__ KT, const float* __restrict__ rq,
+    const float* __restrict__ fk, float* __restrict__ stats, __bf16* __restrict__ dQ, int BH,
+    int L, int Lp, int nqb, int npair, double lam_scale, float eps, int p_rt)
+{
+    static_assert(D == 64 || D == 128, "head dim");
+    using T = BwdTiles<D>;
+    constexpr int DC = D / 32;                 // 32-deep MFMA steps over d
+    constexpr int DS = D / 16;                 // 16-wide output blocks over d
+    constexpr int KOFF = 0, VOFF = T::RM, TOFF = 2 * T::RM;
+    constexpr int FOFF = MODE == 1 ? 2 * T::RM + T::TR : 2 * T::RM;
+    constexpr int BYTES = FOFF + 256;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * BYTES];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, row16 = lane & 15, grp = lane >> 4;
+    const int item = xcd_item((int)blockIdx.x, npair * BH);
+    const int bh = item / npair, pi = item % npair;
+    const size_t hoff = (size_t)bh * L * D;
+
+    const void* kbase = K + hoff;
+    const void* vbase = V + hoff;
+    const unsigned rmbytes = (unsigned)L * D * 2u;
+    const void* ktbase = KT + (size_t)bh * D * Lp;
+    const unsigned trbytes = (unsigned)D * Lp * 2u;
+    const void* fbase = fk + (size_t)bh * L;
+    const unsigned fbytes = (unsigned)L * 4u;
+
+    int rm_ld[T::RM_LOADS], tr_ld[T::TR_LOADS];
+#pragma unroll
+    for (int n = 0; n < T::RM_LOADS; ++n)
+        rm_ld[n] = (int)rm_src<D>((wave * T::RM_LOADS + n) * 64 + lane);
+#pragma unroll
+    for (int n = 0; n < T::TR_LOADS; ++n)
+        tr_ld[n] = (int)tr_src((wave * T::TR_LOADS + n) * 64 + lane, Lp);
+
+    // tile kt of K (and V, K^T as the pass needs) into buffer buf
+    auto issue = [&](int kt, int buf, bool with_v) {
+        unsigned char* base = lds + buf * BYTES;
+#pragma unroll
+        for (int n = 0; n < T::RM_LOADS; ++n)
+            load16_to_lds(kbase, rmbytes, base + KOFF + (wave * T::RM_LOADS + n) * 1024, rm_ld[n],
+                          kt * 64 * D * 2);
+        if (with_v) {
+#pragma unroll
+            for (int n = 0; n < T::RM_LOADS; ++n)
+                load16_to_lds(vbase, rmbytes, base + VOFF + (wave * T::RM_LOADS + n) * 1024,
+                              rm_ld[n], kt * 64 * D * 2);
+            if constexpr (MODE == 1) {
+#pragma unroll
+                for (int n = 0; n < T::TR_LOADS; ++n)
+                    load16_to_lds(ktbase, trbytes, base + TOFF + (wave * T::TR_LOADS + n) * 1024,
+                                  tr_ld[n], kt * 64 * 2);
+            }
+        }
+        if (wave == 0)
+            load4_to_lds(fbase, fbytes, base + FOFF, lane * 4, kt * 64 * 4);
+    };
+
+    int ard[DC];                               // A-operand slot offsets of row-major tiles
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+        ard[dc] = (row16 * T::R + ((4 * dc + grp) ^ T::swz(row16))) * 16;
+
+    const int nblk = (pi == nqb - 1 - pi) ? 1 : 2;
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int qb = blk == 0 ? nqb - 1 - pi : pi;
+        const int qw0 = qb * 64 + wave * 16;
+        const int qwl = min(qw0 + 15, L - 1);
+        const bool wave_active = qw0 < L;
+        const int ntiles = qb + 1;
+        const int qi = qw0 + row16;
+        const bool qvalid = qi < L;
+
+        // query and dO rows of this lane's query (B operands), the row factor
+        bf16x8 qf[DC], gf[DC];
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+            u32x4 w = {0u, 0u, 0u, 0u}, x = {0u, 0u, 0u, 0u};
+            if (qvalid) {
+                w = *reinterpret_cast<const u32x4*>(Q + hoff + (size_t)qi * D + 32 * dc + 8 * grp);
+                x = *reinterpret_cast<const u32x4*>(G + hoff + (size_t)qi * D + 32 * dc + 8 * grp);
+            }
+            qf[dc] = __builtin_bit_cast(bf16x8, w);
+            gf[dc] = __builtin_bit_cast(bf16x8, x);
+        }
+        const float rqi = qvalid ? rq[(size_t)bh * L + qi] : 0.0f;
+        // log2(e) ln d ln i / |q_i|  (Key design 1: log d . log N)
+        const float lam = (float)(lam_scale * log((double)(qi + 1))) * rqi;
+
+        auto mm_block = [&](const unsigned char* base, int off, const bf16x8 (&b)[DC], int ks) {
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc) {
+                const bf16x8 a =
+                    *reinterpret_cast<const bf16x8*>(base + off + ard[dc] + ks * 16 * T::R * 16);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[dc], acc, 0, 0, 0);
+            }
+            return acc;
+        };
+        // scaled scores t (masked: -inf) of block ks, and the key factors
+        auto scores = [&](int kt, const unsigned char* base, int ks, f32x4 acc, bool diag,
+                          f32x4& f4) {
+            f4 = *reinterpret_cast<const f32x4*>(base + FOFF + (16 * ks + 4 * grp) * 4);
+            f32x4 t = acc * (f4 * lam);
+            if (diag) {
+                const int k0 = kt * 64 + 16 * ks + 4 * grp;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    t[r] = (k0 + r <= qi) ? t[r] : -INFINITY;
+            }
+            return t;
+        };
+
+        // ---------------- pass 1 (rowstats): S and the max score ----------------
+        float s1 = 0.0f, tmax = -INFINITY;
+        float c = 0.0f, tc = 0.0f;
+        bool degen = true;
+        // row coefficients (dq reads them; rowstats computes them)
+        float invY = 0.0f, delta = 0.0f, Ac = 0.0f, Ec = 0.0f;
+
+        auto tile_loop = [&](bool with_v, auto body) {
+            __syncthreads();                       // LDS buffers free
+            issue(0, 0, with_v);
+            for (int kt = 0; kt < ntiles; ++kt) {
+                const int buf = kt & 1;
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();                   // tile kt landed; buf^1 free
+                if (kt + 1 < ntiles)
+                    issue(kt + 1, buf ^ 1, with_v);
+                if (!(wave_active && kt * 64 <= qwl))
+                    continue;
+                const unsigned char* base = lds + buf * BYTES;
+                if (kt * 64 + 63 > qw0)
+                    body(kt, base, std::true_type{});
+                else
+                    body(kt, base, std::false_type{});
+            }
+        };
+
+        if constexpr (MODE == 0) {
+            tile_loop(false, [&](int kt, const unsigned char* base, auto diag_tag) {
+                constexpr bool DIAG = decltype(diag_tag)::value;
+                const int nks = DIAG ? min(4, (qwl - kt * 64) / 16 + 1) : 4;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    if (DIAG && ks >= nks)
+                        continue;
+                    f32x4 f4;
+                    const f32x4 t = scores(kt, base, ks, mm_block(base, KOFF, qf, ks), DIAG, f4);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        s1 += softplus2_acc(t[r]);
+                        tmax = fmaxf(tmax, t[r]);
+                    }
+                }
+            });
+            s1 += __shfl_xor(s1, 16);
+            s1 += __shfl_xor(s1, 32);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float o = (qi + 1) <= 3 ? 0.0f : 1.0f;
+            const float tau = o * s1 / (float)(qi + 1);
+            const float gap = softplus2_acc(tmax) - tau;
+            degen = !((float)(qi + 1) * gap / s1 > eps) || !qvalid;
+            c = degen ? 0.0f : 1.0f / gap;
+            tc = tau * c;
+
+            // ---------------- pass 2: Y, P1, P2, Z ----------------
+            float Y = 0.0f, P1 = 0.0f, P2 = 0.0f, Z = 0.0f;
+            tile_loop(true, [&](int kt, const unsigned char* base, auto diag_tag) {
+                constexpr bool DIAG = decltype(diag_tag)::value;
+                const int nks = DIAG ? min(4, (qwl - kt * 64) / 16 + 1) : 4;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    if (DIAG && ks >= nks)
+                        continue;
+                    f32x4 f4;
+                    const f32x4 t = scores(kt, base, ks, mm_block(base, KOFF, qf, ks), DIAG, f4);
+                    const f32x4 dw = mm_block(base, VOFF, gf, ks);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float sp = softplus2_acc(t[r]);
+                        const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(sp, c, -tc), 0.0f, 1.0f);
+                        const float ym = pow_m1<P>(y, p_rt);
+                        const float yp = ym * y;
+                        Y += yp;
+                        P1 = __builtin_fmaf(yp, dw[r], P1);
+                        const float sym = sp * ym;
+                        P2 = __builtin_fmaf(sym, dw[r], P2);
+                        Z += sym;
+                    }
+                }
+            });
+#pragma unroll
+            for (int m = 16; m <= 32; m <<= 1) {
+                Y += __shfl_xor(Y, m);
+                P1 += __shfl_xor(P1, m);
+                P2 += __shfl_xor(P2, m);
+                Z += __shfl_xor(Z, m);
+            }
+            if (qvalid && grp == 0) {
+                float* st = stats + ((size_t)bh * L + qi) * kBwdRowStats;
+                float4 a, b;
+                if (degen) {
+                    a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    b = make_float4(0.0f, 0.0f, lam, rqi);
+                } else {
+                    const float dl = P1 / Y;
+                    const float alpha = (float)p_rt * s1 / (gap * Y);
+                    const float epsr = alpha / s1 * (P2 - dl * Z);
+                    // ln d ln i / (S ln 2), S in base 2: lam_scale ln i / S
+                    const float kappa = (float)(lam_scale * log((double)(qi + 1))) / s1;
+                    a = make_float4(c, tc, 1.0f / Y, dl);
+                    b = make_float4(kappa * alpha, kappa * epsr, lam, rqi);
+                }
+                *reinterpret_cast<float4*>(st) = a;
+                *reinterpret_cast<float4*>(st + 4) = b;
+            }
+        } else {
+            // ---------------- dq: dQ^ = sum_j (dc_ij f_j) k_j ----------------
+            if (qvalid) {
+                const float* st = stats + ((size_t)bh * L + qi) * kBwdRowStats;
+                const float4 a = *reinterpret_cast<const float4*>(st);
+                const float4 b = *reinterpret_cast<const float4*>(st + 4);
+                c = a.x;
+                tc = a.y;
+                invY = a.z;
+                delta = a.w;
+                Ac = b.x;
+                Ec = b.y;
+            }
+            f32x4 acc[DS];
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds)
+                acc[ds] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            // K^T tile: B operand of 16x16x16 = 4 keys of dim row 16 ds + row16
+            int trd[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int slot = 2 * ks + (grp >> 1);   // 16-byte slot of keys 16ks+4grp..
+                trd[ks] = ((slot ^ (row16 & 7)) * 16) + (grp & 1) * 8;
+            }
+            tile_loop(true, [&](int kt, const unsigned char* base, auto diag_tag) {
+                constexpr bool DIAG = decltype(diag_tag)::value;
+                const int nks = DIAG ? min(4, (qwl - kt * 64) / 16 + 1) : 4;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    if (DIAG && ks >= nks)
+                        continue;
+                    f32x4 f4;
+                    const f32x4 t = scores(kt, base, ks, mm_block(base, KOFF, qf, ks), DIAG, f4);
+                    const f32x4 dw = mm_block(base, VOFF, gf, ks);
+                    f32x4 g;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float sp = softplus2_acc(t[r]);
+                        const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(sp, c, -tc), 0.0f, 1.0f);
+                        const float ym = pow_m1<P>(y, p_rt);
+                        const float dcv = sigmoid2(t[r]) * (Ac * ym * (dw[r] - delta) - Ec);
+                        g[r] = dcv * f4[r];
+                    }
+                    const bf16x4 gb = __builtin_convertvector(g, bf16x4);
+#pragma unroll
+                    for (int ds = 0; ds < DS; ++ds) {
+                        const bf16x4 bk = *reinterpret_cast<const bf16x4*>(
+                            base + TOFF + (16 * ds + row16) * 128 + trd[ks]);
+                        acc[ds] = mfma16k16(gb, bk, acc[ds]);
+                    }
+                }
+            });
+            // acc[ds][r] = dQ^[query 4 grp + r of the wave][dim 16 ds + row16]
+            // dq = (dq^ - (dq^ . q^) q^) / |q|, or dq^ / 1e-12 below the clamp
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int qr = qw0 + 4 * grp + r;
+                const bool ok = qr < L;
+                const float rr = ok ? rq[(size_t)bh * L + qr] : 0.0f;
+                float qh[DS], dd = 0.0f;
+#pragma unroll
+                for (int ds = 0; ds < DS; ++ds) {
+                    qh[ds] = ok ? (float)Q[hoff + (size_t)qr * D + 16 * ds + row16] * rr : 0.0f;
+                    dd = __builtin_fmaf(acc[ds][r], qh[ds], dd);
+                }
+#pragma unroll
+                for (int m = 1; m < 16; m <<= 1)
+                    dd += __shfl_xor(dd, m);
+                const bool clamped = !(rr < 1e12f);
+                if (ok) {
+#pragma unroll
+                    for (int ds = 0; ds < DS; ++ds) {
+                        const float v = clamped ? acc[ds][r] * rr : (acc[ds][r] - dd * qh[ds]) * rr;
+                        dQ[hoff + (size_t)qr * D + 16 * ds + row16] = (__bf16)v;
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace lssar

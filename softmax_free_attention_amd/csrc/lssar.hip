@@ -400,6 +400,10 @@ void launch_bwd(const void* q, const void* k, const void* v, const void* dout, v
         hipLaunchKernelGGL((lssar::lssar_bwd_qside_kernel<D, P, 1>), grid, dim3(lssar::kThreads),
                            0, s, Q, K, V, G, KT, rq, fk, st, static_cast<__bf16*>(dq), BH, L,
                            w.Lp, nqb, npair, lam_scale, eps, p);
+        hipLaunchKernelGGL((lssar::lssar_bwd_kside_kernel<D, P>), grid, dim3(lssar::kThreads), 0,
+                           s, Q, K, V, G, QT, GT, fk, st, static_cast<__bf16*>(dk),
+                           static_cast<__bf16*>(dv), BH, L, w.Lp, nqb, npair, p);
+        return;
     } else {
         constexpr int rpb = lssar::kBwdThreads / (D / lssar::DecTraits<T>::EPL);
         hipLaunchKernelGGL((lssar::lssar_bwd_norms_kernel<T, D>),

@@ -460,4 +460,201 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Key-side kernel (dk, dv): lane (row16, grp) owns key row16 of its wave and
+// queries 16 c + 4 grp + r of each 16-query block c of a query tile.
+// ---------------------------------------------------------------------------
+template <int D, int P>
+__global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ G, const __bf16* __restrict__ QT, const __bf16* __restrict__ GT,
+    const float* __restrict__ fk, const float* __restrict__ stats, __bf16* __restrict__ dK,
+    __bf16* __restrict__ dV, int BH, int L, int Lp, int nkb, int npair, int p_rt)
+{
+    static_assert(D == 64 || D == 128, "head dim");
+    using T = BwdTiles<D>;
+    constexpr int DC = D / 32;
+    constexpr int DS = D / 16;
+    constexpr int QOFF = 0, GOFF = T::RM, QTOFF = 2 * T::RM, GTOFF = 2 * T::RM + T::TR;
+    constexpr int SOFF = 2 * T::RM + 2 * T::TR;
+    constexpr int BYTES = SOFF + 64 * kBwdRowStats * 4;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * BYTES];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, row16 = lane & 15, grp = lane >> 4;
+    const int item = xcd_item((int)blockIdx.x, npair * BH);
+    const int bh = item / npair, pi = item % npair;
+    const size_t hoff = (size_t)bh * L * D;
+
+    const void* qbase = Q + hoff;
+    const void* gbase = G + hoff;
+    const unsigned rmbytes = (unsigned)L * D * 2u;
+    const void* qtbase = QT + (size_t)bh * D * Lp;
+    const void* gtbase = GT + (size_t)bh * D * Lp;
+    const unsigned trbytes = (unsigned)D * Lp * 2u;
+    const void* sbase = stats + (size_t)bh * L * kBwdRowStats;
+    const unsigned sbytes = (unsigned)L * kBwdRowStats * 4u;
+
+    int rm_ld[T::RM_LOADS], tr_ld[T::TR_LOADS];
+#pragma unroll
+    for (int n = 0; n < T::RM_LOADS; ++n)
+        rm_ld[n] = (int)rm_src<D>((wave * T::RM_LOADS + n) * 64 + lane);
+#pragma unroll
+    for (int n = 0; n < T::TR_LOADS; ++n)
+        tr_ld[n] = (int)tr_src((wave * T::TR_LOADS + n) * 64 + lane, Lp);
+
+    // query tile qt: Q, dO (row-major), Q^T, dO^T and the 64 rows' coefficients
+    auto issue = [&](int qt, int buf) {
+        unsigned char* base = lds + buf * BYTES;
+#pragma unroll
+        for (int n = 0; n < T::RM_LOADS; ++n) {
+            load16_to_lds(qbase, rmbytes, base + QOFF + (wave * T::RM_LOADS + n) * 1024, rm_ld[n],
+                          qt * 64 * D * 2);
+            load16_to_lds(gbase, rmbytes, base + GOFF + (wave * T::RM_LOADS + n) * 1024, rm_ld[n],
+                          qt * 64 * D * 2);
+        }
+#pragma unroll
+        for (int n = 0; n < T::TR_LOADS; ++n) {
+            load16_to_lds(qtbase, trbytes, base + QTOFF + (wave * T::TR_LOADS + n) * 1024,
+                          tr_ld[n], qt * 64 * 2);
+            load16_to_lds(gtbase, trbytes, base + GTOFF + (wave * T::TR_LOADS + n) * 1024,
+                          tr_ld[n], qt * 64 * 2);
+        }
+        if (wave < 2)
+            load16_to_lds(sbase, sbytes, base + SOFF + wave * 1024, (wave * 64 + lane) * 16,
+                          qt * 64 * kBwdRowStats * 4);
+    };
+
+    int ard[DC];
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+        ard[dc] = (row16 * T::R + ((4 * dc + grp) ^ T::swz(row16))) * 16;
+    int trd[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        trd[c] = (((2 * c + (grp >> 1)) ^ (row16 & 7)) * 16) + (grp & 1) * 8;
+
+    const int nblk = (pi == nkb - 1 - pi) ? 1 : 2;
+    for (int blk = 0; blk < nblk; ++blk) {
+        // blk 0: the earlier key block (more query tiles), blk 1: the later
+        const int kb = blk == 0 ? pi : nkb - 1 - pi;
+        const int kw0 = kb * 64 + wave * 16;       // first key row of this wave
+        const int kj = kw0 + row16;                // this lane's key (0-based)
+        const bool kvalid = kj < L;
+        const int qt0 = kb, ntiles = (L + 63) / 64 - kb;
+
+        bf16x8 kf[DC], vf[DC];
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+            u32x4 w = {0u, 0u, 0u, 0u}, x = {0u, 0u, 0u, 0u};
+            if (kvalid) {
+                w = *reinterpret_cast<const u32x4*>(K + hoff + (size_t)kj * D + 32 * dc + 8 * grp);
+                x = *reinterpret_cast<const u32x4*>(V + hoff + (size_t)kj * D + 32 * dc + 8 * grp);
+            }
+            kf[dc] = __builtin_bit_cast(bf16x8, w);
+            vf[dc] = __builtin_bit_cast(bf16x8, x);
+        }
+        const float fj = kvalid ? fk[(size_t)bh * L + kj] : 0.0f;
+
+        f32x4 adv[DS], adk[DS];
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+            adv[ds] = adk[ds] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+        auto mm_block = [&](const unsigned char* base, int off, const bf16x8 (&b)[DC], int c) {
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc) {
+                const bf16x8 a =
+                    *reinterpret_cast<const bf16x8*>(base + off + ard[dc] + c * 16 * T::R * 16);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[dc], acc, 0, 0, 0);
+            }
+            return acc;
+        };
+
+        auto tile = [&](int qt, const unsigned char* base, auto diag_tag) {
+            constexpr bool DIAG = decltype(diag_tag)::value;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                // query blocks entirely before this wave's first key see none of it
+                if (DIAG && qt * 64 + 16 * c + 15 < kw0)
+                    continue;
+                const f32x4 sc = mm_block(base, QOFF, kf, c);   // S[query][key]
+                const f32x4 dw = mm_block(base, GOFF, vf, c);   // dW[query][key]
+                f32x4 w4, g4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int qrow = 16 * c + 4 * grp + r;       // query in the tile
+                    const float* st = reinterpret_cast<const float*>(base + SOFF) +
+                                      qrow * kBwdRowStats;
+                    const float4 a = *reinterpret_cast<const float4*>(st);
+                    const float4 b = *reinterpret_cast<const float4*>(st + 4);
+                    float t = sc[r] * b.z * fj;                  // lam_i f_j (q . k)
+                    if (DIAG && qt * 64 + qrow < kj)
+                        t = -INFINITY;
+                    const float sp = softplus2_acc(t);
+                    const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(sp, a.x, -a.y), 0.0f, 1.0f);
+                    const float ym = pow_m1<P>(y, p_rt);
+                    w4[r] = ym * y * a.z;
+                    g4[r] = sigmoid2(t) * (b.x * ym * (dw[r] - a.w) - b.y) * b.w;
+                }
+                const bf16x4 wb = __builtin_convertvector(w4, bf16x4);
+                const bf16x4 gb = __builtin_convertvector(g4, bf16x4);
+#pragma unroll
+                for (int ds = 0; ds < DS; ++ds) {
+                    const int off = (16 * ds + row16) * 128 + trd[c];
+                    const bf16x4 bg = *reinterpret_cast<const bf16x4*>(base + GTOFF + off);
+                    const bf16x4 bq = *reinterpret_cast<const bf16x4*>(base + QTOFF + off);
+                    adv[ds] = mfma16k16(wb, bg, adv[ds]);
+                    adk[ds] = mfma16k16(gb, bq, adk[ds]);
+                }
+            }
+        };
+
+        __syncthreads();                           // LDS buffers free
+        issue(qt0, 0);
+        for (int n = 0; n < ntiles; ++n) {
+            const int buf = n & 1, qt = qt0 + n;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (n + 1 < ntiles)
+                issue(qt + 1, buf ^ 1);
+            if (kw0 >= L)
+                continue;
+            const unsigned char* base = lds + buf * BYTES;
+            if (qt == kb)
+                tile(qt, base, std::true_type{});
+            else
+                tile(qt, base, std::false_type{});
+        }
+
+        // adv/adk[ds][r] = grad[key 4 grp + r of the wave][dim 16 ds + row16]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int kr = kw0 + 4 * grp + r;
+            const bool ok = kr < L;
+            const float ff = ok ? fk[(size_t)bh * L + kr] : 0.0f;
+            float kh[DS], dd = 0.0f;
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds) {
+                kh[ds] = ok ? (float)K[hoff + (size_t)kr * D + 16 * ds + row16] * ff : 0.0f;
+                dd = __builtin_fmaf(adk[ds][r], kh[ds], dd);
+            }
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1)
+                dd += __shfl_xor(dd, m);
+            const bool clamped = !(ff < 1e12f);
+            if (ok) {
+#pragma unroll
+                for (int ds = 0; ds < DS; ++ds) {
+                    const float v = clamped ? adk[ds][r] * ff : (adk[ds][r] - dd * kh[ds]) * ff;
+                    dK[hoff + (size_t)kr * D + 16 * ds + row16] = (__bf16)v;
+                    dV[hoff + (size_t)kr * D + 16 * ds + row16] = (__bf16)adv[ds][r];
+                }
+            }
+        }
+    }
+}
+
 }  // namespace lssar

@@ -9,7 +9,8 @@
 //             transposed copies Q^T, K^T, dO^T ([head][d][Lp], zero past L);
 //   rowstats: per query block, the scores S^T = K Q^T and dW^T = V dO^T on
 //             v_mfma_f32_16x16x32_bf16, pass 1 the row's S and max score,
-//             pass 2 the sums Y, P1, P2, Z; writes the row coefficients;
+//             pass 2 the sums Y, P1, P2, Z; writes the row coefficients
+//             (c, tau c, 1/Y, delta, A/|q|, E/|q|, the score factor, 1/|q|);
 //   dq:       per query block, S^T, dW^T, the pair gradients dc_ij f_j, and
 //             dQ^ = (dc f) K on v_mfma_f32_16x16x16_bf16, whose output
 //             layout (lane = one query, four keys) is exactly its A operand;
@@ -29,6 +30,18 @@
 namespace lssar {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Softplus2(t) (exact for every t, as softplus2_acc) and its derivative
+// sigma(t ln 2) = e / (1 + e), e = 2^t, from one exp2.
+__device__ __forceinline__ void sp_sig(float t, float& sp, float& sig)
+{
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float e = __builtin_amdgcn_exp2f(t);
+    const float ope = 1.0f + e;
+    const float series = e * __builtin_fmaf(-0.5f * kLog2e, e, kLog2e);
+    sp = e < (1.0f / 256.0f) ? series : __builtin_amdgcn_logf(ope);
+    sig = e * __builtin_amdgcn_rcpf(ope);
+}
 
 __device__ __forceinline__ f32x4 mfma16k16(bf16x4 a, bf16x4 b, f32x4 c)
 {
@@ -373,8 +386,10 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
                     const float epsr = alpha / s1 * (P2 - dl * Z);
                     // ln d ln i / (S ln 2), S in base 2: lam_scale ln i / S
                     const float kappa = (float)(lam_scale * log((double)(qi + 1))) / s1;
+                    // A and E carry 1 / |q_i|: dk^ sums (dc_ij / |q_i|) q_i, and dq
+                    // = (dq^ - (dq^ . q^) q^) / |q_i| takes the factor from them
                     a = make_float4(c, tc, 1.0f / Y, dl);
-                    b = make_float4(kappa * alpha, kappa * epsr, lam, rqi);
+                    b = make_float4(kappa * alpha * rqi, kappa * epsr * rqi, lam, rqi);
                 }
                 *reinterpret_cast<float4*>(st) = a;
                 *reinterpret_cast<float4*>(st + 4) = b;
@@ -416,10 +431,11 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
                     f32x4 g;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float sp = softplus2_acc(t[r]);
+                        float sp, sg;
+                        sp_sig(t[r], sp, sg);
                         const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(sp, c, -tc), 0.0f, 1.0f);
                         const float ym = pow_m1<P>(y, p_rt);
-                        const float dcv = sigmoid2(t[r]) * (Ac * ym * (dw[r] - delta) - Ec);
+                        const float dcv = sg * (Ac * ym * (dw[r] - delta) - Ec);
                         g[r] = dcv * f4[r];
                     }
                     const bf16x4 gb = __builtin_convertvector(g, bf16x4);
@@ -447,11 +463,12 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
 #pragma unroll
                 for (int m = 1; m < 16; m <<= 1)
                     dd += __shfl_xor(dd, m);
+                // acc already carries 1 / |q| (through the row's coefficients)
                 const bool clamped = !(rr < 1e12f);
                 if (ok) {
 #pragma unroll
                     for (int ds = 0; ds < DS; ++ds) {
-                        const float v = clamped ? acc[ds][r] * rr : (acc[ds][r] - dd * qh[ds]) * rr;
+                        const float v = clamped ? acc[ds][r] : acc[ds][r] - dd * qh[ds];
                         dQ[hoff + (size_t)qr * D + 16 * ds + row16] = (__bf16)v;
                     }
                 }
@@ -593,11 +610,12 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
                     float t = sc[r] * b.z * fj;                  // lam_i f_j (q . k)
                     if (DIAG && qt * 64 + qrow < kj)
                         t = -INFINITY;
-                    const float sp = softplus2_acc(t);
+                    float sp, sg;
+                    sp_sig(t, sp, sg);
                     const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(sp, a.x, -a.y), 0.0f, 1.0f);
                     const float ym = pow_m1<P>(y, p_rt);
                     w4[r] = ym * y * a.z;
-                    g4[r] = sigmoid2(t) * (b.x * ym * (dw[r] - a.w) - b.y) * b.w;
+                    g4[r] = sg * __builtin_fmaf(b.x * ym, dw[r] - a.w, -b.y);
                 }
                 const bf16x4 wb = __builtin_convertvector(w4, bf16x4);
                 const bf16x4 gb = __builtin_convertvector(g4, bf16x4);

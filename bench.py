@@ -23,7 +23,9 @@ entry point, prep included) and "decode" (the decode step over a key/value
 cache: 16 sequences x 12 heads at 8192 cached tokens, the same with ragged
 lengths, and a wide-head case; HBM-bound, reported as GB/s of algorithmic
 bytes and tokens/s; caches drawn N(0,1) on the device, lengths from the
-input generator).
+input generator) and "backward" (lssar_attn_bwd_ws on the bench workload:
+algorithmic TFLOP/s counting 8*d flops per causal pair, the four products
+dO V^T, W^T dO, dC K and dC^T Q; the score recompute is not counted).
 """
 from __future__ import annotations
 
@@ -189,6 +191,29 @@ def time_decode(name, steps, warmup):
                          "bytes": nbytes}}
 
 
+def time_backward(q, k, v, p, steps, warmup, eps=1e-4):
+    """Mean ms of one backward call (four kernels), HIP events on the launch
+    stream, with a seeded N(0,1) dout."""
+    import torch
+    import softmax_free_attention_amd as sfa
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    dout = torch.randn(q.shape, generator=g, device="cuda").to(q.dtype)
+    ws = sfa.bwd_workspace_for(q)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        sfa.lssar_attn_bwd_ws(q, k, v, dout, dq, dk, dv, ws, p=p, eps=eps, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        sfa.lssar_attn_bwd_ws(q, k, v, dout, dq, dk, dv, ws, p=p, eps=eps, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def cpu_baseline(inp, seconds: float):
     """The fp64 oracle, as it stands, on a bounded sample of the workload's
     rows (strided over all heads and positions), on all host cores."""
@@ -250,6 +275,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--calib-mib", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB (read N, "
                          "write N), the reference kernel for scaling rocprofv3 FETCH/WRITE_SIZE")
@@ -311,6 +337,13 @@ def main():
         vt = time_variants(q, k, v, wl.p, args.steps, args.warmup)
         line["variants"] = {n: {"ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
                             for n, ms in vt.items()}
+    if not args.no_backward:
+        log("bench: backward")
+        bms = time_backward(q, k, v, wl.p, max(3, args.steps // 4), 2)
+        bflops = 2 * flops
+        line["backward"] = {"ms": round(bms, 4), "tflops": round(bflops / (bms * 1e-3) / 1e12, 2),
+                            "pct_bf16_peak": round(100 * bflops / (bms * 1e-3) / 1e12 /
+                                                   PEAK_TFLOPS["bf16"], 3)}
     if not args.no_decode:
         log("bench: decode")
         line["decode"] = {n: time_decode(n, 50, 10)

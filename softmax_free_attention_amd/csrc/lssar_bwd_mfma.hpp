@@ -170,6 +170,8 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_prep_kernel(
 // ---------------------------------------------------------------------------
 
 // MODE 0: rowstats (writes 8 coefficients per query row); MODE 1: dq.
+// One key-tile buffer in LDS: a double-buffered loop measured slower, since
+// its LDS and registers cost workgroups per CU that hide the loads better.
 template <int D, int P, int MODE>
 __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
     constexpr int KOFF = 0, VOFF = T::RM, TOFF = 2 * T::RM;
     constexpr int FOFF = MODE == 1 ? 2 * T::RM + T::TR : 2 * T::RM;
     constexpr int BYTES = FOFF + 256;
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[BYTES];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -209,9 +211,9 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
     for (int n = 0; n < T::TR_LOADS; ++n)
         tr_ld[n] = (int)tr_src((wave * T::TR_LOADS + n) * 64 + lane, Lp);
 
-    // tile kt of K (and V, K^T as the pass needs) into buffer buf
-    auto issue = [&](int kt, int buf, bool with_v) {
-        unsigned char* base = lds + buf * BYTES;
+    // tile kt of K (and V, K^T as the pass needs) into LDS
+    auto issue = [&](int kt, bool with_v) {
+        unsigned char* base = lds;
 #pragma unroll
         for (int n = 0; n < T::RM_LOADS; ++n)
             load16_to_lds(kbase, rmbytes, base + KOFF + (wave * T::RM_LOADS + n) * 1024, rm_ld[n],
@@ -295,21 +297,17 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
         float invY = 0.0f, delta = 0.0f, Ac = 0.0f, Ec = 0.0f;
 
         auto tile_loop = [&](bool with_v, auto body) {
-            __syncthreads();                       // LDS buffers free
-            issue(0, 0, with_v);
             for (int kt = 0; kt < ntiles; ++kt) {
-                const int buf = kt & 1;
+                __syncthreads();                   // readers of the previous tile done
+                issue(kt, with_v);
                 __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();                   // tile kt landed; buf^1 free
-                if (kt + 1 < ntiles)
-                    issue(kt + 1, buf ^ 1, with_v);
+                __syncthreads();                   // tile kt landed
                 if (!(wave_active && kt * 64 <= qwl))
                     continue;
-                const unsigned char* base = lds + buf * BYTES;
                 if (kt * 64 + 63 > qw0)
-                    body(kt, base, std::true_type{});
+                    body(kt, lds, std::true_type{});
                 else
-                    body(kt, base, std::false_type{});
+                    body(kt, lds, std::false_type{});
             }
         };
 
@@ -481,6 +479,7 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
 // Key-side kernel (dk, dv): lane (row16, grp) owns key row16 of its wave and
 // queries 16 c + 4 grp + r of each 16-query block c of a query tile.
 // ---------------------------------------------------------------------------
+// One query-tile buffer in LDS, as in the query-side kernels.
 template <int D, int P>
 __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -495,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
     constexpr int QOFF = 0, GOFF = T::RM, QTOFF = 2 * T::RM, GTOFF = 2 * T::RM + T::TR;
     constexpr int SOFF = 2 * T::RM + 2 * T::TR;
     constexpr int BYTES = SOFF + 64 * kBwdRowStats * 4;
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[BYTES];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -522,8 +521,8 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
         tr_ld[n] = (int)tr_src((wave * T::TR_LOADS + n) * 64 + lane, Lp);
 
     // query tile qt: Q, dO (row-major), Q^T, dO^T and the 64 rows' coefficients
-    auto issue = [&](int qt, int buf) {
-        unsigned char* base = lds + buf * BYTES;
+    auto issue = [&](int qt) {
+        unsigned char* base = lds;
 #pragma unroll
         for (int n = 0; n < T::RM_LOADS; ++n) {
             load16_to_lds(qbase, rmbytes, base + QOFF + (wave * T::RM_LOADS + n) * 1024, rm_ld[n],
@@ -630,21 +629,18 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
             }
         };
 
-        __syncthreads();                           // LDS buffers free
-        issue(qt0, 0);
         for (int n = 0; n < ntiles; ++n) {
-            const int buf = n & 1, qt = qt0 + n;
+            const int qt = qt0 + n;
+            __syncthreads();                       // readers of the previous tile done
+            issue(qt);
             __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (n + 1 < ntiles)
-                issue(qt + 1, buf ^ 1);
+            __syncthreads();                       // tile qt landed
             if (kw0 >= L)
                 continue;
-            const unsigned char* base = lds + buf * BYTES;
             if (qt == kb)
-                tile(qt, base, std::true_type{});
+                tile(qt, lds, std::true_type{});
             else
-                tile(qt, base, std::false_type{});
+                tile(qt, lds, std::false_type{});
         }
 
         // adv/adk[ds][r] = grad[key 4 grp + r of the wave][dim 16 ds + row16]

@@ -68,6 +68,8 @@ def _bind(lib):
     lib.lssar_ref_bwd_f64.argtypes = [dp] * 7 + [ctypes.c_int] * 5 + [ctypes.c_double,
                                                                       ctypes.c_int]
     lib.lssar_ref_bwd_f64.restype = ctypes.c_int
+    lib.lssar_ref_rowstats_f64.argtypes = [dp, dp, dp] + [ctypes.c_int] * 5
+    lib.lssar_ref_rowstats_f64.restype = ctypes.c_int
     lib.lssar_ref_threads.argtypes = [ctypes.c_int]
     lib.lssar_ref_threads.restype = ctypes.c_int
     return lib
@@ -138,6 +140,24 @@ def lssar_bwd(q, k, v, dout, p: int, eps: float = DEFAULT_EPS, nthreads: int = 0
     if squeeze:
         return dq[0, 0], dk[0, 0], dv[0, 0]
     return dq, dk, dv
+
+
+def lssar_rowstats(q, k, nthreads: int = 0, lib=None) -> np.ndarray:
+    """Oracle row statistics on [B,H,L,d] (or [L,d]) inputs: [..., L, 2] with
+    S_i = sum_{j<=i} Softplus(s_ij) (stage 1's L1 norm before normalising)
+    and m_i = max_{j<=i} s_ij (the largest unmasked scaled score)."""
+    lib = lib or load()
+    q, k = _f64(q), _f64(k)
+    squeeze = q.ndim == 2
+    if squeeze:
+        q, k = q[None, None], k[None, None]
+    B, H, L, d = q.shape
+    assert k.shape == q.shape
+    st = np.empty((B, H, L, 2), dtype=np.float64)
+    rc = lib.lssar_ref_rowstats_f64(_ptr(q), _ptr(k), _ptr(st), B, H, L, d, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"lssar_ref_rowstats_f64 failed with status {rc}")
+    return st[0, 0] if squeeze else st
 
 
 def threads(nthreads: int = 0, lib=None) -> int:

@@ -44,10 +44,10 @@
  *
  * Two variants from the note's ablation table (section Key experimental
  * data, ablation), selected by arguments of the _ex entry points:
- *   R12 phi = Sigmoid ("Sigmoid + L1 + re-weighting"): the non-negative map
+ *   R14 phi = Sigmoid ("Sigmoid + L1 + re-weighting"): the non-negative map
  *       of Key design 1 becomes the logistic sigmoid 1/(1 + e^-x); the
  *       scores, mask, both L1 normalisations, N, O and ReLU^p stay as above.
- *   R13 LSSA only ("LSSA only, no re-weighting"; also the main-results row
+ *   R15 LSSA only ("LSSA only, no re-weighting"; also the main-results row
  *       "LSSA, normalisation stage only"): stage 1, then out = A V; p and
  *       eps play no part and no row is degenerate (every A_ij with j <= i
  *       is positive).
@@ -59,6 +59,15 @@
  *       the threshold pass none either.
  *   R17 The norm clamp of R6 is differentiated as written: for |x| > 1e-12
  *       d(x/|x|) = (I - x^ x^T) / |x|; below it, I / 1e-12.
+ *
+ * Row statistics (lssar_ref_rowstats_f64), what a training forward keeps for
+ * its backward:
+ *   R19 Per row, the stage-1 L1 norm before normalisation,
+ *       S_i = sum_{j<=i} Softplus(s_ij), and the largest unmasked scaled
+ *       score m_i = max_{j<=i} s_ij with s_ij = log d log i q^_i . k^_j.
+ *       Given the row's own scores, stage 2's row constants (the threshold
+ *       o_i S_i / i and the row maximum i Softplus(m_i) / S_i - o_i)
+ *       depend on nothing else.
  *
  * Build: gcc -O2 -fopenmp -shared -fPIC lssar_ref.c -lm (no -ffast-math).
  */
@@ -80,7 +89,7 @@ static double softplus(double x)
     return log1p(exp(x));
 }
 
-/* Logistic sigmoid 1/(1 + e^-x) (R12), evaluated without overflow. */
+/* Logistic sigmoid 1/(1 + e^-x) (R14), evaluated without overflow. */
 static double sigmoid(double x)
 {
     if (x >= 0.0)
@@ -89,7 +98,7 @@ static double sigmoid(double x)
     return e / (1.0 + e);
 }
 
-/* The non-negative map of stage 1: Softplus (R4) or Sigmoid (R12). */
+/* The non-negative map of stage 1: Softplus (R4) or Sigmoid (R14). */
 static double phi_fn(int phi, double x)
 {
     return phi == LSSAR_REF_PHI_SIGMOID ? sigmoid(x) : softplus(x);
@@ -121,7 +130,7 @@ static void l2_normalise(const double* x, double* y, int d)
  * kh: all L normalised key rows of the head; v: the head's V; a: scratch of
  * L doubles.  Every j in 1..L is computed and then multiplied by the mask
  * M'_ij, as the matrix form on the page does.  phi picks the stage-1 map
- * (R4/R12); reweight = 0 skips stage 2 (R13). */
+ * (R4/R14); reweight = 0 skips stage 2 (R15). */
 static void lssar_row(const double* qh, const double* kh, const double* v,
                       int L, int d, int p, double eps, int phi, int reweight,
                       int row, double* a, double* out)
@@ -303,6 +312,56 @@ int lssar_ref_fwd_f64(const double* q, const double* k, const double* v,
 {
     return lssar_ref_fwd_ex_f64(q, k, v, out, B, H, L, d, p, eps,
                                 LSSAR_REF_PHI_SOFTPLUS, 1, nthreads);
+}
+
+/* R19 for one row: the stage-1 loop of lssar_row (same scale, same mask
+ * M' applied after Softplus) keeping the L1 norm and the largest unmasked
+ * scaled score instead of normalising. */
+static void lssar_row_stats(const double* qh, const double* kh, int L, int d,
+                            int row, double* st)
+{
+    const int i = row + 1;                       /* R2 */
+    const double scale = log((double)d) * log((double)i);   /* R1 */
+    double l1 = 0.0, smax = -INFINITY;
+    for (int j = 1; j <= L; ++j) {
+        const double* kj = kh + (size_t)(j - 1) * d;
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e)
+            dot += qh[e] * kj[e];
+        const double s = scale * dot;
+        const double mask = (j <= i) ? 1.0 : 0.0;   /* M' (R5) */
+        l1 += softplus(s) * mask;
+        if (mask == 1.0 && s > smax)
+            smax = s;
+    }
+    st[0] = l1;
+    st[1] = smax;
+}
+
+int lssar_ref_rowstats_f64(const double* q, const double* k, double* stats,
+                           int B, int H, int L, int d, int nthreads)
+{
+    if (!q || !k || !stats || B < 1 || H < 1 || L < 1 || d < 1)
+        return -1;
+    const size_t head = (size_t)L * d;
+    const long nheads = (long)B * H;
+    double* qh = malloc(sizeof(double) * head);
+    double* kh = malloc(sizeof(double) * head);
+    if (!qh || !kh) {
+        free(qh);
+        free(kh);
+        return -2;
+    }
+    for (long bh = 0; bh < nheads; ++bh) {
+        normalise_head(q + bh * head, k + bh * head, qh, kh, L, d);
+#pragma omp parallel for num_threads(lssar_ref_threads(nthreads)) schedule(dynamic, 16)
+        for (int row = 0; row < L; ++row)
+            lssar_row_stats(qh + (size_t)row * d, kh, L, d, row,
+                            stats + ((size_t)bh * L + row) * 2);
+    }
+    free(qh);
+    free(kh);
+    return 0;
 }
 
 /* ------------------------------------------------------------------------

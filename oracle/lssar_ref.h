@@ -62,6 +62,15 @@ int lssar_ref_bwd_f64(const double* q, const double* k, const double* v,
                       const double* dout, double* dq, double* dk, double* dv,
                       int B, int H, int L, int d, int p, double eps, int nthreads);
 
+/* Row statistics of stage 1 (the lssar_ref.c reading R19): for every row,
+ * stats[2 r] = S_i = sum_{j<=i} Softplus(s_ij), the L1 norm of Key design
+ * 1's row before it is normalised, and stats[2 r + 1] = m_i = max_{j<=i}
+ * s_ij, the largest unmasked scaled score (s_ij = log d log i q^_i . k^_j).
+ * stats is [B, H, L, 2].  Returns 0, -1 on invalid arguments, -2 if scratch
+ * allocation fails. */
+int lssar_ref_rowstats_f64(const double* q, const double* k, double* stats,
+                           int B, int H, int L, int d, int nthreads);
+
 /* Number of OpenMP threads a call with this nthreads argument would use. */
 int lssar_ref_threads(int nthreads);
 

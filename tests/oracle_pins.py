@@ -533,9 +533,66 @@ def bwd_degenerate_rows(lib):
         assert np.array_equal(dv, dv3)
 
 
+# --------------------------------------------------------------------------
+# Row statistics (lssar_ref_rowstats_f64): S_i = sum_{j<=i} Softplus(s_ij)
+# and m_i = max_{j<=i} s_ij, what a training forward keeps for its backward
+# --------------------------------------------------------------------------
+
+def _stats(lib, q, k):
+    return oracle.lssar_rowstats(q, k, nthreads=2, lib=lib)
+
+
+def rowstats_closed_forms(lib):
+    """Orthonormal keys and queries with chosen cosines: s_ij = ln d ln i c_j
+    (c_j = 0 for keys past the chosen ones), so S_i = sum_j Softplus(s_ij) over
+    j <= i and m_i = ln d ln i max_j c_j, at 40 digits.  Includes rows whose
+    cosines are all negative (m_i < 0, while masked keys would score 0), and
+    row 1 (S_1 = ln 2, m_1 = 0)."""
+    L, d = 11, 16
+    cos_rows = [[0.6], [-0.3, -0.8], [-0.5, -0.5, -0.5], [0.6, 0.5, 0.1, -0.3],
+                [0.0, 0.7, 0.7, 0.0, 0.1], [-0.2] * 6, [0.9, -0.4, 0.1],
+                [0.2, 0.3, 0.4, 0.5, 0.6], [-0.5, 0.8], [0.1] * 10, [-0.95]]
+    for seed in (0, 1):
+        Q, K, _ = _build_rows(L, d, cos_rows, seed=400 + seed)
+        st = _stats(lib, Q, K)
+        assert abs(st[0, 0] - math.log(2.0)) < 1e-15 and st[0, 1] == 0.0
+        for i in range(2, L + 1):
+            cos = (list(cos_rows[i - 1]) + [0.0] * i)[:i]
+            with mp.workdps(40):
+                lam = mp.log(d) * mp.log(i)
+                S = mp.fsum(mp.log(1 + mp.exp(lam * mp.mpf(c))) for c in cos)
+                m = lam * max(mp.mpf(c) for c in cos)
+            assert abs(st[i - 1, 0] - float(S)) < 1e-12 * float(S), f"S_{i}"
+            assert abs(st[i - 1, 1] - float(m)) < 1e-12, f"m_{i}"
+
+
+def rowstats_invariants(lib):
+    """Softplus(m_i) <= S_i <= i Softplus(m_i); row i ignores keys j > i
+    (bitwise) and the order of keys j <= i; rows of Q and K enter through their
+    directions only (powers of two rescale exactly)."""
+    r = _rng(2000)
+    L, d = 40, 8
+    Q, K = r.standard_normal((L, d)), r.standard_normal((L, d))
+    st = _stats(lib, Q, K)
+    sp = np.logaddexp(0.0, st[:, 1])
+    i = np.arange(1, L + 1)
+    assert np.all(sp <= st[:, 0] * (1 + 1e-14)) and np.all(st[:, 0] <= i * sp * (1 + 1e-14))
+    cut = 17
+    K2 = K.copy()
+    K2[cut:] = r.standard_normal((L - cut, d))
+    assert np.array_equal(_stats(lib, Q, K2)[:cut], st[:cut])
+    perm = np.concatenate([r.permutation(cut), np.arange(cut, L)])
+    st3 = _stats(lib, Q, K[perm])
+    assert np.max(np.abs(st3[cut - 1] - st[cut - 1])) < 1e-12 * max(1.0, abs(st[cut - 1, 0]))
+    scale_q = 2.0 ** r.integers(-8, 9, size=(L, 1))
+    scale_k = 2.0 ** r.integers(-8, 9, size=(L, 1))
+    st4 = _stats(lib, Q * scale_q, K * scale_k)
+    assert np.max(np.abs(st4 - st) / np.maximum(1.0, np.abs(st))) < 1e-13
+
+
 PINS = [brute_force_matrix_form, row1_is_v1, closed_form_rows, golden_row2_value,
         sigmoid_antisymmetric_pair, onehot_orthonormal, two_way_tie, degenerate_rows,
         v_identity_probe, v_ones, scale_invariance, linearity_in_v, causality,
         permutation_invariance, hard_argmax_limit, bwd_finite_differences,
         bwd_scale_invariance, bwd_dv_is_weights_transposed, bwd_causality_and_row1,
-        bwd_degenerate_rows]
+        bwd_degenerate_rows, rowstats_closed_forms, rowstats_invariants]

@@ -61,6 +61,12 @@ MUTANTS = [
      "dv[(size_t)j * d + e] += A[j] * gi[e];"),
     ("bwd-dk-wrong-operand", "dkh[(size_t)j * d + e] += dc * qi[e];",
      "dkh[(size_t)j * d + e] += dc * kh[(size_t)j * d + e];"),
+    # the row statistics
+    ("stats-mask-leak", "l1 += softplus(s) * mask;", "l1 += softplus(s);"),
+    ("stats-max-over-masked", "if (mask == 1.0 && s > smax)", "if (s > smax)"),
+    ("stats-max-of-softplus", "            smax = s;", "            smax = softplus(s);"),
+    ("stats-unscaled", "const double s = scale * dot;", "const double s = dot;"),
+    ("stats-normalised", "    st[0] = l1;", "    st[0] = l1 / (double)i;"),
     ("bwd-degenerate-passes", "            continue;                            /* R16: no gradient */",
      "            ;"),
 ]

@@ -23,9 +23,12 @@ entry point, prep included) and "decode" (the decode step over a key/value
 cache: 16 sequences x 12 heads at 8192 cached tokens, the same with ragged
 lengths, and a wide-head case; HBM-bound, reported as GB/s of algorithmic
 bytes and tokens/s; caches drawn N(0,1) on the device, lengths from the
-input generator) and "backward" (lssar_attn_bwd_ws on the bench workload:
-algorithmic TFLOP/s counting 8*d flops per causal pair, the four products
-dO V^T, W^T dO, dC K and dC^T Q; the score recompute is not counted).
+input generator) and "backward" (on the bench workload: the training pair's
+backward, lssar_attn_bwd_stats_ws with the row statistics of
+lssar_attn_fwd_stats_ws, and the recomputing lssar_attn_bwd_ws; algorithmic
+TFLOP/s counting 8*d flops per causal pair, the four products dO V^T,
+W^T dO, dC K and dC^T Q; the score recompute is not counted; the training
+forward's time beside the plain forward's).
 """
 from __future__ import annotations
 
@@ -136,6 +139,12 @@ def time_variants(q, k, v, p, steps, warmup, eps=1e-4):
     }
     res = {}
     for name, fn in calls.items():
+        # untimed load first: the clock drops between phases and needs time
+        # under load to come back (see time_path)
+        t_end = time.perf_counter() + 1.0
+        while time.perf_counter() < t_end:
+            fn()
+            torch.cuda.synchronize()
         for _ in range(warmup):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -192,26 +201,46 @@ def time_decode(name, steps, warmup):
 
 
 def time_backward(q, k, v, p, steps, warmup, eps=1e-4):
-    """Mean ms of one backward call (four kernels), HIP events on the launch
-    stream, with a seeded N(0,1) dout."""
+    """Mean ms of the training forward (lssar_attn_fwd_stats_ws), of the
+    backward from its saved row statistics and of the recomputing backward,
+    each call timed with HIP events on the launch stream after a second of
+    untimed calls; seeded N(0,1) dout."""
     import torch
     import softmax_free_attention_amd as sfa
     g = torch.Generator(device="cuda")
     g.manual_seed(7)
     dout = torch.randn(q.shape, generator=g, device="cuda").to(q.dtype)
-    ws = sfa.bwd_workspace_for(q)
+    ws, fws = sfa.bwd_workspace_for(q), sfa.workspace_for(q)
+    out, st = torch.empty_like(q), sfa.stats_for(q)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        sfa.lssar_attn_bwd_ws(q, k, v, dout, dq, dk, dv, ws, p=p, eps=eps, stream=stream)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
-        sfa.lssar_attn_bwd_ws(q, k, v, dout, dq, dk, dv, ws, p=p, eps=eps, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    calls = {
+        "train_fwd": lambda: sfa.lssar_attn_fwd_stats_ws(q, k, v, out, st, fws, p=p, eps=eps,
+                                                         stream=stream),
+        "saved": lambda: sfa.lssar_attn_bwd_stats_ws(q, k, v, dout, st, dq, dk, dv, ws, p=p,
+                                                     eps=eps, stream=stream),
+        "recompute": lambda: sfa.lssar_attn_bwd_ws(q, k, v, dout, dq, dk, dv, ws, p=p, eps=eps,
+                                                   stream=stream),
+    }
+    res = {}
+    for name, fn in calls.items():
+        # untimed load first: the clock drops between phases and needs time
+        # under load to come back (see time_path)
+        t_end = time.perf_counter() + 1.0
+        while time.perf_counter() < t_end:
+            fn()
+            torch.cuda.synchronize()
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    return res
 
 
 def cpu_baseline(inp, seconds: float):
@@ -339,11 +368,15 @@ def main():
                             for n, ms in vt.items()}
     if not args.no_backward:
         log("bench: backward")
-        bms = time_backward(q, k, v, wl.p, max(3, args.steps // 4), 2)
+        bt = time_backward(q, k, v, wl.p, max(3, args.steps // 4), 2)
         bflops = 2 * flops
+        bms = bt["saved"]
         line["backward"] = {"ms": round(bms, 4), "tflops": round(bflops / (bms * 1e-3) / 1e12, 2),
                             "pct_bf16_peak": round(100 * bflops / (bms * 1e-3) / 1e12 /
-                                                   PEAK_TFLOPS["bf16"], 3)}
+                                                   PEAK_TFLOPS["bf16"], 3),
+                            "row_stats": "saved by the training forward",
+                            "recompute_ms": round(bt["recompute"], 4),
+                            "train_fwd_ms": round(bt["train_fwd"], 4)}
     if not args.no_decode:
         log("bench: decode")
         line["decode"] = {n: time_decode(n, 50, 10)

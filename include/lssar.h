@@ -188,6 +188,37 @@ int lssar_attn_bwd_ws(const void* q, const void* k, const void* v,
                       int H, int L, int d, int p, float eps, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Training forward: lssar_attn_fwd_ws (the Softplus method), which also
+ * stores each row's stage-1 statistics for lssar_attn_bwd_stats_ws
+ * (Key design 1: the L1 norm that normalises the Softplus row, and the
+ * largest scaled score of the row; Key design 2's threshold and row maximum
+ * follow from them):
+ *  - row_stats: DEVICE fp64 [B, H, L, 2], 16-byte aligned, overlapping no
+ *    other buffer.  row_stats[r][0] = S_i = sum_{j<=i} Softplus(s_ij) and
+ *    row_stats[r][1] = m_i = max_{j<=i} s_ij, with s_ij = log d log i
+ *    q^_i . k^_j (natural logarithms).  Rows r are (b, h, i - 1) row-major.
+ *  - Values come from the kernels' arithmetic (fp32 for bf16 inputs, fp64
+ *    for fp32 inputs), rounded to fp64.
+ *  - Everything else, including the output and errors, as for
+ *    lssar_attn_fwd_ws (EINVAL also for a null, misaligned or overlapping
+ *    row_stats).  Allocates nothing. */
+int lssar_attn_fwd_stats_ws(const void* q, const void* k, const void* v,
+                            void* out, double* row_stats, int B, int H, int L,
+                            int d, int p, float eps, int dtype, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* lssar_attn_bwd_ws with the row statistics that lssar_attn_fwd_stats_ws
+ * stored for the same q, k, p and eps: the backward reads S_i and m_i
+ * instead of recomputing them (one pass over the keys fewer per query row).
+ * row_stats: DEVICE fp64 [B, H, L, 2], 16-byte aligned, an input (it may
+ * overlap no output and not the workspace).  Everything else as for
+ * lssar_attn_bwd_ws. */
+int lssar_attn_bwd_stats_ws(const void* q, const void* k, const void* v,
+                            const void* dout, const double* row_stats, void* dq,
+                            void* dk, void* dv, int B, int H, int L, int d, int p,
+                            float eps, int dtype, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* lssar_status_str(int status);
 

@@ -26,6 +26,7 @@ __all__ = [
     "LSSAR_PHI_SIGMOID", "lssar_attn_fwd_phi_ws", "lssar_lssa_fwd_ws",
     "lssar_decode_workspace_bytes", "lssar_decode_ws", "decode_workspace_for",
     "lssar_bwd_workspace_bytes", "lssar_attn_bwd_ws", "bwd_workspace_for",
+    "lssar_attn_fwd_stats_ws", "lssar_attn_bwd_stats_ws", "stats_for",
 ]
 
 LSSAR_F32, LSSAR_BF16 = 0, 1
@@ -78,6 +79,10 @@ def lib():
         L.lssar_bwd_workspace_bytes.restype = sz
         L.lssar_attn_bwd_ws.argtypes = [vp] * 7 + [i, i, i, i, i, f, i, vp, sz, vp]
         L.lssar_attn_bwd_ws.restype = i
+        L.lssar_attn_fwd_stats_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+        L.lssar_attn_fwd_stats_ws.restype = i
+        L.lssar_attn_bwd_stats_ws.argtypes = [vp] * 8 + [i, i, i, i, i, f, i, vp, sz, vp]
+        L.lssar_attn_bwd_stats_ws.restype = i
         L.lssar_status_str.argtypes = [i]
         L.lssar_status_str.restype = ctypes.c_char_p
         L.lssar_last_hip_error.argtypes = []
@@ -302,4 +307,50 @@ def lssar_attn_bwd_ws(q, k, v, dout, dq, dk, dv, workspace, *, p: int,
                                  _ptr(dv), B, H, L, d, int(p), float(eps), dt, wp, wn,
                                  _stream_ptr(stream))
     _raise(st, "lssar_attn_bwd_ws")
+    return dq, dk, dv
+
+
+def _check_stats(stats, q):
+    import torch
+    B, H, L, _ = q.shape
+    if not stats.is_cuda or not stats.is_contiguous() or stats.dtype != torch.float64 \
+            or tuple(stats.shape) != (B, H, L, 2):
+        raise ValueError("row statistics must be a contiguous float64 device tensor [B, H, L, 2]")
+
+
+def stats_for(q):
+    """A float64 device tensor [B, H, L, 2] for the row statistics of q's shape."""
+    import torch
+    B, H, L, _ = q.shape
+    return torch.empty((B, H, L, 2), dtype=torch.float64, device=q.device)
+
+
+def lssar_attn_fwd_stats_ws(q, k, v, out, stats, workspace, *, p: int,
+                            eps: float = DEFAULT_EPS, stream=None):
+    """Training forward: out <- LSSAR(q, k, v) and, per row, stats[..., 0] =
+    sum_j Softplus(s_ij) and stats[..., 1] = max_j s_ij for the backward.
+    Returns (out, stats)."""
+    B, H, L, d, dt = _check_qkv(q, k, v, out)
+    _check_stats(stats, q)
+    wp, wn = _ws_args(workspace)
+    st = lib().lssar_attn_fwd_stats_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(stats), B, H,
+                                       L, d, int(p), float(eps), dt, wp, wn, _stream_ptr(stream))
+    _raise(st, "lssar_attn_fwd_stats_ws")
+    return out, stats
+
+
+def lssar_attn_bwd_stats_ws(q, k, v, dout, stats, dq, dk, dv, workspace, *, p: int,
+                            eps: float = DEFAULT_EPS, stream=None):
+    """lssar_attn_bwd_ws with the row statistics of lssar_attn_fwd_stats_ws
+    (same q, k, p, eps).  Returns (dq, dk, dv)."""
+    B, H, L, d, dt = _check_qkv(q, k, v, dout)
+    _check_qkv(dq, dk, dv)
+    if dq.shape != q.shape or dq.dtype != q.dtype:
+        raise ValueError("gradients must match q in shape and dtype")
+    _check_stats(stats, q)
+    wp, wn = _ws_args(workspace)
+    st = lib().lssar_attn_bwd_stats_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(stats),
+                                       _ptr(dq), _ptr(dk), _ptr(dv), B, H, L, d, int(p),
+                                       float(eps), dt, wp, wn, _stream_ptr(stream))
+    _raise(st, "lssar_attn_bwd_stats_ws")
     return dq, dk, dv

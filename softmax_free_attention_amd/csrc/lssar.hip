@@ -13,6 +13,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 #include <type_traits>
 
 #include "lssar_bwd.hpp"
@@ -160,7 +161,7 @@ int run_prep(const void* k, const void* v, void* ws, int B, int H, int L, int d,
 
 template <int D, int P, int PHI, bool RW>
 void launch_fwd(const void* q, const void* k, const void* v, void* ws, void* out, int BH, int L,
-                int dtype, double lam_scale, float eps, int p, hipStream_t s)
+                int dtype, double lam_scale, float eps, int p, double* stats, hipStream_t s)
 {
     const Layout w = layout(1, BH, L, D, dtype);
     if (dtype == LSSAR_BF16) {
@@ -173,7 +174,7 @@ void launch_fwd(const void* q, const void* k, const void* v, void* ws, void* out
                            dim3((unsigned)(npair * BH)),
                            dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(q),
                            static_cast<const __bf16*>(k), vt, static_cast<__bf16*>(out), fk, BH,
-                           L, w.Lp, nqb, npair, lam_scale, eps, p);
+                           L, w.Lp, nqb, npair, lam_scale, eps, p, stats);
     } else {
         const int nqb = (L + lssar::kBQ32 - 1) / lssar::kBQ32;
         hipLaunchKernelGGL((lssar::lssar_fwd_f32_kernel<D, P, PHI, RW>),
@@ -181,7 +182,7 @@ void launch_fwd(const void* q, const void* k, const void* v, void* ws, void* out
                            dim3(lssar::kThreads), 0, s, static_cast<const float*>(q),
                            static_cast<const float*>(k), static_cast<const float*>(v),
                            static_cast<float*>(out), static_cast<const double*>(ws), BH, L, nqb,
-                           lam_scale, eps, p);
+                           lam_scale, eps, p, stats);
     }
 }
 
@@ -195,10 +196,10 @@ constexpr Variant kLssar = {LSSAR_PHI_SOFTPLUS, true};
 
 template <int D, int PHI>
 void dispatch_p(const void* q, const void* k, const void* v, void* ws, void* out, int BH, int L,
-                int dtype, double lam_scale, float eps, int p, hipStream_t s)
+                int dtype, double lam_scale, float eps, int p, double* stats, hipStream_t s)
 {
 #define LSSAR_LAUNCH(PV) \
-    launch_fwd<D, PV, PHI, true>(q, k, v, ws, out, BH, L, dtype, lam_scale, eps, p, s)
+    launch_fwd<D, PV, PHI, true>(q, k, v, ws, out, BH, L, dtype, lam_scale, eps, p, stats, s)
     if constexpr (PHI == lssar::kPhiSoftplus) {
         switch (p) {
         case 1: LSSAR_LAUNCH(1); break;
@@ -217,39 +218,61 @@ void dispatch_p(const void* q, const void* k, const void* v, void* ws, void* out
 #undef LSSAR_LAUNCH
 }
 
+// stats: null, or (the Softplus method only) where the rows' statistics go.
 template <int D>
 void dispatch_variant(const void* q, const void* k, const void* v, void* ws, void* out, int BH,
                       int L, int dtype, double lam_scale, float eps, int p, Variant var,
-                      hipStream_t s)
+                      double* stats, hipStream_t s)
 {
     if (!var.reweight)
         launch_fwd<D, 1, lssar::kPhiSoftplus, false>(q, k, v, ws, out, BH, L, dtype, lam_scale,
-                                                     eps, p, s);
+                                                     eps, p, nullptr, s);
     else if (var.phi == LSSAR_PHI_SIGMOID)
-        dispatch_p<D, lssar::kPhiSigmoid>(q, k, v, ws, out, BH, L, dtype, lam_scale, eps, p, s);
+        dispatch_p<D, lssar::kPhiSigmoid>(q, k, v, ws, out, BH, L, dtype, lam_scale, eps, p,
+                                          nullptr, s);
     else
-        dispatch_p<D, lssar::kPhiSoftplus>(q, k, v, ws, out, BH, L, dtype, lam_scale, eps, p, s);
+        dispatch_p<D, lssar::kPhiSoftplus>(q, k, v, ws, out, BH, L, dtype, lam_scale, eps, p,
+                                           stats, s);
 }
 
 int run_fwd(const void* q, const void* k, const void* v, void* ws, void* out, int B, int H, int L,
-            int d, int p, float eps, int dtype, hipStream_t s, Variant var = kLssar)
+            int d, int p, float eps, int dtype, hipStream_t s, Variant var = kLssar,
+            double* stats = nullptr)
 {
     // log2(e) * ln(d): the per-row factor is this times ln(i) / |q_i|
     const double lam_scale = std::log((double)d) / std::log(2.0);
     if (d == 64)
-        dispatch_variant<64>(q, k, v, ws, out, B * H, L, dtype, lam_scale, eps, p, var, s);
+        dispatch_variant<64>(q, k, v, ws, out, B * H, L, dtype, lam_scale, eps, p, var, stats, s);
     else
-        dispatch_variant<128>(q, k, v, ws, out, B * H, L, dtype, lam_scale, eps, p, var, s);
+        dispatch_variant<128>(q, k, v, ws, out, B * H, L, dtype, lam_scale, eps, p, var, stats,
+                              s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return hip_fail(e);
     return LSSAR_OK;
 }
 
-// Validation, prep and attention kernel on a caller-owned workspace.
+// Row statistics buffer ([B, H, L, 2] doubles): non-null, 16-byte aligned,
+// overlapping none of the other buffers.
+int validate_stats(const void* stats, int B, int H, int L, std::initializer_list<const void*> ts,
+                   size_t tbytes, const void* ws, size_t ws_bytes)
+{
+    if (!stats || !aligned16(stats))
+        return LSSAR_EINVAL;
+    const size_t sb = (size_t)B * H * L * 2 * sizeof(double);
+    for (const void* t : ts)
+        if (overlaps(stats, sb, t, tbytes))
+            return LSSAR_EINVAL;
+    if (overlaps(stats, sb, ws, ws_bytes))
+        return LSSAR_EINVAL;
+    return LSSAR_OK;
+}
+
+// Validation, prep and attention kernel on a caller-owned workspace; stats
+// (the Softplus method only): null, or where the rows' statistics go.
 int fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H, int L, int d,
            int p, float eps, int dtype, void* workspace, size_t workspace_bytes, void* stream,
-           Variant var)
+           Variant var, double* stats = nullptr)
 {
     int st = validate(q, k, v, out, B, H, L, d, p, eps, dtype);
     if (st != LSSAR_OK)
@@ -262,7 +285,7 @@ int fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H,
     st = run_prep(k, v, workspace, B, H, L, d, dtype, s);
     if (st != LSSAR_OK)
         return st;
-    return run_fwd(q, k, v, workspace, out, B, H, L, d, p, eps, dtype, s, var);
+    return run_fwd(q, k, v, workspace, out, B, H, L, d, p, eps, dtype, s, var, stats);
 }
 
 // ---------------------------------------------------------------------------
@@ -367,10 +390,11 @@ BwdLayout bwd_layout(long long B, long long H, long long L, int d, int dtype)
     return w;
 }
 
+// saved: null (the row statistics are recomputed), or the training forward's.
 template <typename T, int D, int P>
 void launch_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
                 void* dv, void* ws, int BH, int L, int p, float eps, double lam_scale,
-                hipStream_t s)
+                const double* saved, hipStream_t s)
 {
     using C = typename lssar::DecTraits<T>::C;
     constexpr bool BF = std::is_same<T, __bf16>::value;
@@ -396,10 +420,10 @@ void launch_bwd(const void* q, const void* k, const void* v, const void* dout, v
         const dim3 grid((unsigned)(npair * BH));
         hipLaunchKernelGGL((lssar::lssar_bwd_qside_kernel<D, P, 0>), grid, dim3(lssar::kThreads),
                            0, s, Q, K, V, G, KT, rq, fk, st, static_cast<__bf16*>(dq), BH, L,
-                           w.Lp, nqb, npair, lam_scale, eps, p);
+                           w.Lp, nqb, npair, lam_scale, eps, p, saved);
         hipLaunchKernelGGL((lssar::lssar_bwd_qside_kernel<D, P, 1>), grid, dim3(lssar::kThreads),
                            0, s, Q, K, V, G, KT, rq, fk, st, static_cast<__bf16*>(dq), BH, L,
-                           w.Lp, nqb, npair, lam_scale, eps, p);
+                           w.Lp, nqb, npair, lam_scale, eps, p, nullptr);
         hipLaunchKernelGGL((lssar::lssar_bwd_kside_kernel<D, P>), grid, dim3(lssar::kThreads), 0,
                            s, Q, K, V, G, QT, GT, fk, st, static_cast<__bf16*>(dk),
                            static_cast<__bf16*>(dv), BH, L, w.Lp, nqb, npair, p);
@@ -411,7 +435,7 @@ void launch_bwd(const void* q, const void* k, const void* v, const void* dout, v
                            s, Q, K, rq, fk, nrows);
         hipLaunchKernelGGL((lssar::lssar_bwd_rowstats_kernel<T, D, P>), dim3(g4),
                            dim3(lssar::kBwdThreads), 0, s, Q, K, V, G, rq, fk, st, L, nrows,
-                           lam_scale, eps, p);
+                           lam_scale, eps, p, saved);
         hipLaunchKernelGGL((lssar::lssar_bwd_dq_kernel<T, D, P>), dim3(g4),
                            dim3(lssar::kBwdThreads), 0, s, Q, K, V, G, fk, st,
                            static_cast<T*>(dq), L, nrows, p);
@@ -424,10 +448,10 @@ void launch_bwd(const void* q, const void* k, const void* v, const void* dout, v
 template <typename T, int D>
 void bwd_dispatch_p(const void* q, const void* k, const void* v, const void* dout, void* dq,
                     void* dk, void* dv, void* ws, int BH, int L, int p, float eps,
-                    double lam_scale, hipStream_t s)
+                    double lam_scale, const double* saved, hipStream_t s)
 {
 #define LSSAR_BWD(PV) \
-    launch_bwd<T, D, PV>(q, k, v, dout, dq, dk, dv, ws, BH, L, p, eps, lam_scale, s)
+    launch_bwd<T, D, PV>(q, k, v, dout, dq, dk, dv, ws, BH, L, p, eps, lam_scale, saved, s)
     switch (p) {
     case 1: LSSAR_BWD(1); break;
     case 2: LSSAR_BWD(2); break;
@@ -455,6 +479,22 @@ int lssar_attn_fwd_ws(const void* q, const void* k, const void* v, void* out, in
 {
     return fwd_ws(q, k, v, out, B, H, L, d, p, eps, dtype, workspace, workspace_bytes, stream,
                   kLssar);
+}
+
+int lssar_attn_fwd_stats_ws(const void* q, const void* k, const void* v, void* out,
+                            double* row_stats, int B, int H, int L, int d, int p, float eps,
+                            int dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    int st = validate_shape(B, H, L, d, dtype);
+    if (st != LSSAR_OK)
+        return st;
+    const size_t tb = (size_t)B * H * L * d * elem_bytes(dtype);
+    st = validate_stats(row_stats, B, H, L, {q, k, v, out}, tb, workspace,
+                        workspace ? layout(B, H, L, d, dtype).total() : 0);
+    if (st != LSSAR_OK)
+        return st;
+    return fwd_ws(q, k, v, out, B, H, L, d, p, eps, dtype, workspace, workspace_bytes, stream,
+                  kLssar, row_stats);
 }
 
 int lssar_attn_fwd_phi_ws(const void* q, const void* k, const void* v, void* out, int B, int H,
@@ -597,9 +637,15 @@ size_t lssar_bwd_workspace_bytes(int B, int H, int L, int d, int dtype)
     return bwd_layout(B, H, L, d, dtype).total();
 }
 
-int lssar_attn_bwd_ws(const void* q, const void* k, const void* v, const void* dout, void* dq,
-                      void* dk, void* dv, int B, int H, int L, int d, int p, float eps, int dtype,
-                      void* workspace, size_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Validation and launch of the backward; saved: null, or the training
+// forward's row statistics (validated by the caller).
+int bwd_ws(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+           void* dv, int B, int H, int L, int d, int p, float eps, int dtype, void* workspace,
+           size_t workspace_bytes, void* stream, const double* saved)
 {
     if (!dout || !dq || !dk || !dv)
         return LSSAR_EINVAL;
@@ -634,22 +680,54 @@ int lssar_attn_bwd_ws(const void* q, const void* k, const void* v, const void* d
     if (dtype == LSSAR_BF16) {
         if (d == 64)
             bwd_dispatch_p<__bf16, 64>(q, k, v, dout, dq, dk, dv, workspace, BH, L, p, eps,
-                                       lam_scale, s);
+                                       lam_scale, saved, s);
         else
             bwd_dispatch_p<__bf16, 128>(q, k, v, dout, dq, dk, dv, workspace, BH, L, p, eps,
-                                        lam_scale, s);
+                                        lam_scale, saved, s);
     } else {
         if (d == 64)
             bwd_dispatch_p<float, 64>(q, k, v, dout, dq, dk, dv, workspace, BH, L, p, eps,
-                                      lam_scale, s);
+                                      lam_scale, saved, s);
         else
             bwd_dispatch_p<float, 128>(q, k, v, dout, dq, dk, dv, workspace, BH, L, p, eps,
-                                       lam_scale, s);
+                                       lam_scale, saved, s);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return hip_fail(e);
     return LSSAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lssar_attn_bwd_ws(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                      void* dk, void* dv, int B, int H, int L, int d, int p, float eps, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream)
+{
+    return bwd_ws(q, k, v, dout, dq, dk, dv, B, H, L, d, p, eps, dtype, workspace,
+                  workspace_bytes, stream, nullptr);
+}
+
+int lssar_attn_bwd_stats_ws(const void* q, const void* k, const void* v, const void* dout,
+                            const double* row_stats, void* dq, void* dk, void* dv, int B, int H,
+                            int L, int d, int p, float eps, int dtype, void* workspace,
+                            size_t workspace_bytes, void* stream)
+{
+    int st = validate_shape(B, H, L, d, dtype);
+    if (st != LSSAR_OK)
+        return st;
+    if (!dq || !dk || !dv)
+        return LSSAR_EINVAL;
+    // an input: it may share memory with other inputs, not with outputs or the workspace
+    const size_t tb = (size_t)B * H * L * d * elem_bytes(dtype);
+    st = validate_stats(row_stats, B, H, L, {dq, dk, dv}, tb, workspace,
+                        workspace ? bwd_layout(B, H, L, d, dtype).total() : 0);
+    if (st != LSSAR_OK)
+        return st;
+    return bwd_ws(q, k, v, dout, dq, dk, dv, B, H, L, d, p, eps, dtype, workspace,
+                  workspace_bytes, stream, row_stats);
 }
 
 const char* lssar_status_str(int status)
@@ -666,6 +744,6 @@ const char* lssar_status_str(int status)
 
 int lssar_last_hip_error(void) { return g_last_hip_error; }
 
-int lssar_version(void) { return 500; }
+int lssar_version(void) { return 600; }
 
 }  // extern "C"

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kBwdThreads) void lssar_bwd_rowstats_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const typename DecTraits<T>::C* __restrict__ rq,
     const typename DecTraits<T>::C* __restrict__ fk, typename DecTraits<T>::C* __restrict__ stats,
-    int L, long nrows, double lam_scale, float eps, int p_rt)
+    int L, long nrows, double lam_scale, float eps, int p_rt, const double* __restrict__ saved)
 {
     using C = typename DecTraits<T>::C;
     using M = BwdMath<C>;
@@ -171,24 +171,28 @@ __global__ __launch_bounds__(kBwdThreads) void lssar_bwd_rowstats_kernel(
     // log2(e) ln d ln i / |q_i|  (Key design 1: log d . log N)
     const C lam = (C)(lam_scale * log((double)i)) * rq[grow];
 
-    // pass 1: S and the max score
+    // pass 1: S and the max score, or the forward's saved statistics
     C s1 = 0, tmax = -INFINITY;
-    for (int j0 = 0; j0 < i; j0 += RPW) {
-        const int j = j0 + ksl;
-        C kv[EPL];
-        for (int e = 0; e < EPL; ++e)
-            kv[e] = 0;
-        if (j < i)
-            load_piece(Kh + (size_t)j * D, sub, kv);
-        const C dot = group_dot<C, EPL, LPK>(qv, kv);
-        if (j < i && sub == 0) {
-            const C t = dot * lam * fkh[j];
-            s1 += M::sp(t);
-            tmax = dmax(tmax, t);
+    if (saved) {
+        load_row_stats(saved, (size_t)grow, s1, tmax);
+    } else {
+        for (int j0 = 0; j0 < i; j0 += RPW) {
+            const int j = j0 + ksl;
+            C kv[EPL];
+            for (int e = 0; e < EPL; ++e)
+                kv[e] = 0;
+            if (j < i)
+                load_piece(Kh + (size_t)j * D, sub, kv);
+            const C dot = group_dot<C, EPL, LPK>(qv, kv);
+            if (j < i && sub == 0) {
+                const C t = dot * lam * fkh[j];
+                s1 += M::sp(t);
+                tmax = dmax(tmax, t);
+            }
         }
+        s1 = wave_sum(s1);
+        tmax = wave_max(tmax);
     }
-    s1 = wave_sum(s1);
-    tmax = wave_max(tmax);
     const C o = i <= 3 ? (C)0 : (C)1;
     const C tau = o * s1 / (C)i;
     const C gap = M::sp(tmax) - tau;

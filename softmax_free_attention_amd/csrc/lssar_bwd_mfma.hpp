@@ -170,6 +170,8 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_prep_kernel(
 // ---------------------------------------------------------------------------
 
 // MODE 0: rowstats (writes 8 coefficients per query row); MODE 1: dq.
+// saved: null (pass 1 recomputes S and the max score), or the rows' statistics
+// from a training forward.
 // One key-tile buffer in LDS: a double-buffered loop measured slower, since
 // its LDS and registers cost workgroups per CU that hide the loads better.
 template <int D, int P, int MODE>
@@ -177,7 +179,8 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ G, const __bf16* __restrict__ KT, const float* __restrict__ rq,
     const float* __restrict__ fk, float* __restrict__ stats, __bf16* __restrict__ dQ, int BH,
-    int L, int Lp, int nqb, int npair, double lam_scale, float eps, int p_rt)
+    int L, int Lp, int nqb, int npair, double lam_scale, float eps, int p_rt,
+    const double* __restrict__ saved)
 {
     static_assert(D == 64 || D == 128, "head dim");
     using T = BwdTiles<D>;
@@ -312,26 +315,33 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
         };
 
         if constexpr (MODE == 0) {
-            tile_loop(false, [&](int kt, const unsigned char* base, auto diag_tag) {
-                constexpr bool DIAG = decltype(diag_tag)::value;
-                const int nks = DIAG ? min(4, (qwl - kt * 64) / 16 + 1) : 4;
+            if (saved) {
+                // the forward's statistics (natural units) replace pass 1
+                if (qvalid)
+                    load_row_stats(saved, (size_t)bh * L + qi, s1, tmax);
+            } else {
+                tile_loop(false, [&](int kt, const unsigned char* base, auto diag_tag) {
+                    constexpr bool DIAG = decltype(diag_tag)::value;
+                    const int nks = DIAG ? min(4, (qwl - kt * 64) / 16 + 1) : 4;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    if (DIAG && ks >= nks)
-                        continue;
-                    f32x4 f4;
-                    const f32x4 t = scores(kt, base, ks, mm_block(base, KOFF, qf, ks), DIAG, f4);
+                    for (int ks = 0; ks < 4; ++ks) {
+                        if (DIAG && ks >= nks)
+                            continue;
+                        f32x4 f4;
+                        const f32x4 t =
+                            scores(kt, base, ks, mm_block(base, KOFF, qf, ks), DIAG, f4);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        s1 += softplus2_acc(t[r]);
-                        tmax = fmaxf(tmax, t[r]);
+                        for (int r = 0; r < 4; ++r) {
+                            s1 += softplus2_acc(t[r]);
+                            tmax = fmaxf(tmax, t[r]);
+                        }
                     }
-                }
-            });
-            s1 += __shfl_xor(s1, 16);
-            s1 += __shfl_xor(s1, 32);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                });
+                s1 += __shfl_xor(s1, 16);
+                s1 += __shfl_xor(s1, 32);
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            }
             const float o = (qi + 1) <= 3 ? 0.0f : 1.0f;
             const float tau = o * s1 / (float)(qi + 1);
             const float gap = softplus2_acc(tmax) - tau;

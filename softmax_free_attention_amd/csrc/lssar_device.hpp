@@ -441,25 +441,54 @@ __device__ __forceinline__ void load4_to_lds(const void* base, unsigned nbytes, 
         (lds_void*)lds, 4, (int)voffset, (int)soffset, 0, 0);
 }
 
+// Row statistics a training forward keeps for its backward: the stage-1 L1
+// norm S_i = sum_{j<=i} Softplus(s_ij) and the largest unmasked scaled score
+// m_i, in natural units (the kernels work in base 2: t = s log2(e) and
+// Softplus2(t) = Softplus(s) / ln 2).  ST is [rows, 2] doubles.
+__device__ __forceinline__ void save_row_stats(double* ST, size_t row, double s1_base2,
+                                               double tmax_base2)
+{
+    constexpr double kLn2 = 0.69314718055994530942;
+    *reinterpret_cast<double2*>(ST + 2 * row) = make_double2(s1_base2 * kLn2, tmax_base2 * kLn2);
+}
+
+// The backward's read of them, back in base 2.
+template <typename C>
+__device__ __forceinline__ void load_row_stats(const double* ST, size_t row, C& s1_base2,
+                                               C& tmax_base2)
+{
+    constexpr double kLog2e = 1.4426950408889634074;
+    const double2 sv = *reinterpret_cast<const double2*>(ST + 2 * row);
+    s1_base2 = (C)(sv.x * kLog2e);
+    tmax_base2 = (C)(sv.y * kLog2e);
+}
+
 // PHI: stage-1 map; RW: false = stage 1 only (no pass 1, weights phi(t)).
+// ST: null, or where the Softplus method stores each row's statistics.
+// Tiles: double-buffered at d = 64, where registers cap the occupancy at 4
+// waves per SIMD anyway; one buffer at d = 128, with registers capped for 3
+// waves per SIMD, which the 66 KB of two buffers would not allow (measured:
+// 5% faster than two buffers at 2 waves).
 template <int D, int P, int PHI, bool RW>
-__global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ VT, __bf16* __restrict__ O,
     const float* __restrict__ FK, int BH, int L, int Lp, int nqb, int npair,
-    double lam_scale, float eps, int p_rt)
+    double lam_scale, float eps, int p_rt, double* __restrict__ ST)
 {
     static_assert(D == 64 || D == 128, "head dim");
     using T = Bf16Tile<D>;
     constexpr int DC = D / 32;                 // MFMA k-steps over d
     constexpr int DS = D / 16;                 // 16-row blocks of O^T
 
-    // One LDS object: the two tile buffers, then the deep-row flags.  (A
+    // One LDS object: the NB tile buffers, then the deep-row flags.  (A
     // second __shared__ object makes the compiler wait for the in-flight
     // LDS-direct loads before every LDS read in the tile loops.)
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * T::BYTES + 16];
+    constexpr int NB = D == 64 ? 2 : 1;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[NB * T::BYTES + 16];
     auto smem = [&](int buf) { return lds + buf * T::BYTES; };
-    int* const flags = reinterpret_cast<int*>(lds + 2 * T::BYTES);
+    int* const flags = reinterpret_cast<int*>(lds + NB * T::BYTES);
 
     const int tid = threadIdx.x;
     // wave index in a scalar register, so per-wave decisions are uniform branches
@@ -652,38 +681,61 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
             else
                 s1 += pos_sum;
         };
-        auto run_pass1 = [&](auto kind_tag) {
-            __syncthreads();                       // LDS buffers free
-            issue(0, 0, false);
+        // Tiles 0..ntiles-1 of K (and V^T) through LDS; body runs on every
+        // tile that reaches the wave's rows (diagonal tiles masked).
+        auto tile_loop = [&](bool with_v, auto body) {
+            if constexpr (NB == 2) {
+                __syncthreads();                   // earlier readers done with the buffers
+                issue(0, 0, with_v);
+            }
             for (int kt = 0; kt < ntiles; ++kt) {
-                const int buf = kt & 1;
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();                   // tile kt landed; buf^1 free
-                if (kt + 1 < ntiles)
-                    issue(kt + 1, buf ^ 1, false);
+                int buf = 0;
+                if constexpr (NB == 2) {
+                    buf = kt & 1;
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();               // tile kt landed; buf^1 free
+                    if (kt + 1 < ntiles)
+                        issue(kt + 1, buf ^ 1, with_v);
+                } else {
+                    __syncthreads();               // readers of the previous tile done
+                    issue(kt, 0, with_v);
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();               // tile kt landed
+                }
                 if (!(wave_active && kt * kBK <= qwl))
                     continue;
                 if (kt * kBK + kBK - 1 > qw0)
-                    pass1_tile(kt, smem(buf), std::true_type{}, kind_tag);
+                    body(kt, smem(buf), std::true_type{});
                 else
-                    pass1_tile(kt, smem(buf), std::false_type{}, kind_tag);
+                    body(kt, smem(buf), std::false_type{});
             }
+        };
+        auto run_pass1 = [&](auto kind_tag) {
+            tile_loop(false, [&](int kt, const unsigned char* base, auto diag_tag) {
+                pass1_tile(kt, base, diag_tag, kind_tag);
+            });
         };
 
         RowConst rc = {0.0f, 0.0f, false};
         if constexpr (RW) {
-            if constexpr (REDO) {
+            if constexpr (REDO)
                 run_pass1(std::integral_constant<int, kPass1Acc>{});
-                const float trow = row_max(tmax);
-                rc = row_constants_sp(qi + 1, row_sum(s1), softplus2_acc(trow), eps);
-            } else {
+            else
                 run_pass1(std::integral_constant<int, kPass1Sum>{});
-                const float trow = row_max(tmax);
-                rc = row_constants<PHI>(qi + 1, row_sum(s1), trow, eps);
+            const float trow = row_max(tmax);
+            const float s1r = row_sum(s1);
+            if constexpr (REDO) {
+                rc = row_constants_sp(qi + 1, s1r, softplus2_acc(trow), eps);
+            } else {
+                rc = row_constants<PHI>(qi + 1, s1r, trow, eps);
                 if constexpr (PHI == kPhiSoftplus)
                     if (qi < L && trow < kDeep)
                         flags[blk] = 1;
             }
+            // a redone block stores again, after its first store
+            if constexpr (PHI == kPhiSoftplus)
+                if (ST && qi < L && grp == 0)
+                    save_row_stats(ST, (size_t)bh * L + qi, s1r, trow);
         }
 
         // ---------------- pass 2: re-weight, P.V and the weight sum ----------------
@@ -749,21 +801,7 @@ __global__ __launch_bounds__(kThreads) void lssar_fwd_bf16_kernel(
             }
         };
 
-        __syncthreads();                           // earlier readers done with the buffers
-        issue(0, 0, true);
-        for (int kt = 0; kt < ntiles; ++kt) {
-            const int buf = kt & 1;
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (kt + 1 < ntiles)
-                issue(kt + 1, buf ^ 1, true);
-            if (!(wave_active && kt * kBK <= qwl))
-                continue;
-            if (kt * kBK + kBK - 1 > qw0)
-                pass2_tile(kt, smem(buf), std::true_type{});
-            else
-                pass2_tile(kt, smem(buf), std::false_type{});
-        }
+        tile_loop(true, pass2_tile);
         if constexpr (!RW && PHI == kPhiSoftplus && !REDO)
             if (qi < L && dacc[0] < (float)(qi + 1) * kDeepMean)
                 flags[blk] = 1;
@@ -803,7 +841,7 @@ __global__ __launch_bounds__(kThreads, 1) void lssar_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K,
     const float* __restrict__ V, float* __restrict__ O,
     const double* __restrict__ FK, int BH, int L, int nqb, double lam_scale,
-    float eps, int p_rt)
+    float eps, int p_rt, double* __restrict__ ST)
 {
     static_assert(D == 64 || D == 128, "head dim");
     constexpr int DK = D / 4;                  // MFMA k-steps over d
@@ -936,6 +974,9 @@ __global__ __launch_bounds__(kThreads, 1) void lssar_fwd_f32_kernel(
             t = fmax(t, __shfl_xor(t, 16));
             t = fmax(t, __shfl_xor(t, 32));
             rc[qs] = row_constants_f64<PHI>(qi[qs] + 1, s, t, eps);
+            if constexpr (PHI == kPhiSoftplus)
+                if (ST && qi[qs] < L && grp == 0)
+                    save_row_stats(ST, (size_t)bh * L + qi[qs], s, t);
         }
     }
 

@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
     for n in ("lssar_attn_fwd", "lssar_attn_fwd_ws", "lssar_workspace_bytes",
               "lssar_status_str", "lssar_prep", "lssar_attn_fwd_prepped",
               "lssar_attn_fwd_phi_ws", "lssar_lssa_fwd_ws", "lssar_decode_ws",
-              "lssar_decode_workspace_bytes", "lssar_attn_bwd_ws", "lssar_bwd_workspace_bytes"):
+              "lssar_decode_workspace_bytes", "lssar_attn_bwd_ws", "lssar_bwd_workspace_bytes",
+              "lssar_attn_fwd_stats_ws", "lssar_attn_bwd_stats_ws"):
         assert n in names
 
 
@@ -64,7 +65,7 @@ def test_library_has_no_oracle_dependency(L):
 
 
 def test_version_and_status_strings(L):
-    assert sfa.lssar_version() == 500
+    assert sfa.lssar_version() == 600
     assert sfa.lssar_status_str(0) == "ok"
     for st in (-1, -2, -3, -4, 7):
         s = sfa.lssar_status_str(st)
@@ -248,4 +249,46 @@ def test_bwd_validates_before_any_hip_call(L):
     assert call(ws=0) == sfa.LSSAR_EWORKSPACE
     assert call(wsb=1000) == sfa.LSSAR_EWORKSPACE
     assert call(ws=A + 6 * S + 256) == sfa.LSSAR_EWORKSPACE     # overlaps dv
+    assert sfa.lssar_last_hip_error() == 0
+
+
+def test_stats_entries_validate_before_any_hip_call(L):
+    """The training forward and the backward with saved statistics check the
+    statistics buffer (null, misaligned, overlapping) on the host first."""
+    S = STEP
+    st0 = A + 9 * S
+    fbase = dict(q=A, k=A + S, v=A + 2 * S, out=A + 3 * S, st=st0, B=1, H=2, Ln=64, d=64, p=3,
+                 eps=1e-4, dt=1, ws=A + 7 * S, wsb=1 << 24)
+
+    def fwd(**kw):
+        a = dict(fbase, **kw)
+        return L.lssar_attn_fwd_stats_ws(a["q"], a["k"], a["v"], a["out"], a["st"], a["B"],
+                                         a["H"], a["Ln"], a["d"], a["p"], a["eps"], a["dt"],
+                                         a["ws"], a["wsb"], None)
+
+    assert fwd(st=0) == sfa.LSSAR_EINVAL
+    assert fwd(st=st0 + 8) == sfa.LSSAR_EINVAL                  # misaligned
+    assert fwd(st=A + 3 * S + 128) == sfa.LSSAR_EINVAL          # overlaps out
+    assert fwd(st=A + 7 * S + 256) == sfa.LSSAR_EINVAL          # overlaps the workspace
+    assert fwd(d=96) == sfa.LSSAR_EUNSUPPORTED
+    assert fwd(out=0) == sfa.LSSAR_EINVAL
+    assert fwd(wsb=1000) == sfa.LSSAR_EWORKSPACE
+
+    bbase = dict(q=A, k=A + S, v=A + 2 * S, g=A + 3 * S, st=st0, dq=A + 4 * S, dk=A + 5 * S,
+                 dv=A + 6 * S, B=1, H=2, Ln=64, d=64, p=3, eps=1e-4, dt=1, ws=A + 7 * S,
+                 wsb=1 << 24)
+
+    def bwd(**kw):
+        a = dict(bbase, **kw)
+        return L.lssar_attn_bwd_stats_ws(a["q"], a["k"], a["v"], a["g"], a["st"], a["dq"],
+                                         a["dk"], a["dv"], a["B"], a["H"], a["Ln"], a["d"],
+                                         a["p"], a["eps"], a["dt"], a["ws"], a["wsb"], None)
+
+    assert bwd(st=0) == sfa.LSSAR_EINVAL
+    assert bwd(st=st0 + 8) == sfa.LSSAR_EINVAL
+    assert bwd(st=A + 5 * S + 64) == sfa.LSSAR_EINVAL           # overlaps dk
+    assert bwd(st=A + 7 * S) == sfa.LSSAR_EINVAL                # overlaps the workspace
+    assert bwd(g=0) == sfa.LSSAR_EINVAL
+    assert bwd(p=0) == sfa.LSSAR_EINVAL
+    assert bwd(ws=0) == sfa.LSSAR_EWORKSPACE
     assert sfa.lssar_last_hip_error() == 0

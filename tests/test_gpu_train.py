@@ -1,0 +1,217 @@
+"""Training pair on the HIP path: lssar_attn_fwd_stats_ws (forward that keeps
+each row's stage-1 statistics) and lssar_attn_bwd_stats_ws (backward that
+reads them), against the fp64 oracle.
+
+Statistics bar.  S_i = sum_j Softplus(s_ij) and m_i = max_j s_ij.  For fp32
+inputs the kernels work in fp64: relative 1e-9.  For bf16 inputs the scores
+come from an fp32 dot product of the raw inputs, so |ds| <= log d log i
+(d + 3) u with u = 2^-24 (rows of unit norm after the fp32 factors), about
+1.7e-5 ln i at d = 64 and 3.3e-5 ln i at d = 128.  S_i moves by at most
+sum_j sigmoid(s_ij) |ds_ij| <= S_i |ds| (sigmoid(s) <= Softplus(s) for every
+s), plus the fp32 summation, i u S_i, plus i u for the log of the running
+product of the factors (1 + e^-|s|) (each rounded product shifts the log by
+at most u).  m_i moves by |ds| plus the roundings of the two fp32 factors.
+The test allows twice these bounds.
+
+Gradients: the bars of the recomputing backward (relative to each tensor's
+largest reference entry).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import lssar_inputs as gen
+import oracle
+from gpu_util import to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+BWD_TOL = {"f32": 1e-5, "bf16": 2e-2}
+U32 = 2.0 ** -24
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import softmax_free_attention_amd as sfa
+    sfa.lib()
+
+
+def run_train_fwd(q, k, v, p, eps=1e-4):
+    import softmax_free_attention_amd as sfa
+    out, st = torch.empty_like(q), sfa.stats_for(q)
+    sfa.lssar_attn_fwd_stats_ws(q, k, v, out, st, sfa.workspace_for(q), p=p, eps=eps)
+    torch.cuda.synchronize()
+    return out, st
+
+
+def run_stats_bwd(q, k, v, g, st, p, eps=1e-4):
+    import softmax_free_attention_amd as sfa
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    sfa.lssar_attn_bwd_stats_ws(q, k, v, g, st, dq, dk, dv, sfa.bwd_workspace_for(q), p=p,
+                                eps=eps)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def stats_bounds(L, d, dtype, S, m):
+    """Per-row allowed |error| of S and m (module docstring)."""
+    i = np.arange(1, L + 1, dtype=np.float64)
+    if dtype == "f32":
+        return 1e-9 * np.abs(S) + 1e-12, 1e-9 * np.maximum(1.0, np.abs(m))
+    ds = math.log(d) * np.log(np.maximum(i, 2.0)) * (d + 3) * U32
+    tol_s = 2.0 * ((ds + i * U32) * np.abs(S) + i * U32) + 1e-7
+    tol_m = 2.0 * ds + 4 * U32 * np.abs(m) + 1e-7
+    return tol_s, tol_m
+
+
+def check_stats(got, want, d, dtype, what):
+    """got, want: [..., L, 2]; returns the worst error / allowed ratio."""
+    L = want.shape[-2]
+    worst = 0.0
+    for idx in np.ndindex(want.shape[:-2]):
+        S, m = want[idx][:, 0], want[idx][:, 1]
+        tol_s, tol_m = stats_bounds(L, d, dtype, S, m)
+        es = np.abs(got[idx][:, 0] - S)
+        em = np.abs(got[idx][:, 1] - m)
+        assert np.all(es <= tol_s), \
+            f"{what} {idx}: S row {int(np.argmax(es / tol_s)) + 1} err {es.max():.3e}"
+        assert np.all(em <= tol_m), \
+            f"{what} {idx}: m row {int(np.argmax(em / tol_m)) + 1} err {em.max():.3e}"
+        worst = max(worst, float(np.max(es / tol_s)), float(np.max(em / tol_m)))
+    return worst
+
+
+def _inputs(L, d, dtype, p, seed, H=2, B=1, name="gpt2s"):
+    inp = gen.make_inputs(name, B=B, H=H, L=L, d=d, dtype=dtype, p=p, seed=seed)
+    r = np.random.default_rng(seed + 77)
+    g = r.standard_normal(inp.q.shape).astype(np.float32)
+    if dtype == "bf16":
+        g = gen.round_to_bf16(g)
+    return inp.q, inp.k, inp.v, g
+
+
+def _check_grads(got, want, dtype, what):
+    errs = []
+    for name, a, b in zip(("dq", "dk", "dv"), got, want):
+        scale = max(1.0, float(np.max(np.abs(b))))
+        err = float(np.max(np.abs(a - b)))
+        errs.append(err / scale)
+        assert err <= BWD_TOL[dtype] * scale, \
+            f"{what} {name}: max-abs {err:.3e} > {BWD_TOL[dtype]} * {scale:.3g}"
+    return errs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_stats_and_output_small_shapes(dtype, d):
+    """Statistics against the oracle's; the output is bitwise that of
+    lssar_attn_fwd_ws (the statistics only add stores)."""
+    import softmax_free_attention_amd as sfa
+    for L in (1, 2, 3, 4, 5, 17, 64, 65, 130, 257):
+        q, k, v, _ = _inputs(L, d, dtype, 15, seed=L + 11)
+        dev = [to_device(a, dtype) for a in (q, k, v)]
+        out, st = run_train_fwd(*dev, 15)
+        ref = torch.empty_like(dev[0])
+        sfa.lssar_attn_fwd_ws(*dev, ref, sfa.workspace_for(dev[0]), p=15)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int8) if dtype == "bf16" else out,
+                           ref.view(torch.int8) if dtype == "bf16" else ref)
+        worst = check_stats(st.cpu().numpy(), oracle.lssar_rowstats(q, k), d, dtype,
+                            f"{dtype} d={d} L={L}")
+        print(f"stats {dtype} d={d} L={L}: worst err/bound {worst:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("p", [1, 3, 15])
+def test_saved_stats_backward_parity(dtype, d, p):
+    for L in (1, 2, 3, 4, 5, 17, 64, 65, 130, 257):
+        q, k, v, g = _inputs(L, d, dtype, p, seed=L + 5)
+        dev = [to_device(a, dtype) for a in (q, k, v, g)]
+        _, st = run_train_fwd(*dev[:3], p)
+        got = [to_host(t) for t in run_stats_bwd(*dev, st, p)]
+        errs = _check_grads(got, oracle.lssar_bwd(q, k, v, g, p), dtype,
+                            f"{dtype} d={d} p={p} L={L}")
+        print(f"saved-stats bwd {dtype} d={d} p={p} L={L}: rel max-abs {max(errs):.2e}",
+              flush=True)
+
+
+def test_deep_and_degenerate_rows():
+    """Anti-aligned rows (every score far below 0: the forward's redone
+    blocks store the statistics) and zero queries (degenerate rows >= 4)."""
+    from test_gpu_deep_rows import anti_aligned
+    for dtype in ("f32", "bf16"):
+        q, k, v, _ = anti_aligned(200, 64, dtype, seed=7)
+        g = np.random.default_rng(8).standard_normal(q.shape).astype(np.float32)
+        if dtype == "bf16":
+            g = gen.round_to_bf16(g)
+        dev = [to_device(a, dtype) for a in (q, k, v, g)]
+        _, st = run_train_fwd(*dev[:3], 15)
+        worst = check_stats(st.cpu().numpy(), oracle.lssar_rowstats(q, k), 64, dtype,
+                            f"deep {dtype}")
+        got = [to_host(t) for t in run_stats_bwd(*dev, st, 15)]
+        errs = _check_grads(got, oracle.lssar_bwd(q, k, v, g, 15), dtype, f"deep {dtype}")
+        print(f"deep {dtype}: stats err/bound {worst:.3f}, grads rel {max(errs):.2e}",
+              flush=True)
+
+        q2, k2, v2, g2 = _inputs(150, 64, dtype, 15, seed=95)
+        q2 = q2.copy()
+        q2[:, :, [4, 50, 149]] = 0.0
+        dev = [to_device(a, dtype) for a in (q2, k2, v2, g2)]
+        _, st = run_train_fwd(*dev[:3], 15)
+        check_stats(st.cpu().numpy(), oracle.lssar_rowstats(q2, k2), 64, dtype,
+                    f"degenerate {dtype}")
+        got = [to_host(t) for t in run_stats_bwd(*dev, st, 15)]
+        assert np.all(got[0][:, :, [4, 50, 149]] == 0.0)
+        _check_grads(got, oracle.lssar_bwd(q2, k2, v2, g2, 15), dtype, f"degenerate {dtype}")
+
+
+def test_deterministic():
+    q, k, v, g = _inputs(500, 128, "bf16", 15, seed=97, H=3)
+    dev = [to_device(a, "bf16") for a in (q, k, v, g)]
+    o1, s1 = run_train_fwd(*dev[:3], 15)
+    o2, s2 = run_train_fwd(*dev[:3], 15)
+    assert torch.equal(s1, s2) and torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    a = run_stats_bwd(*dev, s1, 15)
+    b = run_stats_bwd(*dev, s1, 15)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("name,heads", [("x8_planted", [(0, 0), (0, 5)]),
+                                        ("wide", [(1, 31)])])
+def test_full_workload_sampled_heads(name, heads):
+    """Full-size workloads: statistics and gradients of a few whole heads
+    against the oracle; all gradients against the recomputing backward."""
+    import softmax_free_attention_amd as sfa
+    inp = gen.make_inputs(name)
+    wl = inp.wl
+    r = np.random.default_rng(99)
+    g = gen.round_to_bf16(r.standard_normal(inp.q.shape).astype(np.float32))
+    dev = [to_device(a, wl.dtype) for a in (inp.q, inp.k, inp.v, g)]
+    _, st = run_train_fwd(*dev[:3], wl.p)
+    got_t = run_stats_bwd(*dev, st, wl.p)
+    rec = [torch.empty_like(dev[0]) for _ in range(3)]
+    sfa.lssar_attn_bwd_ws(*dev, *rec, sfa.bwd_workspace_for(dev[0]), p=wl.p)
+    torch.cuda.synchronize()
+    sth = st.cpu().numpy()
+    got = [to_host(t) for t in got_t]
+    worst_s = worst_g = 0.0
+    for b, h in heads:
+        want_st = oracle.lssar_rowstats(inp.q[b, h], inp.k[b, h])
+        worst_s = max(worst_s, check_stats(sth[b, h][None], want_st[None], wl.d, wl.dtype,
+                                           f"{name} b={b} h={h}"))
+        want = oracle.lssar_bwd(inp.q[b, h], inp.k[b, h], inp.v[b, h], g[b, h], wl.p)
+        errs = _check_grads([x[b, h] for x in got], want, wl.dtype, f"{name} b={b} h={h}")
+        worst_g = max(worst_g, max(errs))
+    for a, b_ in zip(got, (to_host(t) for t in rec)):
+        scale = max(1.0, float(np.max(np.abs(b_))))
+        assert float(np.max(np.abs(a - b_))) <= 2e-2 * scale
+    print(f"{name}: stats err/bound {worst_s:.3f}, grads rel {worst_g:.2e}", flush=True)

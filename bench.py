@@ -217,8 +217,8 @@ def time_backward(q, k, v, p, steps, warmup, eps=1e-4):
     calls = {
         "train_fwd": lambda: sfa.lssar_attn_fwd_stats_ws(q, k, v, out, st, fws, p=p, eps=eps,
                                                          stream=stream),
-        "saved": lambda: sfa.lssar_attn_bwd_stats_ws(q, k, v, dout, st, dq, dk, dv, ws, p=p,
-                                                     eps=eps, stream=stream),
+        "saved": lambda: sfa.lssar_attn_bwd_stats_ws(q, k, v, out, dout, st, dq, dk, dv, ws,
+                                                     p=p, eps=eps, stream=stream),
         "recompute": lambda: sfa.lssar_attn_bwd_ws(q, k, v, dout, dq, dk, dv, ws, p=p, eps=eps,
                                                    stream=stream),
     }

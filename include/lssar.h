@@ -207,17 +207,23 @@ int lssar_attn_fwd_stats_ws(const void* q, const void* k, const void* v,
                             int d, int p, float eps, int dtype, void* workspace,
                             size_t workspace_bytes, void* stream);
 
-/* lssar_attn_bwd_ws with the row statistics that lssar_attn_fwd_stats_ws
- * stored for the same q, k, p and eps: the backward reads S_i and m_i
- * instead of recomputing them (one pass over the keys fewer per query row).
- * row_stats: DEVICE fp64 [B, H, L, 2], 16-byte aligned, an input (it may
- * overlap no output and not the workspace).  Everything else as for
- * lssar_attn_bwd_ws. */
+/* lssar_attn_bwd_ws with what lssar_attn_fwd_stats_ws produced for the same
+ * q, k, v, p and eps: its output out and its row statistics.  The backward
+ * reads S_i and m_i instead of recomputing them (one pass over the keys per
+ * query row fewer).  For bf16 inputs at d = 64 the row coefficients and dq
+ * come from a single pass: dout_i . out_i serves as a first value of the
+ * stage-2 L1 normalisation's row term delta_i = sum_j W_ij dout_i . v_j,
+ * which the pass then corrects to its own weights' value.  The other paths
+ * compute delta_i from the weights alone and do not read out.
+ *  - out: DEVICE [B, H, L, d], the forward's output (same dtype);
+ *    row_stats: DEVICE fp64 [B, H, L, 2]; both 16-byte aligned inputs that
+ *    overlap no output and not the workspace.
+ *  - Everything else as for lssar_attn_bwd_ws. */
 int lssar_attn_bwd_stats_ws(const void* q, const void* k, const void* v,
-                            const void* dout, const double* row_stats, void* dq,
-                            void* dk, void* dv, int B, int H, int L, int d, int p,
-                            float eps, int dtype, void* workspace,
-                            size_t workspace_bytes, void* stream);
+                            const void* out, const void* dout,
+                            const double* row_stats, void* dq, void* dk, void* dv,
+                            int B, int H, int L, int d, int p, float eps, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* lssar_status_str(int status);

@@ -81,7 +81,7 @@ def lib():
         L.lssar_attn_bwd_ws.restype = i
         L.lssar_attn_fwd_stats_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
         L.lssar_attn_fwd_stats_ws.restype = i
-        L.lssar_attn_bwd_stats_ws.argtypes = [vp] * 8 + [i, i, i, i, i, f, i, vp, sz, vp]
+        L.lssar_attn_bwd_stats_ws.argtypes = [vp] * 9 + [i, i, i, i, i, f, i, vp, sz, vp]
         L.lssar_attn_bwd_stats_ws.restype = i
         L.lssar_status_str.argtypes = [i]
         L.lssar_status_str.restype = ctypes.c_char_p
@@ -339,18 +339,19 @@ def lssar_attn_fwd_stats_ws(q, k, v, out, stats, workspace, *, p: int,
     return out, stats
 
 
-def lssar_attn_bwd_stats_ws(q, k, v, dout, stats, dq, dk, dv, workspace, *, p: int,
+def lssar_attn_bwd_stats_ws(q, k, v, out, dout, stats, dq, dk, dv, workspace, *, p: int,
                             eps: float = DEFAULT_EPS, stream=None):
-    """lssar_attn_bwd_ws with the row statistics of lssar_attn_fwd_stats_ws
-    (same q, k, p, eps).  Returns (dq, dk, dv)."""
+    """lssar_attn_bwd_ws with the output and row statistics of
+    lssar_attn_fwd_stats_ws (same q, k, v, p, eps).  Returns (dq, dk, dv)."""
     B, H, L, d, dt = _check_qkv(q, k, v, dout)
+    _check_qkv(q, out, dout)
     _check_qkv(dq, dk, dv)
     if dq.shape != q.shape or dq.dtype != q.dtype:
         raise ValueError("gradients must match q in shape and dtype")
     _check_stats(stats, q)
     wp, wn = _ws_args(workspace)
-    st = lib().lssar_attn_bwd_stats_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(stats),
-                                       _ptr(dq), _ptr(dk), _ptr(dv), B, H, L, d, int(p),
-                                       float(eps), dt, wp, wn, _stream_ptr(stream))
+    st = lib().lssar_attn_bwd_stats_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                                       _ptr(stats), _ptr(dq), _ptr(dk), _ptr(dv), B, H, L, d,
+                                       int(p), float(eps), dt, wp, wn, _stream_ptr(stream))
     _raise(st, "lssar_attn_bwd_stats_ws")
     return dq, dk, dv

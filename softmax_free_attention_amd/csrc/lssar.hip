@@ -390,11 +390,12 @@ BwdLayout bwd_layout(long long B, long long H, long long L, int d, int dtype)
     return w;
 }
 
-// saved: null (the row statistics are recomputed), or the training forward's.
+// saved, out: null (the row statistics are recomputed), or the training
+// forward's row statistics and output.
 template <typename T, int D, int P>
 void launch_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
                 void* dv, void* ws, int BH, int L, int p, float eps, double lam_scale,
-                const double* saved, hipStream_t s)
+                const double* saved, const void* out, hipStream_t s)
 {
     using C = typename lssar::DecTraits<T>::C;
     constexpr bool BF = std::is_same<T, __bf16>::value;
@@ -418,12 +419,27 @@ void launch_bwd(const void* q, const void* k, const void* v, const void* dout, v
                            dim3(lssar::kThreads), 0, s, Q, K, G, rq, fk, QT, KT, GT, L, w.Lp);
         const int nqb = (L + 63) / 64, npair = (nqb + 1) / 2;
         const dim3 grid((unsigned)(npair * BH));
-        hipLaunchKernelGGL((lssar::lssar_bwd_qside_kernel<D, P, 0>), grid, dim3(lssar::kThreads),
-                           0, s, Q, K, V, G, KT, rq, fk, st, static_cast<__bf16*>(dq), BH, L,
-                           w.Lp, nqb, npair, lam_scale, eps, p, saved);
-        hipLaunchKernelGGL((lssar::lssar_bwd_qside_kernel<D, P, 1>), grid, dim3(lssar::kThreads),
-                           0, s, Q, K, V, G, KT, rq, fk, st, static_cast<__bf16*>(dq), BH, L,
-                           w.Lp, nqb, npair, lam_scale, eps, p, nullptr);
+        bool fused = false;
+        if constexpr (D == 64) {
+            if (saved) {
+                // row coefficients and dq in one pass over the keys
+                hipLaunchKernelGGL((lssar::lssar_bwd_qside_kernel<D, P, 2>), grid,
+                                   dim3(lssar::kThreads), 0, s, Q, K, V, G, KT, rq, fk, st,
+                                   static_cast<__bf16*>(dq), BH, L, w.Lp, nqb, npair, lam_scale,
+                                   eps, p, saved, static_cast<const __bf16*>(out));
+                fused = true;
+            }
+        }
+        if (!fused) {
+            hipLaunchKernelGGL((lssar::lssar_bwd_qside_kernel<D, P, 0>), grid,
+                               dim3(lssar::kThreads), 0, s, Q, K, V, G, KT, rq, fk, st,
+                               static_cast<__bf16*>(dq), BH, L, w.Lp, nqb, npair, lam_scale, eps,
+                               p, saved, nullptr);
+            hipLaunchKernelGGL((lssar::lssar_bwd_qside_kernel<D, P, 1>), grid,
+                               dim3(lssar::kThreads), 0, s, Q, K, V, G, KT, rq, fk, st,
+                               static_cast<__bf16*>(dq), BH, L, w.Lp, nqb, npair, lam_scale, eps,
+                               p, nullptr, nullptr);
+        }
         hipLaunchKernelGGL((lssar::lssar_bwd_kside_kernel<D, P>), grid, dim3(lssar::kThreads), 0,
                            s, Q, K, V, G, QT, GT, fk, st, static_cast<__bf16*>(dk),
                            static_cast<__bf16*>(dv), BH, L, w.Lp, nqb, npair, p);
@@ -448,10 +464,10 @@ void launch_bwd(const void* q, const void* k, const void* v, const void* dout, v
 template <typename T, int D>
 void bwd_dispatch_p(const void* q, const void* k, const void* v, const void* dout, void* dq,
                     void* dk, void* dv, void* ws, int BH, int L, int p, float eps,
-                    double lam_scale, const double* saved, hipStream_t s)
+                    double lam_scale, const double* saved, const void* out, hipStream_t s)
 {
 #define LSSAR_BWD(PV) \
-    launch_bwd<T, D, PV>(q, k, v, dout, dq, dk, dv, ws, BH, L, p, eps, lam_scale, saved, s)
+    launch_bwd<T, D, PV>(q, k, v, dout, dq, dk, dv, ws, BH, L, p, eps, lam_scale, saved, out, s)
     switch (p) {
     case 1: LSSAR_BWD(1); break;
     case 2: LSSAR_BWD(2); break;
@@ -641,11 +657,11 @@ size_t lssar_bwd_workspace_bytes(int B, int H, int L, int d, int dtype)
 
 namespace {
 
-// Validation and launch of the backward; saved: null, or the training
-// forward's row statistics (validated by the caller).
+// Validation and launch of the backward; saved, out: null, or the training
+// forward's row statistics and output (validated by the caller).
 int bwd_ws(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
            void* dv, int B, int H, int L, int d, int p, float eps, int dtype, void* workspace,
-           size_t workspace_bytes, void* stream, const double* saved)
+           size_t workspace_bytes, void* stream, const double* saved, const void* out)
 {
     if (!dout || !dq || !dk || !dv)
         return LSSAR_EINVAL;
@@ -680,17 +696,17 @@ int bwd_ws(const void* q, const void* k, const void* v, const void* dout, void* 
     if (dtype == LSSAR_BF16) {
         if (d == 64)
             bwd_dispatch_p<__bf16, 64>(q, k, v, dout, dq, dk, dv, workspace, BH, L, p, eps,
-                                       lam_scale, saved, s);
+                                       lam_scale, saved, out, s);
         else
             bwd_dispatch_p<__bf16, 128>(q, k, v, dout, dq, dk, dv, workspace, BH, L, p, eps,
-                                        lam_scale, saved, s);
+                                        lam_scale, saved, out, s);
     } else {
         if (d == 64)
             bwd_dispatch_p<float, 64>(q, k, v, dout, dq, dk, dv, workspace, BH, L, p, eps,
-                                      lam_scale, saved, s);
+                                      lam_scale, saved, out, s);
         else
             bwd_dispatch_p<float, 128>(q, k, v, dout, dq, dk, dv, workspace, BH, L, p, eps,
-                                       lam_scale, saved, s);
+                                       lam_scale, saved, out, s);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -707,27 +723,32 @@ int lssar_attn_bwd_ws(const void* q, const void* k, const void* v, const void* d
                       void* workspace, size_t workspace_bytes, void* stream)
 {
     return bwd_ws(q, k, v, dout, dq, dk, dv, B, H, L, d, p, eps, dtype, workspace,
-                  workspace_bytes, stream, nullptr);
+                  workspace_bytes, stream, nullptr, nullptr);
 }
 
-int lssar_attn_bwd_stats_ws(const void* q, const void* k, const void* v, const void* dout,
-                            const double* row_stats, void* dq, void* dk, void* dv, int B, int H,
-                            int L, int d, int p, float eps, int dtype, void* workspace,
-                            size_t workspace_bytes, void* stream)
+int lssar_attn_bwd_stats_ws(const void* q, const void* k, const void* v, const void* out,
+                            const void* dout, const double* row_stats, void* dq, void* dk,
+                            void* dv, int B, int H, int L, int d, int p, float eps, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream)
 {
     int st = validate_shape(B, H, L, d, dtype);
     if (st != LSSAR_OK)
         return st;
-    if (!dq || !dk || !dv)
+    if (!dq || !dk || !dv || !out || !aligned16(out))
         return LSSAR_EINVAL;
-    // an input: it may share memory with other inputs, not with outputs or the workspace
+    // inputs: they may share memory with other inputs, not with outputs or the workspace
     const size_t tb = (size_t)B * H * L * d * elem_bytes(dtype);
-    st = validate_stats(row_stats, B, H, L, {dq, dk, dv}, tb, workspace,
-                        workspace ? bwd_layout(B, H, L, d, dtype).total() : 0);
+    const size_t wsb = workspace ? bwd_layout(B, H, L, d, dtype).total() : 0;
+    st = validate_stats(row_stats, B, H, L, {dq, dk, dv}, tb, workspace, wsb);
     if (st != LSSAR_OK)
         return st;
+    for (const void* o : {dq, dk, dv})
+        if (overlaps(out, tb, o, tb))
+            return LSSAR_EINVAL;
+    if (overlaps(out, tb, workspace, wsb))
+        return LSSAR_EINVAL;
     return bwd_ws(q, k, v, dout, dq, dk, dv, B, H, L, d, p, eps, dtype, workspace,
-                  workspace_bytes, stream, row_stats);
+                  workspace_bytes, stream, row_stats, out);
 }
 
 const char* lssar_status_str(int status)

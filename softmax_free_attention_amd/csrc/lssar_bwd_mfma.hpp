@@ -169,25 +169,33 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_prep_kernel(
 // wave and keys 16 ks + 4 grp + r of each 16-key block ks of a tile.
 // ---------------------------------------------------------------------------
 
-// MODE 0: rowstats (writes 8 coefficients per query row); MODE 1: dq.
-// saved: null (pass 1 recomputes S and the max score), or the rows' statistics
-// from a training forward.
+// MODE 0: rowstats (writes 8 coefficients per query row; saved: null, or
+// the training forward's row statistics, which replace pass 1); MODE 1: dq
+// (reads the coefficients); MODE 2 (d = 64): both in one pass, from the
+// training forward's row statistics (saved) and output (O).
 // One key-tile buffer in LDS: a double-buffered loop measured slower, since
 // its LDS and registers cost workgroups per CU that hide the loads better.
+// MODE 2 keeps three d-wide accumulators and four row sums beside the
+// scores; capped for 3 waves per SIMD it spills some bytes and still runs
+// faster than at 2 (measured: x8 10% faster than MODE 0 + MODE 1).  At
+// d = 128 the accumulators alone take 96 VGPRs, and the two-kernel path is
+// faster.
 template <int D, int P, int MODE>
-__global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ G, const __bf16* __restrict__ KT, const float* __restrict__ rq,
     const float* __restrict__ fk, float* __restrict__ stats, __bf16* __restrict__ dQ, int BH,
     int L, int Lp, int nqb, int npair, double lam_scale, float eps, int p_rt,
-    const double* __restrict__ saved)
+    const double* __restrict__ saved, const __bf16* __restrict__ O)
 {
     static_assert(D == 64 || D == 128, "head dim");
+    static_assert(MODE != 2 || D == 64, "the one-pass mode is for d = 64");
     using T = BwdTiles<D>;
     constexpr int DC = D / 32;                 // 32-deep MFMA steps over d
     constexpr int DS = D / 16;                 // 16-wide output blocks over d
     constexpr int KOFF = 0, VOFF = T::RM, TOFF = 2 * T::RM;
-    constexpr int FOFF = MODE == 1 ? 2 * T::RM + T::TR : 2 * T::RM;
+    constexpr int FOFF = MODE >= 1 ? 2 * T::RM + T::TR : 2 * T::RM;
     constexpr int BYTES = FOFF + 256;
     __shared__ __attribute__((aligned(1024))) unsigned char lds[BYTES];
 
@@ -226,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
             for (int n = 0; n < T::RM_LOADS; ++n)
                 load16_to_lds(vbase, rmbytes, base + VOFF + (wave * T::RM_LOADS + n) * 1024,
                               rm_ld[n], kt * 64 * D * 2);
-            if constexpr (MODE == 1) {
+            if constexpr (MODE >= 1) {
 #pragma unroll
                 for (int n = 0; n < T::TR_LOADS; ++n)
                     load16_to_lds(ktbase, trbytes, base + TOFF + (wave * T::TR_LOADS + n) * 1024,
@@ -314,9 +322,84 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
             }
         };
 
+        // stage-2 row constants from S and the max score (degenerate: c = 0)
+        float gap = 0.0f;
+        auto row_consts = [&]() {
+            const float o = (qi + 1) <= 3 ? 0.0f : 1.0f;
+            const float tau = o * s1 / (float)(qi + 1);
+            gap = softplus2_acc(tmax) - tau;
+            degen = !((float)(qi + 1) * gap / s1 > eps) || !qvalid;
+            c = degen ? 0.0f : 1.0f / gap;
+            tc = tau * c;
+        };
+        // the 8 coefficients of the row for the dq and key-side kernels, from
+        // Y = sum y^p, delta = dO . out and Pd = sum sp y^(p-1) (dW - delta)
+        auto row_coefs = [&](float Y, float dl, float Pd) {
+            const float alpha = (float)p_rt * s1 / (gap * Y);
+            const float epsr = alpha / s1 * Pd;
+            // ln d ln i / (S ln 2), S in base 2: lam_scale ln i / S
+            const float kappa = (float)(lam_scale * log((double)(qi + 1))) / s1;
+            // A and E carry 1 / |q_i|: dk^ sums (dc_ij / |q_i|) q_i, and dq
+            // = (dq^ - (dq^ . q^) q^) / |q_i| takes the factor from them
+            const float a_ = degen ? 0.0f : kappa * alpha * rqi;
+            const float e_ = degen ? 0.0f : kappa * epsr * rqi;
+            if (qvalid && grp == 0) {
+                float* st = stats + ((size_t)bh * L + qi) * kBwdRowStats;
+                const float4 a = degen ? make_float4(0.0f, 0.0f, 0.0f, 0.0f)
+                                       : make_float4(c, tc, 1.0f / Y, dl);
+                *reinterpret_cast<float4*>(st) = a;
+                *reinterpret_cast<float4*>(st + 4) = make_float4(a_, e_, lam, rqi);
+            }
+            Ac = a_;
+            Ec = e_;
+        };
+        // K^T tile: B operand of 16x16x16 = 4 keys of dim row 16 ds + row16
+        int trd[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int slot = 2 * ks + (grp >> 1);   // 16-byte slot of keys 16ks+4grp..
+            trd[ks] = ((slot ^ (row16 & 7)) * 16) + (grp & 1) * 8;
+        }
+        auto mm_kt = [&](const unsigned char* base, int ks, bf16x4 g, f32x4 (&acc)[DS]) {
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds) {
+                const bf16x4 bk = *reinterpret_cast<const bf16x4*>(
+                    base + TOFF + (16 * ds + row16) * 128 + trd[ks]);
+                acc[ds] = mfma16k16(g, bk, acc[ds]);
+            }
+        };
+        // acc[ds][r] = dQ^[query 4 grp + r of the wave][dim 16 ds + row16], with
+        // 1 / |q| carried by the coefficients;
+        // dq = (dq^ - (dq^ . q^) q^) / |q|, or dq^ / 1e-12 below the clamp
+        auto store_dq = [&](const f32x4 (&acc)[DS]) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int qr = qw0 + 4 * grp + r;
+                const bool ok = qr < L;
+                const float rr = ok ? rq[(size_t)bh * L + qr] : 0.0f;
+                float qh[DS], dd = 0.0f;
+#pragma unroll
+                for (int ds = 0; ds < DS; ++ds) {
+                    qh[ds] = ok ? (float)Q[hoff + (size_t)qr * D + 16 * ds + row16] * rr : 0.0f;
+                    dd = __builtin_fmaf(acc[ds][r], qh[ds], dd);
+                }
+#pragma unroll
+                for (int m = 1; m < 16; m <<= 1)
+                    dd += __shfl_xor(dd, m);
+                const bool clamped = !(rr < 1e12f);
+                if (ok) {
+#pragma unroll
+                    for (int ds = 0; ds < DS; ++ds) {
+                        const float v = clamped ? acc[ds][r] : acc[ds][r] - dd * qh[ds];
+                        dQ[hoff + (size_t)qr * D + 16 * ds + row16] = (__bf16)v;
+                    }
+                }
+            }
+        };
+
         if constexpr (MODE == 0) {
             if (saved) {
-                // the forward's statistics (natural units) replace pass 1
+                // the training forward's statistics replace pass 1
                 if (qvalid)
                     load_row_stats(saved, (size_t)bh * L + qi, s1, tmax);
             } else {
@@ -342,12 +425,7 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
                 tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
                 tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
             }
-            const float o = (qi + 1) <= 3 ? 0.0f : 1.0f;
-            const float tau = o * s1 / (float)(qi + 1);
-            const float gap = softplus2_acc(tmax) - tau;
-            degen = !((float)(qi + 1) * gap / s1 > eps) || !qvalid;
-            c = degen ? 0.0f : 1.0f / gap;
-            tc = tau * c;
+            row_consts();
 
             // ---------------- pass 2: Y, P1, P2, Z ----------------
             float Y = 0.0f, P1 = 0.0f, P2 = 0.0f, Z = 0.0f;
@@ -382,27 +460,9 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
                 P2 += __shfl_xor(P2, m);
                 Z += __shfl_xor(Z, m);
             }
-            if (qvalid && grp == 0) {
-                float* st = stats + ((size_t)bh * L + qi) * kBwdRowStats;
-                float4 a, b;
-                if (degen) {
-                    a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    b = make_float4(0.0f, 0.0f, lam, rqi);
-                } else {
-                    const float dl = P1 / Y;
-                    const float alpha = (float)p_rt * s1 / (gap * Y);
-                    const float epsr = alpha / s1 * (P2 - dl * Z);
-                    // ln d ln i / (S ln 2), S in base 2: lam_scale ln i / S
-                    const float kappa = (float)(lam_scale * log((double)(qi + 1))) / s1;
-                    // A and E carry 1 / |q_i|: dk^ sums (dc_ij / |q_i|) q_i, and dq
-                    // = (dq^ - (dq^ . q^) q^) / |q_i| takes the factor from them
-                    a = make_float4(c, tc, 1.0f / Y, dl);
-                    b = make_float4(kappa * alpha * rqi, kappa * epsr * rqi, lam, rqi);
-                }
-                *reinterpret_cast<float4*>(st) = a;
-                *reinterpret_cast<float4*>(st + 4) = b;
-            }
-        } else {
+            const float dl = P1 / Y;
+            row_coefs(Y, dl, P2 - dl * Z);
+        } else if constexpr (MODE == 1) {
             // ---------------- dq: dQ^ = sum_j (dc_ij f_j) k_j ----------------
             if (qvalid) {
                 const float* st = stats + ((size_t)bh * L + qi) * kBwdRowStats;
@@ -419,13 +479,6 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds)
                 acc[ds] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            // K^T tile: B operand of 16x16x16 = 4 keys of dim row 16 ds + row16
-            int trd[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int slot = 2 * ks + (grp >> 1);   // 16-byte slot of keys 16ks+4grp..
-                trd[ks] = ((slot ^ (row16 & 7)) * 16) + (grp & 1) * 8;
-            }
             tile_loop(true, [&](int kt, const unsigned char* base, auto diag_tag) {
                 constexpr bool DIAG = decltype(diag_tag)::value;
                 const int nks = DIAG ? min(4, (qwl - kt * 64) / 16 + 1) : 4;
@@ -446,41 +499,96 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_qside_kernel(
                         const float dcv = sg * (Ac * ym * (dw[r] - delta) - Ec);
                         g[r] = dcv * f4[r];
                     }
-                    const bf16x4 gb = __builtin_convertvector(g, bf16x4);
-#pragma unroll
-                    for (int ds = 0; ds < DS; ++ds) {
-                        const bf16x4 bk = *reinterpret_cast<const bf16x4*>(
-                            base + TOFF + (16 * ds + row16) * 128 + trd[ks]);
-                        acc[ds] = mfma16k16(gb, bk, acc[ds]);
-                    }
+                    mm_kt(base, ks, __builtin_convertvector(g, bf16x4), acc);
                 }
             });
-            // acc[ds][r] = dQ^[query 4 grp + r of the wave][dim 16 ds + row16]
-            // dq = (dq^ - (dq^ . q^) q^) / |q|, or dq^ / 1e-12 below the clamp
+            store_dq(acc);
+        } else {
+            // ------- rowstats and dq in one pass, from the training forward's
+            // row statistics.  delta = sum_j W_ij dW_ij must be the one of
+            // this pass's own weights (on peaked rows an error in it is
+            // multiplied by A_i), so the forward's output gives only an
+            // offset d0 = dO . out, and with h = y^(p-1) (dW - d0):
+            //   delta - d0 = sum y h / Y                       (= Dl)
+            //   dq^_i = A_i (sum sigma h k^ - Dl sum sigma y^(p-1) k^)
+            //           - E_i sum sigma k^
+            // A_i and E_i need the row's full sums, so they and Dl scale the
+            // three accumulated vectors at the end -------
+            float d0 = 0.0f;
+            if (qvalid) {
+                load_row_stats(saved, (size_t)bh * L + qi, s1, tmax);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int qr = qw0 + 4 * grp + r;
-                const bool ok = qr < L;
-                const float rr = ok ? rq[(size_t)bh * L + qr] : 0.0f;
-                float qh[DS], dd = 0.0f;
+                for (int dc = 0; dc < DC; ++dc) {
+                    const u32x4 w =
+                        *reinterpret_cast<const u32x4*>(O + hoff + (size_t)qi * D + 32 * dc + 8 * grp);
+                    const u32x4 x = __builtin_bit_cast(u32x4, gf[dc]);
 #pragma unroll
-                for (int ds = 0; ds < DS; ++ds) {
-                    qh[ds] = ok ? (float)Q[hoff + (size_t)qr * D + 16 * ds + row16] * rr : 0.0f;
-                    dd = __builtin_fmaf(acc[ds][r], qh[ds], dd);
-                }
-#pragma unroll
-                for (int m = 1; m < 16; m <<= 1)
-                    dd += __shfl_xor(dd, m);
-                // acc already carries 1 / |q| (through the row's coefficients)
-                const bool clamped = !(rr < 1e12f);
-                if (ok) {
-#pragma unroll
-                    for (int ds = 0; ds < DS; ++ds) {
-                        const float v = clamped ? acc[ds][r] : acc[ds][r] - dd * qh[ds];
-                        dQ[hoff + (size_t)qr * D + 16 * ds + row16] = (__bf16)v;
+                    for (int e = 0; e < 4; ++e) {
+                        d0 = __builtin_fmaf(bf16lo(w[e]), bf16lo(x[e]), d0);
+                        d0 = __builtin_fmaf(bf16hi(w[e]), bf16hi(x[e]), d0);
                     }
                 }
             }
+            d0 += __shfl_xor(d0, 16);
+            d0 += __shfl_xor(d0, 32);
+            row_consts();
+
+            f32x4 acc1[DS], acc2[DS], acc3[DS];
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds)
+                acc1[ds] = acc2[ds] = acc3[ds] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            float Y = 0.0f, P1 = 0.0f, Pd = 0.0f, Z = 0.0f;
+            tile_loop(true, [&](int kt, const unsigned char* base, auto diag_tag) {
+                constexpr bool DIAG = decltype(diag_tag)::value;
+                const int nks = DIAG ? min(4, (qwl - kt * 64) / 16 + 1) : 4;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    if (DIAG && ks >= nks)
+                        continue;
+                    f32x4 f4;
+                    const f32x4 t = scores(kt, base, ks, mm_block(base, KOFF, qf, ks), DIAG, f4);
+                    const f32x4 dw = mm_block(base, VOFF, gf, ks);
+                    f32x4 g1, g2, g3;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float sp, sg;
+                        sp_sig(t[r], sp, sg);
+                        const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(sp, c, -tc), 0.0f, 1.0f);
+                        const float ym = pow_m1<P>(y, p_rt);
+                        Y = __builtin_fmaf(ym, y, Y);
+                        Z = __builtin_fmaf(sp, ym, Z);
+                        const float h = ym * (dw[r] - d0);
+                        P1 = __builtin_fmaf(y, h, P1);
+                        Pd = __builtin_fmaf(sp, h, Pd);
+                        g2[r] = sg * f4[r];
+                        g1[r] = g2[r] * h;
+                        g3[r] = g2[r] * ym;
+                    }
+                    mm_kt(base, ks, __builtin_convertvector(g1, bf16x4), acc1);
+                    mm_kt(base, ks, __builtin_convertvector(g2, bf16x4), acc2);
+                    mm_kt(base, ks, __builtin_convertvector(g3, bf16x4), acc3);
+                }
+            });
+#pragma unroll
+            for (int m = 16; m <= 32; m <<= 1) {
+                Y += __shfl_xor(Y, m);
+                Z += __shfl_xor(Z, m);
+                P1 += __shfl_xor(P1, m);
+                Pd += __shfl_xor(Pd, m);
+            }
+            const float Dl = degen ? 0.0f : P1 / Y;
+            row_coefs(Y, d0 + Dl, Pd - Dl * Z);
+            // the coefficients of query 4 grp + r sit in lane 4 grp + r
+            f32x4 acc[DS];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int src = 4 * grp + r;
+                const float a = __shfl(Ac, src), e = __shfl(Ec, src), ad = a * __shfl(Dl, src);
+#pragma unroll
+                for (int ds = 0; ds < DS; ++ds)
+                    acc[ds][r] = a * acc1[ds][r] - ad * acc3[ds][r] - e * acc2[ds][r];
+            }
+            store_dq(acc);
         }
     }
 }

@@ -274,16 +274,21 @@ def test_stats_entries_validate_before_any_hip_call(L):
     assert fwd(out=0) == sfa.LSSAR_EINVAL
     assert fwd(wsb=1000) == sfa.LSSAR_EWORKSPACE
 
-    bbase = dict(q=A, k=A + S, v=A + 2 * S, g=A + 3 * S, st=st0, dq=A + 4 * S, dk=A + 5 * S,
-                 dv=A + 6 * S, B=1, H=2, Ln=64, d=64, p=3, eps=1e-4, dt=1, ws=A + 7 * S,
-                 wsb=1 << 24)
+    bbase = dict(q=A, k=A + S, v=A + 2 * S, o=A + 8 * S, g=A + 3 * S, st=st0, dq=A + 4 * S,
+                 dk=A + 5 * S, dv=A + 6 * S, B=1, H=2, Ln=64, d=64, p=3, eps=1e-4, dt=1,
+                 ws=A + 7 * S, wsb=1 << 24)
 
     def bwd(**kw):
         a = dict(bbase, **kw)
-        return L.lssar_attn_bwd_stats_ws(a["q"], a["k"], a["v"], a["g"], a["st"], a["dq"],
-                                         a["dk"], a["dv"], a["B"], a["H"], a["Ln"], a["d"],
-                                         a["p"], a["eps"], a["dt"], a["ws"], a["wsb"], None)
+        return L.lssar_attn_bwd_stats_ws(a["q"], a["k"], a["v"], a["o"], a["g"], a["st"],
+                                         a["dq"], a["dk"], a["dv"], a["B"], a["H"], a["Ln"],
+                                         a["d"], a["p"], a["eps"], a["dt"], a["ws"], a["wsb"],
+                                         None)
 
+    assert bwd(o=0) == sfa.LSSAR_EINVAL
+    assert bwd(o=A + 8 * S + 8) == sfa.LSSAR_EINVAL              # misaligned
+    assert bwd(o=A + 4 * S + 64) == sfa.LSSAR_EINVAL             # overlaps dq
+    assert bwd(o=A + 7 * S + 256) == sfa.LSSAR_EINVAL            # overlaps the workspace
     assert bwd(st=0) == sfa.LSSAR_EINVAL
     assert bwd(st=st0 + 8) == sfa.LSSAR_EINVAL
     assert bwd(st=A + 5 * S + 64) == sfa.LSSAR_EINVAL           # overlaps dk

@@ -51,10 +51,10 @@ def run_train_fwd(q, k, v, p, eps=1e-4):
     return out, st
 
 
-def run_stats_bwd(q, k, v, g, st, p, eps=1e-4):
+def run_stats_bwd(q, k, v, out, g, st, p, eps=1e-4):
     import softmax_free_attention_amd as sfa
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    sfa.lssar_attn_bwd_stats_ws(q, k, v, g, st, dq, dk, dv, sfa.bwd_workspace_for(q), p=p,
+    sfa.lssar_attn_bwd_stats_ws(q, k, v, out, g, st, dq, dk, dv, sfa.bwd_workspace_for(q), p=p,
                                 eps=eps)
     torch.cuda.synchronize()
     return dq, dk, dv
@@ -135,8 +135,8 @@ def test_saved_stats_backward_parity(dtype, d, p):
     for L in (1, 2, 3, 4, 5, 17, 64, 65, 130, 257):
         q, k, v, g = _inputs(L, d, dtype, p, seed=L + 5)
         dev = [to_device(a, dtype) for a in (q, k, v, g)]
-        _, st = run_train_fwd(*dev[:3], p)
-        got = [to_host(t) for t in run_stats_bwd(*dev, st, p)]
+        out, st = run_train_fwd(*dev[:3], p)
+        got = [to_host(t) for t in run_stats_bwd(*dev[:3], out, dev[3], st, p)]
         errs = _check_grads(got, oracle.lssar_bwd(q, k, v, g, p), dtype,
                             f"{dtype} d={d} p={p} L={L}")
         print(f"saved-stats bwd {dtype} d={d} p={p} L={L}: rel max-abs {max(errs):.2e}",
@@ -153,10 +153,10 @@ def test_deep_and_degenerate_rows():
         if dtype == "bf16":
             g = gen.round_to_bf16(g)
         dev = [to_device(a, dtype) for a in (q, k, v, g)]
-        _, st = run_train_fwd(*dev[:3], 15)
+        out, st = run_train_fwd(*dev[:3], 15)
         worst = check_stats(st.cpu().numpy(), oracle.lssar_rowstats(q, k), 64, dtype,
                             f"deep {dtype}")
-        got = [to_host(t) for t in run_stats_bwd(*dev, st, 15)]
+        got = [to_host(t) for t in run_stats_bwd(*dev[:3], out, dev[3], st, 15)]
         errs = _check_grads(got, oracle.lssar_bwd(q, k, v, g, 15), dtype, f"deep {dtype}")
         print(f"deep {dtype}: stats err/bound {worst:.3f}, grads rel {max(errs):.2e}",
               flush=True)
@@ -165,10 +165,10 @@ def test_deep_and_degenerate_rows():
         q2 = q2.copy()
         q2[:, :, [4, 50, 149]] = 0.0
         dev = [to_device(a, dtype) for a in (q2, k2, v2, g2)]
-        _, st = run_train_fwd(*dev[:3], 15)
+        out, st = run_train_fwd(*dev[:3], 15)
         check_stats(st.cpu().numpy(), oracle.lssar_rowstats(q2, k2), 64, dtype,
                     f"degenerate {dtype}")
-        got = [to_host(t) for t in run_stats_bwd(*dev, st, 15)]
+        got = [to_host(t) for t in run_stats_bwd(*dev[:3], out, dev[3], st, 15)]
         assert np.all(got[0][:, :, [4, 50, 149]] == 0.0)
         _check_grads(got, oracle.lssar_bwd(q2, k2, v2, g2, 15), dtype, f"degenerate {dtype}")
 
@@ -179,8 +179,8 @@ def test_deterministic():
     o1, s1 = run_train_fwd(*dev[:3], 15)
     o2, s2 = run_train_fwd(*dev[:3], 15)
     assert torch.equal(s1, s2) and torch.equal(o1.view(torch.int16), o2.view(torch.int16))
-    a = run_stats_bwd(*dev, s1, 15)
-    b = run_stats_bwd(*dev, s1, 15)
+    a = run_stats_bwd(*dev[:3], o1, dev[3], s1, 15)
+    b = run_stats_bwd(*dev[:3], o1, dev[3], s1, 15)
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
@@ -196,8 +196,8 @@ def test_full_workload_sampled_heads(name, heads):
     r = np.random.default_rng(99)
     g = gen.round_to_bf16(r.standard_normal(inp.q.shape).astype(np.float32))
     dev = [to_device(a, wl.dtype) for a in (inp.q, inp.k, inp.v, g)]
-    _, st = run_train_fwd(*dev[:3], wl.p)
-    got_t = run_stats_bwd(*dev, st, wl.p)
+    out, st = run_train_fwd(*dev[:3], wl.p)
+    got_t = run_stats_bwd(*dev[:3], out, dev[3], st, wl.p)
     rec = [torch.empty_like(dev[0]) for _ in range(3)]
     sfa.lssar_attn_bwd_ws(*dev, *rec, sfa.bwd_workspace_for(dev[0]), p=wl.p)
     torch.cuda.synchronize()

@@ -14,14 +14,17 @@
 //   dq:       per query block, S^T, dW^T, the pair gradients dc_ij f_j, and
 //             dQ^ = (dc f) K on v_mfma_f32_16x16x16_bf16, whose output
 //             layout (lane = one query, four keys) is exactly its A operand;
+//   one pass (d = 64, from a training forward's row statistics and output):
+//             rowstats' second pass and dq together, the row coefficients
+//             applied to accumulated vectors at the end;
 //   dkdv:     per key block, S = Q K^T and dW = dO V^T (lane = one key, four
 //             queries), then dV = W^T dO and dK^ = (dc / |q|)^T Q on
 //             v_mfma_f32_16x16x16_bf16 with dO^T and Q^T as B operands.
 // A workgroup is 4 waves x 16 rows (queries, or keys in dkdv) of a 64-row
 // block; paired blocks {n-1-pi, pi} give every workgroup the same number of
 // 64-row tiles.  Tiles of the other side stream through LDS by LDS-direct
-// buffer loads, double-buffered, as in the forward kernel.  Softplus is
-// softplus2_acc (exact for every score) and its derivative is sigmoid2.
+// buffer loads into one buffer.  Softplus is exact for every score
+// (softplus2_acc, or sp_sig with its derivative from the same exp2).
 #pragma once
 
 #include "lssar_bwd.hpp"
@@ -305,7 +308,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
         float c = 0.0f, tc = 0.0f;
         bool degen = true;
         // row coefficients (dq reads them; rowstats computes them)
-        float invY = 0.0f, delta = 0.0f, Ac = 0.0f, Ec = 0.0f;
+        float delta = 0.0f, Ac = 0.0f, Ec = 0.0f;
 
         auto tile_loop = [&](bool with_v, auto body) {
             for (int kt = 0; kt < ntiles; ++kt) {
@@ -470,7 +473,6 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 const float4 b = *reinterpret_cast<const float4*>(st + 4);
                 c = a.x;
                 tc = a.y;
-                invY = a.z;
                 delta = a.w;
                 Ac = b.x;
                 Ec = b.y;

@@ -36,14 +36,18 @@
 // Softplus), and stage 2 may be left out ("LSSA only": out = A V, one pass
 // over the keys with weights phi(s_ij) normalised by their sum).
 //
-// Tiling (bf16): a workgroup of 4 waves owns 128 consecutive query rows of
-// one (batch, head); each wave owns 32 rows.  Keys stream through LDS in
-// tiles of 64, double-buffered.  Scores are computed transposed,
-// S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: each lane then holds 4 keys of
-// ONE query row, so row sums stay per lane until one cross-lane reduction
-// per pass, and the lane's weights are already the B operand of
-// O^T = V^T P^T.  V tiles are transposed into LDS when staged.  The weight
-// sum rides the same MFMA as one extra 16-row block of ones under V^T.
+// Tiling (bf16): a workgroup of 4 waves owns a pair of 64-row query blocks
+// of one (batch, head), 16 rows per wave.  Keys stream through LDS in tiles
+// of 64 (double-buffered at d = 64, one buffer at d = 128).  Scores are
+// computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: each lane
+// then holds 4 keys of ONE query row, so row sums stay per lane until one
+// cross-lane reduction per pass, and the lane's weights are already the B
+// operand of O^T = V^T P^T (V^T comes transposed from the prep kernel).  The
+// weight sum is one more MFMA of the same weights against a block of ones.
+//
+// Training forward: when given a statistics buffer, the Softplus method
+// stores each row's S1 and largest score after pass 1 (natural units) for
+// the backward, which then need not recompute them.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -314,9 +314,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: the LSSAR forward is sharded over (batch, head) "
-              f"units with no communication, and this build runs and reports the single-GPU "
-              f"share (got --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the LSSAR forward shards over (batch, head) "
+              f"units with no communication, so one GPU's share at its real shape is what it "
+              f"runs and reports (got --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
 
     import torch

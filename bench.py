@@ -13,8 +13,10 @@ Default workload: 8x length extrapolation, B=1 H=12 L=8192 d=64 bf16 p=15
 with 16 planted keys per head (cosine 0.9 to one query), seed 0.
 
 Prints ONE JSON line.  Extra objects: "roofline" for the attention kernel
-(its mean duration from HIP events recorded on the launch stream inside the
-timed region), "cpu_baseline" (the fp64 oracle on a bounded row sample, on
+(its mean duration from HIP events recorded around each kernel on the
+launch stream, over K more steps right after the K timed ones: events
+between the two kernels of a step add a gap of several microseconds, so the
+timed steps carry none), "cpu_baseline" (the fp64 oracle on a bounded row sample, on
 the host's cores), "sweep" (the same path at L = 1K..16K, H=12, d=64,
 p=15, B = 16384/L, on device-generated N(0,1) inputs) and "variants" (the
 note's two ablation variants on the same resident inputs: the Sigmoid
@@ -89,28 +91,39 @@ def upload(inp):
 
 def time_path(q, k, v, p, steps, warmup, eps=1e-4, settle_s=0.0):
     """Run warmup + timed steps; returns (wall_s, fwd_ms_mean, prep_ms_mean).
-    A step is lssar_prep then lssar_attn_fwd_prepped (what lssar_attn_fwd_ws
-    launches), with HIP events recorded between them on the launch stream.
-    Before the warmup steps the same step runs untimed for settle_s seconds:
-    the GPU clock needs a couple of seconds of load to reach its steady
-    state, and a few milliseconds of warmup alone would time the ramp."""
+    A step is one lssar_attn_fwd_ws call (the prep kernel, then the attention
+    kernel); wall_s covers the timed steps, between torch.cuda.synchronize()
+    calls.  Then the same number of steps run as lssar_prep and
+    lssar_attn_fwd_prepped with HIP events recorded around each kernel on the
+    launch stream, for the kernels' own mean durations (the events between
+    the two launches add a gap, so that loop is not the timed one).  Before
+    the warmup steps the same step runs untimed for settle_s seconds: the GPU
+    clock needs a couple of seconds of load to reach its steady state, and a
+    few milliseconds of warmup alone would time the ramp."""
     import torch
     import softmax_free_attention_amd as sfa
     ws = sfa.workspace_for(q)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
+
+    def step():
+        sfa.lssar_attn_fwd_ws(q, k, v, out, ws, p=p, eps=eps, stream=stream)
+
     t_end = time.perf_counter() + settle_s
     while time.perf_counter() < t_end:
         for _ in range(8):
-            sfa.lssar_prep(k, v, ws, stream=stream)
-            sfa.lssar_attn_fwd_prepped(q, k, v, ws, out, p=p, eps=eps, stream=stream)
+            step()
         torch.cuda.synchronize()
     for _ in range(warmup):
-        sfa.lssar_prep(k, v, ws, stream=stream)
-        sfa.lssar_attn_fwd_prepped(q, k, v, ws, out, p=p, eps=eps, stream=stream)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for s in range(steps):
         ev[s][0].record(stream)
         sfa.lssar_prep(k, v, ws, stream=stream)
@@ -118,7 +131,6 @@ def time_path(q, k, v, p, steps, warmup, eps=1e-4, settle_s=0.0):
         sfa.lssar_attn_fwd_prepped(q, k, v, ws, out, p=p, eps=eps, stream=stream)
         ev[s][2].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     fwd = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     prep = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     return wall, fwd, prep

@@ -1,0 +1,41 @@
+"""Host-side behaviour of bench.py that needs no GPU: the refusal of more
+than one GPU, and the rule that the recorded HBM traffic is reported only
+for the kernel source it was measured on."""
+from __future__ import annotations
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_recorded_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
+    src = tmp_path / "kernel.hpp"
+    src.write_text("// kernel source\n")
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    rec = tmp_path / "traffic.json"
+    rec.write_text(json.dumps({"w": {"kernel_sha256_16": bench.kernel_hash(),
+                                     "bytes_per_launch": 1234}}))
+    monkeypatch.setattr(bench, "TRAFFIC_RECORD", str(rec))
+    assert bench.recorded_traffic("w") == 1234
+    assert bench.recorded_traffic("other") is None
+    src.write_text("// kernel source, changed\n")
+    assert bench.recorded_traffic("w") is None
+
+
+if __name__ == "__main__":
+    sys.exit(pytest.main([__file__, "-q"]))

@@ -46,10 +46,23 @@ __device__ __forceinline__ void sp_sig(float t, float& sp, float& sig)
     sig = e * __builtin_amdgcn_rcpf(ope);
 }
 
-__device__ __forceinline__ f32x4 mfma16k16(bf16x4 a, bf16x4 b, f32x4 c)
+// Four fp32 values as the bf16 operand of the 16x16x16 MFMA (round to
+// nearest even).  Packed two by two into 32-bit words: a bf16x4 bit-cast to
+// the operand type compiles to one conversion per element plus merges.
+__device__ __forceinline__ s16x4 pack_bf16x4(f32x4 x)
 {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 lo = __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2);
+    const bf16x2 hi = __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2);
+    const u32x2 u = {__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+    return __builtin_bit_cast(s16x4, u);
+}
+
+__device__ __forceinline__ f32x4 mfma16k16(s16x4 a, bf16x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
 // LDS layouts of one 64-row tile:
@@ -363,7 +376,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             const int slot = 2 * ks + (grp >> 1);   // 16-byte slot of keys 16ks+4grp..
             trd[ks] = ((slot ^ (row16 & 7)) * 16) + (grp & 1) * 8;
         }
-        auto mm_kt = [&](const unsigned char* base, int ks, bf16x4 g, f32x4 (&acc)[DS]) {
+        auto mm_kt = [&](const unsigned char* base, int ks, s16x4 g, f32x4 (&acc)[DS]) {
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds) {
                 const bf16x4 bk = *reinterpret_cast<const bf16x4*>(
@@ -501,7 +514,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                         const float dcv = sg * (Ac * ym * (dw[r] - delta) - Ec);
                         g[r] = dcv * f4[r];
                     }
-                    mm_kt(base, ks, __builtin_convertvector(g, bf16x4), acc);
+                    mm_kt(base, ks, pack_bf16x4(g), acc);
                 }
             });
             store_dq(acc);
@@ -566,9 +579,9 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                         g1[r] = g2[r] * h;
                         g3[r] = g2[r] * ym;
                     }
-                    mm_kt(base, ks, __builtin_convertvector(g1, bf16x4), acc1);
-                    mm_kt(base, ks, __builtin_convertvector(g2, bf16x4), acc2);
-                    mm_kt(base, ks, __builtin_convertvector(g3, bf16x4), acc3);
+                    mm_kt(base, ks, pack_bf16x4(g1), acc1);
+                    mm_kt(base, ks, pack_bf16x4(g2), acc2);
+                    mm_kt(base, ks, pack_bf16x4(g3), acc3);
                 }
             });
 #pragma unroll
@@ -736,8 +749,8 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
                     w4[r] = ym * y * a.z;
                     g4[r] = sg * __builtin_fmaf(b.x * ym, dw[r] - a.w, -b.y);
                 }
-                const bf16x4 wb = __builtin_convertvector(w4, bf16x4);
-                const bf16x4 gb = __builtin_convertvector(g4, bf16x4);
+                const s16x4 wb = pack_bf16x4(w4);
+                const s16x4 gb = pack_bf16x4(g4);
 #pragma unroll
                 for (int ds = 0; ds < DS; ++ds) {
                     const int off = (16 * ds + row16) * 128 + trd[c];

@@ -167,14 +167,13 @@ void launch_fwd(const void* q, const void* k, const void* v, void* ws, void* out
     if (dtype == LSSAR_BF16) {
         const float* fk = static_cast<const float*>(ws);
         const int nqb = (L + lssar::kBQ16 - 1) / lssar::kBQ16;
-        const int npair = (nqb + 1) / 2;
         const __bf16* vt =
             reinterpret_cast<const __bf16*>(static_cast<unsigned char*>(ws) + w.fk_bytes);
         hipLaunchKernelGGL((lssar::lssar_fwd_bf16_kernel<D, P, PHI, RW>),
-                           dim3((unsigned)(npair * BH)),
+                           dim3((unsigned)(nqb * BH)),
                            dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(q),
                            static_cast<const __bf16*>(k), vt, static_cast<__bf16*>(out), fk, BH,
-                           L, w.Lp, nqb, npair, lam_scale, eps, p, stats);
+                           L, w.Lp, nqb, lam_scale, eps, p, stats);
     } else {
         const int nqb = (L + lssar::kBQ32 - 1) / lssar::kBQ32;
         hipLaunchKernelGGL((lssar::lssar_fwd_f32_kernel<D, P, PHI, RW>),

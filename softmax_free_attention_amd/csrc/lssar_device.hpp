@@ -36,8 +36,8 @@
 // Softplus), and stage 2 may be left out ("LSSA only": out = A V, one pass
 // over the keys with weights phi(s_ij) normalised by their sum).
 //
-// Tiling (bf16): a workgroup of 4 waves owns a pair of 64-row query blocks
-// of one (batch, head), 16 rows per wave.  Keys stream through LDS in tiles
+// Tiling (bf16): a workgroup of 4 waves owns one 64-row query block of one
+// (batch, head), 16 rows per wave; the largest blocks are dispatched first.  Keys stream through LDS in tiles
 // of 64 (double-buffered at d = 64, one buffer at d = 128).  Scores are
 // computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: each lane
 // then holds 4 keys of ONE query row, so row sums stay per lane until one
@@ -389,10 +389,14 @@ __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
 // bf16 attention kernel
 // ---------------------------------------------------------------------------
 //
-// A workgroup of 4 waves owns query blocks of 64 rows of one (batch, head);
-// each wave owns 16 rows (lane & 15).  The causal work of block qb grows
-// with qb, so a workgroup takes the pair {nqb-1-pi, pi}: every workgroup does
-// the same number of key tiles.  Keys stream through LDS in tiles of 64 with
+// A workgroup of 4 waves owns one query block of 64 rows of one (batch,
+// head); each wave owns 16 rows (lane & 15).  The causal work of block qb
+// grows with qb, so workgroups are numbered largest block first across all
+// heads and the hardware fills freed slots with ever smaller blocks (greedy
+// longest-first).  Pairing blocks {nqb-1-pi, pi} per workgroup instead gives
+// every workgroup the same work, but half as many waves: at B = 1, H = 12,
+// L = 8192 that leaves 3 of the 4 wave slots per SIMD filled, and measured
+// 15% slower.  Keys stream through LDS in tiles of 64 with
 // buffer loads that write LDS directly (16 bytes per lane, zero past the end
 // of the tensor), double-buffered.  LDS tiles are arrays of 16-byte slots,
 // XOR-swizzled so that the 16 lanes reading one MFMA operand hit distinct
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ VT, __bf16* __restrict__ O,
-    const float* __restrict__ FK, int BH, int L, int Lp, int nqb, int npair,
+    const float* __restrict__ FK, int BH, int L, int Lp, int nqb,
     double lam_scale, float eps, int p_rt, double* __restrict__ ST)
 {
     static_assert(D == 64 || D == 128, "head dim");
@@ -499,9 +503,9 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int row16 = lane & 15, grp = lane >> 4;
-    const int item = xcd_item((int)blockIdx.x, npair * BH);
-    const int bh = item / npair;
-    const int pi = item % npair;
+    // one query block per workgroup, the largest first across all heads
+    const int qb = nqb - 1 - (int)blockIdx.x / BH;
+    const int bh = (int)blockIdx.x % BH;
     const size_t hoff = (size_t)bh * L * D;
     const __bf16* Qh = Q + hoff;
     __bf16* Oh = O + hoff;
@@ -556,19 +560,15 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
 
     const __bf16 one = (__bf16)1.0f;
     const bf16x8 ones = {one, one, one, one, one, one, one, one};
-    const int nblk = (pi == nqb - 1 - pi) ? 1 : 2;
+    // the block's deep-row flag; the block's first barrier orders this store
+    // before any lane sets it, and it is read after a barrier that follows
+    // the block
+    if (tid == 0)
+        flags[0] = 0;
 
-    // deep-row flags of the workgroup's (up to) two query blocks; the first
-    // barrier of block 0 orders these stores before any flag is set.  The
-    // flags are read once, after a barrier that follows every block.
-    if (tid < 2)
-        flags[tid] = 0;
-
-    // One query block (blk 0: the pair's later block, blk 1: the earlier).
-    // REDO: the block computed again with softplus2_acc (deep rows).
-    auto block_body = [&](int blk, auto redo_tag) {
+    // The query block; REDO: computed again with softplus2_acc (deep rows).
+    auto block_body = [&](auto redo_tag) {
         constexpr bool REDO = decltype(redo_tag)::value;
-        const int qb = blk == 0 ? nqb - 1 - pi : pi;
         const int q0 = qb * kBQ16;
         const int qw0 = q0 + wave * kMQ16;         // first query row of this wave
         const int qwl = min(qw0 + kMQ16 - 1, L - 1);  // last valid query row
@@ -734,7 +734,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
                 rc = row_constants<PHI>(qi + 1, s1r, trow, eps);
                 if constexpr (PHI == kPhiSoftplus)
                     if (qi < L && trow < kDeep)
-                        flags[blk] = 1;
+                        flags[0] = 1;
             }
             // a redone block stores again, after its first store
             if constexpr (PHI == kPhiSoftplus)
@@ -808,7 +808,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
         tile_loop(true, pass2_tile);
         if constexpr (!RW && PHI == kPhiSoftplus && !REDO)
             if (qi < L && dacc[0] < (float)(qi + 1) * kDeepMean)
-                flags[blk] = 1;
+                flags[0] = 1;
 
         // ---------------- finalize: out_i = U_i / D_i (0 if degenerate) ----------------
         if (qi < L) {
@@ -822,13 +822,11 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
         }
     };
 
-    for (int blk = 0; blk < nblk; ++blk)
-        block_body(blk, std::false_type{});
+    block_body(std::false_type{});
     if constexpr (PHI == kPhiSoftplus) {
-        __syncthreads();                           // every block's flag is set
-        for (int blk = 0; blk < nblk; ++blk)
-            if (flags[blk])
-                block_body(blk, std::true_type{});
+        __syncthreads();                           // every lane's flag store is done
+        if (flags[0])
+            block_body(std::true_type{});
     }
 }
 

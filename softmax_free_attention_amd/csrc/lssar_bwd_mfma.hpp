@@ -213,7 +213,9 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
     constexpr int KOFF = 0, VOFF = T::RM, TOFF = 2 * T::RM;
     constexpr int FOFF = MODE >= 1 ? 2 * T::RM + T::TR : 2 * T::RM;
     constexpr int BYTES = FOFF + 256;
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[BYTES];
+    // one LDS object: the tiles, then (MODE 0) the block's deep-row flag
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[BYTES + 16];
+    int* const deep_flag = reinterpret_cast<int*>(lds + BYTES);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -419,27 +421,56 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 if (qvalid)
                     load_row_stats(saved, (size_t)bh * L + qi, s1, tmax);
             } else {
-                tile_loop(false, [&](int kt, const unsigned char* base, auto diag_tag) {
-                    constexpr bool DIAG = decltype(diag_tag)::value;
-                    const int nks = DIAG ? min(4, (qwl - kt * 64) / 16 + 1) : 4;
+                // pass 1 as in the forward: sum max(t, 0) plus log2 of the
+                // product of the factors 1 + 2^-|t| (one exp2 per pair), and
+                // for a block with a deep row the exact Softplus (softplus2_acc)
+                auto pass1 = [&](auto acc_tag) {
+                    constexpr bool ACC = decltype(acc_tag)::value;
+                    s1 = 0.0f;
+                    tmax = -INFINITY;
+                    tile_loop(false, [&](int kt, const unsigned char* base, auto diag_tag) {
+                        constexpr bool DIAG = decltype(diag_tag)::value;
+                        const int nks = DIAG ? min(4, (qwl - kt * 64) / 16 + 1) : 4;
+                        float pos = 0.0f, prod = 1.0f;
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        if (DIAG && ks >= nks)
-                            continue;
-                        f32x4 f4;
-                        const f32x4 t =
-                            scores(kt, base, ks, mm_block(base, KOFF, qf, ks), DIAG, f4);
+                        for (int ks = 0; ks < 4; ++ks) {
+                            if (DIAG && ks >= nks)
+                                continue;
+                            f32x4 f4;
+                            const f32x4 t =
+                                scores(kt, base, ks, mm_block(base, KOFF, qf, ks), DIAG, f4);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            s1 += softplus2_acc(t[r]);
-                            tmax = fmaxf(tmax, t[r]);
+                            for (int r = 0; r < 4; ++r) {
+                                if constexpr (ACC) {
+                                    pos += softplus2_acc(t[r]);
+                                } else {
+                                    pos += fmaxf(t[r], 0.0f);
+                                    prod = __builtin_fmaf(prod, __builtin_amdgcn_exp2f(-fabsf(t[r])),
+                                                          prod);
+                                }
+                                tmax = fmaxf(tmax, t[r]);
+                            }
                         }
-                    }
-                });
-                s1 += __shfl_xor(s1, 16);
-                s1 += __shfl_xor(s1, 32);
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                        if constexpr (ACC)
+                            s1 += pos;
+                        else
+                            s1 += pos + __builtin_amdgcn_logf(prod);
+                    });
+                    s1 += __shfl_xor(s1, 16);
+                    s1 += __shfl_xor(s1, 32);
+                    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+                    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                };
+                // the block's flag: cleared before the first tile barrier,
+                // set by lanes of deep rows, read after one more barrier
+                if (tid == 0)
+                    *deep_flag = 0;
+                pass1(std::false_type{});
+                if (qvalid && tmax < kDeep)
+                    *deep_flag = 1;
+                __syncthreads();
+                if (*deep_flag)
+                    pass1(std::true_type{});
             }
             row_consts();
 

@@ -48,10 +48,13 @@ METRIC = "LSSAR causal attn fwd TFLOP/s (% bf16 MFMA peak) at L=1K..16K, 1 GPU"
 # MI355X published dense peaks (256 CUs, 2.4 GHz)
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
-# HBM traffic of the attention kernel measured with rocprofv3 --pmc
-# (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration factor),
-# valid only for the kernel source whose hash is recorded with it.
+# HBM traffic and VALU activity of the attention kernel measured with
+# rocprofv3 --pmc (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
+# calibration factor; SQ_ACTIVE_INST_VALU), valid only for the kernel source
+# whose hash is recorded with them.
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_record.json")
+N_SIMDS = 256 * 4            # compute units x SIMDs per unit
+CLOCK_HZ = 2.4e9             # peak engine clock
 KERNEL_SRC = os.path.join(ROOT, "softmax_free_attention_amd", "csrc", "lssar_device.hpp")
 
 
@@ -64,7 +67,9 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
+def recorded_counters(workload: str):
+    """The counter record of the attention kernel on this workload, or None
+    when there is none or it was taken on other kernel source."""
     try:
         with open(TRAFFIC_RECORD) as f:
             rec = json.load(f)
@@ -73,7 +78,27 @@ def recorded_traffic(workload: str):
     ent = rec.get(workload)
     if not ent or ent.get("kernel_sha256_16") != kernel_hash():
         return None
-    return ent.get("bytes_per_launch")
+    return ent
+
+
+def recorded_traffic(workload: str):
+    ent = recorded_counters(workload)
+    return ent.get("bytes_per_launch") if ent else None
+
+
+def valu_roofline(workload: str, kernel_ms: float):
+    """VALU issue against its capacity: the recorded VALU-active SIMD cycles
+    per launch over 1024 SIMDs x 2.4 GHz x the launch duration measured
+    now.  The kernel's elementwise chain, not its contractions, sets its
+    time, so this is the fraction that says how close it runs to its
+    bound.  None without a record for the current kernel source."""
+    ent = recorded_counters(workload)
+    if not ent or "valu_active_simd_cycles" not in ent:
+        return None
+    cap = N_SIMDS * CLOCK_HZ * kernel_ms * 1e-3
+    return {"active_simd_cycles": ent["valu_active_simd_cycles"],
+            "capacity_simd_cycles": round(cap), "frac": round(ent["valu_active_simd_cycles"] / cap, 4),
+            "valu_insts": ent.get("valu_insts"), "mfma_insts": ent.get("mfma_insts")}
 
 
 def upload(inp):
@@ -364,7 +389,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "lssar_fwd_bf16_kernel" if wl.dtype == "bf16"
                      else "lssar_fwd_f32_kernel",
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 5), "traffic": traffic},
+                     "frac": round(achieved / peak, 5), "traffic": traffic,
+                     "valu": valu_roofline(wl.name, fwd_ms)},
     }
     if args.calib_mib > 0:
         n = args.calib_mib * (1 << 20) // 4

@@ -1,6 +1,6 @@
 """Host-side behaviour of bench.py that needs no GPU: the refusal of more
-than one GPU, and the rule that the recorded HBM traffic is reported only
-for the kernel source it was measured on."""
+than one GPU, and the rule that the recorded HBM traffic and VALU activity
+are reported only for the kernel source they were measured on."""
 from __future__ import annotations
 
 import json
@@ -35,6 +35,21 @@ def test_recorded_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
     assert bench.recorded_traffic("other") is None
     src.write_text("// kernel source, changed\n")
     assert bench.recorded_traffic("w") is None
+
+
+def test_valu_fraction_from_the_record(tmp_path, monkeypatch):
+    src = tmp_path / "kernel.hpp"
+    src.write_text("// kernel source\n")
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    rec = tmp_path / "traffic.json"
+    cycles = bench.N_SIMDS * bench.CLOCK_HZ * 1e-3 * 0.5      # half of a 1 ms launch
+    rec.write_text(json.dumps({"w": {"kernel_sha256_16": bench.kernel_hash(),
+                                     "valu_active_simd_cycles": cycles}}))
+    monkeypatch.setattr(bench, "TRAFFIC_RECORD", str(rec))
+    assert bench.valu_roofline("w", 1.0)["frac"] == pytest.approx(0.5)
+    assert bench.valu_roofline("w", 2.0)["frac"] == pytest.approx(0.25)
+    src.write_text("// kernel source, changed\n")
+    assert bench.valu_roofline("w", 1.0) is None
 
 
 if __name__ == "__main__":

@@ -10,7 +10,9 @@
 //   rowstats: per query block, the scores S^T = K Q^T and dW^T = V dO^T on
 //             v_mfma_f32_16x16x32_bf16, pass 1 the row's S and max score,
 //             pass 2 the sums Y, P1, P2, Z; writes the row coefficients
-//             (c, tau c, 1/Y, delta, A/|q|, E/|q|, the score factor, 1/|q|);
+//             (c, tau c, 1/Y, -delta A/|q|, A/|q|, E/|q|, the score factor,
+//             1/|q|; the pair gradient sigma (y^(p-1) (A dW - A delta) - E)
+//             then costs two fma and a multiply);
 //   dq:       per query block, S^T, dW^T, the pair gradients dc_ij f_j, and
 //             dQ^ = (dc f) K on v_mfma_f32_16x16x16_bf16, whose output
 //             layout (lane = one query, four keys) is exactly its A operand;
@@ -323,7 +325,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
         float c = 0.0f, tc = 0.0f;
         bool degen = true;
         // row coefficients (dq reads them; rowstats computes them)
-        float delta = 0.0f, Ac = 0.0f, Ec = 0.0f;
+        float adl = 0.0f, Ac = 0.0f, Ec = 0.0f;    // adl = -A delta
 
         auto tile_loop = [&](bool with_v, auto body) {
             for (int kt = 0; kt < ntiles; ++kt) {
@@ -364,7 +366,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             if (qvalid && grp == 0) {
                 float* st = stats + ((size_t)bh * L + qi) * kBwdRowStats;
                 const float4 a = degen ? make_float4(0.0f, 0.0f, 0.0f, 0.0f)
-                                       : make_float4(c, tc, 1.0f / Y, dl);
+                                       : make_float4(c, tc, 1.0f / Y, -dl * a_);
                 *reinterpret_cast<float4*>(st) = a;
                 *reinterpret_cast<float4*>(st + 4) = make_float4(a_, e_, lam, rqi);
             }
@@ -517,7 +519,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 const float4 b = *reinterpret_cast<const float4*>(st + 4);
                 c = a.x;
                 tc = a.y;
-                delta = a.w;
+                adl = a.w;
                 Ac = b.x;
                 Ec = b.y;
             }
@@ -542,7 +544,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                         sp_sig(t[r], sp, sg);
                         const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(sp, c, -tc), 0.0f, 1.0f);
                         const float ym = pow_m1<P>(y, p_rt);
-                        const float dcv = sg * (Ac * ym * (dw[r] - delta) - Ec);
+                        const float dcv = sg * __builtin_fmaf(ym, __builtin_fmaf(Ac, dw[r], adl), -Ec);
                         g[r] = dcv * f4[r];
                     }
                     mm_kt(base, ks, pack_bf16x4(g), acc);
@@ -778,7 +780,7 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
                     const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(sp, a.x, -a.y), 0.0f, 1.0f);
                     const float ym = pow_m1<P>(y, p_rt);
                     w4[r] = ym * y * a.z;
-                    g4[r] = sg * __builtin_fmaf(b.x * ym, dw[r] - a.w, -b.y);
+                    g4[r] = sg * __builtin_fmaf(ym, __builtin_fmaf(b.x, dw[r], a.w), -b.y);
                 }
                 const s16x4 wb = pack_bf16x4(w4);
                 const s16x4 gb = pack_bf16x4(g4);

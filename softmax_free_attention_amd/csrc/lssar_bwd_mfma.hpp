@@ -6,7 +6,10 @@
 // Boosts Length Extrapolation in Large Language Models", Method details);
 // these kernels evaluate them on the matrix cores:
 //   prep:     key factors f_j = 1/|k_j|, query factors 1/|q_i|, and the
-//             transposed copies Q^T, K^T, dO^T ([head][d][Lp], zero past L);
+//             transposed copies Q^T, K^T, dO^T ([head][d][Lp], zero past L;
+//             in dims 8..15 of every 16 the two 8-byte halves of each
+//             16-byte group swap places, so that the 16 lanes of an MFMA
+//             operand read, dims e and e + 8, use disjoint LDS banks);
 //   rowstats: per query block, the scores S^T = K Q^T and dW^T = V dO^T on
 //             v_mfma_f32_16x16x32_bf16, pass 1 the row's S and max score,
 //             pass 2 the sums Y, P1, P2, Z; writes the row coefficients
@@ -175,6 +178,10 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_prep_kernel(
             for (int h = 0; h < 4; ++h) {
                 lo[h] = __builtin_amdgcn_perm(wv[2 * h + 1], wv[2 * h], 0x05040100u);
                 hi[h] = __builtin_amdgcn_perm(wv[2 * h + 1], wv[2 * h], 0x07060302u);
+            }
+            if (m & 4) {                       // dims 8..15 of every 16: halves swapped
+                lo = u32x4{lo[2], lo[3], lo[0], lo[1]};
+                hi = u32x4{hi[2], hi[3], hi[0], hi[1]};
             }
             *reinterpret_cast<u32x4*>(Th + (size_t)(2 * m) * Lp + kb * 64 + 8 * p8) = lo;
             *reinterpret_cast<u32x4*>(Th + (size_t)(2 * m + 1) * Lp + kb * 64 + 8 * p8) = hi;
@@ -378,7 +385,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int slot = 2 * ks + (grp >> 1);   // 16-byte slot of keys 16ks+4grp..
-            trd[ks] = ((slot ^ (row16 & 7)) * 16) + (grp & 1) * 8;
+            trd[ks] = ((slot ^ (row16 & 7)) * 16) + (((grp & 1) ^ (row16 >> 3)) * 8);
         }
         auto mm_kt = [&](const unsigned char* base, int ks, s16x4 g, f32x4 (&acc)[DS]) {
 #pragma unroll
@@ -685,6 +692,15 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
 #pragma unroll
     for (int n = 0; n < T::TR_LOADS; ++n)
         tr_ld[n] = (int)tr_src((wave * T::TR_LOADS + n) * 64 + lane, Lp);
+    // the tile's coefficient rows in LDS in the order (r, c, g) of query
+    // 16 c + 4 g + r: the four lane groups, which read rows 4 apart at
+    // once, then read 128 consecutive bytes instead of one bank four times
+    int st_src;
+    {
+        const int u = wave * 64 + lane;        // 16-byte unit of the LDS copy
+        const int pos = u >> 1, r = pos >> 4, c = (pos >> 2) & 3, g = pos & 3;
+        st_src = (16 * c + 4 * g + r) * kBwdRowStats * 4 + (u & 1) * 16;
+    }
 
     // query tile qt: Q, dO (row-major), Q^T, dO^T and the 64 rows' coefficients
     auto issue = [&](int qt) {
@@ -704,7 +720,7 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
                           tr_ld[n], qt * 64 * 2);
         }
         if (wave < 2)
-            load16_to_lds(sbase, sbytes, base + SOFF + wave * 1024, (wave * 64 + lane) * 16,
+            load16_to_lds(sbase, sbytes, base + SOFF + wave * 1024, st_src,
                           qt * 64 * kBwdRowStats * 4);
     };
 
@@ -715,7 +731,7 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
     int trd[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-        trd[c] = (((2 * c + (grp >> 1)) ^ (row16 & 7)) * 16) + (grp & 1) * 8;
+        trd[c] = (((2 * c + (grp >> 1)) ^ (row16 & 7)) * 16) + (((grp & 1) ^ (row16 >> 3)) * 8);
 
     const int nblk = (pi == nkb - 1 - pi) ? 1 : 2;
     for (int blk = 0; blk < nblk; ++blk) {
@@ -769,7 +785,7 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
                 for (int r = 0; r < 4; ++r) {
                     const int qrow = 16 * c + 4 * grp + r;       // query in the tile
                     const float* st = reinterpret_cast<const float*>(base + SOFF) +
-                                      qrow * kBwdRowStats;
+                                      (16 * r + 4 * c + grp) * kBwdRowStats;
                     const float4 a = *reinterpret_cast<const float4*>(st);
                     const float4 b = *reinterpret_cast<const float4*>(st + 4);
                     float t = sc[r] * b.z * fj;                  // lam_i f_j (q . k)

@@ -51,6 +51,18 @@ __device__ __forceinline__ void sp_sig(float t, float& sp, float& sig)
     sig = e * __builtin_amdgcn_rcpf(ope);
 }
 
+// The same with Softplus2 as plain log2(1 + 2^t), the forward's evaluation
+// for rows whose largest score is at least kDeep: there it differs from the
+// exact value only where 2^t < 1/256, by at most 2^-24 log2(e) absolute,
+// and such scores lie far below the row's largest.
+__device__ __forceinline__ void sp_sig_plain(float t, float& sp, float& sig)
+{
+    const float e = __builtin_amdgcn_exp2f(t);
+    const float ope = 1.0f + e;
+    sp = __builtin_amdgcn_logf(ope);
+    sig = e * __builtin_amdgcn_rcpf(ope);
+}
+
 // Four fp32 values as the bf16 operand of the 16x16x16 MFMA (round to
 // nearest even).  Packed two by two into 32-bit words: a bf16x4 bit-cast to
 // the operand type compiles to one conversion per element plus merges.
@@ -222,7 +234,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
     constexpr int KOFF = 0, VOFF = T::RM, TOFF = 2 * T::RM;
     constexpr int FOFF = MODE >= 1 ? 2 * T::RM + T::TR : 2 * T::RM;
     constexpr int BYTES = FOFF + 256;
-    // one LDS object: the tiles, then (MODE 0) the block's deep-row flag
+    // one LDS object: the tiles, then (MODE 0, 2) the block's deep-row flag
     __shared__ __attribute__((aligned(1024))) unsigned char lds[BYTES + 16];
     int* const deep_flag = reinterpret_cast<int*>(lds + BYTES);
 
@@ -568,10 +580,28 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             //   dq^_i = A_i (sum sigma h k^ - Dl sum sigma y^(p-1) k^)
             //           - E_i sum sigma k^
             // A_i and E_i need the row's full sums, so they and Dl scale the
-            // three accumulated vectors at the end -------
+            // three accumulated vectors at the end.  At p = 15 a block
+            // without a deep row (largest score below kDeep) takes plain
+            // log2(1 + 2^t), as the forward does, and a block with one the
+            // exact Softplus (a uniform branch); at other p the plain path
+            // would cost spills (p = 3: 95 spilled VGPRs against 36) and
+            // every block takes the exact one -------
+            constexpr bool kPlain = P == 15;
+            if (qvalid)
+                load_row_stats(saved, (size_t)bh * L + qi, s1, tmax);
+            bool blk_deep = true;
+            if constexpr (kPlain) {
+                __syncthreads();                   // earlier readers of the flag done
+                if (tid == 0)
+                    deep_flag[0] = 0;
+                __syncthreads();
+                if (qvalid && tmax < kDeep)
+                    deep_flag[0] = 1;
+                __syncthreads();
+                blk_deep = deep_flag[0] != 0;
+            }
             float d0 = 0.0f;
             if (qvalid) {
-                load_row_stats(saved, (size_t)bh * L + qi, s1, tmax);
 #pragma unroll
                 for (int dc = 0; dc < DC; ++dc) {
                     const u32x4 w =
@@ -593,7 +623,8 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             for (int ds = 0; ds < DS; ++ds)
                 acc1[ds] = acc2[ds] = acc3[ds] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             float Y = 0.0f, P1 = 0.0f, Pd = 0.0f, Z = 0.0f;
-            tile_loop(true, [&](int kt, const unsigned char* base, auto diag_tag) {
+            auto one_pass = [&](auto exact_tag) {
+              tile_loop(true, [&](int kt, const unsigned char* base, auto diag_tag) {
                 constexpr bool DIAG = decltype(diag_tag)::value;
                 const int nks = DIAG ? min(4, (qwl - kt * 64) / 16 + 1) : 4;
 #pragma unroll
@@ -607,7 +638,10 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         float sp, sg;
-                        sp_sig(t[r], sp, sg);
+                        if constexpr (decltype(exact_tag)::value)
+                            sp_sig(t[r], sp, sg);
+                        else
+                            sp_sig_plain(t[r], sp, sg);
                         const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(sp, c, -tc), 0.0f, 1.0f);
                         const float ym = pow_m1<P>(y, p_rt);
                         Y = __builtin_fmaf(ym, y, Y);
@@ -623,7 +657,12 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                     mm_kt(base, ks, pack_bf16x4(g2), acc2);
                     mm_kt(base, ks, pack_bf16x4(g3), acc3);
                 }
-            });
+              });
+            };
+            if (!kPlain || blk_deep)
+                one_pass(std::true_type{});
+            else if constexpr (kPlain)
+                one_pass(std::false_type{});
 #pragma unroll
             for (int m = 16; m <= 32; m <<= 1) {
                 Y += __shfl_xor(Y, m);

@@ -173,6 +173,33 @@ def test_deep_and_degenerate_rows():
         _check_grads(got, oracle.lssar_bwd(q2, k2, v2, g2, 15), dtype, f"degenerate {dtype}")
 
 
+def test_deep_block_among_plain_blocks():
+    """bf16, d = 64, p = 15: one query block whose rows all score below -4
+    (keys anti-aligned with those queries) among blocks whose rows do not.
+    The one-pass kernel takes the exact Softplus on that block and plain
+    log2(1 + 2^t) on the others within the same launch."""
+    r = np.random.default_rng(21)
+    L, d = 256, 64
+    u = r.standard_normal(d)
+    u /= np.linalg.norm(u)
+    K = -u[None] * r.uniform(0.5, 2.0, (L, 1)) + 0.03 * r.standard_normal((L, d))
+    Q = -u[None] * r.uniform(0.5, 2.0, (L, 1)) + 0.03 * r.standard_normal((L, d))
+    Q[128:192] = -Q[128:192]                   # block 2: every score negative
+    V = r.standard_normal((L, d))
+    G = r.standard_normal((L, d))
+    q, k, v, g = (gen.round_to_bf16(x[None, None].astype(np.float32)) for x in (Q, K, V, G))
+    qn = q[0, 0].astype(np.float64) / np.linalg.norm(q[0, 0], axis=-1, keepdims=True)
+    kn = k[0, 0].astype(np.float64) / np.linalg.norm(k[0, 0], axis=-1, keepdims=True)
+    t = np.log(d) * np.log(np.arange(1, L + 1))[:, None] * (qn @ kn.T) / np.log(2.0)
+    tmax = np.array([t[i, :i + 1].max() for i in range(L)])
+    assert np.all(tmax[128:192] < -4.0) and np.all(tmax[4:128] > -4.0) and np.all(tmax[192:] > -4.0)
+    dev = [to_device(a, "bf16") for a in (q, k, v, g)]
+    out, st = run_train_fwd(*dev[:3], 15)
+    got = [to_host(x) for x in run_stats_bwd(*dev[:3], out, dev[3], st, 15)]
+    errs = _check_grads(got, oracle.lssar_bwd(q, k, v, g, 15), "bf16", "deep block")
+    print(f"deep block among plain blocks: grads rel {max(errs):.2e}", flush=True)
+
+
 def test_deterministic():
     q, k, v, g = _inputs(500, 128, "bf16", 15, seed=97, H=3)
     dev = [to_device(a, "bf16") for a in (q, k, v, g)]

@@ -44,7 +44,7 @@
 namespace lssar {
 
 constexpr int kBwdThreads = 256;   // 4 waves, one row each
-constexpr int kBwdRowStats = 8;    // c, tc, invY, delta (bf16 kernels: -delta Acoef), Acoef, Ecoef, lam, rq per row
+constexpr int kBwdRowStats = 8;    // c, tc, invY, delta, Acoef, Ecoef, lam, rq per row (bf16 kernels: -delta Acoef for delta, the largest score for rq)
 
 template <typename C>
 struct BwdMath;

@@ -14,8 +14,8 @@
 //             v_mfma_f32_16x16x32_bf16, pass 1 the row's S and max score,
 //             pass 2 the sums Y, P1, P2, Z; writes the row coefficients
 //             (c, tau c, 1/Y, -delta A/|q|, A/|q|, E/|q|, the score factor,
-//             1/|q|; the pair gradient sigma (y^(p-1) (A dW - A delta) - E)
-//             then costs two fma and a multiply);
+//             the largest score; the pair gradient sigma (y^(p-1) (A dW -
+//             A delta) - E) then costs two fma and a multiply);
 //   dq:       per query block, S^T, dW^T, the pair gradients dc_ij f_j, and
 //             dQ^ = (dc f) K on v_mfma_f32_16x16x16_bf16, whose output
 //             layout (lane = one query, four keys) is exactly its A operand;
@@ -387,10 +387,17 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 const float4 a = degen ? make_float4(0.0f, 0.0f, 0.0f, 0.0f)
                                        : make_float4(c, tc, 1.0f / Y, -dl * a_);
                 *reinterpret_cast<float4*>(st) = a;
-                *reinterpret_cast<float4*>(st + 4) = make_float4(a_, e_, lam, rqi);
+                *reinterpret_cast<float2*>(st + 4) = make_float2(a_, e_);
+                st[6] = lam;
             }
             Ac = a_;
             Ec = e_;
+        };
+        // the row's largest score, stored as soon as it is known (kept to the
+        // end it would cost a register through the pass-2 loop)
+        auto store_tmax = [&]() {
+            if (qvalid && grp == 0)
+                stats[((size_t)bh * L + qi) * kBwdRowStats + 7] = tmax;
         };
         // K^T tile: B operand of 16x16x16 = 4 keys of dim row 16 ds + row16
         int trd[4];
@@ -493,6 +500,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 if (*deep_flag)
                     pass1(std::true_type{});
             }
+            store_tmax();
             row_consts();
 
             // ---------------- pass 2: Y, P1, P2, Z ----------------
@@ -589,6 +597,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             constexpr bool kPlain = P == 15;
             if (qvalid)
                 load_row_stats(saved, (size_t)bh * L + qi, s1, tmax);
+            store_tmax();
             bool blk_deep = true;
             if constexpr (kPlain) {
                 __syncthreads();                   // earlier readers of the flag done
@@ -810,7 +819,7 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
             return acc;
         };
 
-        auto tile = [&](int qt, const unsigned char* base, auto diag_tag) {
+        auto tile = [&](int qt, const unsigned char* base, auto diag_tag, auto exact_tag) {
             constexpr bool DIAG = decltype(diag_tag)::value;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -831,7 +840,10 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
                     if (DIAG && qt * 64 + qrow < kj)
                         t = -INFINITY;
                     float sp, sg;
-                    sp_sig(t, sp, sg);
+                    if constexpr (decltype(exact_tag)::value)
+                        sp_sig(t, sp, sg);
+                    else
+                        sp_sig_plain(t, sp, sg);
                     const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(sp, a.x, -a.y), 0.0f, 1.0f);
                     const float ym = pow_m1<P>(y, p_rt);
                     w4[r] = ym * y * a.z;
@@ -858,10 +870,28 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
             __syncthreads();                       // tile qt landed
             if (kw0 >= L)
                 continue;
-            if (qt == kb)
-                tile(qt, lds, std::true_type{});
-            else
-                tile(qt, lds, std::false_type{});
+            // at d = 64, p = 15 a tile whose 64 query rows all have their
+            // largest score at or above kDeep takes plain log2(1 + 2^t) (a
+            // wave-uniform choice; rows past L read as zeros); elsewhere the
+            // second path would cost occupancy (d = 128: 1 wave per SIMD
+            // instead of 2), and every tile is exact
+            constexpr bool kPlain = D == 64 && P == 15;
+            bool exact = true;
+            if constexpr (kPlain) {
+                const float tm = reinterpret_cast<const float*>(lds + SOFF)[lane * kBwdRowStats + 7];
+                exact = __any(tm < kDeep);
+            }
+            if (exact) {
+                if (qt == kb)
+                    tile(qt, lds, std::true_type{}, std::true_type{});
+                else
+                    tile(qt, lds, std::false_type{}, std::true_type{});
+            } else if constexpr (kPlain) {
+                if (qt == kb)
+                    tile(qt, lds, std::true_type{}, std::false_type{});
+                else
+                    tile(qt, lds, std::false_type{}, std::false_type{});
+            }
         }
 
         // adv/adk[ds][r] = grad[key 4 grp + r of the wave][dim 16 ds + row16]

@@ -504,8 +504,13 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             row_consts();
 
             // ---------------- pass 2: Y, P1, P2, Z ----------------
+            // (d = 64, p = 15, recomputed statistics: a block without a deep
+            // row takes plain log2(1 + 2^t); the flag is final after pass 1)
+            constexpr bool kPlain = D == 64 && P == 15;
+            const bool exact = !kPlain || saved || *deep_flag;
             float Y = 0.0f, P1 = 0.0f, P2 = 0.0f, Z = 0.0f;
-            tile_loop(true, [&](int kt, const unsigned char* base, auto diag_tag) {
+            auto pass2 = [&](auto exact_tag) {
+              tile_loop(true, [&](int kt, const unsigned char* base, auto diag_tag) {
                 constexpr bool DIAG = decltype(diag_tag)::value;
                 const int nks = DIAG ? min(4, (qwl - kt * 64) / 16 + 1) : 4;
 #pragma unroll
@@ -517,7 +522,9 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                     const f32x4 dw = mm_block(base, VOFF, gf, ks);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float sp = softplus2_acc(t[r]);
+                        const float sp = decltype(exact_tag)::value
+                                             ? softplus2_acc(t[r])
+                                             : __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(t[r]));
                         const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(sp, c, -tc), 0.0f, 1.0f);
                         const float ym = pow_m1<P>(y, p_rt);
                         const float yp = ym * y;
@@ -528,7 +535,12 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                         Z += sym;
                     }
                 }
-            });
+              });
+            };
+            if (exact)
+                pass2(std::true_type{});
+            else if constexpr (kPlain)
+                pass2(std::false_type{});
 #pragma unroll
             for (int m = 16; m <= 32; m <<= 1) {
                 Y += __shfl_xor(Y, m);
@@ -550,11 +562,27 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 Ac = b.x;
                 Ec = b.y;
             }
+            // (d = 64, p = 15: a block without a deep row, by the largest
+            // scores in the coefficient records, takes plain log2(1 + 2^t))
+            constexpr bool kPlain = D == 64 && P == 15;
+            bool exact = true;
+            if constexpr (kPlain) {
+                const float tm = qvalid ? stats[((size_t)bh * L + qi) * kBwdRowStats + 7] : 0.0f;
+                __syncthreads();                   // earlier readers of the flag done
+                if (tid == 0)
+                    deep_flag[0] = 0;
+                __syncthreads();
+                if (tm < kDeep)
+                    deep_flag[0] = 1;
+                __syncthreads();
+                exact = deep_flag[0] != 0;
+            }
             f32x4 acc[DS];
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds)
                 acc[ds] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            tile_loop(true, [&](int kt, const unsigned char* base, auto diag_tag) {
+            auto dq_pass = [&](auto exact_tag) {
+              tile_loop(true, [&](int kt, const unsigned char* base, auto diag_tag) {
                 constexpr bool DIAG = decltype(diag_tag)::value;
                 const int nks = DIAG ? min(4, (qwl - kt * 64) / 16 + 1) : 4;
 #pragma unroll
@@ -568,7 +596,10 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         float sp, sg;
-                        sp_sig(t[r], sp, sg);
+                        if constexpr (decltype(exact_tag)::value)
+                            sp_sig(t[r], sp, sg);
+                        else
+                            sp_sig_plain(t[r], sp, sg);
                         const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(sp, c, -tc), 0.0f, 1.0f);
                         const float ym = pow_m1<P>(y, p_rt);
                         const float dcv = sg * __builtin_fmaf(ym, __builtin_fmaf(Ac, dw[r], adl), -Ec);
@@ -576,7 +607,12 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                     }
                     mm_kt(base, ks, pack_bf16x4(g), acc);
                 }
-            });
+              });
+            };
+            if (exact)
+                dq_pass(std::true_type{});
+            else if constexpr (kPlain)
+                dq_pass(std::false_type{});
             store_dq(acc);
         } else {
             // ------- rowstats and dq in one pass, from the training forward's

@@ -165,8 +165,7 @@ int lssar_decode_ws(const void* q, const void* k_cache, const void* v_cache,
 /* Workspace of lssar_attn_bwd_ws and lssar_attn_bwd_stats_ws, in bytes (0
  * for invalid sizes): per row of Q and K one inverse norm, and 8
  * coefficients per query row (fp32 for bf16 inputs, fp64 for fp32 inputs);
- * for bf16 inputs also transposed copies of Q, K and dout (bf16, d x Lp per
- * head, Lp = L rounded up to 64); each part rounded up to 256 bytes. */
+ * each part rounded up to 256 bytes. */
 size_t lssar_bwd_workspace_bytes(int B, int H, int L, int d, int dtype);
 
 /* Backward of lssar_attn_fwd_ws for the loss sum over rows of dout_i .

@@ -367,13 +367,11 @@ void decode_dispatch_p(const void* q, const void* kc, const void* vc, const int*
 // ---------------------------------------------------------------------------
 
 // Workspace: [rq: C per query row][fk: C per key row][stats: 8 C per query
-// row], C = fp32 for bf16 inputs and fp64 for fp32 inputs; for bf16 inputs
-// also [Q^T][K^T][dO^T] (bf16 [head][d][Lp], Lp = L rounded up to 64); each
-// part rounded up to 256 bytes.
+// row], C = fp32 for bf16 inputs and fp64 for fp32 inputs; each part rounded
+// up to 256 bytes.
 struct BwdLayout {
-    size_t rq_bytes, fk_bytes, st_bytes, tr_bytes;
-    int Lp;
-    size_t total() const { return rq_bytes + fk_bytes + st_bytes + 3 * tr_bytes; }
+    size_t rq_bytes, fk_bytes, st_bytes;
+    size_t total() const { return rq_bytes + fk_bytes + st_bytes; }
 };
 
 BwdLayout bwd_layout(long long B, long long H, long long L, int d, int dtype)
@@ -381,11 +379,9 @@ BwdLayout bwd_layout(long long B, long long H, long long L, int d, int dtype)
     const size_t cb = dtype == LSSAR_F32 ? 8 : 4;
     const size_t rows = (size_t)(B * H * L);
     BwdLayout w;
-    w.Lp = (int)((L + 63) / 64 * 64);
     w.rq_bytes = round256(cb * rows);
     w.fk_bytes = round256(cb * rows);
     w.st_bytes = round256(cb * rows * lssar::kBwdRowStats);
-    w.tr_bytes = dtype == LSSAR_BF16 ? round256((size_t)(B * H * d) * (size_t)w.Lp * 2) : 0;
     return w;
 }
 
@@ -410,38 +406,34 @@ void launch_bwd(const void* q, const void* k, const void* v, const void* dout, v
     const T* G = static_cast<const T*>(dout);
     const unsigned g4 = (unsigned)((nrows + 3) / 4);
     if constexpr (BF) {
-        unsigned char* tb = base + w.rq_bytes + w.fk_bytes + w.st_bytes;
-        __bf16* QT = reinterpret_cast<__bf16*>(tb);
-        __bf16* KT = reinterpret_cast<__bf16*>(tb + w.tr_bytes);
-        __bf16* GT = reinterpret_cast<__bf16*>(tb + 2 * w.tr_bytes);
-        hipLaunchKernelGGL((lssar::lssar_bwd_prep_kernel<D>), dim3(w.Lp / 64, BH),
-                           dim3(lssar::kThreads), 0, s, Q, K, G, rq, fk, QT, KT, GT, L, w.Lp);
         const int nqb = (L + 63) / 64, npair = (nqb + 1) / 2;
+        hipLaunchKernelGGL((lssar::lssar_bwd_prep_kernel<D>), dim3((unsigned)nqb, BH),
+                           dim3(lssar::kThreads), 0, s, Q, K, rq, fk, L);
         const dim3 grid((unsigned)(npair * BH));
         bool fused = false;
         if constexpr (D == 64) {
             if (saved) {
                 // row coefficients and dq in one pass over the keys
                 hipLaunchKernelGGL((lssar::lssar_bwd_qside_kernel<D, P, 2>), grid,
-                                   dim3(lssar::kThreads), 0, s, Q, K, V, G, KT, rq, fk, st,
-                                   static_cast<__bf16*>(dq), BH, L, w.Lp, nqb, npair, lam_scale,
-                                   eps, p, saved, static_cast<const __bf16*>(out));
+                                   dim3(lssar::kThreads), 0, s, Q, K, V, G, rq, fk, st,
+                                   static_cast<__bf16*>(dq), BH, L, nqb, npair, lam_scale, eps, p,
+                                   saved, static_cast<const __bf16*>(out));
                 fused = true;
             }
         }
         if (!fused) {
             hipLaunchKernelGGL((lssar::lssar_bwd_qside_kernel<D, P, 0>), grid,
-                               dim3(lssar::kThreads), 0, s, Q, K, V, G, KT, rq, fk, st,
-                               static_cast<__bf16*>(dq), BH, L, w.Lp, nqb, npair, lam_scale, eps,
-                               p, saved, nullptr);
+                               dim3(lssar::kThreads), 0, s, Q, K, V, G, rq, fk, st,
+                               static_cast<__bf16*>(dq), BH, L, nqb, npair, lam_scale, eps, p,
+                               saved, nullptr);
             hipLaunchKernelGGL((lssar::lssar_bwd_qside_kernel<D, P, 1>), grid,
-                               dim3(lssar::kThreads), 0, s, Q, K, V, G, KT, rq, fk, st,
-                               static_cast<__bf16*>(dq), BH, L, w.Lp, nqb, npair, lam_scale, eps,
-                               p, nullptr, nullptr);
+                               dim3(lssar::kThreads), 0, s, Q, K, V, G, rq, fk, st,
+                               static_cast<__bf16*>(dq), BH, L, nqb, npair, lam_scale, eps, p,
+                               nullptr, nullptr);
         }
         hipLaunchKernelGGL((lssar::lssar_bwd_kside_kernel<D, P>), grid, dim3(lssar::kThreads), 0,
-                           s, Q, K, V, G, QT, GT, fk, st, static_cast<__bf16*>(dk),
-                           static_cast<__bf16*>(dv), BH, L, w.Lp, nqb, npair, p);
+                           s, Q, K, V, G, fk, st, static_cast<__bf16*>(dk),
+                           static_cast<__bf16*>(dv), BH, L, nqb, npair, p);
         return;
     } else {
         constexpr int rpb = lssar::kBwdThreads / (D / lssar::DecTraits<T>::EPL);

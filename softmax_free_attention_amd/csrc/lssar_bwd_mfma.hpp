@@ -5,11 +5,7 @@
 // Key designs 1-3 of the paper note "Softplus Attention with Re-weighting
 // Boosts Length Extrapolation in Large Language Models", Method details);
 // these kernels evaluate them on the matrix cores:
-//   prep:     key factors f_j = 1/|k_j|, query factors 1/|q_i|, and the
-//             transposed copies Q^T, K^T, dO^T ([head][d][Lp], zero past L;
-//             in dims 8..15 of every 16 the two 8-byte halves of each
-//             16-byte group swap places, so that the 16 lanes of an MFMA
-//             operand read, dims e and e + 8, use disjoint LDS banks);
+//   prep:     key factors f_j = 1/|k_j| and query factors 1/|q_i|;
 //   rowstats: per query block, the scores S^T = K Q^T and dW^T = V dO^T on
 //             v_mfma_f32_16x16x32_bf16, pass 1 the row's S and max score,
 //             pass 2 the sums Y, P1, P2, Z; writes the row coefficients
@@ -24,12 +20,16 @@
 //             applied to accumulated vectors at the end;
 //   dkdv:     per key block, S = Q K^T and dW = dO V^T (lane = one key, four
 //             queries), then dV = W^T dO and dK^ = (dc / |q|)^T Q on
-//             v_mfma_f32_16x16x16_bf16 with dO^T and Q^T as B operands.
+//             v_mfma_f32_16x16x16_bf16.
 // A workgroup is 4 waves x 16 rows (queries, or keys in dkdv) of a 64-row
 // block; paired blocks {n-1-pi, pi} give every workgroup the same number of
 // 64-row tiles.  Tiles of the other side stream through LDS by LDS-direct
-// buffer loads into one buffer.  Softplus is exact for every score
-// (softplus2_acc, or sp_sig with its derivative from the same exp2).
+// buffer loads into one buffer, row-major only: the 16x16x16 B operands
+// (K in dq, Q and dO in dkdv; four consecutive rows of one dim) come from
+// the same tiles by the LDS transpose read (ds_read_b64_tr_b16).  Softplus
+// is exact (softplus2_acc, or sp_sig with its derivative from the same
+// exp2), except that at d = 64, p = 15 blocks and tiles without a deep row
+// take plain log2(1 + 2^t), the forward's rule.
 #pragma once
 
 #include "lssar_bwd.hpp"
@@ -63,6 +63,15 @@ __device__ __forceinline__ void sp_sig_plain(float t, float& sp, float& sig)
     sig = e * __builtin_amdgcn_rcpf(ope);
 }
 
+// Four 16-bit elements by the LDS transpose read (ds_read_b64_tr_b16): see
+// the key-side kernel for the lane layout.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const unsigned char* p)
+{
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    return __builtin_bit_cast(bf16x4, v);
+}
+
 // Four fp32 values as the bf16 operand of the 16x16x16 MFMA (round to
 // nearest even).  Packed two by two into 32-bit words: a bf16x4 bit-cast to
 // the operand type compiles to one conversion per element plus merges.
@@ -82,24 +91,21 @@ __device__ __forceinline__ f32x4 mfma16k16(s16x4 a, bf16x4 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
-// LDS layouts of one 64-row tile:
-//  * row-major: 64 rows x D bf16 as 16-byte slots, slot c of row r at
-//    r * R + (c ^ swz(r)), R = D / 8 (the forward's K tile layout);
-//  * transposed: D rows (dims) x 64 bf16 (the tile's rows), 8 slots per
-//    dim row, slot c of dim row e at e * 8 + (c ^ (e & 7)).
+// LDS layout of one 64-row tile: 64 rows x D bf16 as 16-byte slots, slot
+// c of row r at r * R + (c ^ swz(r)), R = D / 8 (the forward's K tile
+// layout).  The 16x16x32 A operands read 16-byte slots of 16 rows; the
+// 16x16x16 B operands (four consecutive rows of one dim) come from the same
+// tile by the LDS transpose read.
 template <int D>
 struct BwdTiles {
     static constexpr int R = D / 8;
-    static constexpr int RM = 64 * D * 2;        // bytes of a row-major tile
-    static constexpr int TR = D * 64 * 2;        // bytes of a transposed tile
+    static constexpr int RM = 64 * D * 2;        // bytes of a tile
     static constexpr int RM_LOADS = RM / 1024 / kWaves;   // wave-loads per wave
-    static constexpr int TR_LOADS = TR / 1024 / kWaves;
     __device__ static int swz(int r) { return R == 8 ? ((r >> 1) & 7) : (r & 15); }
 };
 
-// Bytes of a 16-byte slot (slot index s of the tile) in the global tensor:
-// row-major source [rows][D] (row stride D*2) and transposed source
-// [D][Lp] (row stride Lp*2).
+// Bytes of the tile's 16-byte slot s in the global tensor [rows][D] (row
+// stride D*2).
 template <int D>
 __device__ __forceinline__ unsigned rm_src(int s)
 {
@@ -107,24 +113,16 @@ __device__ __forceinline__ unsigned rm_src(int s)
     const int r = s / T::R, c = (s % T::R) ^ T::swz(r);
     return (unsigned)((r * D + c * 8) * 2);
 }
-__device__ __forceinline__ unsigned tr_src(int s, int Lp)
-{
-    const int e = s / 8, c = (s % 8) ^ (e & 7);
-    return (unsigned)(e * Lp * 2 + c * 16);
-}
 
 // ---------------------------------------------------------------------------
-// Prep: factors and transposes, one workgroup per (64-row block, head)
+// Prep: row factors, one workgroup per (64-row block, head)
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void lssar_bwd_prep_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ G,
-    float* __restrict__ rq, float* __restrict__ fk, __bf16* __restrict__ QT,
-    __bf16* __restrict__ KT, __bf16* __restrict__ GT, int L, int Lp)
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, float* __restrict__ rq,
+    float* __restrict__ fk, int L)
 {
-    constexpr int RS = D + 2;                  // LDS row stride (elements), odd word count
     constexpr int LPR = D / 8;
-    __shared__ __attribute__((aligned(16))) uint32_t tile[64 * RS / 2];
     const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
     const size_t hoff = (size_t)bh * L * D;
 
@@ -156,49 +154,6 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_prep_kernel(
             fk[(size_t)bh * L + rg] = (float)(1.0 / fmax(sqrt(sk), 1e-12));
         }
     }
-
-    // transposes of the block of Q, K and dO: [bh][e][kb*64 + r]
-    const __bf16* srcs[3] = {Q, K, G};
-    __bf16* dsts[3] = {QT, KT, GT};
-#pragma unroll
-    for (int m3 = 0; m3 < 3; ++m3) {
-        __syncthreads();
-#pragma unroll
-        for (int n = 0; n < 64 * D / 8 / kThreads; ++n) {
-            const int c = tid + n * kThreads;
-            const int row = c / (D / 8), col8 = c % (D / 8);
-            const int rg = kb * 64 + row;
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (rg < L)
-                w = *reinterpret_cast<const u32x4*>(srcs[m3] + hoff + (size_t)rg * D + col8 * 8);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                tile[(row * RS + col8 * 8) / 2 + e] = w[e];
-        }
-        __syncthreads();
-        __bf16* Th = dsts[m3] + (size_t)bh * D * Lp;
-#pragma unroll
-        for (int n = 0; n < (D / 2) * 8 / kThreads; ++n) {
-            const int c = tid + n * kThreads;
-            const int m = c / 8, p8 = c % 8;
-            uint32_t wv[8];
-#pragma unroll
-            for (int h = 0; h < 8; ++h)
-                wv[h] = tile[((8 * p8 + h) * RS) / 2 + m];     // (x[r][2m], x[r][2m+1])
-            u32x4 lo, hi;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                lo[h] = __builtin_amdgcn_perm(wv[2 * h + 1], wv[2 * h], 0x05040100u);
-                hi[h] = __builtin_amdgcn_perm(wv[2 * h + 1], wv[2 * h], 0x07060302u);
-            }
-            if (m & 4) {                       // dims 8..15 of every 16: halves swapped
-                lo = u32x4{lo[2], lo[3], lo[0], lo[1]};
-                hi = u32x4{hi[2], hi[3], hi[0], hi[1]};
-            }
-            *reinterpret_cast<u32x4*>(Th + (size_t)(2 * m) * Lp + kb * 64 + 8 * p8) = lo;
-            *reinterpret_cast<u32x4*>(Th + (size_t)(2 * m + 1) * Lp + kb * 64 + 8 * p8) = hi;
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -221,9 +176,9 @@ template <int D, int P, int MODE>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ G, const __bf16* __restrict__ KT, const float* __restrict__ rq,
-    const float* __restrict__ fk, float* __restrict__ stats, __bf16* __restrict__ dQ, int BH,
-    int L, int Lp, int nqb, int npair, double lam_scale, float eps, int p_rt,
+    const __bf16* __restrict__ G, const float* __restrict__ rq, const float* __restrict__ fk,
+    float* __restrict__ stats, __bf16* __restrict__ dQ, int BH, int L, int nqb, int npair,
+    double lam_scale, float eps, int p_rt,
     const double* __restrict__ saved, const __bf16* __restrict__ O)
 {
     static_assert(D == 64 || D == 128, "head dim");
@@ -231,8 +186,8 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
     using T = BwdTiles<D>;
     constexpr int DC = D / 32;                 // 32-deep MFMA steps over d
     constexpr int DS = D / 16;                 // 16-wide output blocks over d
-    constexpr int KOFF = 0, VOFF = T::RM, TOFF = 2 * T::RM;
-    constexpr int FOFF = MODE >= 1 ? 2 * T::RM + T::TR : 2 * T::RM;
+    constexpr int KOFF = 0, VOFF = T::RM;
+    constexpr int FOFF = 2 * T::RM;
     constexpr int BYTES = FOFF + 256;
     // one LDS object: the tiles, then (MODE 0, 2) the block's deep-row flag
     __shared__ __attribute__((aligned(1024))) unsigned char lds[BYTES + 16];
@@ -248,20 +203,15 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
     const void* kbase = K + hoff;
     const void* vbase = V + hoff;
     const unsigned rmbytes = (unsigned)L * D * 2u;
-    const void* ktbase = KT + (size_t)bh * D * Lp;
-    const unsigned trbytes = (unsigned)D * Lp * 2u;
     const void* fbase = fk + (size_t)bh * L;
     const unsigned fbytes = (unsigned)L * 4u;
 
-    int rm_ld[T::RM_LOADS], tr_ld[T::TR_LOADS];
+    int rm_ld[T::RM_LOADS];
 #pragma unroll
     for (int n = 0; n < T::RM_LOADS; ++n)
         rm_ld[n] = (int)rm_src<D>((wave * T::RM_LOADS + n) * 64 + lane);
-#pragma unroll
-    for (int n = 0; n < T::TR_LOADS; ++n)
-        tr_ld[n] = (int)tr_src((wave * T::TR_LOADS + n) * 64 + lane, Lp);
 
-    // tile kt of K (and V, K^T as the pass needs) into LDS
+    // tile kt of K (and V as the pass needs) into LDS
     auto issue = [&](int kt, bool with_v) {
         unsigned char* base = lds;
 #pragma unroll
@@ -273,12 +223,6 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             for (int n = 0; n < T::RM_LOADS; ++n)
                 load16_to_lds(vbase, rmbytes, base + VOFF + (wave * T::RM_LOADS + n) * 1024,
                               rm_ld[n], kt * 64 * D * 2);
-            if constexpr (MODE >= 1) {
-#pragma unroll
-                for (int n = 0; n < T::TR_LOADS; ++n)
-                    load16_to_lds(ktbase, trbytes, base + TOFF + (wave * T::TR_LOADS + n) * 1024,
-                                  tr_ld[n], kt * 64 * 2);
-            }
         }
         if (wave == 0)
             load4_to_lds(fbase, fbytes, base + FOFF, lane * 4, kt * 64 * 4);
@@ -399,18 +343,22 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             if (qvalid && grp == 0)
                 stats[((size_t)bh * L + qi) * kBwdRowStats + 7] = tmax;
         };
-        // K^T tile: B operand of 16x16x16 = 4 keys of dim row 16 ds + row16
-        int trd[4];
+        // B operand of 16x16x16 (four consecutive keys 16 ks + 4 grp + 0..3
+        // of dim 16 ds + row16) from the row-major K tile by the LDS
+        // transpose read, as in the key-side kernel: lane j of group grp
+        // names key 16 ks + 4 grp + j / 4, dims 16 ds + 4 (j % 4) + 0..3
+        int trr[DS];
+        {
+            const int x = 4 * grp + (row16 >> 2);
+            const int X = ((row16 >> 1) & 1) ^ T::swz(x);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int slot = 2 * ks + (grp >> 1);   // 16-byte slot of keys 16ks+4grp..
-            trd[ks] = ((slot ^ (row16 & 7)) * 16) + (((grp & 1) ^ (row16 >> 3)) * 8);
+            for (int ds = 0; ds < DS; ++ds)
+                trr[ds] = (x * T::R + ((2 * ds) ^ X)) * 16 + (row16 & 1) * 8;
         }
         auto mm_kt = [&](const unsigned char* base, int ks, s16x4 g, f32x4 (&acc)[DS]) {
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds) {
-                const bf16x4 bk = *reinterpret_cast<const bf16x4*>(
-                    base + TOFF + (16 * ds + row16) * 128 + trd[ks]);
+                const bf16x4 bk = lds_read_tr16(base + KOFF + ks * 16 * T::R * 16 + trr[ds]);
                 acc[ds] = mfma16k16(g, bk, acc[ds]);
             }
         };
@@ -698,9 +646,15 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                         g1[r] = g2[r] * h;
                         g3[r] = g2[r] * ym;
                     }
-                    mm_kt(base, ks, pack_bf16x4(g1), acc1);
-                    mm_kt(base, ks, pack_bf16x4(g2), acc2);
-                    mm_kt(base, ks, pack_bf16x4(g3), acc3);
+                    // one operand read feeds the three products
+                    const s16x4 p1 = pack_bf16x4(g1), p2 = pack_bf16x4(g2), p3 = pack_bf16x4(g3);
+#pragma unroll
+                    for (int ds = 0; ds < DS; ++ds) {
+                        const bf16x4 bk = lds_read_tr16(base + KOFF + ks * 16 * T::R * 16 + trr[ds]);
+                        acc1[ds] = mfma16k16(p1, bk, acc1[ds]);
+                        acc2[ds] = mfma16k16(p2, bk, acc2[ds]);
+                        acc3[ds] = mfma16k16(p3, bk, acc3[ds]);
+                    }
                 }
               });
             };
@@ -740,16 +694,15 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
 template <int D, int P>
 __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ G, const __bf16* __restrict__ QT, const __bf16* __restrict__ GT,
-    const float* __restrict__ fk, const float* __restrict__ stats, __bf16* __restrict__ dK,
-    __bf16* __restrict__ dV, int BH, int L, int Lp, int nkb, int npair, int p_rt)
+    const __bf16* __restrict__ G, const float* __restrict__ fk, const float* __restrict__ stats,
+    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int BH, int L, int nkb, int npair, int p_rt)
 {
     static_assert(D == 64 || D == 128, "head dim");
     using T = BwdTiles<D>;
     constexpr int DC = D / 32;
     constexpr int DS = D / 16;
-    constexpr int QOFF = 0, GOFF = T::RM, QTOFF = 2 * T::RM, GTOFF = 2 * T::RM + T::TR;
-    constexpr int SOFF = 2 * T::RM + 2 * T::TR;
+    constexpr int QOFF = 0, GOFF = T::RM;
+    constexpr int SOFF = 2 * T::RM;
     constexpr int BYTES = SOFF + 64 * kBwdRowStats * 4;
     __shared__ __attribute__((aligned(1024))) unsigned char lds[BYTES];
 
@@ -763,19 +716,13 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
     const void* qbase = Q + hoff;
     const void* gbase = G + hoff;
     const unsigned rmbytes = (unsigned)L * D * 2u;
-    const void* qtbase = QT + (size_t)bh * D * Lp;
-    const void* gtbase = GT + (size_t)bh * D * Lp;
-    const unsigned trbytes = (unsigned)D * Lp * 2u;
     const void* sbase = stats + (size_t)bh * L * kBwdRowStats;
     const unsigned sbytes = (unsigned)L * kBwdRowStats * 4u;
 
-    int rm_ld[T::RM_LOADS], tr_ld[T::TR_LOADS];
+    int rm_ld[T::RM_LOADS];
 #pragma unroll
     for (int n = 0; n < T::RM_LOADS; ++n)
         rm_ld[n] = (int)rm_src<D>((wave * T::RM_LOADS + n) * 64 + lane);
-#pragma unroll
-    for (int n = 0; n < T::TR_LOADS; ++n)
-        tr_ld[n] = (int)tr_src((wave * T::TR_LOADS + n) * 64 + lane, Lp);
     // the tile's coefficient rows in LDS in the order (r, c, g) of query
     // 16 c + 4 g + r: the four lane groups, which read rows 4 apart at
     // once, then read 128 consecutive bytes instead of one bank four times
@@ -786,7 +733,7 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
         st_src = (16 * c + 4 * g + r) * kBwdRowStats * 4 + (u & 1) * 16;
     }
 
-    // query tile qt: Q, dO (row-major), Q^T, dO^T and the 64 rows' coefficients
+    // query tile qt: Q, dO (row-major) and the 64 rows' coefficients
     auto issue = [&](int qt) {
         unsigned char* base = lds;
 #pragma unroll
@@ -795,13 +742,6 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
                           qt * 64 * D * 2);
             load16_to_lds(gbase, rmbytes, base + GOFF + (wave * T::RM_LOADS + n) * 1024, rm_ld[n],
                           qt * 64 * D * 2);
-        }
-#pragma unroll
-        for (int n = 0; n < T::TR_LOADS; ++n) {
-            load16_to_lds(qtbase, trbytes, base + QTOFF + (wave * T::TR_LOADS + n) * 1024,
-                          tr_ld[n], qt * 64 * 2);
-            load16_to_lds(gtbase, trbytes, base + GTOFF + (wave * T::TR_LOADS + n) * 1024,
-                          tr_ld[n], qt * 64 * 2);
         }
         if (wave < 2)
             load16_to_lds(sbase, sbytes, base + SOFF + wave * 1024, st_src,
@@ -812,10 +752,20 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
         ard[dc] = (row16 * T::R + ((4 * dc + grp) ^ T::swz(row16))) * 16;
-    int trd[4];
+    // B operands of the 16x16x16 products (four consecutive queries of one
+    // dim) straight from the row-major tiles by the LDS transpose read: in
+    // each 16-lane group, lane j names four consecutive dims of one query
+    // row, and lane 4q + e receives element e of lanes q, q + 4, q + 8 and
+    // q + 12.  Lane j of group grp names query 16 c + 4 grp + j / 4, dims
+    // 16 ds + 4 (j % 4) + 0..3; the rows' slot swizzle does not depend on c.
+    int trr[DS];
+    {
+        const int x = 4 * grp + (row16 >> 2);
+        const int X = ((row16 >> 1) & 1) ^ T::swz(x);
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-        trd[c] = (((2 * c + (grp >> 1)) ^ (row16 & 7)) * 16) + (((grp & 1) ^ (row16 >> 3)) * 8);
+        for (int ds = 0; ds < DS; ++ds)
+            trr[ds] = (x * T::R + ((2 * ds) ^ X)) * 16 + (row16 & 1) * 8;
+    }
 
     const int nblk = (pi == nkb - 1 - pi) ? 1 : 2;
     for (int blk = 0; blk < nblk; ++blk) {
@@ -889,9 +839,9 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
                 const s16x4 gb = pack_bf16x4(g4);
 #pragma unroll
                 for (int ds = 0; ds < DS; ++ds) {
-                    const int off = (16 * ds + row16) * 128 + trd[c];
-                    const bf16x4 bg = *reinterpret_cast<const bf16x4*>(base + GTOFF + off);
-                    const bf16x4 bq = *reinterpret_cast<const bf16x4*>(base + QTOFF + off);
+                    const int off = c * 16 * T::R * 16 + trr[ds];
+                    const bf16x4 bg = lds_read_tr16(base + GOFF + off);
+                    const bf16x4 bq = lds_read_tr16(base + QOFF + off);
                     adv[ds] = mfma16k16(wb, bg, adv[ds]);
                     adk[ds] = mfma16k16(gb, bq, adk[ds]);
                 }

@@ -74,7 +74,9 @@ enum {
 
 /* Workspace for every entry point that takes one, in bytes: one inverse key
  * norm per key row (fp32 for bf16 inputs: 4*B*H*L; fp64 for fp32 inputs:
- * 8*B*H*L), rounded up to 256.  Returns 0 for invalid sizes. */
+ * 8*B*H*L; rounded up to 256), plus for bf16 inputs a transposed copy of V
+ * (B*H*d*Lp bf16, Lp = L rounded up to 64, rounded up to 256).  Returns 0
+ * for invalid sizes. */
 size_t lssar_workspace_bytes(int B, int H, int L, int d, int dtype);
 
 /* LSSAR causal attention forward (Key designs 1-3 above) with a
@@ -93,12 +95,12 @@ int lssar_attn_fwd(const void* q, const void* k, const void* v, void* out,
                    int B, int H, int L, int d, int p, float eps, int dtype,
                    void* stream);
 
-/* The prep step alone (the prep kernel).  Writes into the workspace the
+/* The prep step alone (the prep kernels).  Writes into the workspace the
  * factors fk[bh*L + j] = 1 / max(|k_j|_2, 1e-12) (Key design 1's
  * K_j <- K_j / |K_j|_2, kept as a factor of the score; fp32 for bf16
- * inputs, fp64 for fp32 inputs).  v is validated like k but not read (the
- * attention kernel reads it).  Workspace rules as for lssar_attn_fwd_ws; a
- * bad workspace is LSSAR_EWORKSPACE. */
+ * inputs, fp64 for fp32 inputs) and, for bf16 inputs, V transposed per head
+ * for the attention kernel.  Workspace rules as for
+ * lssar_attn_fwd_ws; a bad workspace is LSSAR_EWORKSPACE. */
 int lssar_prep(const void* k, const void* v, void* workspace,
                size_t workspace_bytes, int B, int H, int L, int d, int dtype,
                void* stream);

@@ -193,7 +193,8 @@ def _ws_args(workspace):
 
 
 def lssar_prep(k, v, workspace, *, stream=None):
-    """The prep step (prep kernel): key-row inverse norms into the workspace."""
+    """The prep step (prep kernels): key-row inverse norms and, for bf16, V^T, into
+    the workspace."""
     B, H, L, d, dt = _check_qkv(k, k, v)
     wp, wn = _ws_args(workspace)
     st = lib().lssar_prep(_ptr(k), _ptr(v), wp, wn, B, H, L, d, dt, _stream_ptr(stream))

@@ -46,16 +46,19 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout: [fk: inverse key norm per key row, fp32 for bf16 inputs
-// and fp64 for fp32 inputs], rounded up to 256 bytes.
+// and fp64 for fp32 inputs][Vt: bf16 V^T, bf16 inputs only]
 struct Layout {
-    size_t fk_bytes;
-    size_t total() const { return fk_bytes; }
+    size_t fk_bytes, vt_bytes;
+    int Lp;
+    size_t total() const { return fk_bytes + vt_bytes; }
 };
 
-Layout layout(long long B, long long H, long long L, int /*d*/, int dtype)
+Layout layout(long long B, long long H, long long L, int d, int dtype)
 {
     Layout w;
+    w.Lp = (int)((L + lssar::kBK - 1) / lssar::kBK * lssar::kBK);
     w.fk_bytes = round256((size_t)((dtype == LSSAR_F32 ? 8 : 4) * B * H * L));
+    w.vt_bytes = dtype == LSSAR_BF16 ? round256((size_t)(B * H * d) * (size_t)w.Lp * 2) : 0;
     return w;
 }
 
@@ -123,24 +126,26 @@ void launch_knorm_f32(const void* k, double* fk, long nrows, hipStream_t s)
 }
 
 template <int D>
-void launch_prep_bf16(const void* k, float* fk, int BH, int L, hipStream_t s)
+void launch_prep_bf16(const void* k, const void* v, float* fk, void* vt, int BH, int L, int Lp,
+                      hipStream_t s)
 {
-    hipLaunchKernelGGL((lssar::lssar_prep_bf16_kernel<D>),
-                       dim3((unsigned)((L + lssar::kBK - 1) / lssar::kBK), BH),
-                       dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(k), fk, L);
+    hipLaunchKernelGGL((lssar::lssar_prep_bf16_kernel<D>), dim3(Lp / lssar::kBK, BH),
+                       dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(k),
+                       static_cast<const __bf16*>(v), fk, static_cast<__bf16*>(vt), L, Lp);
 }
 
 int run_prep(const void* k, const void* v, void* ws, int B, int H, int L, int d, int dtype,
              hipStream_t s)
 {
-    (void)v;                                   // read by the attention kernel only
+    const Layout w = layout(B, H, L, d, dtype);
     const long nrows = (long)B * H * L;
     if (dtype == LSSAR_BF16) {
         float* fk = static_cast<float*>(ws);
+        void* vt = static_cast<unsigned char*>(ws) + w.fk_bytes;
         if (d == 64)
-            launch_prep_bf16<64>(k, fk, B * H, L, s);
+            launch_prep_bf16<64>(k, v, fk, vt, B * H, L, w.Lp, s);
         else
-            launch_prep_bf16<128>(k, fk, B * H, L, s);
+            launch_prep_bf16<128>(k, v, fk, vt, B * H, L, w.Lp, s);
     } else {
         double* fk = static_cast<double*>(ws);
         if (d == 64)
@@ -158,14 +163,17 @@ template <int D, int P, int PHI, bool RW>
 void launch_fwd(const void* q, const void* k, const void* v, void* ws, void* out, int BH, int L,
                 int dtype, double lam_scale, float eps, int p, double* stats, hipStream_t s)
 {
+    const Layout w = layout(1, BH, L, D, dtype);
     if (dtype == LSSAR_BF16) {
         const float* fk = static_cast<const float*>(ws);
         const int nqb = (L + lssar::kBQ16 - 1) / lssar::kBQ16;
+        const __bf16* vt =
+            reinterpret_cast<const __bf16*>(static_cast<unsigned char*>(ws) + w.fk_bytes);
         hipLaunchKernelGGL((lssar::lssar_fwd_bf16_kernel<D, P, PHI, RW>),
                            dim3((unsigned)(nqb * BH)),
                            dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(q),
-                           static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
-                           static_cast<__bf16*>(out), fk, BH, L, nqb, lam_scale, eps, p, stats);
+                           static_cast<const __bf16*>(k), vt, static_cast<__bf16*>(out), fk, BH,
+                           L, w.Lp, nqb, lam_scale, eps, p, stats);
     } else {
         const int nqb = (L + lssar::kBQ32 - 1) / lssar::kBQ32;
         hipLaunchKernelGGL((lssar::lssar_fwd_f32_kernel<D, P, PHI, RW>),

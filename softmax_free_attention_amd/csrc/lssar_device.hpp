@@ -297,13 +297,33 @@ __global__ __launch_bounds__(kThreads) void lssar_knorm_f32_kernel(const float* 
         fk[row] = 1.0 / fmax(sqrt(ss), 1e-12);
 }
 
+// Position of key `key` (0..63 of a 64-key block) inside a row of V^T.  With
+// key = 32 c + 16 h + 4 g + r the position is 32 c + 8 g + 4 h + r, so the 8
+// keys that lane group g feeds to one 32-key MFMA step (taken from two
+// 16-key score blocks) sit in one 16-byte word.
+__device__ __forceinline__ int vt_pos(int key)
+{
+    return (key & 32) + (((key >> 2) & 3) << 3) + (((key >> 4) & 1) << 2) + (key & 3);
+}
+__device__ __forceinline__ int vt_key(int pos)
+{
+    return (pos & 32) + (((pos >> 2) & 1) << 4) + (((pos >> 3) & 3) << 2) + (pos & 3);
+}
+
 // Prep for the bf16 kernel, one workgroup per (64-key block kb, head bh):
-// fk[bh*L + j] = 1 / max(|k_j|_2, 1e-12) for the block's keys (fp64 sum).
+//  * fk[bh*L + j] = 1 / max(|k_j|_2, 1e-12) for the block's keys (fp64 sum);
+//  * Vt[bh][e][kb*64 + vt_pos(j)] = V[bh][kb*64 + j][e], zero for keys >= L;
+//    rows of Vt hold Lp (L rounded up to 64) entries.
+// V goes through LDS: each thread then gathers two adjacent dims of 8 keys
+// with 4-byte LDS reads and writes two 16-byte pieces of V^T.
 template <int D>
 __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
-    const __bf16* __restrict__ K, float* __restrict__ fk, int L)
+    const __bf16* __restrict__ K, const __bf16* __restrict__ V, float* __restrict__ fk,
+    __bf16* __restrict__ Vt, int L, int Lp)
 {
+    constexpr int RS = D + 2;                  // LDS row stride (elements), odd word count
     constexpr int LPR = D / 8;                 // lanes per key row for the norms
+    __shared__ __attribute__((aligned(16))) uint32_t tile[64 * RS / 2];
     const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
     const size_t hoff = (size_t)bh * L * D;
 
@@ -328,6 +348,40 @@ __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
             ss += __shfl_xor(ss, m, LPR);
         if (kg < L && sub == 0)
             fk[(size_t)bh * L + kg] = (float)(1.0 / fmax(sqrt(ss), 1e-12));
+    }
+
+    // V block -> LDS (row stride RS elements: 4-byte aligned rows)
+#pragma unroll
+    for (int n = 0; n < 64 * D / 8 / kThreads; ++n) {
+        const int c = tid + n * kThreads;
+        const int key = c / (D / 8), col8 = c % (D / 8);
+        const int kg = kb * 64 + key;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (kg < L)
+            w = *reinterpret_cast<const u32x4*>(V + hoff + (size_t)kg * D + col8 * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            tile[(key * RS + col8 * 8) / 2 + e] = w[e];
+    }
+    __syncthreads();
+    // V^T: thread -> dims (2m, 2m+1), positions 8 p8 .. 8 p8 + 7
+    __bf16* Vth = Vt + (size_t)bh * D * Lp;
+#pragma unroll
+    for (int n = 0; n < (D / 2) * 8 / kThreads; ++n) {
+        const int c = tid + n * kThreads;
+        const int m = c / 8, p8 = c % 8;
+        uint32_t wv[8];
+#pragma unroll
+        for (int h = 0; h < 8; ++h)
+            wv[h] = tile[(vt_key(8 * p8 + h) * RS) / 2 + m];     // (v[key][2m], v[key][2m+1])
+        u32x4 lo, hi;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            lo[h] = __builtin_amdgcn_perm(wv[2 * h + 1], wv[2 * h], 0x05040100u);
+            hi[h] = __builtin_amdgcn_perm(wv[2 * h + 1], wv[2 * h], 0x07060302u);
+        }
+        *reinterpret_cast<u32x4*>(Vth + (size_t)(2 * m) * Lp + kb * 64 + 8 * p8) = lo;
+        *reinterpret_cast<u32x4*>(Vth + (size_t)(2 * m + 1) * Lp + kb * 64 + 8 * p8) = hi;
     }
 }
 
@@ -361,28 +415,16 @@ template <int D>
 struct Bf16Tile {
     static constexpr int R = D / 8;                       // 16-byte slots per K row
     static constexpr int KBYTES = kBK * D * 2;            // K tile
-    static constexpr int VBYTES = kBK * D * 2;            // V tile (same layout)
+    static constexpr int VBYTES = D * kBK * 2;            // V^T tile
     static constexpr int FBYTES = kBK * 4;                // key factors
     static constexpr int BYTES = KBYTES + VBYTES + FBYTES;
     static constexpr int KLOADS = KBYTES / 1024 / kWaves; // 1 KB wave-loads per wave
-    // XOR swizzle of a K or V row's slots (key & 15 is all that matters)
+    static constexpr int VLOADS = VBYTES / 1024 / kWaves;
+    // XOR swizzle of a K row's slots (key & 15 is all that matters)
     __device__ static int kswz(int key) { return R == 8 ? ((key >> 1) & 7) : (key & 15); }
+    // XOR swizzle of a V^T row's 8 slots
+    __device__ static int vswz(int e) { return (e >> 1) & 7; }
 };
-
-// Four 16-bit elements by the LDS transpose read (ds_read_b64_tr_b16).  In
-// each group of 16 lanes, lane j names four consecutive elements M[j][0..3]
-// (8 bytes); lane 4 q + e receives M[q][e], M[q+4][e], M[q+8][e] and
-// M[q+12][e].  With lane j naming row base + j / 4, columns c0 + 4 (j % 4)
-// + 0..3 of a row-major tile, lane i receives column c0 + i of rows base +
-// 0..3: four consecutive k of one n, as the 16x16x16 B and (twice) the
-// 16x16x32 A operands take them.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ bf16x4 lds_read_tr16(const unsigned char* p)
-{
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-    return __builtin_bit_cast(bf16x4, v);
-}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -439,8 +481,8 @@ template <int D, int P, int PHI, bool RW>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-    const __bf16* __restrict__ V, __bf16* __restrict__ O,
-    const float* __restrict__ FK, int BH, int L, int nqb,
+    const __bf16* __restrict__ VT, __bf16* __restrict__ O,
+    const float* __restrict__ FK, int BH, int L, int Lp, int nqb,
     double lam_scale, float eps, int p_rt, double* __restrict__ ST)
 {
     static_assert(D == 64 || D == 128, "head dim");
@@ -468,42 +510,37 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
     const __bf16* Qh = Q + hoff;
     __bf16* Oh = O + hoff;
 
-    // this head's K, V and key factors; buffer reads past them return zeros
+    // this head's K, V^T and key factors; buffer reads past them return zeros
     const void* kbase = K + hoff;
     const unsigned kbytes = (unsigned)L * D * 2u;
-    const void* vbase = V + hoff;
+    const void* vbase = VT + (size_t)bh * D * Lp;
+    const unsigned vbytes = (unsigned)D * Lp * 2u;
     const void* fbase = FK + (size_t)bh * L;
     const unsigned fbytes = (unsigned)L * 4u;
 
     // per-lane byte offsets (within a tile) of the 16-byte slots this lane loads
-    // per-lane byte offsets (within a K or V tile) of the 16-byte slots this
-    // lane loads
-    int kld[T::KLOADS];
+    int kld[T::KLOADS], vld[T::VLOADS];
 #pragma unroll
     for (int n = 0; n < T::KLOADS; ++n) {
         const int slot = (wave * T::KLOADS + n) * 64 + lane;
         const int key = slot / T::R, c = (slot % T::R) ^ T::kswz(key);
         kld[n] = (key * D + c * 8) * 2;
     }
-    // per-lane LDS byte offsets of the MFMA operand slots (16 ks rows further
-    // on are constant offsets)
-    int krd[DC];
+#pragma unroll
+    for (int n = 0; n < T::VLOADS; ++n) {
+        const int slot = (wave * T::VLOADS + n) * 64 + lane;
+        const int e = slot / 8, c = (slot % 8) ^ T::vswz(e);
+        vld[n] = (e * Lp + c * 8) * 2;
+    }
+    // per-lane LDS byte offsets of the MFMA operand slots (16 ks / 16 ds rows
+    // further on are constant offsets)
+    int krd[DC], vrd[2];
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
         krd[dc] = (row16 * T::R + ((4 * dc + grp) ^ T::kswz(row16))) * 16;
-    // P.V's A operand, dims 16 ds + row16 of the 8 keys 32 c2 + 4 grp + 0..3
-    // and 32 c2 + 16 + 4 grp + 0..3 (the order in which the weights' B
-    // operand holds them), by two transpose reads from the V tile: lane j of
-    // group grp names key 32 c2 + 4 grp + j / 4 (+ 16), dims 16 ds + 4 (j % 4)
-    // + 0..3.  The rows' slot swizzle does not depend on c2 or the + 16.
-    int vtr[DS];
-    {
-        const int x = 4 * grp + (row16 >> 2);
-        const int X = ((row16 >> 1) & 1) ^ T::kswz(x);
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds)
-            vtr[ds] = T::KBYTES + (x * T::R + ((2 * ds) ^ X)) * 16 + (row16 & 1) * 8;
-    }
+    for (int c2 = 0; c2 < 2; ++c2)
+        vrd[c2] = T::KBYTES + (row16 * 8 + ((4 * c2 + grp) ^ T::vswz(row16))) * 16;
 
     auto issue = [&](int kt, int buf, bool with_v) {
         unsigned char* base = smem(buf);
@@ -513,9 +550,9 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
                             kt * kBK * D * 2);
         if (with_v) {
 #pragma unroll
-            for (int n = 0; n < T::KLOADS; ++n)
-                load16_to_lds(vbase, kbytes, base + T::KBYTES + (wave * T::KLOADS + n) * 1024,
-                                kld[n], kt * kBK * D * 2);
+            for (int n = 0; n < T::VLOADS; ++n)
+                load16_to_lds(vbase, vbytes, base + T::KBYTES + (wave * T::VLOADS + n) * 1024,
+                                vld[n], kt * kBK * 2);
         }
         if (wave == 0)
             load4_to_lds(fbase, fbytes, base + T::KBYTES + T::VBYTES, lane * 4, kt * kBK * 4);
@@ -760,10 +797,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
                 const bf16x8 bfr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
                 for (int ds = 0; ds < DS; ++ds) {
-                    const unsigned char* vp = base + vtr[ds] + c2 * 32 * T::R * 16;
-                    const bf16x4 v0 = lds_read_tr16(vp);
-                    const bf16x4 v1 = lds_read_tr16(vp + 16 * T::R * 16);
-                    const bf16x8 a = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + vrd[c2] +
+                                                                      ds * 16 * 8 * 16);
                     oacc[ds] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfr, oacc[ds], 0, 0, 0);
                 }
                 dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bfr, dacc, 0, 0, 0);

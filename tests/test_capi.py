@@ -79,9 +79,9 @@ def test_workspace_bytes(L):
     assert sfa.lssar_workspace_bytes(2, 3, 5, 128, sfa.LSSAR_F32) == 256
     assert sfa.lssar_workspace_bytes(1, 1, 100, 64, sfa.LSSAR_F32) == 1024
     assert sfa.lssar_workspace_bytes(1, 1, 32, 64, sfa.LSSAR_F32) == 256
-    # bf16: one fp32 factor per key row, rounded up to 256 bytes
-    assert sfa.lssar_workspace_bytes(1, 12, 8192, 64, sfa.LSSAR_BF16) == 4 * 12 * 8192
-    assert sfa.lssar_workspace_bytes(2, 3, 77, 128, sfa.LSSAR_BF16) == 2048
+    # bf16: plus V^T with rows padded to a multiple of 64 keys
+    assert sfa.lssar_workspace_bytes(1, 12, 8192, 64, sfa.LSSAR_BF16) == 4 * 12 * 8192 + 12 * 64 * 8192 * 2
+    assert sfa.lssar_workspace_bytes(2, 3, 77, 128, sfa.LSSAR_BF16) == 2048 + 6 * 128 * 128 * 2
     assert sfa.lssar_workspace_bytes(0, 1, 1, 64, 0) == 0
     assert sfa.lssar_workspace_bytes(1, 1, 1, 96, 0) == 0
     assert sfa.lssar_workspace_bytes(1, 1, 1, 64, 5) == 0
@@ -140,7 +140,7 @@ def test_stage_entries_validate(L):
     assert L.lssar_prep(k, v, 0, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
     assert L.lssar_prep(k, v, ws + 16, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
     assert L.lssar_prep(k, v, ws, 64, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
-    assert L.lssar_prep(k, v, v, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
+    assert L.lssar_prep(k, v, v - 256, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
     # prepped: the fused-call checks plus the workspace
     q, o = A + 2 * STEP, A + 3 * STEP
     assert L.lssar_attn_fwd_prepped(q, k, v, 0, 1 << 20, o, 1, 1, 8, 64, 3, 1e-4, 1,
@@ -272,7 +272,7 @@ def test_stats_entries_validate_before_any_hip_call(L):
     assert fwd(st=A + 7 * S + 256) == sfa.LSSAR_EINVAL          # overlaps the workspace
     assert fwd(d=96) == sfa.LSSAR_EUNSUPPORTED
     assert fwd(out=0) == sfa.LSSAR_EINVAL
-    assert fwd(wsb=256) == sfa.LSSAR_EWORKSPACE                 # needs 512
+    assert fwd(wsb=1000) == sfa.LSSAR_EWORKSPACE
 
     bbase = dict(q=A, k=A + S, v=A + 2 * S, o=A + 8 * S, g=A + 3 * S, st=st0, dq=A + 4 * S,
                  dk=A + 5 * S, dv=A + 6 * S, B=1, H=2, Ln=64, d=64, p=3, eps=1e-4, dt=1,

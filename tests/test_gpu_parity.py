@@ -179,7 +179,8 @@ def test_bitwise_determinism_and_entry_points_agree():
 
 def test_prep_workspace_contents():
     """The prep step writes 1/max(|k_j|, 1e-12) per key row (fp32 for bf16,
-    fp64 for fp32 inputs), and nothing past the factors."""
+    fp64 for fp32 inputs) and, for bf16, V^T with
+    every 64-key block permuted for the attention kernel, zero past L."""
     import softmax_free_attention_amd as sfa
     for dtype, d in (("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)):
         L = 77
@@ -196,14 +197,18 @@ def test_prep_workspace_contents():
         fk = raw[:fdt().itemsize * nrow].view(fdt).reshape(2, 3, L)
         want = 1.0 / np.maximum(np.linalg.norm(k.astype(np.float64), axis=-1), 1e-12)
         assert np.max(np.abs(fk / want - 1.0)) < (1e-6 if dtype == "bf16" else 1e-14)
-        # the rest of the workspace is untouched (prefilled with 0xA5)
-        ws2 = sfa.workspace_for(kt)
-        pad = torch.full((ws2.numel() + 4096,), 0xA5, dtype=torch.uint8, device=ws2.device)
-        sfa.lssar_prep(kt, vt, pad[:ws2.numel()])
-        torch.cuda.synchronize()
-        assert torch.all(pad[ws2.numel():] == 0xA5)
-        np.testing.assert_array_equal(pad[:fdt().itemsize * nrow].cpu().numpy(),
-                                      raw[:fdt().itemsize * nrow])
+        if dtype == "bf16":
+            Lp = 128
+            off = (4 * nrow + 255) // 256 * 256
+            vtt = raw[off:off + 2 * 3 * d * Lp * 2].view(np.uint16).reshape(2, 3, d, Lp)
+            vtt = (vtt.astype(np.uint32) << 16).view(np.float32)
+            # position pos of block kb holds key 32c + 16h + 4g + r for
+            # pos = 32c + 8g + 4h + r
+            pos = np.arange(Lp)
+            key = (pos & ~63) + (pos & 32) + ((pos >> 2) & 1) * 16 + ((pos >> 3) & 3) * 4 + (pos & 3)
+            vp = np.zeros((2, 3, Lp, d), np.float32)
+            vp[:, :, :L] = inp.v
+            assert np.array_equal(vtt, np.swapaxes(vp[:, :, key], -1, -2))
 
 
 def test_causality_and_scale_invariance():

@@ -756,6 +756,6 @@ const char* lssar_status_str(int status)
 
 int lssar_last_hip_error(void) { return g_last_hip_error; }
 
-int lssar_version(void) { return 600; }
+int lssar_version(void) { return 700; }
 
 }  // extern "C"

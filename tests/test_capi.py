@@ -65,7 +65,7 @@ def test_library_has_no_oracle_dependency(L):
 
 
 def test_version_and_status_strings(L):
-    assert sfa.lssar_version() == 600
+    assert sfa.lssar_version() == 700
     assert sfa.lssar_status_str(0) == "ok"
     for st in (-1, -2, -3, -4, 7):
         s = sfa.lssar_status_str(st)

@@ -690,7 +690,8 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
 // Key-side kernel (dk, dv): lane (row16, grp) owns key row16 of its wave and
 // queries 16 c + 4 grp + r of each 16-query block c of a query tile.
 // ---------------------------------------------------------------------------
-// One query-tile buffer in LDS, as in the query-side kernels.
+// Query tiles stream through LDS, double-buffered at d = 64 (one buffer at
+// d = 128, as in the query-side kernels).
 template <int D, int P>
 __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -703,8 +704,11 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
     constexpr int DS = D / 16;
     constexpr int QOFF = 0, GOFF = T::RM;
     constexpr int SOFF = 2 * T::RM;
-    constexpr int BYTES = SOFF + 64 * kBwdRowStats * 4;
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[BYTES];
+    constexpr int BYTES = SOFF + 64 * kBwdRowStats * 4;   // one tile buffer
+    // d = 64: two buffers (36 KB; 141 VGPRs give 3 waves per SIMD, and
+    // capped for 4 the kernel spills and runs no faster); d = 128: one
+    constexpr int NB = D == 64 ? 2 : 1;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[NB * BYTES];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -734,8 +738,8 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
     }
 
     // query tile qt: Q, dO (row-major) and the 64 rows' coefficients
-    auto issue = [&](int qt) {
-        unsigned char* base = lds;
+    auto issue = [&](int qt, int buf) {
+        unsigned char* base = lds + buf * BYTES;
 #pragma unroll
         for (int n = 0; n < T::RM_LOADS; ++n) {
             load16_to_lds(qbase, rmbytes, base + QOFF + (wave * T::RM_LOADS + n) * 1024, rm_ld[n],
@@ -848,14 +852,9 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
             }
         };
 
-        for (int n = 0; n < ntiles; ++n) {
-            const int qt = qt0 + n;
-            __syncthreads();                       // readers of the previous tile done
-            issue(qt);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();                       // tile qt landed
+        auto run_tile = [&](int qt, const unsigned char* base) {
             if (kw0 >= L)
-                continue;
+                return;
             // at d = 64, p = 15 a tile whose 64 query rows all have their
             // largest score at or above kDeep takes plain log2(1 + 2^t) (a
             // wave-uniform choice; rows past L read as zeros); elsewhere the
@@ -864,19 +863,39 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
             constexpr bool kPlain = D == 64 && P == 15;
             bool exact = true;
             if constexpr (kPlain) {
-                const float tm = reinterpret_cast<const float*>(lds + SOFF)[lane * kBwdRowStats + 7];
+                const float tm = reinterpret_cast<const float*>(base + SOFF)[lane * kBwdRowStats + 7];
                 exact = __any(tm < kDeep);
             }
             if (exact) {
                 if (qt == kb)
-                    tile(qt, lds, std::true_type{}, std::true_type{});
+                    tile(qt, base, std::true_type{}, std::true_type{});
                 else
-                    tile(qt, lds, std::false_type{}, std::true_type{});
+                    tile(qt, base, std::false_type{}, std::true_type{});
             } else if constexpr (kPlain) {
                 if (qt == kb)
-                    tile(qt, lds, std::true_type{}, std::false_type{});
+                    tile(qt, base, std::true_type{}, std::false_type{});
                 else
-                    tile(qt, lds, std::false_type{}, std::false_type{});
+                    tile(qt, base, std::false_type{}, std::false_type{});
+            }
+        };
+        if constexpr (NB == 2) {
+            __syncthreads();                       // earlier readers done with both buffers
+            issue(qt0, 0);
+            for (int n = 0; n < ntiles; ++n) {
+                const int buf = n & 1;
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();                   // tile n landed; buffer buf ^ 1 free
+                if (n + 1 < ntiles)
+                    issue(qt0 + n + 1, buf ^ 1);
+                run_tile(qt0 + n, lds + buf * BYTES);
+            }
+        } else {
+            for (int n = 0; n < ntiles; ++n) {
+                __syncthreads();                   // readers of the previous tile done
+                issue(qt0 + n, 0);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();                   // tile landed
+                run_tile(qt0 + n, lds);
             }
         }
 

@@ -38,6 +38,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -114,8 +115,10 @@ def upload(inp):
     return out
 
 
-def time_path(q, k, v, p, steps, warmup, eps=1e-4, settle_s=0.0):
-    """Run warmup + timed steps; returns (wall_s, fwd_ms_mean, prep_ms_mean).
+def time_path(q, k, v, p, steps, warmup, eps=1e-4, settle_s=0.0, repeats=5):
+    """Run warmup + timed steps; returns (wall_s, fwd_ms_mean, prep_ms_mean,
+    reps): reps holds ms per step of the timed block and of repeats - 1 more
+    blocks of the same steps right after it, for the spread.
     A step is one lssar_attn_fwd_ws call (the prep kernel, then the attention
     kernel); wall_s covers the timed steps, between torch.cuda.synchronize()
     calls.  Then the same number of steps run as lssar_prep and
@@ -147,6 +150,13 @@ def time_path(q, k, v, p, steps, warmup, eps=1e-4, settle_s=0.0):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    reps = [wall / steps * 1e3]
+    for _ in range(repeats - 1):
+        t1 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        reps.append((time.perf_counter() - t1) / steps * 1e3)
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for s in range(steps):
@@ -158,7 +168,7 @@ def time_path(q, k, v, p, steps, warmup, eps=1e-4, settle_s=0.0):
     torch.cuda.synchronize()
     fwd = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     prep = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    return wall, fwd, prep
+    return wall, fwd, prep, reps
 
 
 def time_variants(q, k, v, p, steps, warmup, eps=1e-4):
@@ -321,7 +331,7 @@ def sweep(steps, warmup):
         shape = (B, 12, L, 64)
         q, k, v = (torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
                    .to(torch.bfloat16) for _ in range(3))
-        wall, fwd, prep = time_path(q, k, v, 15, steps, warmup, settle_s=0.3)
+        wall, fwd, prep, _ = time_path(q, k, v, 15, steps, warmup, settle_s=0.3, repeats=1)
         flops = 4 * 64 * B * 12 * L * (L + 1) // 2
         res[str(L)] = {"B": B, "tflops": round(flops * steps / wall / 1e12, 2),
                        "kernel_tflops": round(flops / (fwd * 1e-3) / 1e12, 2),
@@ -369,8 +379,8 @@ def main():
     inp = gen.make_inputs(wl)
     q, k, v = upload(inp)
     log(f"bench: timing {args.steps} steps after {args.warmup} warmup")
-    wall, fwd_ms, prep_ms = time_path(q, k, v, wl.p, args.steps, args.warmup,
-                                      settle_s=args.settle_seconds)
+    wall, fwd_ms, prep_ms, reps = time_path(q, k, v, wl.p, args.steps, args.warmup,
+                                            settle_s=args.settle_seconds)
     flops = wl.flops
     value = flops * args.steps / wall / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
@@ -385,6 +395,10 @@ def main():
                    "structure": wl.structure, "seed": wl.seed, "eps": 1e-4},
         "pct_of_bf16_mfma_peak": round(100 * value / PEAK_TFLOPS["bf16"], 3),
         "tokens_per_s": round(wl.B * wl.L * args.steps / wall, 1),
+        # ms per step of the timed block and four more blocks of K steps
+        "repeats": {"n": len(reps), "ms_per_step_median": round(statistics.median(reps), 5),
+                    "ms_per_step_min": round(min(reps), 5),
+                    "ms_per_step_p90": round(sorted(reps)[max(0, int(0.9 * len(reps) + 0.5) - 1)], 5)},
         "kernel_ms": {"lssar_fwd": round(fwd_ms, 5), "lssar_prep": round(prep_ms, 5)},
         "roofline": {"bound": "mfma", "kernel": "lssar_fwd_bf16_kernel" if wl.dtype == "bf16"
                      else "lssar_fwd_f32_kernel",

@@ -115,6 +115,28 @@ def upload(inp):
     return out
 
 
+def time_cold(q, k, v, p, steps, eps=1e-4):
+    """Mean time of one lssar_attn_fwd_ws call when each follows a 512 MiB
+    write (a fill that evicts the inputs from L2 and the Infinity Cache),
+    HIP events around each call on the launch stream."""
+    import torch
+    import softmax_free_attention_amd as sfa
+    ws = sfa.workspace_for(q)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=q.device)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for s in range(steps):
+        scratch.fill_(s & 0xFF)
+        ev[s][0].record(stream)
+        sfa.lssar_attn_fwd_ws(q, k, v, out, ws, p=p, eps=eps, stream=stream)
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    del scratch
+    return {"ms": round(ms, 5), "steps": steps, "flush_mib": 512}
+
+
 def time_path(q, k, v, p, steps, warmup, eps=1e-4, settle_s=0.0, repeats=5):
     """Run warmup + timed steps; returns (wall_s, fwd_ms_mean, prep_ms_mean,
     reps): reps holds ms per step of the timed block and of repeats - 1 more
@@ -357,6 +379,8 @@ def main():
                          "write N), the reference kernel for scaling rocprofv3 FETCH/WRITE_SIZE")
     ap.add_argument("--settle-seconds", type=float, default=3.0,
                     help="untimed load before the warmup steps, for the GPU clock to settle")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time steps that each follow a 512 MiB write (cold caches)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -413,6 +437,9 @@ def main():
         torch.add(src, 0.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if args.cold:
+        log("bench: cold-cache steps")
+        line["cold"] = time_cold(q, k, v, wl.p, args.steps)
     if not args.no_variants:
         log("bench: ablation variants")
         vt = time_variants(q, k, v, wl.p, args.steps, args.warmup)

@@ -687,12 +687,13 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
         };
         // Tiles 0..ntiles-1 of K (and V^T) through LDS; body runs on every
         // tile that reaches the wave's rows (diagonal tiles masked).
+        // Tiles 0..ntiles-2 lie wholly before every row of the block and the
+        // last tile (keys 64 qb..64 qb + 63) holds its diagonal, so the loop
+        // runs the unmasked body and the diagonal tile follows it: with both
+        // bodies inside the loop, their accumulators were copied back at
+        // every iteration (20 moves per tile in pass 2).
         auto tile_loop = [&](bool with_v, auto body) {
-            if constexpr (NB == 2) {
-                __syncthreads();                   // earlier readers done with the buffers
-                issue(0, 0, with_v);
-            }
-            for (int kt = 0; kt < ntiles; ++kt) {
+            auto step = [&](int kt, auto diag_tag) {
                 int buf = 0;
                 if constexpr (NB == 2) {
                     buf = kt & 1;
@@ -706,13 +707,16 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
                     __builtin_amdgcn_s_waitcnt(0);
                     __syncthreads();               // tile kt landed
                 }
-                if (!(wave_active && kt * kBK <= qwl))
-                    continue;
-                if (kt * kBK + kBK - 1 > qw0)
-                    body(kt, smem(buf), std::true_type{});
-                else
-                    body(kt, smem(buf), std::false_type{});
+                if (wave_active)
+                    body(kt, smem(buf), diag_tag);
+            };
+            if constexpr (NB == 2) {
+                __syncthreads();                   // earlier readers done with the buffers
+                issue(0, 0, with_v);
             }
+            for (int kt = 0; kt + 1 < ntiles; ++kt)
+                step(kt, std::false_type{});
+            step(ntiles - 1, std::true_type{});
         };
         auto run_pass1 = [&](auto kind_tag) {
             tile_loop(false, [&](int kt, const unsigned char* base, auto diag_tag) {

@@ -290,19 +290,21 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
         // row coefficients (dq reads them; rowstats computes them)
         float adl = 0.0f, Ac = 0.0f, Ec = 0.0f;    // adl = -A delta
 
+        // tiles 0..ntiles-2 lie before every row of the block, the last one
+        // holds its diagonal: the loop runs the unmasked body only (with both
+        // bodies in the loop their accumulators were copied at every tile)
         auto tile_loop = [&](bool with_v, auto body) {
-            for (int kt = 0; kt < ntiles; ++kt) {
+            auto step = [&](int kt, auto diag_tag) {
                 __syncthreads();                   // readers of the previous tile done
                 issue(kt, with_v);
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();                   // tile kt landed
-                if (!(wave_active && kt * 64 <= qwl))
-                    continue;
-                if (kt * 64 + 63 > qw0)
-                    body(kt, lds, std::true_type{});
-                else
-                    body(kt, lds, std::false_type{});
-            }
+                if (wave_active)
+                    body(kt, lds, diag_tag);
+            };
+            for (int kt = 0; kt + 1 < ntiles; ++kt)
+                step(kt, std::false_type{});
+            step(ntiles - 1, std::true_type{});
         };
 
         // stage-2 row constants from S and the max score (degenerate: c = 0)
@@ -852,7 +854,7 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
             }
         };
 
-        auto run_tile = [&](int qt, const unsigned char* base) {
+        auto run_tile = [&](int qt, const unsigned char* base, auto diag_tag) {
             if (kw0 >= L)
                 return;
             // at d = 64, p = 15 a tile whose 64 query rows all have their
@@ -866,38 +868,36 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
                 const float tm = reinterpret_cast<const float*>(base + SOFF)[lane * kBwdRowStats + 7];
                 exact = __any(tm < kDeep);
             }
-            if (exact) {
-                if (qt == kb)
-                    tile(qt, base, std::true_type{}, std::true_type{});
-                else
-                    tile(qt, base, std::false_type{}, std::true_type{});
-            } else if constexpr (kPlain) {
-                if (qt == kb)
-                    tile(qt, base, std::true_type{}, std::false_type{});
-                else
-                    tile(qt, base, std::false_type{}, std::false_type{});
-            }
+            if (exact)
+                tile(qt, base, diag_tag, std::true_type{});
+            else if constexpr (kPlain)
+                tile(qt, base, diag_tag, std::false_type{});
         };
-        if constexpr (NB == 2) {
-            __syncthreads();                       // earlier readers done with both buffers
-            issue(qt0, 0);
-            for (int n = 0; n < ntiles; ++n) {
+        // the first query tile (qt = kb) holds the diagonal, the later ones
+        // lie wholly after every key of the block: it is peeled off the loop
+        auto step = [&](int n, auto diag_tag) {
+            if constexpr (NB == 2) {
                 const int buf = n & 1;
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();                   // tile n landed; buffer buf ^ 1 free
                 if (n + 1 < ntiles)
                     issue(qt0 + n + 1, buf ^ 1);
-                run_tile(qt0 + n, lds + buf * BYTES);
-            }
-        } else {
-            for (int n = 0; n < ntiles; ++n) {
+                run_tile(qt0 + n, lds + buf * BYTES, diag_tag);
+            } else {
                 __syncthreads();                   // readers of the previous tile done
                 issue(qt0 + n, 0);
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();                   // tile landed
-                run_tile(qt0 + n, lds);
+                run_tile(qt0 + n, lds, diag_tag);
             }
+        };
+        if constexpr (NB == 2) {
+            __syncthreads();                       // earlier readers done with both buffers
+            issue(qt0, 0);
         }
+        step(0, std::true_type{});
+        for (int n = 1; n < ntiles; ++n)
+            step(n, std::false_type{});
 
         // adv/adk[ds][r] = grad[key 4 grp + r of the wave][dim 16 ds + row16]
 #pragma unroll

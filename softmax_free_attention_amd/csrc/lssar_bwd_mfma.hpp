@@ -168,10 +168,10 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_prep_kernel(
 // One key-tile buffer in LDS: a double-buffered loop measured slower, since
 // its LDS and registers cost workgroups per CU that hide the loads better.
 // MODE 2 keeps three d-wide accumulators and four row sums beside the
-// scores; capped for 3 waves per SIMD it spills some bytes and still runs
-// faster than at 2 (measured: x8 10% faster than MODE 0 + MODE 1).  At
-// d = 128 the accumulators alone take 96 VGPRs, and the two-kernel path is
-// faster.
+// scores; capped for 3 waves per SIMD it fits without spills (164 VGPRs)
+// and runs faster than at 2 (x8 9% faster; and faster than MODE 0 +
+// MODE 1).  At d = 128 the accumulators alone take 96 VGPRs, and the
+// two-kernel path is faster.
 template <int D, int P, int MODE>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_kernel(

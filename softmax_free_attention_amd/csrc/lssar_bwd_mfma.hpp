@@ -91,6 +91,18 @@ __device__ __forceinline__ f32x4 mfma16k16(s16x4 a, bf16x4 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
+// Two 16x16x16 products into one accumulator, a0 b0 + a1 b1, as one
+// 16x16x32: each lane's eight k-slots hold its four of the first product
+// and then its four of the second, on both operands alike.  On gfx950 the
+// 16x16x16 instruction takes as many cycles as the 16x16x32.
+__device__ __forceinline__ f32x4 mfma16k16x2(s16x4 a0, s16x4 a1, bf16x4 b0, bf16x4 b1, f32x4 c)
+{
+    const bf16x8 a = __builtin_shufflevector(__builtin_bit_cast(bf16x4, a0),
+                                             __builtin_bit_cast(bf16x4, a1), 0, 1, 2, 3, 4, 5, 6, 7);
+    const bf16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // LDS layout of one 64-row tile: 64 rows x D bf16 as 16-byte slots, slot
 // c of row r at r * R + (c ^ swz(r)), R = D / 8 (the forward's K tile
 // layout).  The 16x16x32 A operands read 16-byte slots of 16 rows; the
@@ -364,6 +376,15 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 acc[ds] = mfma16k16(g, bk, acc[ds]);
             }
         };
+        // key blocks ks and ks + 1 together
+        auto mm_kt2 = [&](const unsigned char* base, int ks, s16x4 g0, s16x4 g1, f32x4 (&acc)[DS]) {
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds) {
+                const unsigned char* b = base + KOFF + ks * 16 * T::R * 16 + trr[ds];
+                acc[ds] = mfma16k16x2(g0, g1, lds_read_tr16(b), lds_read_tr16(b + 16 * T::R * 16),
+                                      acc[ds]);
+            }
+        };
         // acc[ds][r] = dQ^[query 4 grp + r of the wave][dim 16 ds + row16], with
         // 1 / |q| carried by the coefficients;
         // dq = (dq^ - (dq^ . q^) q^) / |q|, or dq^ / 1e-12 below the clamp
@@ -535,10 +556,8 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
               tile_loop(true, [&](int kt, const unsigned char* base, auto diag_tag) {
                 constexpr bool DIAG = decltype(diag_tag)::value;
                 const int nks = DIAG ? min(4, (qwl - kt * 64) / 16 + 1) : 4;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    if (DIAG && ks >= nks)
-                        continue;
+                // the pair gradients of key block ks as the bf16 A operand
+                auto grad = [&](int ks) {
                     f32x4 f4;
                     const f32x4 t = scores(kt, base, ks, mm_block(base, KOFF, qf, ks), DIAG, f4);
                     const f32x4 dw = mm_block(base, VOFF, gf, ks);
@@ -555,7 +574,20 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                         const float dcv = sg * __builtin_fmaf(ym, __builtin_fmaf(Ac, dw[r], adl), -Ec);
                         g[r] = dcv * f4[r];
                     }
-                    mm_kt(base, ks, pack_bf16x4(g), acc);
+                    return pack_bf16x4(g);
+                };
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int ks = 2 * h;
+                    if (DIAG && ks >= nks)
+                        continue;
+                    const s16x4 g0 = grad(ks);
+                    if (DIAG && ks + 1 >= nks) {
+                        mm_kt(base, ks, g0, acc);
+                        continue;
+                    }
+                    const s16x4 g1 = grad(ks + 1);
+                    mm_kt2(base, ks, g0, g1, acc);
                 }
               });
             };
@@ -622,10 +654,9 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
               tile_loop(true, [&](int kt, const unsigned char* base, auto diag_tag) {
                 constexpr bool DIAG = decltype(diag_tag)::value;
                 const int nks = DIAG ? min(4, (qwl - kt * 64) / 16 + 1) : 4;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    if (DIAG && ks >= nks)
-                        continue;
+                // the three pair-gradient products of key block ks as bf16 A
+                // operands; the row sums are taken in key order
+                auto grads = [&](int ks, s16x4& p1, s16x4& p2, s16x4& p3) {
                     f32x4 f4;
                     const f32x4 t = scores(kt, base, ks, mm_block(base, KOFF, qf, ks), DIAG, f4);
                     const f32x4 dw = mm_block(base, VOFF, gf, ks);
@@ -648,8 +679,19 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                         g1[r] = g2[r] * h;
                         g3[r] = g2[r] * ym;
                     }
+                    p1 = pack_bf16x4(g1);
+                    p2 = pack_bf16x4(g2);
+                    p3 = pack_bf16x4(g3);
+                };
+                // one key block at a time: pairing them in 16x16x32 products
+                // needs six operands live and spills at this register cap
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    if (DIAG && ks >= nks)
+                        continue;
+                    s16x4 p1, p2, p3;
+                    grads(ks, p1, p2, p3);
                     // one operand read feeds the three products
-                    const s16x4 p1 = pack_bf16x4(g1), p2 = pack_bf16x4(g2), p3 = pack_bf16x4(g3);
 #pragma unroll
                     for (int ds = 0; ds < DS; ++ds) {
                         const bf16x4 bk = lds_read_tr16(base + KOFF + ks * 16 * T::R * 16 + trr[ds]);
@@ -813,11 +855,8 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
 
         auto tile = [&](int qt, const unsigned char* base, auto diag_tag, auto exact_tag) {
             constexpr bool DIAG = decltype(diag_tag)::value;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                // query blocks entirely before this wave's first key see none of it
-                if (DIAG && qt * 64 + 16 * c + 15 < kw0)
-                    continue;
+            // weights and pair gradients of 16-query block c as bf16 A operands
+            auto operands = [&](int c, s16x4& wb, s16x4& gb) {
                 const f32x4 sc = mm_block(base, QOFF, kf, c);   // S[query][key]
                 const f32x4 dw = mm_block(base, GOFF, vf, c);   // dW[query][key]
                 f32x4 w4, g4;
@@ -841,15 +880,53 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
                     w4[r] = ym * y * a.z;
                     g4[r] = sg * __builtin_fmaf(ym, __builtin_fmaf(b.x, dw[r], a.w), -b.y);
                 }
-                const s16x4 wb = pack_bf16x4(w4);
-                const s16x4 gb = pack_bf16x4(g4);
+                wb = pack_bf16x4(w4);
+                gb = pack_bf16x4(g4);
+            };
+            auto mm_one = [&](int c, s16x4 wb, s16x4 gb) {
 #pragma unroll
                 for (int ds = 0; ds < DS; ++ds) {
                     const int off = c * 16 * T::R * 16 + trr[ds];
-                    const bf16x4 bg = lds_read_tr16(base + GOFF + off);
-                    const bf16x4 bq = lds_read_tr16(base + QOFF + off);
-                    adv[ds] = mfma16k16(wb, bg, adv[ds]);
-                    adk[ds] = mfma16k16(gb, bq, adk[ds]);
+                    adv[ds] = mfma16k16(wb, lds_read_tr16(base + GOFF + off), adv[ds]);
+                    adk[ds] = mfma16k16(gb, lds_read_tr16(base + QOFF + off), adk[ds]);
+                }
+            };
+            // d = 128: one block at a time (pairs need 256 VGPRs there)
+            if constexpr (D != 64) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (DIAG && qt * 64 + 16 * c + 15 < kw0)
+                        continue;
+                    s16x4 wb, gb;
+                    operands(c, wb, gb);
+                    mm_one(c, wb, gb);
+                }
+                return;
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int c = 2 * h;
+                // query blocks entirely before this wave's first key see none
+                // of it (a leading run of blocks)
+                if (DIAG && qt * 64 + 16 * (c + 1) + 15 < kw0)
+                    continue;
+                s16x4 wb1, gb1;
+                if (DIAG && qt * 64 + 16 * c + 15 < kw0) {
+                    operands(c + 1, wb1, gb1);
+                    mm_one(c + 1, wb1, gb1);
+                    continue;
+                }
+                s16x4 wb0, gb0;
+                operands(c, wb0, gb0);
+                operands(c + 1, wb1, gb1);
+#pragma unroll
+                for (int ds = 0; ds < DS; ++ds) {
+                    const int off = c * 16 * T::R * 16 + trr[ds];
+                    const int off1 = off + 16 * T::R * 16;
+                    adv[ds] = mfma16k16x2(wb0, wb1, lds_read_tr16(base + GOFF + off),
+                                          lds_read_tr16(base + GOFF + off1), adv[ds]);
+                    adk[ds] = mfma16k16x2(gb0, gb1, lds_read_tr16(base + QOFF + off),
+                                          lds_read_tr16(base + QOFF + off1), adk[ds]);
                 }
             }
         };

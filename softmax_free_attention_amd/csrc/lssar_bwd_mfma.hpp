@@ -683,21 +683,37 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                     p2 = pack_bf16x4(g2);
                     p3 = pack_bf16x4(g3);
                 };
-                // one key block at a time: pairing them in 16x16x32 products
-                // needs six operands live and spills at this register cap
+                // the first product one key block at a time, the other two
+                // for pairs of blocks (all three paired would need six
+                // operands live and spill at this register cap)
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
+                for (int h = 0; h < 2; ++h) {
+                    const int ks = 2 * h;
                     if (DIAG && ks >= nks)
                         continue;
                     s16x4 p1, p2, p3;
                     grads(ks, p1, p2, p3);
-                    // one operand read feeds the three products
+                    const bool one = DIAG && ks + 1 >= nks;
 #pragma unroll
                     for (int ds = 0; ds < DS; ++ds) {
                         const bf16x4 bk = lds_read_tr16(base + KOFF + ks * 16 * T::R * 16 + trr[ds]);
                         acc1[ds] = mfma16k16(p1, bk, acc1[ds]);
-                        acc2[ds] = mfma16k16(p2, bk, acc2[ds]);
-                        acc3[ds] = mfma16k16(p3, bk, acc3[ds]);
+                        if (one) {
+                            acc2[ds] = mfma16k16(p2, bk, acc2[ds]);
+                            acc3[ds] = mfma16k16(p3, bk, acc3[ds]);
+                        }
+                    }
+                    if (one)
+                        continue;
+                    s16x4 q1, q2, q3;
+                    grads(ks + 1, q1, q2, q3);
+#pragma unroll
+                    for (int ds = 0; ds < DS; ++ds) {
+                        const unsigned char* b = base + KOFF + ks * 16 * T::R * 16 + trr[ds];
+                        const bf16x4 b0 = lds_read_tr16(b), b1 = lds_read_tr16(b + 16 * T::R * 16);
+                        acc1[ds] = mfma16k16(q1, b1, acc1[ds]);
+                        acc2[ds] = mfma16k16x2(p2, q2, b0, b1, acc2[ds]);
+                        acc3[ds] = mfma16k16x2(p3, q3, b0, b1, acc3[ds]);
                     }
                 }
               });

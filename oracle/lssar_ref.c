@@ -128,12 +128,19 @@ static void l2_normalise(const double* x, double* y, int d)
 
 /* One output row.  qh: the normalised query row i (0-based row = i-1);
  * kh: all L normalised key rows of the head; v: the head's V; a: scratch of
- * L doubles.  Every j in 1..L is computed and then multiplied by the mask
+ * 2 L doubles.  Every j in 1..L is computed and then multiplied by the mask
  * M'_ij, as the matrix form on the page does.  phi picks the stage-1 map
- * (R4/R14); reweight = 0 skips stage 2 (R15). */
-static void lssar_row(const double* qh, const double* kh, const double* v,
-                      int L, int d, int p, double eps, int phi, int reweight,
-                      int row, double* a, double* out)
+ * (R4/R14); reweight = 0 skips stage 2 (R15).
+ *
+ * Self-check of stage 2: with m the row's largest entry of A (.) N - O,
+ * ReLU(x)^p and (ReLU(x)/m)^p differ by the constant factor m^-p, which the
+ * second L1 normalisation removes, so both give the same weights in exact
+ * arithmetic.  The second form stays in [0, 1] at every p; the literal one
+ * can leave fp64's range (x can reach i - 1).  Returns 0, or 1 when the two
+ * normalised weight rows differ anywhere by more than 1e-12. */
+static int lssar_row(const double* qh, const double* kh, const double* v,
+                     int L, int d, int p, double eps, int phi, int reweight,
+                     int row, double* a, double* out)
 {
     const int i = row + 1;                       /* R2: 1-based row index */
     const double scale = log((double)d) * log((double)i);   /* log d . log N_ij, R1 */
@@ -163,14 +170,20 @@ static void lssar_row(const double* qh, const double* kh, const double* v,
         }
         if (!(m > eps)) {                            /* degenerate row (R10) */
             memset(out, 0, sizeof(double) * (size_t)d);
-            return;
+            return 0;
         }
-        double l1b = 0.0;
+        double* b = a + L;                           /* the rescaled form */
+        double l1b = 0.0, l1c = 0.0;
         for (int j = 0; j < L; ++j) {
+            b[j] = ipow(fmax(a[j], 0.0) / m, p);
+            l1c += b[j];
             double r = a[j] > 0.0 ? a[j] : 0.0;      /* ReLU */
             a[j] = ipow(r, p);                       /* ^p */
             l1b += a[j];
         }
+        for (int j = 0; j < L; ++j)
+            if (!(fabs(a[j] / l1b - b[j] / l1c) <= 1e-12))
+                return 1;
         for (int j = 0; j < L; ++j)                  /* A_i <- A_i / |A_i|_1 */
             a[j] /= l1b;
     }
@@ -183,6 +196,7 @@ static void lssar_row(const double* qh, const double* kh, const double* v,
         for (int e = 0; e < d; ++e)
             out[e] += a[j] * vj[e];
     }
+    return 0;
 }
 
 static int bad_args(const void* q, const void* k, const void* v, const void* out,
@@ -232,24 +246,27 @@ int lssar_ref_head_rows_ex_f64(const double* q, const double* k, const double* v
         return -2;
     }
     normalise_head(q, k, qh, kh, L, d);
-    int fail = 0;
+    int fail = 0, range = 0;
 #pragma omp parallel num_threads(lssar_ref_threads(nthreads))
     {
-        double* a = malloc(sizeof(double) * (size_t)L);
+        double* a = malloc(sizeof(double) * 2 * (size_t)L);
         if (!a) {
 #pragma omp atomic write
             fail = 1;
         } else {
 #pragma omp for schedule(dynamic, 1)
             for (int r = 0; r < nrows; ++r)
-                lssar_row(qh + (size_t)rows[r] * d, kh, v, L, d, p, eps, phi,
-                          reweight, rows[r], a, out + (size_t)r * d);
+                if (lssar_row(qh + (size_t)rows[r] * d, kh, v, L, d, p, eps, phi,
+                              reweight, rows[r], a, out + (size_t)r * d)) {
+#pragma omp atomic write
+                    range = 1;
+                }
         }
         free(a);
     }
     free(qh);
     free(kh);
-    return fail ? -2 : 0;
+    return fail ? -2 : range ? -3 : 0;
 }
 
 int lssar_ref_fwd_ex_f64(const double* q, const double* k, const double* v,
@@ -272,10 +289,10 @@ int lssar_ref_fwd_ex_f64(const double* q, const double* k, const double* v,
     for (long bh = 0; bh < nheads; ++bh)
         normalise_head(q + bh * head, k + bh * head, qh + bh * head,
                        kh + bh * head, L, d);
-    int fail = 0;
+    int fail = 0, range = 0;
 #pragma omp parallel num_threads(nt)
     {
-        double* a = malloc(sizeof(double) * (size_t)L);
+        double* a = malloc(sizeof(double) * 2 * (size_t)L);
         if (!a) {
 #pragma omp atomic write
             fail = 1;
@@ -285,16 +302,19 @@ int lssar_ref_fwd_ex_f64(const double* q, const double* k, const double* v,
             for (long t = 0; t < nheads * L; ++t) {
                 long bh = t / L;
                 int row = (int)(t % L);
-                lssar_row(qh + bh * head + (size_t)row * d, kh + bh * head,
-                          v + bh * head, L, d, p, eps, phi, reweight, row, a,
-                          out + bh * head + (size_t)row * d);
+                if (lssar_row(qh + bh * head + (size_t)row * d, kh + bh * head,
+                              v + bh * head, L, d, p, eps, phi, reweight, row, a,
+                              out + bh * head + (size_t)row * d)) {
+#pragma omp atomic write
+                    range = 1;
+                }
             }
         }
         free(a);
     }
     free(qh);
     free(kh);
-    return fail ? -2 : 0;
+    return fail ? -2 : range ? -3 : 0;
 }
 
 int lssar_ref_head_rows_f64(const double* q, const double* k, const double* v,

@@ -25,7 +25,12 @@ extern "C" {
 
 /* Full forward over all B*H heads and L rows.  nthreads <= 0 uses the
  * OpenMP default.  Returns 0, or -1 on invalid arguments (null pointer,
- * B/H/L/d < 1, p < 1, eps < 0 or NaN), or -2 if scratch allocation fails. */
+ * B/H/L/d < 1, p < 1, eps < 0 or NaN), -2 if scratch allocation fails, or
+ * -3 if a row's literal ReLU^p weights (Key design 2) left fp64's range:
+ * every re-weighted row is also computed with its entries divided by the
+ * row maximum before the power, which the L1 normalisation makes
+ * equivalent, and the two must agree to 1e-12 (the output is then not
+ * trustworthy; x^p can reach (i - 1)^p). */
 int lssar_ref_fwd_f64(const double* q, const double* k, const double* v,
                       double* out, int B, int H, int L, int d, int p,
                       double eps, int nthreads);

@@ -590,9 +590,71 @@ def rowstats_invariants(lib):
     assert np.max(np.abs(st4 - st) / np.maximum(1.0, np.abs(st))) < 1e-13
 
 
+# --------------------------------------------------------------------------
+# The row-sampling entry, and the oracle's own stage-2 self-check
+# --------------------------------------------------------------------------
+
+def rows_entry_matches_forward(lib):
+    """The row-sampling entry (the checker wherever a workload is too large
+    for the full forward) returns bitwise the rows of the full forward, which
+    every other pin checks, for sorted, unsorted and repeated row sets that
+    include the first and the last row, in all three modes."""
+    r = _rng(1500)
+    for (L, d, p) in [(37, 8, 3), (64, 16, 15), (9, 4, 1), (130, 64, 15)]:
+        Q, K, V = (r.standard_normal((L, d)) for _ in range(3))
+        Q[L // 3] = 0.0                               # a degenerate row among them
+        sets = [np.arange(L), r.permutation(L)[: max(1, L // 2)],
+                np.array([L - 1, 0, min(3, L - 1), min(3, L - 1), L - 1, 1, 0]),
+                np.array([L // 3, L - 1]), np.array([0])]
+        for mode in MODES:
+            full = _fwd(lib, Q, K, V, p, mode=mode)
+            for rows in sets:
+                got = oracle.lssar_rows(Q, K, V, rows, p, nthreads=2, lib=lib, phi=mode[0],
+                                        reweight=mode[1])
+                assert got.shape == (len(rows), d)
+                assert np.array_equal(got, full[rows]), \
+                    f"rows entry differs from the forward: L={L} p={p} {mode} rows={rows[:8]}"
+
+
+def rescaled_form_self_check(lib):
+    """Every re-weighted row is also computed with its entries divided by the
+    row maximum m before the power (Key design 2: the factor m^-p cancels in
+    the L1 normalisation), and the oracle refuses (status -3) when the two
+    disagree.  One-hot rows over orthonormal keys at d = 64 reach
+    m = i Softplus(ln 64 ln i) / S1_i - 1 = 13.5 at i = 40, whose literal
+    400th power overflows fp64; at p = 15 both forms agree and the output is
+    the one-hot closed form v_m(i).  (The Sigmoid map keeps m below 1 on
+    these rows, sigma <= 1 against a row mean of at least 1/2, so its
+    literal power cannot overflow and only the closed form is checked.)"""
+    L, d = 40, 64
+    r = _rng(1600)
+    E = _ortho(d, 1601)
+    K = E[:L] * r.uniform(0.5, 3.0, size=(L, 1))
+    mi = [int(r.integers(0, i + 1)) for i in range(L)]
+    Q = np.stack([K[mi[i]] * r.uniform(0.1, 5.0) for i in range(L)])
+    V = r.standard_normal((L, d))
+    for mode in RW_MODES:
+        out = _fwd(lib, Q, K, V, 15, mode=mode)
+        for i in range(3, L):
+            assert np.max(np.abs(out[i] - V[mi[i]])) < 1e-12, f"one-hot row {i + 1} {mode}"
+        if mode[0] != SP:
+            continue
+        refused = 0
+        for call in (lambda: _fwd(lib, Q, K, V, 400, mode=mode),
+                     lambda: oracle.lssar_rows(Q, K, V, [L - 1], 400, nthreads=2, lib=lib,
+                                               phi=mode[0], reweight=mode[1])):
+            try:
+                call()
+            except ValueError as e:
+                assert "status -3" in str(e), str(e)
+                refused += 1
+        assert refused == 2, f"the literal 400th power overflowed unnoticed ({mode})"
+
+
 PINS = [brute_force_matrix_form, row1_is_v1, closed_form_rows, golden_row2_value,
         sigmoid_antisymmetric_pair, onehot_orthonormal, two_way_tie, degenerate_rows,
         v_identity_probe, v_ones, scale_invariance, linearity_in_v, causality,
         permutation_invariance, hard_argmax_limit, bwd_finite_differences,
         bwd_scale_invariance, bwd_dv_is_weights_transposed, bwd_causality_and_row1,
-        bwd_degenerate_rows, rowstats_closed_forms, rowstats_invariants]
+        bwd_degenerate_rows, rowstats_closed_forms, rowstats_invariants,
+        rows_entry_matches_forward, rescaled_form_self_check]

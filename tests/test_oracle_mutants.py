@@ -67,6 +67,12 @@ MUTANTS = [
     ("stats-max-of-softplus", "            smax = s;", "            smax = softplus(s);"),
     ("stats-unscaled", "const double s = scale * dot;", "const double s = dot;"),
     ("stats-normalised", "    st[0] = l1;", "    st[0] = l1 / (double)i;"),
+    # the row-sampling entry and the stage-2 self-check
+    ("rows-row-index", "reweight, rows[r], a, out", "reweight, r, a, out"),
+    ("rows-query-row", "lssar_row(qh + (size_t)rows[r] * d", "lssar_row(qh + (size_t)r * d"),
+    ("selfcheck-off", "if (!(fabs(a[j] / l1b - b[j] / l1c) <= 1e-12))", "if (0)"),
+    ("selfcheck-power", "b[j] = ipow(fmax(a[j], 0.0) / m, p);",
+     "b[j] = ipow(fmax(a[j], 0.0) / m, p - 1);"),
     ("bwd-degenerate-passes", "            continue;                            /* R16: no gradient */",
      "            ;"),
 ]

@@ -30,7 +30,10 @@ backward, lssar_attn_bwd_stats_ws with the row statistics of
 lssar_attn_fwd_stats_ws, and the recomputing lssar_attn_bwd_ws; algorithmic
 TFLOP/s counting 8*d flops per causal pair, the four products dO V^T,
 W^T dO, dC K and dC^T Q; the score recompute is not counted; the training
-forward's time beside the plain forward's).
+forward's time beside the plain forward's) and "configs" (the GPT-2-small
+workload, B8 H12 L1024 d64 p=3, and the wide-head workload, B2 H32 L4096
+d128 p=15 with rank-8 correlated Q and K, each as its own whole step on its
+seeded inputs).
 """
 from __future__ import annotations
 
@@ -227,6 +230,31 @@ def time_variants(q, k, v, p, steps, warmup, eps=1e-4):
     return res
 
 
+def time_configs(names, steps, warmup):
+    """The other full-size workloads, each as its own whole step (prep plus
+    attention kernel, one lssar_attn_fwd_ws call) on its seeded inputs:
+    wall time of K back-to-back steps after a second of untimed load, and
+    the two kernels' mean durations from HIP events."""
+    import lssar_inputs as gen
+    res = {}
+    for name in names:
+        wl = gen.WORKLOADS[name]
+        inp = gen.make_inputs(wl)
+        q, k, v = upload(inp)
+        wall, fwd, prep, _ = time_path(q, k, v, wl.p, steps, warmup, settle_s=1.0, repeats=1)
+        ms = wall / steps * 1e3
+        res[name] = {"B": wl.B, "H": wl.H, "L": wl.L, "d": wl.d, "p": wl.p, "dtype": wl.dtype,
+                     "structure": wl.structure, "ms_per_step": round(ms, 5),
+                     "tflops": round(wl.flops / (ms * 1e-3) / 1e12, 2),
+                     "pct_bf16_peak": round(100 * wl.flops / (ms * 1e-3) / 1e12 /
+                                            PEAK_TFLOPS["bf16"], 3),
+                     "tokens_per_s": round(wl.B * wl.L / (ms * 1e-3), 1),
+                     "kernel_ms": {"lssar_fwd": round(fwd, 5), "lssar_prep": round(prep, 5)},
+                     "kernel_tflops": round(wl.flops / (fwd * 1e-3) / 1e12, 2)}
+        del q, k, v, inp
+    return res
+
+
 def time_decode(name, steps, warmup):
     """Mean time of one decode step (lssar_decode_ws: three kernels) on a
     device-generated cache, HIP events on the launch stream."""
@@ -340,7 +368,43 @@ def cpu_baseline(inp, seconds: float):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{n * len(heads)} of {total_rows} query rows ({n} evenly strided rows in "
                       f"each of {len(heads)} heads), fp64 literal oracle, {dt:.1f} s",
+            "cpu_model": cpu_model(), "one_thread": one_thread_times(),
             "seconds": dt}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def one_thread_times():
+    """The oracle on one thread: the tiny fp32 workload (B1 H1 L128 d64,
+    p=3) in full, and the GPT-2-small workload (B8 H12 L1024 d64, p=3) on 4
+    of its 96 heads, scaled to all 96."""
+    import lssar_inputs as gen
+    import oracle
+    res = {}
+    inp = gen.make_inputs("tiny")
+    t0 = time.perf_counter()
+    oracle.lssar_fwd(inp.q, inp.k, inp.v, inp.wl.p, nthreads=1)
+    res["tiny_s"] = round(time.perf_counter() - t0, 4)
+    inp = gen.make_inputs("gpt2s")
+    heads = [(0, 0), (2, 5), (5, 7), (7, 11)]
+    t0 = time.perf_counter()
+    for b, h in heads:
+        oracle.lssar_fwd(inp.q[b, h], inp.k[b, h], inp.v[b, h], inp.wl.p, nthreads=1)
+    dt = time.perf_counter() - t0
+    nh = inp.wl.B * inp.wl.H
+    res["gpt2s_s"] = round(dt * nh / len(heads), 2)
+    res["gpt2s_sample"] = f"{len(heads)} of {nh} heads in {dt:.2f} s, scaled to {nh}"
+    return res
 
 
 def sweep(steps, warmup):
@@ -374,6 +438,8 @@ def main():
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the GPT-2-small (p=3) and wide-head (d=128) workloads")
     ap.add_argument("--calib-mib", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB (read N, "
                          "write N), the reference kernel for scaling rocprofv3 FETCH/WRITE_SIZE")
@@ -440,6 +506,10 @@ def main():
     if args.cold:
         log("bench: cold-cache steps")
         line["cold"] = time_cold(q, k, v, wl.p, args.steps)
+    if not args.no_configs:
+        log("bench: other workloads")
+        others = [n for n in ("gpt2s", "wide") if n != wl.name]
+        line["configs"] = time_configs(others, args.steps, args.warmup)
     if not args.no_variants:
         log("bench: ablation variants")
         vt = time_variants(q, k, v, wl.p, args.steps, args.warmup)

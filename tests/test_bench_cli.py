@@ -54,3 +54,12 @@ def test_valu_fraction_from_the_record(tmp_path, monkeypatch):
 
 if __name__ == "__main__":
     sys.exit(pytest.main([__file__, "-q"]))
+
+
+def test_cpu_baseline_context():
+    """The CPU model and the oracle's one-thread times reported beside the
+    CPU baseline (host only)."""
+    assert bench.cpu_model() and bench.cpu_model() != ""
+    res = bench.one_thread_times()
+    assert res["tiny_s"] > 0 and res["gpt2s_s"] > 0
+    assert "4 of 96 heads" in res["gpt2s_sample"]

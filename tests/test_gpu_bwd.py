@@ -1,10 +1,12 @@
 """Backward (lssar_attn_bwd_ws) on the HIP path vs the fp64 oracle backward.
 
-Bars, relative to the largest reference gradient entry g_max of each tensor
-(gradients have no natural unit scale): max-abs <= 1e-5 * max(1, g_max) for
-fp32 inputs (the kernels compute in fp64); <= 2e-2 * max(1, g_max) for bf16
-inputs, where every output element is rounded to bf16 (2^-9 relative) and
-the scores come from bf16 inputs with fp32 accumulation, as in the forward.
+Bars (gpu_util.check_grads), per tensor: max-abs <= 1e-5 * max(1, g_max)
+for fp32 inputs (the kernels compute in fp64) and <= 1e-2 * max(1, g_max)
+for bf16 inputs, where every output element is rounded to bf16 (2^-9
+relative) and the scores come from bf16 inputs with fp32 accumulation, as in
+the forward; g_max is the tensor's largest reference entry.  Beside it a
+norm-wise bar, ||err||_F <= 2e-7 (fp32) or 5e-3 (bf16) times ||want||_F,
+holds the ordinary entries of a tensor with outliers to their own size.
 """
 from __future__ import annotations
 
@@ -13,13 +15,11 @@ import pytest
 
 import lssar_inputs as gen
 import oracle
-from gpu_util import to_device, to_host
+from gpu_util import check_grads, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-
-BWD_TOL = {"f32": 1e-5, "bf16": 2e-2}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -48,20 +48,12 @@ def _inputs(L, d, dtype, p, seed, H=2, name="gpt2s"):
     return inp.q, inp.k, inp.v, g
 
 
-def _check(got, want, dtype, what):
-    errs = []
-    for name, a, b in zip(("dq", "dk", "dv"), got, want):
-        scale = max(1.0, float(np.max(np.abs(b))))
-        err = float(np.max(np.abs(a - b)))
-        errs.append(err / scale)
-        assert err <= BWD_TOL[dtype] * scale, \
-            f"{what} {name}: max-abs {err:.3e} > {BWD_TOL[dtype]} * {scale:.3g}"
-    return errs
+_check = check_grads
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("p", [1, 3, 15, 7])
+@pytest.mark.parametrize("p", [1, 2, 3, 15, 7])
 def test_small_shapes_bwd_parity(dtype, d, p):
     for L in (1, 2, 3, 4, 5, 17, 64, 65, 130, 257):
         q, k, v, g = _inputs(L, d, dtype, p, seed=L + 5)
@@ -131,7 +123,7 @@ def test_deterministic():
 
 
 @pytest.mark.parametrize("name,heads", [("gpt2s", [(0, 0), (3, 7), (7, 11)]),
-                                        ("x8_planted", [(0, 5)])])
+                                        ("x8_planted", [(0, 5), (0, 11)])])
 def test_full_workload_sampled_heads(name, heads):
     """Full-size workloads; the oracle backward on a few whole heads."""
     inp = gen.make_inputs(name)

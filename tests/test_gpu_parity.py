@@ -2,9 +2,11 @@
 
 Bars: max-abs 1e-5 for fp32 inputs, 3e-2 for bf16 inputs (fp32
 accumulation).  Small shapes are compared in full (several 64-key tiles and
-128-row query blocks, ragged tails, L = 1..5 edge cases); the five workloads
-at full size are compared on sampled rows, in the launch configuration the
-bench times, plus invariants that hold at any size.
+128-row query blocks, ragged tails, L = 1..5 edge cases).  At full size, in
+the launch configuration the bench times: every row of the GPT-2-small and
+8x-extrapolation workloads, whole heads of the 16x and wide-head workloads
+plus sampled rows across their other heads, and invariants that hold at any
+size.
 """
 from __future__ import annotations
 
@@ -92,7 +94,48 @@ def _sample_rows(wl, meta, rng):
     return out
 
 
-@pytest.mark.parametrize("name", ["gpt2s", "x8_planted", "x16", "wide"])
+def _worst_row(got, want):
+    """Largest per-row max-abs error and the (..., row) index where it is."""
+    err = np.max(np.abs(got - want), axis=-1)
+    idx = np.unravel_index(int(np.argmax(err)), err.shape)
+    return float(err[idx]), tuple(int(x) for x in idx)
+
+
+@pytest.mark.parametrize("name", ["gpt2s", "x8_planted"])
+def test_full_workload_every_row(name):
+    """Every row of the workload against the oracle's full forward."""
+    inp = _full(name)
+    wl = inp.wl
+    print(f"{name}: B{wl.B} H{wl.H} L{wl.L} d{wl.d} p{wl.p}, every row", flush=True)
+    got = _gpu_out(inp)
+    want = oracle.lssar_fwd(inp.q, inp.k, inp.v, wl.p)
+    err, (b, h, r) = _worst_row(got, want)
+    print(f"{name}: all {wl.B * wl.H * wl.L} rows, max-abs {err:.3e} at b={b} h={h} row={r + 1}",
+          flush=True)
+    assert err <= BF16_TOL, f"{name}: max-abs {err:.3e} at b={b} h={h} row={r + 1}"
+    assert np.array_equal(got[:, :, 0], inp.v[:, :, 0].astype(np.float64))
+
+
+@pytest.mark.parametrize("name,heads", [
+    ("x16", [(0, 0), (0, 11)]),
+    ("wide", [(0, 0), (0, 9), (0, 17), (0, 31), (1, 2), (1, 15), (1, 24), (1, 31)])])
+def test_full_workload_whole_heads(name, heads):
+    """Whole heads of the larger workloads against the oracle's forward."""
+    inp = _full(name)
+    wl = inp.wl
+    print(f"{name}: B{wl.B} H{wl.H} L{wl.L} d{wl.d} p{wl.p}, heads {heads}", flush=True)
+    got = _gpu_out(inp)
+    worst = (0.0, None)
+    for b, h in heads:
+        want = oracle.lssar_fwd(inp.q[b, h], inp.k[b, h], inp.v[b, h], wl.p)
+        err, (r,) = _worst_row(got[b, h], want)
+        print(f"{name} b={b} h={h}: {wl.L} rows, max-abs {err:.3e} at row {r + 1}", flush=True)
+        assert err <= BF16_TOL, f"{name} b={b} h={h}: max-abs {err:.3e} at row {r + 1}"
+        worst = max(worst, (err, (b, h, r + 1)), key=lambda x: x[0])
+    print(f"{name}: whole heads max-abs {worst[0]:.3e} at (b, h, row) {worst[1]}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["x16", "wide"])
 def test_full_workload_sampled_parity(name):
     inp = _full(name)
     wl = inp.wl

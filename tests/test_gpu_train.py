@@ -13,8 +13,8 @@ product of the factors (1 + e^-|s|) (each rounded product shifts the log by
 at most u).  m_i moves by |ds| plus the roundings of the two fp32 factors.
 The test allows twice these bounds.
 
-Gradients: the bars of the recomputing backward (relative to each tensor's
-largest reference entry).
+Gradients: the bars of the recomputing backward (gpu_util.check_grads:
+max-abs relative to each tensor's largest reference entry, and norm-wise).
 """
 from __future__ import annotations
 
@@ -25,13 +25,12 @@ import pytest
 
 import lssar_inputs as gen
 import oracle
-from gpu_util import to_device, to_host
+from gpu_util import GRAD_MAXABS, check_grads, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-BWD_TOL = {"f32": 1e-5, "bf16": 2e-2}
 U32 = 2.0 ** -24
 
 
@@ -97,15 +96,7 @@ def _inputs(L, d, dtype, p, seed, H=2, B=1, name="gpt2s"):
     return inp.q, inp.k, inp.v, g
 
 
-def _check_grads(got, want, dtype, what):
-    errs = []
-    for name, a, b in zip(("dq", "dk", "dv"), got, want):
-        scale = max(1.0, float(np.max(np.abs(b))))
-        err = float(np.max(np.abs(a - b)))
-        errs.append(err / scale)
-        assert err <= BWD_TOL[dtype] * scale, \
-            f"{what} {name}: max-abs {err:.3e} > {BWD_TOL[dtype]} * {scale:.3g}"
-    return errs
+_check_grads = check_grads
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -130,7 +121,7 @@ def test_stats_and_output_small_shapes(dtype, d):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("p", [1, 3, 15])
+@pytest.mark.parametrize("p", [1, 2, 3, 15, 7])
 def test_saved_stats_backward_parity(dtype, d, p):
     for L in (1, 2, 3, 4, 5, 17, 64, 65, 130, 257):
         q, k, v, g = _inputs(L, d, dtype, p, seed=L + 5)
@@ -177,7 +168,14 @@ def test_deep_block_among_plain_blocks():
     """bf16, d = 64, p = 15: one query block whose rows all score below -4
     (keys anti-aligned with those queries) among blocks whose rows do not.
     The one-pass kernel takes the exact Softplus on that block and plain
-    log2(1 + 2^t) on the others within the same launch."""
+    log2(1 + 2^t) on the others within the same launch.
+
+    Max-abs bar 2e-2 (norm-wise bar as everywhere): keys 128..191 collect
+    pair gradients from the deep rows, whose scale factor A_i is large, and
+    from the ordinary rows after them, with opposite signs; each enters the
+    dk product rounded to bf16, and the largest dk entry (about 305) keeps
+    an error of 1.2e-2 of itself (measured) while the tensor's norm-wise
+    error is 3.4e-3, as on ordinary inputs."""
     r = np.random.default_rng(21)
     L, d = 256, 64
     u = r.standard_normal(d)
@@ -196,7 +194,8 @@ def test_deep_block_among_plain_blocks():
     dev = [to_device(a, "bf16") for a in (q, k, v, g)]
     out, st = run_train_fwd(*dev[:3], 15)
     got = [to_host(x) for x in run_stats_bwd(*dev[:3], out, dev[3], st, 15)]
-    errs = _check_grads(got, oracle.lssar_bwd(q, k, v, g, 15), "bf16", "deep block")
+    errs = _check_grads(got, oracle.lssar_bwd(q, k, v, g, 15), "bf16", "deep block",
+                        maxabs=2e-2)
     print(f"deep block among plain blocks: grads rel {max(errs):.2e}", flush=True)
 
 
@@ -240,5 +239,5 @@ def test_full_workload_sampled_heads(name, heads):
         worst_g = max(worst_g, max(errs))
     for a, b_ in zip(got, (to_host(t) for t in rec)):
         scale = max(1.0, float(np.max(np.abs(b_))))
-        assert float(np.max(np.abs(a - b_))) <= 2e-2 * scale
+        assert float(np.max(np.abs(a - b_))) <= GRAD_MAXABS[wl.dtype] * scale
     print(f"{name}: stats err/bound {worst_s:.3f}, grads rel {worst_g:.2e}", flush=True)

@@ -236,6 +236,21 @@ int lssar_last_hip_error(void);
 /* ABI version: 10000 * major + 100 * minor + patch. */
 int lssar_version(void);
 
+/* Dispatch order of the bf16 forward kernel (lssar_attn_fwd_ws and its
+ * variants, d = 64 or 128) for the shape B, H, L: no part of the method,
+ * a query of how the work is spread over the GPU.  The kernel has one
+ * workgroup per 64-row query block; each of the 8 XCDs takes a contiguous
+ * slice of the heads' block pairs {pi, nqb - 1 - pi} (equal work per XCD)
+ * and runs its blocks largest first; workgroup w runs on XCD w % 8.
+ *  - Returns the number of workgroups launched (>= B * H * ceil(L / 64)),
+ *    or LSSAR_EINVAL for a shape the forward rejects.
+ *  - items: HOST int array, or NULL to query the count only; else it needs
+ *    room for the returned count (capacity, in elements; LSSAR_EINVAL if
+ *    smaller) and receives for workgroup w the block (b H + h) nqb + qb it
+ *    computes, or -1 for a workgroup that exits at once.
+ *  - No HIP call; thread-safe. */
+long long lssar_fwd_schedule(int B, int H, int L, int* items, long long capacity);
+
 #ifdef __cplusplus
 }
 #endif

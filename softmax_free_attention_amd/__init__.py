@@ -27,6 +27,7 @@ __all__ = [
     "lssar_decode_workspace_bytes", "lssar_decode_ws", "decode_workspace_for",
     "lssar_bwd_workspace_bytes", "lssar_attn_bwd_ws", "bwd_workspace_for",
     "lssar_attn_fwd_stats_ws", "lssar_attn_bwd_stats_ws", "stats_for",
+    "lssar_fwd_schedule",
 ]
 
 LSSAR_F32, LSSAR_BF16 = 0, 1
@@ -89,6 +90,9 @@ def lib():
         L.lssar_last_hip_error.restype = i
         L.lssar_version.argtypes = []
         L.lssar_version.restype = i
+        L.lssar_fwd_schedule.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_int),
+                                         ctypes.c_longlong]
+        L.lssar_fwd_schedule.restype = ctypes.c_longlong
         _lib = L
     return _lib
 
@@ -103,6 +107,19 @@ def lssar_last_hip_error() -> int:
 
 def lssar_version() -> int:
     return int(lib().lssar_version())
+
+
+def lssar_fwd_schedule(B: int, H: int, L: int):
+    """The bf16 forward's dispatch order: a list with, for each workgroup,
+    the query block (b H + h) nqb + qb it computes, or -1 (exits at once)."""
+    n = int(lib().lssar_fwd_schedule(B, H, L, None, 0))
+    if n < 0:
+        raise LssarError(n, "lssar_fwd_schedule")
+    buf = (ctypes.c_int * n)()
+    rc = int(lib().lssar_fwd_schedule(B, H, L, buf, n))
+    if rc != n:
+        raise LssarError(rc, "lssar_fwd_schedule")
+    return list(buf)
 
 
 def lssar_workspace_bytes(B: int, H: int, L: int, d: int, dtype: int) -> int:

@@ -46,11 +46,12 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout: [fk: inverse key norm per key row, fp32 for bf16 inputs
-// and fp64 for fp32 inputs][Vt: bf16 V^T, bf16 inputs only]
+// and fp64 for fp32 inputs][Vt: bf16 V^T, bf16 inputs only][sched: the
+// attention kernel's (head, block) per workgroup, int2, bf16 inputs only]
 struct Layout {
-    size_t fk_bytes, vt_bytes;
+    size_t fk_bytes, vt_bytes, sched_bytes;
     int Lp;
-    size_t total() const { return fk_bytes + vt_bytes; }
+    size_t total() const { return fk_bytes + vt_bytes + sched_bytes; }
 };
 
 Layout layout(long long B, long long H, long long L, int d, int dtype)
@@ -59,6 +60,11 @@ Layout layout(long long B, long long H, long long L, int d, int dtype)
     w.Lp = (int)((L + lssar::kBK - 1) / lssar::kBK * lssar::kBK);
     w.fk_bytes = round256((size_t)((dtype == LSSAR_F32 ? 8 : 4) * B * H * L));
     w.vt_bytes = dtype == LSSAR_BF16 ? round256((size_t)(B * H * d) * (size_t)w.Lp * 2) : 0;
+    w.sched_bytes = 0;
+    if (dtype == LSSAR_BF16) {
+        const int nqb = (int)((L + lssar::kBQ16 - 1) / lssar::kBQ16);
+        w.sched_bytes = round256((size_t)lssar::FwdSched((int)(B * H), nqb).grid() * 8);
+    }
     return w;
 }
 
@@ -77,7 +83,9 @@ int validate_shape(int B, int H, int L, int d, int dtype)
         return LSSAR_EUNSUPPORTED;
     const long long bh = (long long)B * H;
     const long long nqb = (L + lssar::kBQ16 - 1) / lssar::kBQ16;
-    if (bh > (1LL << 31) - 1 || bh * nqb > (1LL << 31) - 1 || bh * L * d > (1LL << 46))
+    // the forward's grid (lssar_sched.hpp) has at most B H (nqb + 1) + 16
+    // workgroups
+    if (bh > (1LL << 31) - 1 || bh * (nqb + 1) + 16 > (1LL << 31) - 1 || bh * L * d > (1LL << 46))
         return LSSAR_EINVAL;
     return LSSAR_OK;
 }
@@ -126,12 +134,13 @@ void launch_knorm_f32(const void* k, double* fk, long nrows, hipStream_t s)
 }
 
 template <int D>
-void launch_prep_bf16(const void* k, const void* v, float* fk, void* vt, int BH, int L, int Lp,
-                      hipStream_t s)
+void launch_prep_bf16(const void* k, const void* v, float* fk, void* vt, int2* sched, int BH,
+                      int L, int Lp, hipStream_t s)
 {
     hipLaunchKernelGGL((lssar::lssar_prep_bf16_kernel<D>), dim3(Lp / lssar::kBK, BH),
                        dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(k),
-                       static_cast<const __bf16*>(v), fk, static_cast<__bf16*>(vt), L, Lp);
+                       static_cast<const __bf16*>(v), fk, static_cast<__bf16*>(vt), sched, BH,
+                       L, Lp);
 }
 
 int run_prep(const void* k, const void* v, void* ws, int B, int H, int L, int d, int dtype,
@@ -142,10 +151,12 @@ int run_prep(const void* k, const void* v, void* ws, int B, int H, int L, int d,
     if (dtype == LSSAR_BF16) {
         float* fk = static_cast<float*>(ws);
         void* vt = static_cast<unsigned char*>(ws) + w.fk_bytes;
+        int2* sched =
+            reinterpret_cast<int2*>(static_cast<unsigned char*>(ws) + w.fk_bytes + w.vt_bytes);
         if (d == 64)
-            launch_prep_bf16<64>(k, v, fk, vt, B * H, L, w.Lp, s);
+            launch_prep_bf16<64>(k, v, fk, vt, sched, B * H, L, w.Lp, s);
         else
-            launch_prep_bf16<128>(k, v, fk, vt, B * H, L, w.Lp, s);
+            launch_prep_bf16<128>(k, v, fk, vt, sched, B * H, L, w.Lp, s);
     } else {
         double* fk = static_cast<double*>(ws);
         if (d == 64)
@@ -169,11 +180,13 @@ void launch_fwd(const void* q, const void* k, const void* v, void* ws, void* out
         const int nqb = (L + lssar::kBQ16 - 1) / lssar::kBQ16;
         const __bf16* vt =
             reinterpret_cast<const __bf16*>(static_cast<unsigned char*>(ws) + w.fk_bytes);
+        const int2* sched = reinterpret_cast<const int2*>(static_cast<unsigned char*>(ws) +
+                                                          w.fk_bytes + w.vt_bytes);
         hipLaunchKernelGGL((lssar::lssar_fwd_bf16_kernel<D, P, PHI, RW>),
-                           dim3((unsigned)(nqb * BH)),
+                           dim3((unsigned)lssar::FwdSched(BH, nqb).grid()),
                            dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(q),
-                           static_cast<const __bf16*>(k), vt, static_cast<__bf16*>(out), fk, BH,
-                           L, w.Lp, nqb, lam_scale, eps, p, stats);
+                           static_cast<const __bf16*>(k), vt, static_cast<__bf16*>(out), fk,
+                           sched, L, w.Lp, lam_scale, eps, p, stats);
     } else {
         const int nqb = (L + lssar::kBQ32 - 1) / lssar::kBQ32;
         hipLaunchKernelGGL((lssar::lssar_fwd_f32_kernel<D, P, PHI, RW>),
@@ -756,6 +769,24 @@ const char* lssar_status_str(int status)
 
 int lssar_last_hip_error(void) { return g_last_hip_error; }
 
-int lssar_version(void) { return 700; }
+int lssar_version(void) { return 800; }
+
+long long lssar_fwd_schedule(int B, int H, int L, int* items, long long capacity)
+{
+    if (validate_shape(B, H, L, 64, LSSAR_BF16) != LSSAR_OK)
+        return LSSAR_EINVAL;
+    const int BH = B * H, nqb = (L + lssar::kBQ16 - 1) / lssar::kBQ16;
+    const lssar::FwdSched sc(BH, nqb);
+    const long long grid = sc.grid();
+    if (items) {
+        if (capacity < grid)
+            return LSSAR_EINVAL;
+        for (long long w = 0; w < grid; ++w) {
+            int bh, qb;
+            items[w] = sc.item((int)w, bh, qb) ? bh * nqb + qb : -1;
+        }
+    }
+    return grid;
+}
 
 }  // extern "C"

@@ -37,7 +37,8 @@
 // over the keys with weights phi(s_ij) normalised by their sum).
 //
 // Tiling (bf16): a workgroup of 4 waves owns one 64-row query block of one
-// (batch, head), 16 rows per wave; the largest blocks are dispatched first.  Keys stream through LDS in tiles
+// (batch, head), 16 rows per wave; each XCD takes a slice of the heads and
+// runs its blocks largest first (lssar_sched.hpp).  Keys stream through LDS in tiles
 // of 64 (double-buffered at d = 64, one buffer at d = 128).  Scores are
 // computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: each lane
 // then holds 4 keys of ONE query row, so row sums stay per lane until one
@@ -54,6 +55,8 @@
 #include <stdint.h>
 
 #include <type_traits>
+
+#include "lssar_sched.hpp"
 
 namespace lssar {
 
@@ -316,16 +319,31 @@ __device__ __forceinline__ int vt_key(int pos)
 //    rows of Vt hold Lp (L rounded up to 64) entries.
 // V goes through LDS: each thread then gathers two adjacent dims of 8 keys
 // with 4-byte LDS reads and writes two 16-byte pieces of V^T.
+//  * sched[w] = (bh, qb) for the attention kernel's workgroup w
+//    (lssar_sched.hpp): each workgroup enters the query block qb = kb of
+//    its head (the blocks and the 64-key blocks coincide), and the first
+//    workgroup also marks the empty indices (-1, -1).
 template <int D>
 __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
     const __bf16* __restrict__ K, const __bf16* __restrict__ V, float* __restrict__ fk,
-    __bf16* __restrict__ Vt, int L, int Lp)
+    __bf16* __restrict__ Vt, int2* __restrict__ sched, int BH, int L, int Lp)
 {
     constexpr int RS = D + 2;                  // LDS row stride (elements), odd word count
     constexpr int LPR = D / 8;                 // lanes per key row for the norms
     __shared__ __attribute__((aligned(16))) uint32_t tile[64 * RS / 2];
     const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
     const size_t hoff = (size_t)bh * L * D;
+
+    if (tid == 0) {
+        const FwdSched sc(BH, Lp / kBK);
+        sched[sc.index_of(bh, kb)] = make_int2(bh, kb);
+        if (kb == 0 && bh == 0) {
+            const int m = (int)(sc.grid() / kSchedXcds);
+            for (int x = 0; x < kSchedXcds; ++x)
+                for (int l = sc.count(x); l < m; ++l)
+                    sched[l * kSchedXcds + x] = make_int2(-1, -1);
+        }
+    }
 
     // key norms: 64 rows x LPR lanes, 16 bytes per lane per step
 #pragma unroll
@@ -391,12 +409,12 @@ __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
 //
 // A workgroup of 4 waves owns one query block of 64 rows of one (batch,
 // head); each wave owns 16 rows (lane & 15).  The causal work of block qb
-// grows with qb, so workgroups are numbered largest block first across all
-// heads and the hardware fills freed slots with ever smaller blocks (greedy
-// longest-first).  Pairing blocks {nqb-1-pi, pi} per workgroup instead gives
-// every workgroup the same work, but half as many waves: at B = 1, H = 12,
-// L = 8192 that leaves 3 of the 4 wave slots per SIMD filled, and measured
-// 15% slower.  Keys stream through LDS in tiles of 64 with
+// grows with qb, so each XCD runs the blocks of its slice of heads largest
+// first and the hardware fills freed slots with ever smaller blocks (greedy
+// longest-first; lssar_sched.hpp).  Pairing blocks {nqb-1-pi, pi} per
+// workgroup instead gives every workgroup the same work, but half as many
+// waves: at B = 1, H = 12, L = 8192 that leaves 3 of the 4 wave slots per
+// SIMD filled, and measured 15% slower.  Keys stream through LDS in tiles of 64 with
 // buffer loads that write LDS directly (16 bytes per lane, zero past the end
 // of the tensor), double-buffered.  LDS tiles are arrays of 16-byte slots,
 // XOR-swizzled so that the 16 lanes reading one MFMA operand hit distinct
@@ -411,19 +429,23 @@ __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
 // t = -inf, which adds exactly 0 to every sum in both passes (2^-inf = 0,
 // max(-inf, 0) = 0; in pass 2 Softplus2 = 0 gives y = clamp(-tau c) = 0).
 
-template <int D>
+// One tile of BK keys: K (BK rows of D), V^T (D rows of BK keys) and the BK
+// key factors (the area holds 64; the loader writes 64).
+template <int D, int BK>
 struct Bf16Tile {
     static constexpr int R = D / 8;                       // 16-byte slots per K row
-    static constexpr int KBYTES = kBK * D * 2;            // K tile
-    static constexpr int VBYTES = D * kBK * 2;            // V^T tile
-    static constexpr int FBYTES = kBK * 4;                // key factors
+    static constexpr int VS = BK / 8;                     // 16-byte slots per V^T row
+    static constexpr int KBYTES = BK * D * 2;             // K tile
+    static constexpr int VBYTES = D * BK * 2;             // V^T tile
+    static constexpr int FBYTES = 64 * 4;                 // key factors
     static constexpr int BYTES = KBYTES + VBYTES + FBYTES;
     static constexpr int KLOADS = KBYTES / 1024 / kWaves; // 1 KB wave-loads per wave
     static constexpr int VLOADS = VBYTES / 1024 / kWaves;
     // XOR swizzle of a K row's slots (key & 15 is all that matters)
     __device__ static int kswz(int key) { return R == 8 ? ((key >> 1) & 7) : (key & 15); }
-    // XOR swizzle of a V^T row's 8 slots
-    __device__ static int vswz(int e) { return (e >> 1) & 7; }
+    // XOR swizzle of a V^T row's VS slots: the 16 lanes reading one MFMA
+    // operand (rows e..e+15, one slot each) then cover all 64 banks
+    __device__ static int vswz(int e) { return VS == 8 ? ((e >> 1) & 7) : ((e >> 2) & 3); }
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -473,27 +495,31 @@ __device__ __forceinline__ void load_row_stats(const double* ST, size_t row, C& 
 
 // PHI: stage-1 map; RW: false = stage 1 only (no pass 1, weights phi(t)).
 // ST: null, or where the Softplus method stores each row's statistics.
-// Tiles: double-buffered at d = 64, where registers cap the occupancy at 4
-// waves per SIMD anyway; one buffer at d = 128, with registers capped for 3
-// waves per SIMD, which the 66 KB of two buffers would not allow (measured:
-// 5% faster than two buffers at 2 waves).
+// Tiles: two buffers of 64 keys at d = 64 and of 32 keys at d = 128, 33 KB
+// of LDS either way, so four workgroups (4 waves per SIMD) fit a CU.  At
+// d = 128 a 32-key tile costs a wave as many MFMAs as a 64-key tile at
+// d = 64; 64-key tiles there allowed one buffer only (two need 66 KB and
+// halve the occupancy), which left every tile load exposed.
 template <int D, int P, int PHI, bool RW>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel(
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ VT, __bf16* __restrict__ O,
-    const float* __restrict__ FK, int BH, int L, int Lp, int nqb,
+    const float* __restrict__ FK, const int2* __restrict__ sched, int L, int Lp,
     double lam_scale, float eps, int p_rt, double* __restrict__ ST)
 {
     static_assert(D == 64 || D == 128, "head dim");
-    using T = Bf16Tile<D>;
+    constexpr int BK = D == 64 ? 64 : 32;      // keys per tile
+    using T = Bf16Tile<D, BK>;
     constexpr int DC = D / 32;                 // MFMA k-steps over d
     constexpr int DS = D / 16;                 // 16-row blocks of O^T
+    constexpr int KS = BK / 16;                // 16-key score blocks per tile
+    constexpr int C2 = BK / 32;                // 32-key P.V steps per tile
 
     // One LDS object: the NB tile buffers, then the deep-row flags.  (A
     // second __shared__ object makes the compiler wait for the in-flight
     // LDS-direct loads before every LDS read in the tile loops.)
-    constexpr int NB = D == 64 ? 2 : 1;
+    constexpr int NB = 2;
     __shared__ __attribute__((aligned(1024))) unsigned char lds[NB * T::BYTES + 16];
     auto smem = [&](int buf) { return lds + buf * T::BYTES; };
     int* const flags = reinterpret_cast<int*>(lds + NB * T::BYTES);
@@ -503,9 +529,13 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int row16 = lane & 15, grp = lane >> 4;
-    // one query block per workgroup, the largest first across all heads
-    const int qb = nqb - 1 - (int)blockIdx.x / BH;
-    const int bh = (int)blockIdx.x % BH;
+    // one query block per workgroup, from the prep kernel's table: XCD-local
+    // slices of the heads, the largest block first within each
+    // (lssar_sched.hpp); an empty index exits
+    const int2 it = sched[blockIdx.x];
+    const int bh = it.x, qb = it.y;
+    if (bh < 0)
+        return;
     const size_t hoff = (size_t)bh * L * D;
     const __bf16* Qh = Q + hoff;
     __bf16* Oh = O + hoff;
@@ -529,33 +559,33 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
 #pragma unroll
     for (int n = 0; n < T::VLOADS; ++n) {
         const int slot = (wave * T::VLOADS + n) * 64 + lane;
-        const int e = slot / 8, c = (slot % 8) ^ T::vswz(e);
+        const int e = slot / T::VS, c = (slot % T::VS) ^ T::vswz(e);
         vld[n] = (e * Lp + c * 8) * 2;
     }
     // per-lane LDS byte offsets of the MFMA operand slots (16 ks / 16 ds rows
     // further on are constant offsets)
-    int krd[DC], vrd[2];
+    int krd[DC], vrd[C2];
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
         krd[dc] = (row16 * T::R + ((4 * dc + grp) ^ T::kswz(row16))) * 16;
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2)
-        vrd[c2] = T::KBYTES + (row16 * 8 + ((4 * c2 + grp) ^ T::vswz(row16))) * 16;
+    for (int c2 = 0; c2 < C2; ++c2)
+        vrd[c2] = T::KBYTES + (row16 * T::VS + ((4 * c2 + grp) ^ T::vswz(row16))) * 16;
 
     auto issue = [&](int kt, int buf, bool with_v) {
         unsigned char* base = smem(buf);
 #pragma unroll
         for (int n = 0; n < T::KLOADS; ++n)
             load16_to_lds(kbase, kbytes, base + (wave * T::KLOADS + n) * 1024, kld[n],
-                            kt * kBK * D * 2);
+                            kt * BK * D * 2);
         if (with_v) {
 #pragma unroll
             for (int n = 0; n < T::VLOADS; ++n)
                 load16_to_lds(vbase, vbytes, base + T::KBYTES + (wave * T::VLOADS + n) * 1024,
-                                vld[n], kt * kBK * 2);
+                                vld[n], kt * BK * 2);
         }
         if (wave == 0)
-            load4_to_lds(fbase, fbytes, base + T::KBYTES + T::VBYTES, lane * 4, kt * kBK * 4);
+            load4_to_lds(fbase, fbytes, base + T::KBYTES + T::VBYTES, lane * 4, kt * BK * 4);
     };
 
     const __bf16 one = (__bf16)1.0f;
@@ -573,7 +603,10 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
         const int qw0 = q0 + wave * kMQ16;         // first query row of this wave
         const int qwl = min(qw0 + kMQ16 - 1, L - 1);  // last valid query row
         const bool wave_active = qw0 < L;
-        const int ntiles = qb + 1;
+        // key tiles up to the block's last row; tiles from kdiag on reach
+        // into the block (one at d = 64, up to two at d = 128)
+        const int ntiles = (min(L, q0 + kBQ16) + BK - 1) / BK;
+        const int kdiag = q0 / BK;
         const int qi = qw0 + row16;                // this lane's query row (0-based)
 
         // ---- query rows: B operand of S^T = K Q^T, and the row factor ----
@@ -617,7 +650,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
                 base + T::KBYTES + T::VBYTES + (16 * ks + 4 * grp) * 4);
             f32x4 t = acc * (f4 * lam);
             if (diag) {
-                const int k0 = kt * kBK + 16 * ks + 4 * grp;
+                const int k0 = kt * BK + 16 * ks + 4 * grp;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     t[r] = (k0 + r <= qi) ? t[r] : -INFINITY;
@@ -634,6 +667,13 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
             return fmaxf(x, __shfl_xor(x, 32));
         };
 
+        // 16-key blocks of tile kt with a key at or before the wave's last
+        // row (0 when the whole tile lies after it)
+        auto diag_blocks = [&](int kt) {
+            const int rel = qwl - kt * BK;
+            return rel < 0 ? 0 : min(KS, rel / 16 + 1);
+        };
+
         // ---------------- pass 1: S1 and the row max of the scores ----------------
         float s1 = 0.0f;
         float tmax = -INFINITY;
@@ -641,15 +681,15 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
             constexpr bool DIAG = decltype(diag_tag)::value;
             constexpr int KIND = decltype(kind_tag)::value;
             // 16-key blocks with at least one key <= the wave's last row
-            const int nks = DIAG ? min(4, (qwl - kt * kBK) / 16 + 1) : 4;
-            f32x4 acc[4];
+            const int nks = DIAG ? diag_blocks(kt) : KS;
+            f32x4 acc[KS];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
+            for (int ks = 0; ks < KS; ++ks)
                 if (!DIAG || ks < nks)
                     acc[ks] = qk_block(base, ks);
             float pos_sum = 0.0f, prod = 1.0f;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 0; ks < KS; ++ks) {
                 if (DIAG && ks >= nks)
                     continue;
                 const f32x4 t = scale_block(kt, base, ks, acc[ks], DIAG);
@@ -687,36 +727,31 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
         };
         // Tiles 0..ntiles-1 of K (and V^T) through LDS; body runs on every
         // tile that reaches the wave's rows (diagonal tiles masked).
-        // Tiles 0..ntiles-2 lie wholly before every row of the block and the
-        // last tile (keys 64 qb..64 qb + 63) holds its diagonal, so the loop
-        // runs the unmasked body and the diagonal tile follows it: with both
-        // bodies inside the loop, their accumulators were copied back at
-        // every iteration (20 moves per tile in pass 2).
+        // Tiles 0..kdiag-1 lie wholly before every row of the block and the
+        // rest hold its diagonal, so the loop runs the unmasked body and the
+        // diagonal tiles follow it: with both bodies inside the loop, their
+        // accumulators were copied back at every iteration (20 moves per
+        // tile in pass 2).
         auto tile_loop = [&](bool with_v, auto body) {
             auto step = [&](int kt, auto diag_tag) {
-                int buf = 0;
-                if constexpr (NB == 2) {
-                    buf = kt & 1;
-                    __builtin_amdgcn_s_waitcnt(0);
-                    __syncthreads();               // tile kt landed; buf^1 free
-                    if (kt + 1 < ntiles)
-                        issue(kt + 1, buf ^ 1, with_v);
-                } else {
-                    __syncthreads();               // readers of the previous tile done
-                    issue(kt, 0, with_v);
-                    __builtin_amdgcn_s_waitcnt(0);
-                    __syncthreads();               // tile kt landed
-                }
+                const int buf = kt & 1;
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();                   // tile kt landed; buf^1 free
+                if (kt + 1 < ntiles)
+                    issue(kt + 1, buf ^ 1, with_v);
                 if (wave_active)
                     body(kt, smem(buf), diag_tag);
             };
-            if constexpr (NB == 2) {
-                __syncthreads();                   // earlier readers done with the buffers
-                issue(0, 0, with_v);
-            }
-            for (int kt = 0; kt + 1 < ntiles; ++kt)
+            __syncthreads();                       // earlier readers done with the buffers
+            issue(0, 0, with_v);
+            for (int kt = 0; kt < kdiag; ++kt)
                 step(kt, std::false_type{});
-            step(ntiles - 1, std::true_type{});
+            if constexpr (BK == kBQ16) {
+                step(kdiag, std::true_type{});     // the one diagonal tile
+            } else {
+                for (int kt = kdiag; kt < ntiles; ++kt)
+                    step(kt, std::true_type{});
+            }
         };
         auto run_pass1 = [&](auto kind_tag) {
             tile_loop(false, [&](int kt, const unsigned char* base, auto diag_tag) {
@@ -781,14 +816,14 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
 
         auto pass2_tile = [&](int kt, const unsigned char* base, auto diag_tag) {
             constexpr bool DIAG = decltype(diag_tag)::value;
-            const int nks = DIAG ? min(4, (qwl - kt * kBK) / 16 + 1) : 4;
-            f32x4 acc[4];
+            const int nks = DIAG ? diag_blocks(kt) : KS;
+            f32x4 acc[KS];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
+            for (int ks = 0; ks < KS; ++ks)
                 if (!DIAG || ks < nks)
                     acc[ks] = qk_block(base, ks);
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
+            for (int c2 = 0; c2 < C2; ++c2) {
                 if (DIAG && 2 * c2 >= nks)
                     continue;
                 const f32x4 w0 = weights(scale_block(kt, base, 2 * c2, acc[2 * c2], DIAG));
@@ -802,7 +837,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 3))) void lssar_fwd_bf16_kernel
 #pragma unroll
                 for (int ds = 0; ds < DS; ++ds) {
                     const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + vrd[c2] +
-                                                                      ds * 16 * 8 * 16);
+                                                                      ds * 16 * T::VS * 16);
                     oacc[ds] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfr, oacc[ds], 0, 0, 0);
                 }
                 dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bfr, dacc, 0, 0, 0);

@@ -65,7 +65,7 @@ def test_library_has_no_oracle_dependency(L):
 
 
 def test_version_and_status_strings(L):
-    assert sfa.lssar_version() == 700
+    assert sfa.lssar_version() == 800
     assert sfa.lssar_status_str(0) == "ok"
     for st in (-1, -2, -3, -4, 7):
         s = sfa.lssar_status_str(st)
@@ -79,9 +79,14 @@ def test_workspace_bytes(L):
     assert sfa.lssar_workspace_bytes(2, 3, 5, 128, sfa.LSSAR_F32) == 256
     assert sfa.lssar_workspace_bytes(1, 1, 100, 64, sfa.LSSAR_F32) == 1024
     assert sfa.lssar_workspace_bytes(1, 1, 32, 64, sfa.LSSAR_F32) == 256
-    # bf16: plus V^T with rows padded to a multiple of 64 keys
-    assert sfa.lssar_workspace_bytes(1, 12, 8192, 64, sfa.LSSAR_BF16) == 4 * 12 * 8192 + 12 * 64 * 8192 * 2
-    assert sfa.lssar_workspace_bytes(2, 3, 77, 128, sfa.LSSAR_BF16) == 2048 + 6 * 128 * 128 * 2
+    # bf16: plus V^T with rows padded to a multiple of 64 keys, plus the
+    # attention kernel's dispatch table (8 bytes per workgroup, rounded up)
+    def r256(x):
+        return (x + 255) // 256 * 256
+    assert sfa.lssar_workspace_bytes(1, 12, 8192, 64, sfa.LSSAR_BF16) == \
+        4 * 12 * 8192 + 12 * 64 * 8192 * 2 + r256(8 * 1536)
+    assert sfa.lssar_workspace_bytes(2, 3, 77, 128, sfa.LSSAR_BF16) == \
+        2048 + 6 * 128 * 128 * 2 + r256(8 * len(sfa.lssar_fwd_schedule(2, 3, 77)))
     assert sfa.lssar_workspace_bytes(0, 1, 1, 64, 0) == 0
     assert sfa.lssar_workspace_bytes(1, 1, 1, 96, 0) == 0
     assert sfa.lssar_workspace_bytes(1, 1, 1, 64, 5) == 0
@@ -297,3 +302,31 @@ def test_stats_entries_validate_before_any_hip_call(L):
     assert bwd(p=0) == sfa.LSSAR_EINVAL
     assert bwd(ws=0) == sfa.LSSAR_EWORKSPACE
     assert sfa.lssar_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("B,H,Lq", [(1, 12, 8192), (8, 12, 1024), (2, 32, 4096), (1, 12, 16384),
+                                   (1, 1, 1), (1, 1, 100), (3, 5, 1000), (1, 7, 2113),
+                                   (16, 1, 65), (1, 200, 64)])
+def test_forward_schedule(L, B, H, Lq):
+    """The bf16 forward's dispatch order (host query of the kernels' own
+    schedule code): every query block exactly once; workgroup w on XCD w % 8;
+    each XCD runs its blocks largest first; the XCDs' work (key tiles) is
+    equal up to one pair of blocks; each XCD touches about B H / 8 heads."""
+    nqb = (Lq + 63) // 64
+    items = sfa.lssar_fwd_schedule(B, H, Lq)
+    real = [x for x in items if x >= 0]
+    assert sorted(real) == list(range(B * H * nqb))
+    assert len(items) % 8 == 0
+    work = [0] * 8
+    heads = [set() for _ in range(8)]
+    for x in range(8):
+        sizes = [items[w] % nqb + 1 for w in range(x, len(items), 8) if items[w] >= 0]
+        assert sizes == sorted(sizes, reverse=True)
+        # empty indices only after an XCD's last block
+        tail = [items[w] for w in range(x, len(items), 8)]
+        assert all(t < 0 for t in tail[len(sizes):])
+        work[x] = sum(sizes)
+        heads[x] = {items[w] // nqb for w in range(x, len(items), 8) if items[w] >= 0}
+    assert max(work) - min(work) <= nqb + 1
+    bh = B * H
+    assert max(len(h) for h in heads) <= -(-bh // 8) + 2

@@ -222,8 +222,9 @@ def test_bitwise_determinism_and_entry_points_agree():
 
 def test_prep_workspace_contents():
     """The prep step writes 1/max(|k_j|, 1e-12) per key row (fp32 for bf16,
-    fp64 for fp32 inputs) and, for bf16, V^T with
-    every 64-key block permuted for the attention kernel, zero past L."""
+    fp64 for fp32 inputs) and, for bf16, V^T with every 64-key block
+    permuted for the attention kernel, zero past L, and the attention
+    kernel's dispatch table."""
     import softmax_free_attention_amd as sfa
     for dtype, d in (("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)):
         L = 77
@@ -252,6 +253,26 @@ def test_prep_workspace_contents():
             vp = np.zeros((2, 3, Lp, d), np.float32)
             vp[:, :, :L] = inp.v
             assert np.array_equal(vtt, np.swapaxes(vp[:, :, key], -1, -2))
+            # the attention kernel's dispatch table: (head, block) per
+            # workgroup, as the host-side schedule query gives it
+            items = sfa.lssar_fwd_schedule(2, 3, L)
+            soff = off + (2 * 3 * d * Lp * 2 + 255) // 256 * 256
+            tab = raw[soff:soff + 8 * len(items)].view(np.int32).reshape(-1, 2)
+            nqb = (L + 63) // 64
+            want_tab = np.array([[x // nqb, x % nqb] if x >= 0 else [-1, -1] for x in items])
+            assert np.array_equal(tab, want_tab)
+    for B, H, L in ((1, 12, 8192), (2, 32, 4096), (1, 5, 3000)):
+        k = torch.zeros((B, H, L, 64), dtype=torch.bfloat16, device="cuda")
+        ws = sfa.workspace_for(k)
+        sfa.lssar_prep(k, k, ws)
+        torch.cuda.synchronize()
+        raw = ws.cpu().numpy()
+        off = (4 * B * H * L + 255) // 256 * 256 + (B * H * 64 * ((L + 63) // 64 * 64) * 2 + 255) // 256 * 256
+        items = sfa.lssar_fwd_schedule(B, H, L)
+        tab = raw[off:off + 8 * len(items)].view(np.int32).reshape(-1, 2)
+        nqb = (L + 63) // 64
+        want_tab = np.array([[x // nqb, x % nqb] if x >= 0 else [-1, -1] for x in items])
+        assert np.array_equal(tab, want_tab), (B, H, L)
 
 
 def test_causality_and_scale_invariance():

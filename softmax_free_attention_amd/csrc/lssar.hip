@@ -45,13 +45,14 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace layout: [fk: inverse key norm per key row, fp32 for bf16 inputs
-// and fp64 for fp32 inputs][Vt: bf16 V^T, bf16 inputs only][sched: the
-// attention kernel's (head, block) per workgroup, int2, bf16 inputs only]
+// Workspace layout: [fk: key factor per key row, fp32 for bf16 inputs and
+// fp64 for fp32 inputs][Vt: bf16 V^T, bf16 inputs only][K16: f16 copy of K,
+// rows scaled by powers of two, bf16 inputs only][sched: the attention
+// kernel's (head, block) per workgroup, int2, bf16 inputs only]
 struct Layout {
-    size_t fk_bytes, vt_bytes, sched_bytes;
+    size_t fk_bytes, vt_bytes, k16_bytes, sched_bytes;
     int Lp;
-    size_t total() const { return fk_bytes + vt_bytes + sched_bytes; }
+    size_t total() const { return fk_bytes + vt_bytes + k16_bytes + sched_bytes; }
 };
 
 Layout layout(long long B, long long H, long long L, int d, int dtype)
@@ -60,6 +61,7 @@ Layout layout(long long B, long long H, long long L, int d, int dtype)
     w.Lp = (int)((L + lssar::kBK - 1) / lssar::kBK * lssar::kBK);
     w.fk_bytes = round256((size_t)((dtype == LSSAR_F32 ? 8 : 4) * B * H * L));
     w.vt_bytes = dtype == LSSAR_BF16 ? round256((size_t)(B * H * d) * (size_t)w.Lp * 2) : 0;
+    w.k16_bytes = dtype == LSSAR_BF16 ? round256((size_t)(B * H * d) * (size_t)L * 2) : 0;
     w.sched_bytes = 0;
     if (dtype == LSSAR_BF16) {
         const int nqb = (int)((L + lssar::kBQ16 - 1) / lssar::kBQ16);
@@ -134,13 +136,28 @@ void launch_knorm_f32(const void* k, double* fk, long nrows, hipStream_t s)
 }
 
 template <int D>
-void launch_prep_bf16(const void* k, const void* v, float* fk, void* vt, int2* sched, int BH,
-                      int L, int Lp, hipStream_t s)
+void launch_prep_bf16(const void* k, const void* v, float* fk, void* vt, void* k16, int2* sched,
+                      int BH, int L, int Lp, hipStream_t s)
 {
     hipLaunchKernelGGL((lssar::lssar_prep_bf16_kernel<D>), dim3(Lp / lssar::kBK, BH),
                        dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(k),
-                       static_cast<const __bf16*>(v), fk, static_cast<__bf16*>(vt), sched, BH,
-                       L, Lp);
+                       static_cast<const __bf16*>(v), fk, static_cast<__bf16*>(vt),
+                       static_cast<_Float16*>(k16), sched, BH, L, Lp);
+}
+
+// Where the bf16 workspace parts start.
+struct WsParts {
+    float* fk;
+    __bf16* vt;
+    _Float16* k16;
+    int2* sched;
+};
+WsParts ws_parts(void* ws, const Layout& w)
+{
+    unsigned char* b = static_cast<unsigned char*>(ws);
+    return {reinterpret_cast<float*>(b), reinterpret_cast<__bf16*>(b + w.fk_bytes),
+            reinterpret_cast<_Float16*>(b + w.fk_bytes + w.vt_bytes),
+            reinterpret_cast<int2*>(b + w.fk_bytes + w.vt_bytes + w.k16_bytes)};
 }
 
 int run_prep(const void* k, const void* v, void* ws, int B, int H, int L, int d, int dtype,
@@ -149,14 +166,11 @@ int run_prep(const void* k, const void* v, void* ws, int B, int H, int L, int d,
     const Layout w = layout(B, H, L, d, dtype);
     const long nrows = (long)B * H * L;
     if (dtype == LSSAR_BF16) {
-        float* fk = static_cast<float*>(ws);
-        void* vt = static_cast<unsigned char*>(ws) + w.fk_bytes;
-        int2* sched =
-            reinterpret_cast<int2*>(static_cast<unsigned char*>(ws) + w.fk_bytes + w.vt_bytes);
+        const WsParts pt = ws_parts(ws, w);
         if (d == 64)
-            launch_prep_bf16<64>(k, v, fk, vt, sched, B * H, L, w.Lp, s);
+            launch_prep_bf16<64>(k, v, pt.fk, pt.vt, pt.k16, pt.sched, B * H, L, w.Lp, s);
         else
-            launch_prep_bf16<128>(k, v, fk, vt, sched, B * H, L, w.Lp, s);
+            launch_prep_bf16<128>(k, v, pt.fk, pt.vt, pt.k16, pt.sched, B * H, L, w.Lp, s);
     } else {
         double* fk = static_cast<double*>(ws);
         if (d == 64)
@@ -176,17 +190,23 @@ void launch_fwd(const void* q, const void* k, const void* v, void* ws, void* out
 {
     const Layout w = layout(1, BH, L, D, dtype);
     if (dtype == LSSAR_BF16) {
-        const float* fk = static_cast<const float*>(ws);
         const int nqb = (L + lssar::kBQ16 - 1) / lssar::kBQ16;
-        const __bf16* vt =
-            reinterpret_cast<const __bf16*>(static_cast<unsigned char*>(ws) + w.fk_bytes);
-        const int2* sched = reinterpret_cast<const int2*>(static_cast<unsigned char*>(ws) +
-                                                          w.fk_bytes + w.vt_bytes);
-        hipLaunchKernelGGL((lssar::lssar_fwd_bf16_kernel<D, P, PHI, RW>),
-                           dim3((unsigned)lssar::FwdSched(BH, nqb).grid()),
-                           dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(q),
-                           static_cast<const __bf16*>(k), vt, static_cast<__bf16*>(out), fk,
-                           sched, L, w.Lp, lam_scale, eps, p, stats);
+        const WsParts pt = ws_parts(ws, w);
+        const dim3 grid((unsigned)lssar::FwdSched(BH, nqb).grid());
+        // the training forward (row statistics) computes exact scores
+        if constexpr (PHI == lssar::kPhiSoftplus && RW) {
+            if (stats) {
+                hipLaunchKernelGGL((lssar::lssar_fwd_bf16_kernel<D, P, PHI, RW, true>), grid,
+                                   dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(q),
+                                   pt.k16, pt.vt, static_cast<__bf16*>(out), pt.fk, pt.sched, L,
+                                   w.Lp, lam_scale, eps, p, stats);
+                return;
+            }
+        }
+        hipLaunchKernelGGL((lssar::lssar_fwd_bf16_kernel<D, P, PHI, RW, false>), grid,
+                           dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(q), pt.k16,
+                           pt.vt, static_cast<__bf16*>(out), pt.fk, pt.sched, L, w.Lp, lam_scale,
+                           eps, p, nullptr);
     } else {
         const int nqb = (L + lssar::kBQ32 - 1) / lssar::kBQ32;
         hipLaunchKernelGGL((lssar::lssar_fwd_f32_kernel<D, P, PHI, RW>),

@@ -63,6 +63,7 @@ namespace lssar {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -121,6 +122,16 @@ __device__ __forceinline__ float phi2(float t)
 // is not tracked there).
 constexpr float kDeep = -4.0f;
 constexpr float kDeepMean = 1.0f / 1024.0f;
+
+// Conditioning of a re-weighted row.  The fast query operand (lambda_i q^_i
+// rounded to f16, 2^-11 relative per element) moves a score by up to
+// 2^-11 lambda_i, and the re-weighting turns a score error dt into a
+// relative weight error of about p dt / (y (sp_max - tau)): the row's
+// kappa_i = p lambda_i / (sp_max - tau) (base-2 units) scales it.  A row
+// with kappa_i above kCondMax has its block computed again from the exact
+// query rows.  Long rows of ordinary inputs have kappa near 40 at p = 15;
+// rows of a few keys with nearly tied scores can have any kappa.
+constexpr float kCondMax = 100.0f;
 
 __device__ __forceinline__ float softplus2_acc(float t)
 {
@@ -313,8 +324,23 @@ __device__ __forceinline__ int vt_key(int pos)
     return (pos & 32) + (((pos >> 2) & 1) << 4) + (((pos >> 3) & 3) << 2) + (pos & 3);
 }
 
+// Exponent e that brings a row whose largest magnitude is mx into
+// [2^14, 2^15) when scaled by 2^-e (0 for a zero row): every bf16 value of
+// the row is then an f16 value (no overflow; a value below 2^-29 mx goes
+// subnormal, an error under 2^-24 of the row's largest product).
+__device__ __forceinline__ int f16_row_exponent(float mx)
+{
+    int ex;
+    frexpf(mx, &ex);
+    return mx > 0.0f ? ex - 15 : 0;
+}
+
 // Prep for the bf16 kernel, one workgroup per (64-key block kb, head bh):
-//  * fk[bh*L + j] = 1 / max(|k_j|_2, 1e-12) for the block's keys (fp64 sum);
+//  * K16[bh][j] = k_j 2^-e_j in f16, exact (e_j from f16_row_exponent): the
+//    attention kernel's MFMA operand for K;
+//  * fk[bh*L + j] = 2^e_j / max(|k_j|_2, 1e-12) for the block's keys (fp64
+//    sum of squares, one rounding to fp32), so that fk_j (q . K16_j) =
+//    (q . k_j) / |k_j|;
 //  * Vt[bh][e][kb*64 + vt_pos(j)] = V[bh][kb*64 + j][e], zero for keys >= L;
 //    rows of Vt hold Lp (L rounded up to 64) entries.
 // V goes through LDS: each thread then gathers two adjacent dims of 8 keys
@@ -326,7 +352,8 @@ __device__ __forceinline__ int vt_key(int pos)
 template <int D>
 __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
     const __bf16* __restrict__ K, const __bf16* __restrict__ V, float* __restrict__ fk,
-    __bf16* __restrict__ Vt, int2* __restrict__ sched, int BH, int L, int Lp)
+    __bf16* __restrict__ Vt, _Float16* __restrict__ K16, int2* __restrict__ sched, int BH, int L,
+    int Lp)
 {
     constexpr int RS = D + 2;                  // LDS row stride (elements), odd word count
     constexpr int LPR = D / 8;                 // lanes per key row for the norms
@@ -352,20 +379,35 @@ __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
         const int key = c / LPR, sub = c % LPR;
         const int kg = kb * 64 + key;
         double ss = 0.0;
-        if (kg < L) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(K + hoff + (size_t)kg * D + sub * 8);
+        float mx = 0.0f;
+        float xv[8];
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (kg < L)
+            w = *reinterpret_cast<const u32x4*>(K + hoff + (size_t)kg * D + sub * 8);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const double x = bf16lo(w[e]), y = bf16hi(w[e]);
-                ss = fma(x, x, ss);
-                ss = fma(y, y, ss);
-            }
+        for (int e = 0; e < 4; ++e) {
+            xv[2 * e] = bf16lo(w[e]);
+            xv[2 * e + 1] = bf16hi(w[e]);
+            ss = fma((double)xv[2 * e], (double)xv[2 * e], ss);
+            ss = fma((double)xv[2 * e + 1], (double)xv[2 * e + 1], ss);
+            mx = fmaxf(mx, fmaxf(fabsf(xv[2 * e]), fabsf(xv[2 * e + 1])));
         }
 #pragma unroll
-        for (int m = LPR / 2; m >= 1; m >>= 1)
+        for (int m = LPR / 2; m >= 1; m >>= 1) {
             ss += __shfl_xor(ss, m, LPR);
-        if (kg < L && sub == 0)
-            fk[(size_t)bh * L + kg] = (float)(1.0 / fmax(sqrt(ss), 1e-12));
+            mx = fmaxf(mx, __shfl_xor(mx, m, LPR));
+        }
+        const int ex = f16_row_exponent(mx);
+        if (kg < L) {
+            const float sc = ldexpf(1.0f, -ex);
+            f16x8 h;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                h[i] = (_Float16)(xv[i] * sc);
+            *reinterpret_cast<f16x8*>(K16 + hoff + (size_t)kg * D + sub * 8) = h;
+            if (sub == 0)
+                fk[(size_t)bh * L + kg] = (float)ldexp(1.0 / fmax(sqrt(ss), 1e-12), ex);
+        }
     }
 
     // V block -> LDS (row stride RS elements: 4-byte aligned rows)
@@ -500,10 +542,20 @@ __device__ __forceinline__ void load_row_stats(const double* ST, size_t row, C& 
 // d = 128 a 32-key tile costs a wave as many MFMAs as a 64-key tile at
 // d = 64; 64-key tiles there allowed one buffer only (two need 66 KB and
 // halve the occupancy), which left every tile load exposed.
-template <int D, int P, int PHI, bool RW>
+//
+// Scores.  The prep kernel's K16 rows are exact (k_j scaled by 2^-e_j) and
+// fk_j = 2^e_j / |k_j|.  The query operand is either
+//  * fast: f16(lambda_i q_i / |q_i|), the row factor folded in and rounded
+//    to f16 once (2^-12 relative per element), so that t = acc * fk_j: one
+//    multiply per pair instead of two in each pass; or
+//  * exact: q_i 2^-e_i, exact in f16, with t = acc * (fk_j * lambda_i'),
+//    the scores of the raw inputs with fp32 accumulation.
+// The deep-row redo and the training forward (EXACT: its row statistics
+// feed the backward) take the exact operand; the plain forward the fast one.
+template <int D, int P, int PHI, bool RW, bool EXACT>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+    const __bf16* __restrict__ Q, const _Float16* __restrict__ K16,
     const __bf16* __restrict__ VT, __bf16* __restrict__ O,
     const float* __restrict__ FK, const int2* __restrict__ sched, int L, int Lp,
     double lam_scale, float eps, int p_rt, double* __restrict__ ST)
@@ -541,7 +593,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
     __bf16* Oh = O + hoff;
 
     // this head's K, V^T and key factors; buffer reads past them return zeros
-    const void* kbase = K + hoff;
+    const void* kbase = K16 + hoff;
     const unsigned kbytes = (unsigned)L * D * 2u;
     const void* vbase = VT + (size_t)bh * D * Lp;
     const unsigned vbytes = (unsigned)D * Lp * 2u;
@@ -596,9 +648,11 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
     if (tid == 0)
         flags[0] = 0;
 
-    // The query block; REDO: computed again with softplus2_acc (deep rows).
+    // The query block; REDO: computed again from the exact query operand,
+    // and for Softplus with softplus2_acc (deep or ill-conditioned rows).
     auto block_body = [&](auto redo_tag) {
         constexpr bool REDO = decltype(redo_tag)::value;
+        constexpr bool FAST = !REDO && !EXACT;     // query operand (see above)
         const int q0 = qb * kBQ16;
         const int qw0 = q0 + wave * kMQ16;         // first query row of this wave
         const int qwl = min(qw0 + kMQ16 - 1, L - 1);  // last valid query row
@@ -610,27 +664,45 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
         const int qi = qw0 + row16;                // this lane's query row (0-based)
 
         // ---- query rows: B operand of S^T = K Q^T, and the row factor ----
-        bf16x8 qf[DC];
-        float lam;
+        f16x8 qf[DC];
+        float lam = 0.0f;
+        float lam_row;                             // lambda_i = log2(e) ln d ln i
         {
-            float ss = 0.0f;
+            float ss = 0.0f, mx = 0.0f;
+            u32x4 w[DC];
 #pragma unroll
             for (int dc = 0; dc < DC; ++dc) {
-                u32x4 w = {0u, 0u, 0u, 0u};
+                w[dc] = u32x4{0u, 0u, 0u, 0u};
                 if (qi < L)
-                    w = *reinterpret_cast<const u32x4*>(Qh + (size_t)qi * D + 32 * dc + 8 * grp);
+                    w[dc] = *reinterpret_cast<const u32x4*>(Qh + (size_t)qi * D + 32 * dc + 8 * grp);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float a = bf16lo(w[e]), b = bf16hi(w[e]);
+                    float a = bf16lo(w[dc][e]), b = bf16hi(w[dc][e]);
                     ss = __builtin_fmaf(a, a, ss);
                     ss = __builtin_fmaf(b, b, ss);
+                    mx = fmaxf(mx, fmaxf(fabsf(a), fabsf(b)));
                 }
-                qf[dc] = __builtin_bit_cast(bf16x8, w);
             }
             ss += __shfl_xor(ss, 16);
             ss += __shfl_xor(ss, 32);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
             // log2(e) ln d ln i / max(|q_i|, 1e-12)  (Key design 1: log d . log N)
-            lam = (float)query_factor(lam_scale, qi + 1, (double)ss);
+            const double lamd = query_factor(lam_scale, qi + 1, (double)ss);
+            lam_row = (float)(lam_scale * log((double)(qi + 1)));
+            // fast: lambda_i q^_i rounded to f16; exact: q_i 2^-e_i and the
+            // factor lambda_i 2^e_i / |q_i| applied to the accumulator
+            const int ex = f16_row_exponent(mx);
+            const float sc = FAST ? (float)lamd : ldexpf(1.0f, -ex);
+            if constexpr (!FAST)
+                lam = (float)ldexp(lamd, ex);
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    qf[dc][2 * e] = (_Float16)(bf16lo(w[dc][e]) * sc);
+                    qf[dc][2 * e + 1] = (_Float16)(bf16hi(w[dc][e]) * sc);
+                }
         }
 
         // scores of 16-key block ks: acc[r] = k_(16ks+4grp+r) . q_(row16)
@@ -638,17 +710,22 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int dc = 0; dc < DC; ++dc) {
-                const bf16x8 a =
-                    *reinterpret_cast<const bf16x8*>(base + krd[dc] + ks * 16 * T::R * 16);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[dc], acc, 0, 0, 0);
+                const f16x8 a =
+                    *reinterpret_cast<const f16x8*>(base + krd[dc] + ks * 16 * T::R * 16);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[dc], acc, 0, 0, 0);
             }
             return acc;
         };
-        // t = acc * lam * f_key; masked (t = -inf) on diagonal tiles
+        // t = acc * f_key (fast) or acc * lam * f_key (exact); masked
+        // (t = -inf) on diagonal tiles
         auto scale_block = [&](int kt, const unsigned char* base, int ks, f32x4 acc, bool diag) {
             const f32x4 f4 = *reinterpret_cast<const f32x4*>(
                 base + T::KBYTES + T::VBYTES + (16 * ks + 4 * grp) * 4);
-            f32x4 t = acc * (f4 * lam);
+            f32x4 t;
+            if constexpr (FAST)
+                t = acc * f4;
+            else
+                t = acc * (f4 * lam);
             if (diag) {
                 const int k0 = kt * BK + 16 * ks + 4 * grp;
 #pragma unroll
@@ -759,21 +836,28 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
             });
         };
 
+        constexpr bool ACC = REDO && PHI == kPhiSoftplus;   // softplus2_acc
         RowConst rc = {0.0f, 0.0f, false};
         if constexpr (RW) {
-            if constexpr (REDO)
+            if constexpr (ACC)
                 run_pass1(std::integral_constant<int, kPass1Acc>{});
             else
                 run_pass1(std::integral_constant<int, kPass1Sum>{});
             const float trow = row_max(tmax);
             const float s1r = row_sum(s1);
-            if constexpr (REDO) {
+            if constexpr (ACC) {
                 rc = row_constants_sp(qi + 1, s1r, softplus2_acc(trow), eps);
             } else {
                 rc = row_constants<PHI>(qi + 1, s1r, trow, eps);
-                if constexpr (PHI == kPhiSoftplus)
+                if constexpr (PHI == kPhiSoftplus && !REDO)
                     if (qi < L && trow < kDeep)
                         flags[0] = 1;
+            }
+            // kappa_i = p lambda_i c_i
+            if constexpr (FAST) {
+                const float pf = (float)(P > 0 ? P : p_rt);
+                if (qi < L && pf * lam_row * rc.c > kCondMax)
+                    flags[0] = 1;
             }
             // a redone block stores again, after its first store
             if constexpr (PHI == kPhiSoftplus)
@@ -790,7 +874,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
 
         auto weights = [&](f32x4 t) {
             f32x4 e, w;
-            if constexpr (REDO) {
+            if constexpr (ACC) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     e[r] = softplus2_acc(t[r]);
@@ -862,7 +946,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
     };
 
     block_body(std::false_type{});
-    if constexpr (PHI == kPhiSoftplus) {
+    if constexpr (PHI == kPhiSoftplus || (RW && !EXACT)) {
         __syncthreads();                           // every lane's flag store is done
         if (flags[0])
             block_body(std::true_type{});

@@ -83,10 +83,12 @@ def test_workspace_bytes(L):
     # attention kernel's dispatch table (8 bytes per workgroup, rounded up)
     def r256(x):
         return (x + 255) // 256 * 256
+    # and the f16 copy of K
     assert sfa.lssar_workspace_bytes(1, 12, 8192, 64, sfa.LSSAR_BF16) == \
-        4 * 12 * 8192 + 12 * 64 * 8192 * 2 + r256(8 * 1536)
+        4 * 12 * 8192 + 2 * 12 * 64 * 8192 * 2 + r256(8 * 1536)
     assert sfa.lssar_workspace_bytes(2, 3, 77, 128, sfa.LSSAR_BF16) == \
-        2048 + 6 * 128 * 128 * 2 + r256(8 * len(sfa.lssar_fwd_schedule(2, 3, 77)))
+        2048 + 6 * 128 * 128 * 2 + r256(6 * 77 * 128 * 2) + \
+        r256(8 * len(sfa.lssar_fwd_schedule(2, 3, 77)))
     assert sfa.lssar_workspace_bytes(0, 1, 1, 64, 0) == 0
     assert sfa.lssar_workspace_bytes(1, 1, 1, 96, 0) == 0
     assert sfa.lssar_workspace_bytes(1, 1, 1, 64, 5) == 0

@@ -221,9 +221,10 @@ def test_bitwise_determinism_and_entry_points_agree():
 
 
 def test_prep_workspace_contents():
-    """The prep step writes 1/max(|k_j|, 1e-12) per key row (fp32 for bf16,
-    fp64 for fp32 inputs) and, for bf16, V^T with every 64-key block
-    permuted for the attention kernel, zero past L, and the attention
+    """The prep step writes 1/max(|k_j|, 1e-12) per key row (fp64 for fp32
+    inputs) and, for bf16: V^T with every 64-key block permuted for the
+    attention kernel, zero past L; the exact f16 copy of K (rows scaled by
+    powers of two) with the key factor 2^e_j / |k_j|; and the attention
     kernel's dispatch table."""
     import softmax_free_attention_amd as sfa
     for dtype, d in (("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)):
@@ -240,7 +241,8 @@ def test_prep_workspace_contents():
         fdt = np.float32 if dtype == "bf16" else np.float64
         fk = raw[:fdt().itemsize * nrow].view(fdt).reshape(2, 3, L)
         want = 1.0 / np.maximum(np.linalg.norm(k.astype(np.float64), axis=-1), 1e-12)
-        assert np.max(np.abs(fk / want - 1.0)) < (1e-6 if dtype == "bf16" else 1e-14)
+        if dtype == "f32":
+            assert np.max(np.abs(fk / want - 1.0)) < 1e-14
         if dtype == "bf16":
             Lp = 128
             off = (4 * nrow + 255) // 256 * 256
@@ -253,10 +255,19 @@ def test_prep_workspace_contents():
             vp = np.zeros((2, 3, Lp, d), np.float32)
             vp[:, :, :L] = inp.v
             assert np.array_equal(vtt, np.swapaxes(vp[:, :, key], -1, -2))
+            # K16: each key row scaled by the power of two that brings its
+            # largest magnitude into [2^14, 2^15), exactly, in f16; the key
+            # factor carries that power
+            koff = off + (2 * 3 * d * Lp * 2 + 255) // 256 * 256
+            k16 = raw[koff:koff + 2 * 3 * L * d * 2].view(np.float16).reshape(2, 3, L, d)
+            mx = np.abs(k).max(axis=-1)
+            ex = np.where(mx > 0, np.frexp(mx)[1] - 15, 0)
+            assert np.array_equal(k16.astype(np.float64), k * np.ldexp(1.0, -ex)[..., None])
+            assert np.max(np.abs(fk / (want * np.ldexp(1.0, ex)) - 1.0)) < 1e-6
             # the attention kernel's dispatch table: (head, block) per
             # workgroup, as the host-side schedule query gives it
             items = sfa.lssar_fwd_schedule(2, 3, L)
-            soff = off + (2 * 3 * d * Lp * 2 + 255) // 256 * 256
+            soff = koff + (2 * 3 * L * d * 2 + 255) // 256 * 256
             tab = raw[soff:soff + 8 * len(items)].view(np.int32).reshape(-1, 2)
             nqb = (L + 63) // 64
             want_tab = np.array([[x // nqb, x % nqb] if x >= 0 else [-1, -1] for x in items])
@@ -267,7 +278,9 @@ def test_prep_workspace_contents():
         sfa.lssar_prep(k, k, ws)
         torch.cuda.synchronize()
         raw = ws.cpu().numpy()
-        off = (4 * B * H * L + 255) // 256 * 256 + (B * H * 64 * ((L + 63) // 64 * 64) * 2 + 255) // 256 * 256
+        off = (4 * B * H * L + 255) // 256 * 256 + \
+            (B * H * 64 * ((L + 63) // 64 * 64) * 2 + 255) // 256 * 256 + \
+            (B * H * L * 64 * 2 + 255) // 256 * 256
         items = sfa.lssar_fwd_schedule(B, H, L)
         tab = raw[off:off + 8 * len(items)].view(np.int32).reshape(-1, 2)
         nqb = (L + 63) // 64

@@ -25,7 +25,7 @@ import pytest
 
 import lssar_inputs as gen
 import oracle
-from gpu_util import GRAD_MAXABS, check_grads, to_device, to_host
+from gpu_util import GRAD_MAXABS, check_grads, to_device, to_host, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -102,8 +102,12 @@ _check_grads = check_grads
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_stats_and_output_small_shapes(dtype, d):
-    """Statistics against the oracle's; the output is bitwise that of
-    lssar_attn_fwd_ws (the statistics only add stores)."""
+    """Statistics against the oracle's, and the output against the oracle's
+    forward.  fp32 inputs: the output is bitwise that of lssar_attn_fwd_ws
+    (the statistics only add stores).  bf16 inputs: the training forward
+    computes its scores from the exact query rows, lssar_attn_fwd_ws from
+    query rows with the row factor folded in and rounded to f16, so the two
+    agree to the forward's bar only."""
     import softmax_free_attention_amd as sfa
     for L in (1, 2, 3, 4, 5, 17, 64, 65, 130, 257):
         q, k, v, _ = _inputs(L, d, dtype, 15, seed=L + 11)
@@ -112,8 +116,11 @@ def test_stats_and_output_small_shapes(dtype, d):
         ref = torch.empty_like(dev[0])
         sfa.lssar_attn_fwd_ws(*dev, ref, sfa.workspace_for(dev[0]), p=15)
         torch.cuda.synchronize()
-        assert torch.equal(out.view(torch.int8) if dtype == "bf16" else out,
-                           ref.view(torch.int8) if dtype == "bf16" else ref)
+        if dtype == "f32":
+            assert torch.equal(out, ref)
+        want = oracle.lssar_fwd(q, k, v, 15)
+        err = float(np.max(np.abs(to_host(out) - want)))
+        assert err <= tol_for(dtype), f"{dtype} d={d} L={L}: output max-abs {err:.3e}"
         worst = check_stats(st.cpu().numpy(), oracle.lssar_rowstats(q, k), d, dtype,
                             f"{dtype} d={d} L={L}")
         print(f"stats {dtype} d={d} L={L}: worst err/bound {worst:.3f}", flush=True)

@@ -72,11 +72,12 @@ enum {
                                 lssar_last_hip_error() */
 };
 
-/* Workspace for every entry point that takes one, in bytes: one inverse key
- * norm per key row (fp32 for bf16 inputs: 4*B*H*L; fp64 for fp32 inputs:
- * 8*B*H*L; rounded up to 256), plus for bf16 inputs a transposed copy of V
- * (B*H*d*Lp bf16, Lp = L rounded up to 64, rounded up to 256).  Returns 0
- * for invalid sizes. */
+/* Workspace for every forward entry point that takes one, in bytes, each
+ * part rounded up to 256: one key factor per key row (fp32 for bf16 inputs:
+ * 4*B*H*L; fp64 for fp32 inputs: 8*B*H*L); for bf16 inputs also a
+ * transposed copy of V (B*H*d*Lp bf16, Lp = L rounded up to 64), an f16
+ * copy of K (B*H*L*d f16) and the attention kernel's dispatch table (8
+ * bytes per workgroup, lssar_fwd_schedule).  Returns 0 for invalid sizes. */
 size_t lssar_workspace_bytes(int B, int H, int L, int d, int dtype);
 
 /* LSSAR causal attention forward (Key designs 1-3 above) with a
@@ -96,10 +97,12 @@ int lssar_attn_fwd(const void* q, const void* k, const void* v, void* out,
                    void* stream);
 
 /* The prep step alone (the prep kernels).  Writes into the workspace the
- * factors fk[bh*L + j] = 1 / max(|k_j|_2, 1e-12) (Key design 1's
- * K_j <- K_j / |K_j|_2, kept as a factor of the score; fp32 for bf16
- * inputs, fp64 for fp32 inputs) and, for bf16 inputs, V transposed per head
- * for the attention kernel.  Workspace rules as for
+ * key factors (Key design 1's K_j <- K_j / |K_j|_2, kept as a factor of the
+ * score): for fp32 inputs fk[bh*L + j] = 1 / max(|k_j|_2, 1e-12) in fp64;
+ * for bf16 inputs, with e_j the power of two that brings row j's largest
+ * magnitude into [2^14, 2^15), the exact f16 row k_j 2^-e_j and
+ * fk[bh*L + j] = 2^e_j / max(|k_j|_2, 1e-12) in fp32, V transposed per
+ * head, and the attention kernel's dispatch table.  Workspace rules as for
  * lssar_attn_fwd_ws; a bad workspace is LSSAR_EWORKSPACE. */
 int lssar_prep(const void* k, const void* v, void* workspace,
                size_t workspace_bytes, int B, int H, int L, int d, int dtype,
@@ -200,9 +203,14 @@ int lssar_attn_bwd_ws(const void* q, const void* k, const void* v,
  *    q^_i . k^_j (natural logarithms).  Rows r are (b, h, i - 1) row-major.
  *  - Values come from the kernels' arithmetic (fp32 for bf16 inputs, fp64
  *    for fp32 inputs), rounded to fp64.
- *  - Everything else, including the output and errors, as for
- *    lssar_attn_fwd_ws (EINVAL also for a null, misaligned or overlapping
- *    row_stats).  Allocates nothing. */
+ *  - For bf16 inputs the scores come from the exact query rows (q_i scaled
+ *    by a power of two, exact in f16) with the fp32 factors applied to the
+ *    accumulator; lssar_attn_fwd_ws folds the row factor into the query
+ *    operand and rounds it to f16, so the two outputs agree to the bf16
+ *    parity bar, not bitwise.  fp32 inputs: bitwise the same output.
+ *  - Everything else, including errors, as for lssar_attn_fwd_ws (EINVAL
+ *    also for a null, misaligned or overlapping row_stats).  Allocates
+ *    nothing. */
 int lssar_attn_fwd_stats_ws(const void* q, const void* k, const void* v,
                             void* out, double* row_stats, int B, int H, int L,
                             int d, int p, float eps, int dtype, void* workspace,

@@ -68,8 +68,10 @@ enum {
                                 p > 1024, L > 2^22 */
     LSSAR_EWORKSPACE = -3,   /* workspace null, misaligned, too small or
                                 overlapping a tensor */
-    LSSAR_EHIP = -4          /* a HIP call or kernel launch failed; see
+    LSSAR_EHIP = -4,         /* a HIP call or kernel launch failed; see
                                 lssar_last_hip_error() */
+    LSSAR_ESCRATCH = -5      /* lssar_attn_fwd_noalloc: the input needs more
+                                than its static scratch */
 };
 
 /* Workspace for every forward entry point that takes one, in bytes, each
@@ -95,6 +97,29 @@ int lssar_attn_fwd_ws(const void* q, const void* k, const void* v, void* out,
 int lssar_attn_fwd(const void* q, const void* k, const void* v, void* out,
                    int B, int H, int L, int d, int p, float eps, int dtype,
                    void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * lssar_attn_fwd with no allocation and no workspace argument.  Its
+ * workspace is a static device array of the library, one per GPU, of
+ * lssar_noalloc_scratch_bytes() = 64 MiB, held from the library's first use
+ * on that GPU until the process ends (bf16 at d = 64 fits up to about 250 K
+ * query rows B*H*L, e.g. B1 H12 L16384).
+ *  - Arguments, layout and output as for lssar_attn_fwd_ws on the CURRENT
+ *    device; `stream` must belong to it.
+ *  - LSSAR_ESCRATCH (checked on the host, before any HIP call) if
+ *    lssar_workspace_bytes(B, H, L, d, dtype) exceeds the scratch; other
+ *    errors as for lssar_attn_fwd_ws.
+ *  - Calls no allocator.  Every call on a GPU shares that GPU's scratch:
+ *    calls that overlap in time on one GPU (other streams, other threads)
+ *    race; issue them on one stream.  Each call rewrites all of the scratch
+ *    it reads (nothing needs to start at zero). */
+int lssar_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                           void* out, int B, int H, int L, int d, int p,
+                           float eps, int dtype, void* stream);
+
+/* Size of lssar_attn_fwd_noalloc's per-GPU scratch, in bytes. */
+size_t lssar_noalloc_scratch_bytes(void);
 
 /* The prep step alone (the prep kernels).  Writes into the workspace the
  * key factors (Key design 1's K_j <- K_j / |K_j|_2, kept as a factor of the

@@ -27,12 +27,14 @@ __all__ = [
     "lssar_decode_workspace_bytes", "lssar_decode_ws", "decode_workspace_for",
     "lssar_bwd_workspace_bytes", "lssar_attn_bwd_ws", "bwd_workspace_for",
     "lssar_attn_fwd_stats_ws", "lssar_attn_bwd_stats_ws", "stats_for",
-    "lssar_fwd_schedule",
+    "lssar_fwd_schedule", "lssar_attn_fwd_noalloc", "lssar_noalloc_scratch_bytes",
+    "LSSAR_ESCRATCH",
 ]
 
 LSSAR_F32, LSSAR_BF16 = 0, 1
 LSSAR_PHI_SOFTPLUS, LSSAR_PHI_SIGMOID = 0, 1
 LSSAR_OK, LSSAR_EINVAL, LSSAR_EUNSUPPORTED, LSSAR_EWORKSPACE, LSSAR_EHIP = 0, -1, -2, -3, -4
+LSSAR_ESCRATCH = -5
 DEFAULT_EPS = 1e-4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +95,10 @@ def lib():
         L.lssar_fwd_schedule.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_int),
                                          ctypes.c_longlong]
         L.lssar_fwd_schedule.restype = ctypes.c_longlong
+        L.lssar_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        L.lssar_attn_fwd_noalloc.restype = i
+        L.lssar_noalloc_scratch_bytes.argtypes = []
+        L.lssar_noalloc_scratch_bytes.restype = sz
         _lib = L
     return _lib
 
@@ -191,6 +197,20 @@ def lssar_attn_fwd(q, k, v, out=None, *, p: int, eps: float = DEFAULT_EPS, strea
                               float(eps), dt, _stream_ptr(stream))
     _raise(st, "lssar_attn_fwd")
     return out
+
+
+def lssar_attn_fwd_noalloc(q, k, v, out, *, p: int, eps: float = DEFAULT_EPS, stream=None):
+    """out <- LSSAR(q, k, v) with the library's static per-GPU scratch as the
+    workspace: no allocation (out must be given)."""
+    B, H, L, d, dt = _check_qkv(q, k, v, out)
+    st = lib().lssar_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, L, d, int(p),
+                                      float(eps), dt, _stream_ptr(stream))
+    _raise(st, "lssar_attn_fwd_noalloc")
+    return out
+
+
+def lssar_noalloc_scratch_bytes() -> int:
+    return int(lib().lssar_noalloc_scratch_bytes())
 
 
 def workspace_for(q):

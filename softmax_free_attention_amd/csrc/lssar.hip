@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
+#include <mutex>
 #include <type_traits>
 
 #include "lssar_bwd.hpp"
@@ -576,6 +577,60 @@ int lssar_attn_fwd(const void* q, const void* k, const void* v, void* out, int B
     return st;
 }
 
+// Workspace of lssar_attn_fwd_noalloc: a file-scope device array, one copy
+// per GPU the library runs on, held until the process ends.  Host code never
+// uses its name as an address (on the host it is only a stand-in): each
+// device's address comes from hipGetSymbolAddress, taken once per device
+// with that device current, and is what the kernels receive.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// The current device's copy of `scratch`.
+int scratch_of_current_device(void** ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices)
+        return LSSAR_EUNSUPPORTED;
+    std::call_once(g_scratch_once[dev], [dev] {
+        g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+    });
+    if (g_scratch_err[dev] != hipSuccess)
+        return hip_fail(g_scratch_err[dev]);
+    *ptr = g_scratch_ptr[dev];
+    return LSSAR_OK;
+}
+}  // namespace
+
+int lssar_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, int B, int H,
+                           int L, int d, int p, float eps, int dtype, void* stream)
+{
+    int st = validate(q, k, v, out, B, H, L, d, p, eps, dtype);
+    if (st != LSSAR_OK)
+        return st;
+    if (layout(B, H, L, d, dtype).total() > kScratchBytes)
+        return LSSAR_ESCRATCH;
+    void* ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != LSSAR_OK)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_prep(k, v, ws, B, H, L, d, dtype, s);
+    if (st != LSSAR_OK)
+        return st;
+    return run_fwd(q, k, v, ws, out, B, H, L, d, p, eps, dtype, s);
+}
+
+size_t lssar_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
 int lssar_prep(const void* k, const void* v, void* workspace, size_t workspace_bytes, int B,
                int H, int L, int d, int dtype, void* stream)
 {
@@ -783,6 +838,9 @@ const char* lssar_status_str(int status)
     case LSSAR_EUNSUPPORTED: return "unsupported head dimension, dtype, p or length";
     case LSSAR_EWORKSPACE: return "workspace missing, misaligned, too small or overlapping";
     case LSSAR_EHIP: return "HIP runtime error (see lssar_last_hip_error)";
+    case LSSAR_ESCRATCH:
+        return "input needs more workspace than lssar_attn_fwd_noalloc's static scratch "
+               "(lssar_noalloc_scratch_bytes)";
     default: return "unknown status";
     }
 }

@@ -64,10 +64,23 @@ def test_library_has_no_oracle_dependency(L):
                 assert "lssar_ref" not in src, f
 
 
+def test_noalloc_host_checks(L):
+    """lssar_attn_fwd_noalloc validates on the host before any HIP call: bad
+    arguments, and an input whose workspace exceeds the 64 MiB scratch."""
+    assert sfa.lssar_noalloc_scratch_bytes() == 64 << 20
+    f = L.lssar_attn_fwd_noalloc
+    q, k, v, o = A, A + STEP, A + 2 * STEP, A + 3 * STEP
+    assert f(0, k, v, o, 1, 2, 64, 64, 3, 1e-4, 1, None) == sfa.LSSAR_EINVAL
+    assert f(q, k, v, o, 1, 2, 64, 96, 3, 1e-4, 1, None) == sfa.LSSAR_EUNSUPPORTED
+    assert f(q, k, v, o, 1, 2, 64, 64, 0, 1e-4, 1, None) == sfa.LSSAR_EINVAL
+    assert f(q, k, v, o, 1, 16, 8192, 128, 3, 1e-4, 1, None) == sfa.LSSAR_ESCRATCH
+    assert f(q, k, v, o, 2, 32, 4096, 128, 15, 1e-4, 1, None) == sfa.LSSAR_ESCRATCH
+
+
 def test_version_and_status_strings(L):
     assert sfa.lssar_version() == 800
     assert sfa.lssar_status_str(0) == "ok"
-    for st in (-1, -2, -3, -4, 7):
+    for st in (-1, -2, -3, -4, -5, 7):
         s = sfa.lssar_status_str(st)
         assert isinstance(s, str) and s
     assert sfa.lssar_last_hip_error() == 0

@@ -59,6 +59,11 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_record.json")
 N_SIMDS = 256 * 4            # compute units x SIMDs per unit
 CLOCK_HZ = 2.4e9             # peak engine clock
+# Issue cost per wave64 instruction per SIMD at 4 waves per SIMD, measured by
+# issue_rates.hip (profiles/issue_rates_gfx950.md): fp32 VALU, transcendental
+# (v_exp_f32 / v_log_f32) and 16x16x32 MFMA; MFMA and VALU issue one after
+# the other on a SIMD, so their times add.
+ISSUE_NS = {"valu": 1.23, "trans": 3.58, "mfma": 7.68}
 KERNEL_SRC = os.path.join(ROOT, "softmax_free_attention_amd", "csrc", "lssar_device.hpp")
 
 
@@ -100,9 +105,17 @@ def valu_roofline(workload: str, kernel_ms: float):
     if not ent or "valu_active_simd_cycles" not in ent:
         return None
     cap = N_SIMDS * CLOCK_HZ * kernel_ms * 1e-3
-    return {"active_simd_cycles": ent["valu_active_simd_cycles"],
-            "capacity_simd_cycles": round(cap), "frac": round(ent["valu_active_simd_cycles"] / cap, 4),
-            "valu_insts": ent.get("valu_insts"), "mfma_insts": ent.get("mfma_insts")}
+    out = {"active_simd_cycles": ent["valu_active_simd_cycles"],
+           "capacity_simd_cycles": round(cap), "frac": round(ent["valu_active_simd_cycles"] / cap, 4),
+           "valu_insts": ent.get("valu_insts"), "mfma_insts": ent.get("mfma_insts")}
+    if "valu_trans_insts" in ent:
+        # issue model: the recorded instruction counts at the measured rates
+        trans = ent["valu_trans_insts"]
+        model_us = ((ent["valu_insts"] - trans) * ISSUE_NS["valu"] + trans * ISSUE_NS["trans"] +
+                    ent["mfma_insts"] * ISSUE_NS["mfma"]) / N_SIMDS * 1e-3
+        out["issue_model_us"] = round(model_us, 1)
+        out["issue_frac"] = round(model_us / (kernel_ms * 1e3), 4)
+    return out
 
 
 def upload(inp):
@@ -250,7 +263,8 @@ def time_configs(names, steps, warmup):
                                             PEAK_TFLOPS["bf16"], 3),
                      "tokens_per_s": round(wl.B * wl.L / (ms * 1e-3), 1),
                      "kernel_ms": {"lssar_fwd": round(fwd, 5), "lssar_prep": round(prep, 5)},
-                     "kernel_tflops": round(wl.flops / (fwd * 1e-3) / 1e12, 2)}
+                     "kernel_tflops": round(wl.flops / (fwd * 1e-3) / 1e12, 2),
+                     "traffic": recorded_traffic(name), "valu": valu_roofline(name, fwd)}
         del q, k, v, inp
     return res
 

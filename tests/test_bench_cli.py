@@ -52,9 +52,6 @@ def test_valu_fraction_from_the_record(tmp_path, monkeypatch):
     assert bench.valu_roofline("w", 1.0) is None
 
 
-if __name__ == "__main__":
-    sys.exit(pytest.main([__file__, "-q"]))
-
 
 def test_cpu_baseline_context():
     """The CPU model and the oracle's one-thread times reported beside the
@@ -63,3 +60,25 @@ def test_cpu_baseline_context():
     res = bench.one_thread_times()
     assert res["tiny_s"] > 0 and res["gpt2s_s"] > 0
     assert "4 of 96 heads" in res["gpt2s_sample"]
+
+
+def test_issue_model_from_the_record(tmp_path, monkeypatch):
+    """Recorded instruction counts times the measured issue costs, summed
+    (MFMA and VALU issue one after the other), over 1024 SIMDs."""
+    src = tmp_path / "kernel.hpp"
+    src.write_text("// kernel source\n")
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    rec = tmp_path / "traffic.json"
+    n = 1024 * 1000
+    rec.write_text(json.dumps({"w": {"kernel_sha256_16": bench.kernel_hash(),
+                                     "valu_active_simd_cycles": 1.0, "valu_insts": 3 * n,
+                                     "valu_trans_insts": n, "mfma_insts": n}}))
+    monkeypatch.setattr(bench, "TRAFFIC_RECORD", str(rec))
+    want_us = (2 * bench.ISSUE_NS["valu"] + bench.ISSUE_NS["trans"] + bench.ISSUE_NS["mfma"])
+    got = bench.valu_roofline("w", want_us * 2e-3)
+    assert got["issue_model_us"] == pytest.approx(want_us, abs=0.05)
+    assert got["issue_frac"] == pytest.approx(0.5, abs=1e-3)
+
+
+if __name__ == "__main__":
+    sys.exit(pytest.main([__file__, "-q"]))

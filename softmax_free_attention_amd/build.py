@@ -13,9 +13,6 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "lssar.hip")
-DEPS = [SRC, os.path.join(HERE, "csrc", "lssar_device.hpp"), os.path.join(HERE, "csrc", "lssar_decode.hpp"),
-        os.path.join(HERE, "csrc", "lssar_bwd.hpp"),
-        os.path.join(ROOT, "include", "lssar.h")]
 OUT = os.path.join(HERE, "liblssar.so")
 ARCH = "gfx950"
 

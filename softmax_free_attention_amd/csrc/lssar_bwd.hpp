@@ -44,7 +44,9 @@
 namespace lssar {
 
 constexpr int kBwdThreads = 256;   // 4 waves, one row each
-constexpr int kBwdRowStats = 8;    // c, tc, invY, delta, Acoef, Ecoef, lam, rq per row (bf16 kernels: -delta Acoef for delta, the largest score for rq)
+// c, tc, invY, delta, Acoef, Ecoef, lam, rq per row (the bf16 kernels store
+// c u, tc u, A Y u, -A delta Y u, E, lam, -, the largest score, u = Y^(-1/p))
+constexpr int kBwdRowStats = 8;
 
 template <typename C>
 struct BwdMath;

@@ -9,9 +9,12 @@
 //   rowstats: per query block, the scores S^T = K Q^T and dW^T = V dO^T on
 //             v_mfma_f32_16x16x32_bf16, pass 1 the row's S and max score,
 //             pass 2 the sums Y, P1, P2, Z; writes the row coefficients
-//             (c, tau c, 1/Y, -delta A/|q|, A/|q|, E/|q|, the score factor,
-//             the largest score; the pair gradient sigma (y^(p-1) (A dW -
-//             A delta) - E) then costs two fma and a multiply);
+//             with u = Y^(-1/p): (c u, tau c u, A Y u/|q|, -delta A Y u/|q|,
+//             E/|q|, the score factor, -, the largest score).  With them
+//             y' = clamp((sp - tau) c u, 0, 1) = y u, the weight y^p / Y is
+//             y'^p, and the pair gradient sigma (y^(p-1) (A dW - A delta) -
+//             E) is sigma (y'^(p-1) (A Y u dW - A Y u delta) - E): two fma
+//             and a multiply;
 //   dq:       per query block, S^T, dW^T, the pair gradients dc_ij f_j, and
 //             dQ^ = (dc f) K on v_mfma_f32_16x16x16_bf16, whose output
 //             layout (lane = one query, four keys) is exactly its A operand;
@@ -271,8 +274,10 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
         // log2(e) ln d ln i / |q_i|  (Key design 1: log d . log N)
         const float lam = (float)(lam_scale * log((double)(qi + 1))) * rqi;
 
-        auto mm_block = [&](const unsigned char* base, int off, const bf16x8 (&b)[DC], int ks) {
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        // (init: the accumulator's starting value)
+        auto mm_block = [&](const unsigned char* base, int off, const bf16x8 (&b)[DC], int ks,
+                            float init = 0.0f) {
+            f32x4 acc = {init, init, init, init};
 #pragma unroll
             for (int dc = 0; dc < DC; ++dc) {
                 const bf16x8 a =
@@ -341,12 +346,20 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             const float a_ = degen ? 0.0f : kappa * alpha * rqi;
             const float e_ = degen ? 0.0f : kappa * epsr * rqi;
             if (qvalid && grp == 0) {
+                // u = Y^(-1/p) (Y >= 1: the row's largest score gives y = 1);
+                // (y u)^p = y^p / Y and (y u)^(p-1) Y u = y^(p-1), so the
+                // key side forms the weight with one multiply.  The kernels
+                // clamp y u at 1, not at u (a clamp at 1 is free on the fma):
+                // y u exceeds u only where rounding puts y above 1, and by the
+                // same factor.
+                const float u = degen ? 0.0f
+                                      : __builtin_amdgcn_exp2f(-__builtin_amdgcn_logf(Y) / (float)p_rt);
+                const float yu = Y * u;
                 float* st = stats + ((size_t)bh * L + qi) * kBwdRowStats;
                 const float4 a = degen ? make_float4(0.0f, 0.0f, 0.0f, 0.0f)
-                                       : make_float4(c, tc, 1.0f / Y, -dl * a_);
+                                       : make_float4(c * u, tc * u, a_ * yu, -dl * a_ * yu);
                 *reinterpret_cast<float4*>(st) = a;
-                *reinterpret_cast<float2*>(st + 4) = make_float2(a_, e_);
-                st[6] = lam;
+                *reinterpret_cast<float2*>(st + 4) = make_float2(e_, lam);
             }
             Ac = a_;
             Ec = e_;
@@ -524,14 +537,15 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
         } else if constexpr (MODE == 1) {
             // ---------------- dq: dQ^ = sum_j (dc_ij f_j) k_j ----------------
             if (qvalid) {
+                // (c u, tau c u, A Y u, -A delta Y u, E): y u and the pair
+                // gradient as from (c, tau c, A, -A delta, E), see row_coefs
                 const float* st = stats + ((size_t)bh * L + qi) * kBwdRowStats;
                 const float4 a = *reinterpret_cast<const float4*>(st);
-                const float4 b = *reinterpret_cast<const float4*>(st + 4);
                 c = a.x;
                 tc = a.y;
+                Ac = a.z;
                 adl = a.w;
-                Ac = b.x;
-                Ec = b.y;
+                Ec = st[4];
             }
             // (d = 64, p = 15: a block without a deep row, by the largest
             // scores in the coefficient records, takes plain log2(1 + 2^t))
@@ -659,7 +673,8 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 auto grads = [&](int ks, s16x4& p1, s16x4& p2, s16x4& p3) {
                     f32x4 f4;
                     const f32x4 t = scores(kt, base, ks, mm_block(base, KOFF, qf, ks), DIAG, f4);
-                    const f32x4 dw = mm_block(base, VOFF, gf, ks);
+                    // dW - d0, the offset as the accumulator's start
+                    const f32x4 dw = mm_block(base, VOFF, gf, ks, -d0);
                     f32x4 g1, g2, g3;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
@@ -672,7 +687,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                         const float ym = pow_m1<P>(y, p_rt);
                         Y = __builtin_fmaf(ym, y, Y);
                         Z = __builtin_fmaf(sp, ym, Z);
-                        const float h = ym * (dw[r] - d0);
+                        const float h = ym * dw[r];
                         P1 = __builtin_fmaf(y, h, P1);
                         Pd = __builtin_fmaf(sp, h, Pd);
                         g2[r] = sg * f4[r];
@@ -753,7 +768,8 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
 // Query tiles stream through LDS, double-buffered at d = 64 (one buffer at
 // d = 128, as in the query-side kernels).
 template <int D, int P>
-__global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(3))) void lssar_bwd_kside_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ G, const float* __restrict__ fk, const float* __restrict__ stats,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int BH, int L, int nkb, int npair, int p_rt)
@@ -765,8 +781,9 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
     constexpr int QOFF = 0, GOFF = T::RM;
     constexpr int SOFF = 2 * T::RM;
     constexpr int BYTES = SOFF + 64 * kBwdRowStats * 4;   // one tile buffer
-    // d = 64: two buffers (36 KB; 141 VGPRs give 3 waves per SIMD, and
-    // capped for 4 the kernel spills and runs no faster); d = 128: one
+    // d = 64: two buffers (36 KB); d = 128: one.  Capped for 3 waves per
+    // SIMD: uncapped, the p = 15 instantiation took 236 VGPRs (2 waves, 13%
+    // slower); capped for 4 it spills inside the tile loop (46% slower)
     constexpr int NB = D == 64 ? 2 : 1;
     __shared__ __attribute__((aligned(1024))) unsigned char lds[NB * BYTES];
 
@@ -881,9 +898,10 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
                     const int qrow = 16 * c + 4 * grp + r;       // query in the tile
                     const float* st = reinterpret_cast<const float*>(base + SOFF) +
                                       (16 * r + 4 * c + grp) * kBwdRowStats;
+                    // (c u, tau c u, A Y u, -A delta Y u), (E, lam)
                     const float4 a = *reinterpret_cast<const float4*>(st);
-                    const float4 b = *reinterpret_cast<const float4*>(st + 4);
-                    float t = sc[r] * b.z * fj;                  // lam_i f_j (q . k)
+                    const float2 b = *reinterpret_cast<const float2*>(st + 4);
+                    float t = sc[r] * b.y * fj;                  // lam_i f_j (q . k)
                     if (DIAG && qt * 64 + qrow < kj)
                         t = -INFINITY;
                     float sp, sg;
@@ -893,8 +911,8 @@ __global__ __launch_bounds__(kThreads) void lssar_bwd_kside_kernel(
                         sp_sig_plain(t, sp, sg);
                     const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(sp, a.x, -a.y), 0.0f, 1.0f);
                     const float ym = pow_m1<P>(y, p_rt);
-                    w4[r] = ym * y * a.z;
-                    g4[r] = sg * __builtin_fmaf(ym, __builtin_fmaf(b.x, dw[r], a.w), -b.y);
+                    w4[r] = ym * y;                              // y^p / Y
+                    g4[r] = sg * __builtin_fmaf(ym, __builtin_fmaf(a.z, dw[r], a.w), -b.x);
                 }
                 wb = pack_bf16x4(w4);
                 gb = pack_bf16x4(g4);

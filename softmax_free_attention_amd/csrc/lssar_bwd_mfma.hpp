@@ -107,16 +107,22 @@ __device__ __forceinline__ f32x4 mfma16k16x2(s16x4 a0, s16x4 a1, bf16x4 b0, bf16
 }
 
 // LDS layout of one 64-row tile: 64 rows x D bf16 as 16-byte slots, slot
-// c of row r at r * R + (c ^ swz(r)), R = D / 8 (the forward's K tile
-// layout).  The 16x16x32 A operands read 16-byte slots of 16 rows; the
-// 16x16x16 B operands (four consecutive rows of one dim) come from the same
-// tile by the LDS transpose read.
+// c of row r at r * R + (c ^ swz(r)), R = D / 8.  The 16x16x32 A operands
+// read 16-byte slots of 16 rows; the 16x16x16 B operands (four consecutive
+// rows of one dim) come from the same tile by the LDS transpose read.  The
+// swizzle serves both: in-bounds microbenchmarks of the two read patterns
+// on gfx950 timed the row reads equal to the best of the candidates tried
+// and the transpose reads 1.4x (d = 64) and 1.5x (d = 128) faster than with
+// swz = (r >> 1) & 7 and r & 15.  It depends on r mod 16 only.
 template <int D>
 struct BwdTiles {
     static constexpr int R = D / 8;
     static constexpr int RM = 64 * D * 2;        // bytes of a tile
     static constexpr int RM_LOADS = RM / 1024 / kWaves;   // wave-loads per wave
-    __device__ static int swz(int r) { return R == 8 ? ((r >> 1) & 7) : (r & 15); }
+    __device__ static int swz(int r)
+    {
+        return R == 8 ? (r & 7) : ((((r & 3) << 2) | ((r >> 2) & 3)) ^ ((r >> 1) & 2));
+    }
 };
 
 // Bytes of the tile's 16-byte slot s in the global tensor [rows][D] (row
@@ -336,7 +342,9 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
         };
         // the 8 coefficients of the row for the dq and key-side kernels, from
         // Y = sum y^p, delta = dO . out and Pd = sum sp y^(p-1) (dW - delta)
-        auto row_coefs = [&](float Y, float dl, float Pd) {
+        // (exact: the block evaluates Softplus exactly, stored in field 6 of
+        // every row for the key side's choice of path)
+        auto row_coefs = [&](float Y, float dl, float Pd, bool exact) {
             const float alpha = (float)p_rt * s1 / (gap * Y);
             const float epsr = alpha / s1 * Pd;
             // ln d ln i / (S ln 2), S in base 2: lam_scale ln i / S
@@ -360,6 +368,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                                        : make_float4(c * u, tc * u, a_ * yu, -dl * a_ * yu);
                 *reinterpret_cast<float4*>(st) = a;
                 *reinterpret_cast<float2*>(st + 4) = make_float2(e_, lam);
+                st[6] = exact ? 1.0f : 0.0f;
             }
             Ac = a_;
             Ec = e_;
@@ -533,7 +542,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 Z += __shfl_xor(Z, m);
             }
             const float dl = P1 / Y;
-            row_coefs(Y, dl, P2 - dl * Z);
+            row_coefs(Y, dl, P2 - dl * Z, exact);
         } else if constexpr (MODE == 1) {
             // ---------------- dq: dQ^ = sum_j (dc_ij f_j) k_j ----------------
             if (qvalid) {
@@ -745,7 +754,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 Pd += __shfl_xor(Pd, m);
             }
             const float Dl = degen ? 0.0f : P1 / Y;
-            row_coefs(Y, d0 + Dl, Pd - Dl * Z);
+            row_coefs(Y, d0 + Dl, Pd - Dl * Z, !kPlain || blk_deep);
             // the coefficients of query 4 grp + r sit in lane 4 grp + r
             f32x4 acc[DS];
 #pragma unroll
@@ -785,7 +794,9 @@ __attribute__((amdgpu_waves_per_eu(3))) void lssar_bwd_kside_kernel(
     // SIMD: uncapped, the p = 15 instantiation took 236 VGPRs (2 waves, 13%
     // slower); capped for 4 it spills inside the tile loop (46% slower)
     constexpr int NB = D == 64 ? 2 : 1;
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[NB * BYTES];
+    // the tile buffers, then the key block's deep-block flag
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[NB * BYTES + 16];
+    int* const deep_flag = reinterpret_cast<int*>(lds + NB * BYTES);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -965,50 +976,62 @@ __attribute__((amdgpu_waves_per_eu(3))) void lssar_bwd_kside_kernel(
             }
         };
 
-        auto run_tile = [&](int qt, const unsigned char* base, auto diag_tag) {
-            if (kw0 >= L)
-                return;
-            // at d = 64, p = 15 a tile whose 64 query rows all have their
-            // largest score at or above kDeep takes plain log2(1 + 2^t) (a
-            // wave-uniform choice; rows past L read as zeros); elsewhere the
-            // second path would cost occupancy (d = 128: 1 wave per SIMD
-            // instead of 2), and every tile is exact
-            constexpr bool kPlain = D == 64 && P == 15;
-            bool exact = true;
-            if constexpr (kPlain) {
-                const float tm = reinterpret_cast<const float*>(base + SOFF)[lane * kBwdRowStats + 7];
-                exact = __any(tm < kDeep);
-            }
-            if (exact)
-                tile(qt, base, diag_tag, std::true_type{});
-            else if constexpr (kPlain)
-                tile(qt, base, diag_tag, std::false_type{});
-        };
+        // at d = 64, p = 15 a key block all of whose query blocks (kb and
+        // later) are without a deep row takes plain log2(1 + 2^t) for every
+        // tile, a workgroup-uniform choice made once from the blocks' flags
+        // (record field 6, stored by the query-side kernels); elsewhere the
+        // second path would cost occupancy (d = 128: 1 wave per SIMD instead
+        // of 2), and every tile is exact.  (Chosen per tile inside the loop,
+        // the two paths' accumulators met in different registers: 16
+        // 64-bit copies per tile.)
+        constexpr bool kPlain = D == 64 && P == 15;
+        bool exact = true;
+        if constexpr (kPlain) {
+            bool deep = false;
+            for (int b = kb + tid; b < nkb; b += kThreads)
+                deep = deep || stats[((size_t)bh * L + (size_t)b * 64) * kBwdRowStats + 6] != 0.0f;
+            __syncthreads();                       // earlier readers of the flag done
+            if (tid == 0)
+                *deep_flag = 0;
+            __syncthreads();
+            if (deep)
+                *deep_flag = 1;
+            __syncthreads();
+            exact = *deep_flag != 0;
+        }
         // the first query tile (qt = kb) holds the diagonal, the later ones
         // lie wholly after every key of the block: it is peeled off the loop
-        auto step = [&](int n, auto diag_tag) {
+        auto tile_loop = [&](auto exact_tag) {
+            auto step = [&](int n, auto diag_tag) {
+                if constexpr (NB == 2) {
+                    const int buf = n & 1;
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();               // tile n landed; buffer buf ^ 1 free
+                    if (n + 1 < ntiles)
+                        issue(qt0 + n + 1, buf ^ 1);
+                    if (kw0 < L)
+                        tile(qt0 + n, lds + buf * BYTES, diag_tag, exact_tag);
+                } else {
+                    __syncthreads();               // readers of the previous tile done
+                    issue(qt0 + n, 0);
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();               // tile landed
+                    if (kw0 < L)
+                        tile(qt0 + n, lds, diag_tag, exact_tag);
+                }
+            };
             if constexpr (NB == 2) {
-                const int buf = n & 1;
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();                   // tile n landed; buffer buf ^ 1 free
-                if (n + 1 < ntiles)
-                    issue(qt0 + n + 1, buf ^ 1);
-                run_tile(qt0 + n, lds + buf * BYTES, diag_tag);
-            } else {
-                __syncthreads();                   // readers of the previous tile done
-                issue(qt0 + n, 0);
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();                   // tile landed
-                run_tile(qt0 + n, lds, diag_tag);
+                __syncthreads();                   // earlier readers done with both buffers
+                issue(qt0, 0);
             }
+            step(0, std::true_type{});
+            for (int n = 1; n < ntiles; ++n)
+                step(n, std::false_type{});
         };
-        if constexpr (NB == 2) {
-            __syncthreads();                       // earlier readers done with both buffers
-            issue(qt0, 0);
-        }
-        step(0, std::true_type{});
-        for (int n = 1; n < ntiles; ++n)
-            step(n, std::false_type{});
+        if (exact)
+            tile_loop(std::true_type{});
+        else if constexpr (kPlain)
+            tile_loop(std::false_type{});
 
         // adv/adk[ds][r] = grad[key 4 grp + r of the wave][dim 16 ds + row16]
 #pragma unroll

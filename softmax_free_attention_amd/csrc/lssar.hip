@@ -443,7 +443,8 @@ void launch_bwd(const void* q, const void* k, const void* v, const void* dout, v
         const int nqb = (L + 63) / 64, npair = (nqb + 1) / 2;
         hipLaunchKernelGGL((lssar::lssar_bwd_prep_kernel<D>), dim3((unsigned)nqb, BH),
                            dim3(lssar::kThreads), 0, s, Q, K, rq, fk, L);
-        const dim3 grid((unsigned)(npair * BH));
+        // d = 64: block pairs; d = 128: single blocks in the forward's order
+        const dim3 grid(D == 64 ? (unsigned)(npair * BH) : (unsigned)lssar::FwdSched(BH, nqb).grid());
         bool fused = false;
         if constexpr (D == 64) {
             if (saved) {

@@ -25,14 +25,16 @@
 //             queries), then dV = W^T dO and dK^ = (dc / |q|)^T Q on
 //             v_mfma_f32_16x16x16_bf16.
 // A workgroup is 4 waves x 16 rows (queries, or keys in dkdv) of a 64-row
-// block; paired blocks {n-1-pi, pi} give every workgroup the same number of
-// 64-row tiles.  Tiles of the other side stream through LDS by LDS-direct
-// buffer loads into one buffer, row-major only: the 16x16x16 B operands
-// (K in dq, Q and dO in dkdv; four consecutive rows of one dim) come from
-// the same tiles by the LDS transpose read (ds_read_b64_tr_b16).  Softplus
-// is exact (softplus2_acc, or sp_sig with its derivative from the same
-// exp2), except that at d = 64, p = 15 blocks and tiles without a deep row
-// take plain log2(1 + 2^t), the forward's rule.
+// block; at d = 64 paired blocks {n-1-pi, pi} give every workgroup the same
+// number of 64-row tiles, at d = 128 single blocks run largest first in the
+// forward's XCD-local order (bwd_blocks).  Tiles of the other side stream
+// through LDS by LDS-direct buffer loads, row-major only: the 16x16x16 B
+// operands (K in dq, Q and dO in dkdv; four consecutive rows of one dim)
+// come from the same tiles by the LDS transpose read (ds_read_b64_tr_b16).
+// Softplus is exact (softplus2_acc, or sp_sig with its derivative from the
+// same exp2), except that at d = 64, p = 15 query blocks without a deep
+// row, and key blocks whose query blocks have none, take plain
+// log2(1 + 2^t), the forward's rule.
 #pragma once
 
 #include "lssar_bwd.hpp"
@@ -135,6 +137,38 @@ __device__ __forceinline__ unsigned rm_src(int s)
     return (unsigned)((r * D + c * 8) * 2);
 }
 
+// The 64-row blocks of head bh that a workgroup w takes, the one with more
+// work first (b1 < 0: one block).  Block b of the query side has the work of
+// b + 1 key tiles, key block b of the key side that of nb - b query tiles.
+//  d = 64: the pair {pi, nb - 1 - pi} (equal work for every workgroup), in
+//          the XCD-local order of xcd_item; npair * BH workgroups.
+//  d = 128: one block per workgroup, in the forward's dispatch order
+//          (FwdSched: balanced slices of heads per XCD, largest block first),
+//          FwdSched(BH, nb).grid() workgroups; false for an empty index.
+//  (At d = 128, 3 waves per SIMD, the smaller workgroups ended the key-side
+//  kernel 2.7% sooner; at d = 64 the pairs were faster.)
+template <int D>
+__device__ __forceinline__ bool bwd_blocks(int w, int BH, int nb, bool key_side, int& bh, int& b0,
+                                           int& b1)
+{
+    if constexpr (D == 64) {
+        const int npair = (nb + 1) / 2;
+        const int item = xcd_item(w, npair * BH);
+        bh = item / npair;
+        const int pi = item % npair;
+        b0 = key_side ? pi : nb - 1 - pi;
+        b1 = pi == nb - 1 - pi ? -1 : nb - 1 - b0;
+        return true;
+    } else {
+        int qbx;
+        if (!FwdSched(BH, nb).item(w, bh, qbx))
+            return false;
+        b0 = key_side ? nb - 1 - qbx : qbx;
+        b1 = -1;
+        return true;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Prep: row factors, one workgroup per (64-row block, head)
 // ---------------------------------------------------------------------------
@@ -217,8 +251,9 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, row16 = lane & 15, grp = lane >> 4;
-    const int item = xcd_item((int)blockIdx.x, npair * BH);
-    const int bh = item / npair, pi = item % npair;
+    int bh, blk0, blk1;
+    if (!bwd_blocks<D>((int)blockIdx.x, BH, nqb, false, bh, blk0, blk1))
+        return;
     const size_t hoff = (size_t)bh * L * D;
 
     const void* kbase = K + hoff;
@@ -254,9 +289,9 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
     for (int dc = 0; dc < DC; ++dc)
         ard[dc] = (row16 * T::R + ((4 * dc + grp) ^ T::swz(row16))) * 16;
 
-    const int nblk = (pi == nqb - 1 - pi) ? 1 : 2;
+    const int nblk = blk1 < 0 ? 1 : 2;
     for (int blk = 0; blk < nblk; ++blk) {
-        const int qb = blk == 0 ? nqb - 1 - pi : pi;
+        const int qb = blk == 0 ? blk0 : blk1;
         const int qw0 = qb * 64 + wave * 16;
         const int qwl = min(qw0 + 15, L - 1);
         const bool wave_active = qw0 < L;
@@ -801,8 +836,9 @@ __attribute__((amdgpu_waves_per_eu(3))) void lssar_bwd_kside_kernel(
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, row16 = lane & 15, grp = lane >> 4;
-    const int item = xcd_item((int)blockIdx.x, npair * BH);
-    const int bh = item / npair, pi = item % npair;
+    int bh, blk0, blk1;
+    if (!bwd_blocks<D>((int)blockIdx.x, BH, nkb, true, bh, blk0, blk1))
+        return;
     const size_t hoff = (size_t)bh * L * D;
 
     const void* qbase = Q + hoff;
@@ -859,10 +895,10 @@ __attribute__((amdgpu_waves_per_eu(3))) void lssar_bwd_kside_kernel(
             trr[ds] = (x * T::R + ((2 * ds) ^ X)) * 16 + (row16 & 1) * 8;
     }
 
-    const int nblk = (pi == nkb - 1 - pi) ? 1 : 2;
+    const int nblk = blk1 < 0 ? 1 : 2;
     for (int blk = 0; blk < nblk; ++blk) {
         // blk 0: the earlier key block (more query tiles), blk 1: the later
-        const int kb = blk == 0 ? pi : nkb - 1 - pi;
+        const int kb = blk == 0 ? blk0 : blk1;
         const int kw0 = kb * 64 + wave * 16;       // first key row of this wave
         const int kj = kw0 + row16;                // this lane's key (0-based)
         const bool kvalid = kj < L;

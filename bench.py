@@ -451,6 +451,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-workloads", default="x8_decode,x8_decode_ragged,wide_decode",
+                    help="comma-separated decode workloads to time (a profiler run can take one)")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the GPT-2-small (p=3) and wide-head (d=128) workloads")
@@ -543,7 +545,7 @@ def main():
     if not args.no_decode:
         log("bench: decode")
         line["decode"] = {n: time_decode(n, 50, 10)
-                          for n in ("x8_decode", "x8_decode_ragged", "wide_decode")}
+                          for n in args.decode_workloads.split(",") if n}
     if not args.no_sweep:
         log("bench: L sweep")
         line["sweep"] = sweep(steps=10, warmup=3)

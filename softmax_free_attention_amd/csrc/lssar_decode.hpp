@@ -134,6 +134,47 @@ __device__ __forceinline__ int dec_len(const int* lens, int b, int Lmax)
     return n < 0 ? 0 : (n > Lmax ? Lmax : n);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Elements 2E, 2E + 1 of eight bf16 values.  (A bit-cast of one element of
+// a 32-bit vector was compiled as element 0 for every index; the whole
+// vector is bit-cast and then shuffled instead.)
+template <int E>
+__device__ __forceinline__ bf16x2 bf16_pair(bf16x8 v)
+{
+    return __builtin_shufflevector(v, v, 2 * E, 2 * E + 1);
+}
+
+// sum_e a[e] b[e] + c over eight bf16 pairs by v_dot2c_f32_bf16
+__device__ __forceinline__ float dot8_bf16(bf16x8 a, bf16x8 b, float c)
+{
+    c = __builtin_amdgcn_fdot2_f32_bf16(bf16_pair<0>(a), bf16_pair<0>(b), c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(bf16_pair<1>(a), bf16_pair<1>(b), c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(bf16_pair<2>(a), bf16_pair<2>(b), c, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(bf16_pair<3>(a), bf16_pair<3>(b), c, false);
+}
+
+// Sum of x over each aligned group of N lanes (8 or 16), in every lane of the
+// group, by DPP moves folded into the adds: quad_perm [1,0,3,2] and [2,3,0,1]
+// (lane ^ 1, lane ^ 2), then row_half_mirror (lane i <-> 7 - i within 8:
+// quad against quad) and for 16 row_mirror (i <-> 15 - i).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xf, 0xf, false));
+}
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float x)
+{
+    x += dpp_f32<0xB1>(x);
+    x += dpp_f32<0x4E>(x);
+    x += dpp_f32<0x141>(x);
+    if constexpr (N == 16)
+        x += dpp_f32<0x140>(x);
+    return x;
+}
+
 // Workgroup-wide sum and max of one value per thread, in a fixed order.
 template <typename C>
 __device__ __forceinline__ void block_sum_max(C& s, C& m, C* red)
@@ -191,41 +232,81 @@ __global__ __launch_bounds__(kDecThreads) void lssar_decode_scores_kernel(
         raw[n] = as_raw(buf_load16(cbase, cbytes, (unsigned)(kw + n * KPW + ksl) * RB + sub * 16u),
                         cbase);
 
-    C qv[EPL];
-    unpack(load_raw(Q + (size_t)bh * D + sub * EPL), qv);
-    C qss = 0;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e)
-        qss += qv[e] * qv[e];
-#pragma unroll
-    for (int o = 1; o < LPK; o <<= 1)
-        qss += __shfl_xor(qss, o);
-    // log2(e) ln d ln i / max(|q|, 1e-12), i = len (Key design 1: log d . log N)
-    const C lam = (C)(lam_scale * log((double)len) / fmax(sqrt((double)qss), 1e-12));
-
     C* sh = scores + (size_t)bh * Lmax;
     C s1 = 0, tmax = -INFINITY;
+    if constexpr (std::is_same<T, __bf16>::value) {
+        // bf16: q . k and |k|^2 of each 16-byte piece by v_dot2c_f32_bf16
+        // (two products and the sum with one rounding: on random, tiny and
+        // cancelling inputs as accurate as an fp32 fma chain), the LPK
+        // lanes of a key summed by DPP moves, then one key per lane for the
+        // rest: lane (sub, ksl) takes load n = sub mod NLD (d = 128: the
+        // upper half of each key's 16 lanes repeats the lower and stores
+        // nothing).  Per 64 keys at d = 64 this issues about 150 VALU
+        // instructions instead of 800 with an fp32 fma per element, shuffles
+        // through LDS and the tail on every eighth lane.
+        static_assert(NLD == 8 && (LPK == 8 || LPK == 16), "decode lane layout");
+        const bf16x8 q8 = __builtin_bit_cast(bf16x8, load_raw(Q + (size_t)bh * D + sub * EPL));
+        const float qss = lane_group_sum<LPK>(dot8_bf16(q8, q8, 0.0f));
+        // log2(e) ln d ln i / max(|q|, 1e-12), i = len (Key design 1: log d .
+        // log N), in fp32: ln i = log2(i) ln 2
+        const float lam = (float)lam_scale * (__builtin_amdgcn_logf((float)len) * 0.69314718055994531f) *
+                          __builtin_amdgcn_rsqf(fmaxf(qss, 1e-24f));
+        float dt[NLD], sq[NLD];
 #pragma unroll
-    for (int n = 0; n < NLD; ++n) {
+        for (int n = 0; n < NLD; ++n) {
+            const bf16x8 k8 = __builtin_bit_cast(bf16x8, raw[n]);
+            dt[n] = lane_group_sum<LPK>(dot8_bf16(q8, k8, 0.0f));
+            sq[n] = lane_group_sum<LPK>(dot8_bf16(k8, k8, 0.0f));
+        }
+        const int n = sub & (NLD - 1);
+        float dot = dt[0], ss = sq[0];
+#pragma unroll
+        for (int m = 1; m < NLD; ++m) {
+            dot = n == m ? dt[m] : dot;
+            ss = n == m ? sq[m] : ss;
+        }
         const int key = k0 + kw + n * KPW + ksl;
-        C kv[EPL];
-        unpack(raw[n], kv);
-        C dot = 0, ss = 0;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            dot += qv[e] * kv[e];
-            ss += kv[e] * kv[e];
-        }
-#pragma unroll
-        for (int o = 1; o < LPK; o <<= 1) {
-            dot += __shfl_xor(dot, o);
-            ss += __shfl_xor(ss, o);
-        }
-        if (key < kend && sub == 0) {
-            const C t = dot * lam * inv_norm(ss);
+        if (key < kend && sub < NLD) {
+            // 1 / max(|k|, 1e-12) = rsqrt(max(|k|^2, 1e-24)), v_rsq_f32
+            const float t = dot * lam * __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
             sh[key] = t;
-            s1 += softplus_dec(t);
-            tmax = dmax(tmax, t);
+            s1 = softplus_dec(t);
+            tmax = t;
+        }
+    } else {
+        C qv[EPL];
+        unpack(load_raw(Q + (size_t)bh * D + sub * EPL), qv);
+        C qss = 0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            qss += qv[e] * qv[e];
+#pragma unroll
+        for (int o = 1; o < LPK; o <<= 1)
+            qss += __shfl_xor(qss, o);
+        // log2(e) ln d ln i / max(|q|, 1e-12), i = len (Key design 1: log d . log N)
+        const C lam = (C)(lam_scale * log((double)len) / fmax(sqrt((double)qss), 1e-12));
+#pragma unroll
+        for (int n = 0; n < NLD; ++n) {
+            const int key = k0 + kw + n * KPW + ksl;
+            C kv[EPL];
+            unpack(raw[n], kv);
+            C dot = 0, ss = 0;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                dot += qv[e] * kv[e];
+                ss += kv[e] * kv[e];
+            }
+#pragma unroll
+            for (int o = 1; o < LPK; o <<= 1) {
+                dot += __shfl_xor(dot, o);
+                ss += __shfl_xor(ss, o);
+            }
+            if (key < kend && sub == 0) {
+                const C t = dot * lam * inv_norm(ss);
+                sh[key] = t;
+                s1 += softplus_dec(t);
+                tmax = dmax(tmax, t);
+            }
         }
     }
     block_sum_max(s1, tmax, red);

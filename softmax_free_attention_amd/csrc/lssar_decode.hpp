@@ -175,6 +175,29 @@ __device__ __forceinline__ float lane_group_sum(float x)
     return x;
 }
 
+// The value of lane n of each aligned group of N lanes (8 or 16), by
+// ds_swizzle in bit mode: lane' = (lane & and_mask) | n within 32 lanes.
+template <int PAT>
+__device__ __forceinline__ float swizzle_f32(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), PAT));
+}
+template <int N>
+__device__ __forceinline__ float group_lane(float v, int n)
+{
+    constexpr int kAnd = 31 & ~(N - 1);
+    switch (n) {                               // n is a constant after unrolling
+    case 0: return swizzle_f32<kAnd | (0 << 5)>(v);
+    case 1: return swizzle_f32<kAnd | (1 << 5)>(v);
+    case 2: return swizzle_f32<kAnd | (2 << 5)>(v);
+    case 3: return swizzle_f32<kAnd | (3 << 5)>(v);
+    case 4: return swizzle_f32<kAnd | (4 << 5)>(v);
+    case 5: return swizzle_f32<kAnd | (5 << 5)>(v);
+    case 6: return swizzle_f32<kAnd | (6 << 5)>(v);
+    default: return swizzle_f32<kAnd | (7 << 5)>(v);
+    }
+}
+
 // Workgroup-wide sum and max of one value per thread, in a fixed order.
 template <typename C>
 __device__ __forceinline__ void block_sum_max(C& s, C& m, C* red)
@@ -384,13 +407,24 @@ __global__ __launch_bounds__(kDecThreads) void lssar_decode_pv_kernel(
     const C* sbase = scores + (size_t)bh * Lmax + k0;
     const unsigned sbytes = (unsigned)(kend - k0) * (unsigned)sizeof(C);
     const int kw = wave * (kDecChunk / 4);
+    constexpr bool kOwn = std::is_same<T, __bf16>::value;
     Raw raw[NLD];
     C tk[NLD];
+    // bf16: each lane loads the score of one key, (n, ksl) with n = sub mod
+    // NLD, and forms its weight once; the LPK lanes of key (n, ksl) take it
+    // from lane n of their group by ds_swizzle.  (fp32: every lane forms
+    // the weight of each key it multiplies.)
+    C town = 0;
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
         const unsigned lk = (unsigned)(kw + n * KPW + ksl);
         raw[n] = as_raw(buf_load16(cbase, cbytes, lk * RB + sub * 16u), cbase);
-        tk[n] = buf_load_c(sbase, sbytes, lk * (unsigned)sizeof(C));
+        if constexpr (!kOwn)
+            tk[n] = buf_load_c(sbase, sbytes, lk * (unsigned)sizeof(C));
+    }
+    if constexpr (kOwn) {
+        const unsigned lk = (unsigned)(kw + (sub & (NLD - 1)) * KPW + ksl);
+        town = buf_load_c(sbase, sbytes, lk * (unsigned)sizeof(C));
     }
 
     const DecRow<C> rc = dec_row<C>(part1 + (size_t)bh * nsplit * 2, nvalid, len, eps);
@@ -401,25 +435,39 @@ __global__ __launch_bounds__(kDecThreads) void lssar_decode_pv_kernel(
         return;
     }
 
+    // the weight of key (n, ksl): keys past the chunk (their rows read as
+    // zeros) get weight 0
+    auto weight = [&](C t, int n) {
+        C y = softplus_dec(t) * rc.c - rc.tc;
+        y = y < (C)0 ? (C)0 : (y > (C)1 ? (C)1 : y);
+        const bool valid = kw + n * KPW + ksl < kend - k0;
+        return valid ? pow_chain<P>(y, p_rt) : (C)0;
+    };
     C acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
         acc[e] = 0;
     C dsum = 0;
+    C wown = 0;
+    if constexpr (kOwn) {
+        wown = weight(town, sub & (NLD - 1));
+        dsum = sub < NLD ? wown : (C)0;        // each key once
+    }
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
-        C y = softplus_dec(tk[n]) * rc.c - rc.tc;
-        y = y < (C)0 ? (C)0 : (y > (C)1 ? (C)1 : y);
-        // keys past the chunk (their rows read as zeros) get weight 0
-        const bool valid = kw + n * KPW + ksl < kend - k0;
-        const C w = valid ? pow_chain<P>(y, p_rt) : (C)0;
+        C w;
+        if constexpr (kOwn) {
+            w = group_lane<LPK>(wown, n);
+        } else {
+            w = weight(tk[n], n);
+            if (sub == 0)
+                dsum += w;
+        }
         C vv[EPL];
         unpack(raw[n], vv);
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
             acc[e] += w * vv[e];
-        if (sub == 0)
-            dsum += w;
     }
     // lanes with the same sub hold the same dims: sum over the key slots
 #pragma unroll

@@ -32,9 +32,10 @@
 // operands (K in dq, Q and dO in dkdv; four consecutive rows of one dim)
 // come from the same tiles by the LDS transpose read (ds_read_b64_tr_b16).
 // Softplus is exact (softplus2_acc, or sp_sig with its derivative from the
-// same exp2), except that at d = 64, p = 15 query blocks without a deep
-// row, and key blocks whose query blocks have none, take plain
-// log2(1 + 2^t), the forward's rule.
+// same exp2), except that at d = 64 query blocks without a deep row, and
+// key blocks whose query blocks have none, take plain log2(1 + 2^t), the
+// forward's rule (at every p: p = 3 training backward 139 -> 129 us at
+// B8 H12 L1024, recomputing 178 -> 164 us).
 #pragma once
 
 #include "lssar_bwd.hpp"
@@ -532,9 +533,9 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             row_consts();
 
             // ---------------- pass 2: Y, P1, P2, Z ----------------
-            // (d = 64, p = 15, recomputed statistics: a block without a deep
-            // row takes plain log2(1 + 2^t); the flag is final after pass 1)
-            constexpr bool kPlain = D == 64 && P == 15;
+            // (d = 64, recomputed statistics: a block without a deep row
+            // takes plain log2(1 + 2^t); the flag is final after pass 1)
+            constexpr bool kPlain = D == 64;
             const bool exact = !kPlain || saved || *deep_flag;
             float Y = 0.0f, P1 = 0.0f, P2 = 0.0f, Z = 0.0f;
             auto pass2 = [&](auto exact_tag) {
@@ -591,9 +592,9 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 adl = a.w;
                 Ec = st[4];
             }
-            // (d = 64, p = 15: a block without a deep row, by the largest
-            // scores in the coefficient records, takes plain log2(1 + 2^t))
-            constexpr bool kPlain = D == 64 && P == 15;
+            // (d = 64: a block without a deep row, by the largest scores in
+            // the coefficient records, takes plain log2(1 + 2^t))
+            constexpr bool kPlain = D == 64;
             bool exact = true;
             if constexpr (kPlain) {
                 const float tm = qvalid ? stats[((size_t)bh * L + qi) * kBwdRowStats + 7] : 0.0f;
@@ -664,13 +665,11 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             //   dq^_i = A_i (sum sigma h k^ - Dl sum sigma y^(p-1) k^)
             //           - E_i sum sigma k^
             // A_i and E_i need the row's full sums, so they and Dl scale the
-            // three accumulated vectors at the end.  At p = 15 a block
-            // without a deep row (largest score below kDeep) takes plain
-            // log2(1 + 2^t), as the forward does, and a block with one the
-            // exact Softplus (a uniform branch); at other p the plain path
-            // would cost spills (p = 3: 95 spilled VGPRs against 36) and
-            // every block takes the exact one -------
-            constexpr bool kPlain = P == 15;
+            // three accumulated vectors at the end.  A block without a deep
+            // row (largest score below kDeep) takes plain log2(1 + 2^t), as
+            // the forward does, and a block with one the exact Softplus (a
+            // uniform branch) -------
+            constexpr bool kPlain = true;
             if (qvalid)
                 load_row_stats(saved, (size_t)bh * L + qi, s1, tmax);
             store_tmax();
@@ -1012,15 +1011,14 @@ __attribute__((amdgpu_waves_per_eu(3))) void lssar_bwd_kside_kernel(
             }
         };
 
-        // at d = 64, p = 15 a key block all of whose query blocks (kb and
-        // later) are without a deep row takes plain log2(1 + 2^t) for every
-        // tile, a workgroup-uniform choice made once from the blocks' flags
-        // (record field 6, stored by the query-side kernels); elsewhere the
-        // second path would cost occupancy (d = 128: 1 wave per SIMD instead
-        // of 2), and every tile is exact.  (Chosen per tile inside the loop,
+        // at d = 64 a key block all of whose query blocks (kb and later)
+        // are without a deep row takes plain log2(1 + 2^t) for every tile,
+        // a workgroup-uniform choice made once from the blocks' flags
+        // (record field 6, stored by the query-side kernels); at d = 128
+        // the second path would cost occupancy, and every tile is exact.  (Chosen per tile inside the loop,
         // the two paths' accumulators met in different registers: 16
         // 64-bit copies per tile.)
-        constexpr bool kPlain = D == 64 && P == 15;
+        constexpr bool kPlain = D == 64;
         bool exact = true;
         if constexpr (kPlain) {
             bool deep = false;

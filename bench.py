@@ -243,11 +243,13 @@ def time_variants(q, k, v, p, steps, warmup, eps=1e-4):
     return res
 
 
-def time_configs(names, steps, warmup):
+def time_configs(names, steps, warmup, backward=True):
     """The other full-size workloads, each as its own whole step (prep plus
     attention kernel, one lssar_attn_fwd_ws call) on its seeded inputs:
     wall time of K back-to-back steps after a second of untimed load, and
-    the two kernels' mean durations from HIP events."""
+    the two kernels' mean durations from HIP events.  With backward, also
+    the training pair and the recomputing backward on the same inputs (as
+    time_backward)."""
     import lssar_inputs as gen
     res = {}
     for name in names:
@@ -265,6 +267,14 @@ def time_configs(names, steps, warmup):
                      "kernel_ms": {"lssar_fwd": round(fwd, 5), "lssar_prep": round(prep, 5)},
                      "kernel_tflops": round(wl.flops / (fwd * 1e-3) / 1e12, 2),
                      "traffic": recorded_traffic(name), "valu": valu_roofline(name, fwd)}
+        if backward:
+            bt = time_backward(q, k, v, wl.p, max(3, steps // 4), 2)
+            bflops = 2 * wl.flops               # 8 d flops per causal pair
+            res[name]["backward"] = {
+                "ms": round(bt["saved"], 4),
+                "tflops": round(bflops / (bt["saved"] * 1e-3) / 1e12, 2),
+                "recompute_ms": round(bt["recompute"], 4),
+                "train_fwd_ms": round(bt["train_fwd"], 4)}
         del q, k, v, inp
     return res
 
@@ -525,7 +535,8 @@ def main():
     if not args.no_configs:
         log("bench: other workloads")
         others = [n for n in ("gpt2s", "wide") if n != wl.name]
-        line["configs"] = time_configs(others, args.steps, args.warmup)
+        line["configs"] = time_configs(others, args.steps, args.warmup,
+                                       backward=not args.no_backward)
     if not args.no_variants:
         log("bench: ablation variants")
         vt = time_variants(q, k, v, wl.p, args.steps, args.warmup)

@@ -32,10 +32,12 @@
 // operands (K in dq, Q and dO in dkdv; four consecutive rows of one dim)
 // come from the same tiles by the LDS transpose read (ds_read_b64_tr_b16).
 // Softplus is exact (softplus2_acc, or sp_sig with its derivative from the
-// same exp2), except that at d = 64 query blocks without a deep row, and
-// key blocks whose query blocks have none, take plain log2(1 + 2^t), the
-// forward's rule (at every p: p = 3 training backward 139 -> 129 us at
-// B8 H12 L1024, recomputing 178 -> 164 us).
+// same exp2), except that query blocks without a deep row take plain
+// log2(1 + 2^t), the forward's rule, and at d = 64 so do key blocks whose
+// query blocks have none (at every p: p = 3 training backward 139 -> 129 us
+// at B8 H12 L1024, recomputing 178 -> 164 us; the query side at d = 128:
+// B2 H32 L4096 p = 15 training backward 1864 -> 1813 us, recomputing
+// 2067 -> 2014 us, gradients bitwise unchanged).
 #pragma once
 
 #include "lssar_bwd.hpp"
@@ -474,9 +476,17 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
 
         if constexpr (MODE == 0) {
             if (saved) {
-                // the training forward's statistics replace pass 1
+                // the training forward's statistics replace pass 1; the
+                // block's deep-row flag from their largest scores
                 if (qvalid)
                     load_row_stats(saved, (size_t)bh * L + qi, s1, tmax);
+                __syncthreads();                   // earlier readers of the flag done
+                if (tid == 0)
+                    *deep_flag = 0;
+                __syncthreads();
+                if (qvalid && tmax < kDeep)
+                    *deep_flag = 1;
+                __syncthreads();
             } else {
                 // pass 1 as in the forward: sum max(t, 0) plus log2 of the
                 // product of the factors 1 + 2^-|t| (one exp2 per pair), and
@@ -533,10 +543,9 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             row_consts();
 
             // ---------------- pass 2: Y, P1, P2, Z ----------------
-            // (d = 64, recomputed statistics: a block without a deep row
-            // takes plain log2(1 + 2^t); the flag is final after pass 1)
-            constexpr bool kPlain = D == 64;
-            const bool exact = !kPlain || saved || *deep_flag;
+            // (a block without a deep row takes plain log2(1 + 2^t); the
+            // flag is final after pass 1)
+            const bool exact = *deep_flag;
             float Y = 0.0f, P1 = 0.0f, P2 = 0.0f, Z = 0.0f;
             auto pass2 = [&](auto exact_tag) {
               tile_loop(true, [&](int kt, const unsigned char* base, auto diag_tag) {
@@ -568,7 +577,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             };
             if (exact)
                 pass2(std::true_type{});
-            else if constexpr (kPlain)
+            else
                 pass2(std::false_type{});
 #pragma unroll
             for (int m = 16; m <= 32; m <<= 1) {
@@ -592,21 +601,17 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 adl = a.w;
                 Ec = st[4];
             }
-            // (d = 64: a block without a deep row, by the largest scores in
+            // (a block without a deep row, by the largest scores in
             // the coefficient records, takes plain log2(1 + 2^t))
-            constexpr bool kPlain = D == 64;
-            bool exact = true;
-            if constexpr (kPlain) {
-                const float tm = qvalid ? stats[((size_t)bh * L + qi) * kBwdRowStats + 7] : 0.0f;
-                __syncthreads();                   // earlier readers of the flag done
-                if (tid == 0)
-                    deep_flag[0] = 0;
-                __syncthreads();
-                if (tm < kDeep)
-                    deep_flag[0] = 1;
-                __syncthreads();
-                exact = deep_flag[0] != 0;
-            }
+            const float tm = qvalid ? stats[((size_t)bh * L + qi) * kBwdRowStats + 7] : 0.0f;
+            __syncthreads();                       // earlier readers of the flag done
+            if (tid == 0)
+                deep_flag[0] = 0;
+            __syncthreads();
+            if (tm < kDeep)
+                deep_flag[0] = 1;
+            __syncthreads();
+            const bool exact = deep_flag[0] != 0;
             f32x4 acc[DS];
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds)
@@ -652,7 +657,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             };
             if (exact)
                 dq_pass(std::true_type{});
-            else if constexpr (kPlain)
+            else
                 dq_pass(std::false_type{});
             store_dq(acc);
         } else {
@@ -669,21 +674,17 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             // row (largest score below kDeep) takes plain log2(1 + 2^t), as
             // the forward does, and a block with one the exact Softplus (a
             // uniform branch) -------
-            constexpr bool kPlain = true;
             if (qvalid)
                 load_row_stats(saved, (size_t)bh * L + qi, s1, tmax);
             store_tmax();
-            bool blk_deep = true;
-            if constexpr (kPlain) {
-                __syncthreads();                   // earlier readers of the flag done
-                if (tid == 0)
-                    deep_flag[0] = 0;
-                __syncthreads();
-                if (qvalid && tmax < kDeep)
-                    deep_flag[0] = 1;
-                __syncthreads();
-                blk_deep = deep_flag[0] != 0;
-            }
+            __syncthreads();                       // earlier readers of the flag done
+            if (tid == 0)
+                deep_flag[0] = 0;
+            __syncthreads();
+            if (qvalid && tmax < kDeep)
+                deep_flag[0] = 1;
+            __syncthreads();
+            const bool blk_deep = deep_flag[0] != 0;
             float d0 = 0.0f;
             if (qvalid) {
 #pragma unroll
@@ -776,9 +777,9 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 }
               });
             };
-            if (!kPlain || blk_deep)
+            if (blk_deep)
                 one_pass(std::true_type{});
-            else if constexpr (kPlain)
+            else
                 one_pass(std::false_type{});
 #pragma unroll
             for (int m = 16; m <= 32; m <<= 1) {
@@ -788,7 +789,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 Pd += __shfl_xor(Pd, m);
             }
             const float Dl = degen ? 0.0f : P1 / Y;
-            row_coefs(Y, d0 + Dl, Pd - Dl * Z, !kPlain || blk_deep);
+            row_coefs(Y, d0 + Dl, Pd - Dl * Z, blk_deep);
             // the coefficients of query 4 grp + r sit in lane 4 grp + r
             f32x4 acc[DS];
 #pragma unroll
@@ -1015,9 +1016,10 @@ __attribute__((amdgpu_waves_per_eu(3))) void lssar_bwd_kside_kernel(
         // are without a deep row takes plain log2(1 + 2^t) for every tile,
         // a workgroup-uniform choice made once from the blocks' flags
         // (record field 6, stored by the query-side kernels); at d = 128
-        // the second path would cost occupancy, and every tile is exact.  (Chosen per tile inside the loop,
-        // the two paths' accumulators met in different registers: 16
-        // 64-bit copies per tile.)
+        // the second path spills in the tile loop, and every tile is
+        // exact.  (Chosen per tile inside the loop, the two paths'
+        // accumulators met in different registers: 16 64-bit copies per
+        // tile.)
         constexpr bool kPlain = D == 64;
         bool exact = true;
         if constexpr (kPlain) {

@@ -77,9 +77,10 @@ enum {
 /* Workspace for every forward entry point that takes one, in bytes, each
  * part rounded up to 256: one key factor per key row (fp32 for bf16 inputs:
  * 4*B*H*L; fp64 for fp32 inputs: 8*B*H*L); for bf16 inputs also a
- * transposed copy of V (B*H*d*Lp bf16, Lp = L rounded up to 64), an f16
- * copy of K (B*H*L*d f16) and the attention kernel's dispatch table (8
- * bytes per workgroup, lssar_fwd_schedule).  Returns 0 for invalid sizes. */
+ * transposed copy of V (B*H*d*Lp bf16, Lp = L rounded up to 64), two f16
+ * copies of K (B*H*L*d f16 each: exact rows scaled by powers of two, and
+ * the normalised rows) and the attention kernel's dispatch table (8 bytes
+ * per workgroup, lssar_fwd_schedule).  Returns 0 for invalid sizes. */
 size_t lssar_workspace_bytes(int B, int H, int L, int d, int dtype);
 
 /* LSSAR causal attention forward (Key designs 1-3 above) with a
@@ -102,7 +103,7 @@ int lssar_attn_fwd(const void* q, const void* k, const void* v, void* out,
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * lssar_attn_fwd with no allocation and no workspace argument.  Its
  * workspace is a static device array of the library, one per GPU, of
- * lssar_noalloc_scratch_bytes() = 64 MiB, held from the library's first use
+ * lssar_noalloc_scratch_bytes() = 96 MiB, held from the library's first use
  * on that GPU until the process ends (bf16 at d = 64 fits up to about 250 K
  * query rows B*H*L, e.g. B1 H12 L16384).
  *  - Arguments, layout and output as for lssar_attn_fwd_ws on the CURRENT
@@ -126,8 +127,9 @@ size_t lssar_noalloc_scratch_bytes(void);
  * score): for fp32 inputs fk[bh*L + j] = 1 / max(|k_j|_2, 1e-12) in fp64;
  * for bf16 inputs, with e_j the power of two that brings row j's largest
  * magnitude into [2^14, 2^15), the exact f16 row k_j 2^-e_j and
- * fk[bh*L + j] = 2^e_j / max(|k_j|_2, 1e-12) in fp32, V transposed per
- * head, and the attention kernel's dispatch table.  Workspace rules as for
+ * fk[bh*L + j] = 2^e_j / max(|k_j|_2, 1e-12) in fp32, the normalised row
+ * k_j / max(|k_j|_2, 1e-12) rounded to f16, V transposed per head, and the
+ * attention kernel's dispatch table.  Workspace rules as for
  * lssar_attn_fwd_ws; a bad workspace is LSSAR_EWORKSPACE. */
 int lssar_prep(const void* k, const void* v, void* workspace,
                size_t workspace_bytes, int B, int H, int L, int d, int dtype,

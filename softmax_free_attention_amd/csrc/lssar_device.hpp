@@ -141,6 +141,21 @@ __device__ __forceinline__ float softplus2_acc(float t)
     return e < (1.0f / 256.0f) ? series : __builtin_amdgcn_logf(1.0f + e);
 }
 
+// Maxima of scores straight from the matrix cores.  fmaxf ignores a quiet
+// NaN, and in IEEE mode the compiler quiets both operands first (one
+// v_max_f32 x, x per score) unless it can prove them canonical, which it
+// cannot for an MFMA result; the NaN-propagating maximum needs no quieting
+// (v_maximum3_f32).  Scores of finite inputs are never NaN, and a masked
+// pair's -inf behaves the same under both.
+__device__ __forceinline__ float max_scores(float a, float b)
+{
+    return __builtin_elementwise_maximum(a, b);
+}
+__device__ __forceinline__ float max3_scores(float a, float b, float c)
+{
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
 // What a run of pass 1 accumulates: S1 (in product form) and the row max,
 // S1 from softplus2_acc and the row max (blocks computed again), or the row
 // max alone.
@@ -341,6 +356,9 @@ __device__ __forceinline__ int f16_row_exponent(float mx)
 //  * fk[bh*L + j] = 2^e_j / max(|k_j|_2, 1e-12) for the block's keys (fp64
 //    sum of squares, one rounding to fp32), so that fk_j (q . K16_j) =
 //    (q . k_j) / |k_j|;
+//  * KN16[bh][j] = f16(k_j / max(|k_j|_2, 1e-12)) (unless KN16 is null): the
+//    normalised key rounded to f16, the fast path's operand, whose scores
+//    need no per-pair key factor;
 //  * Vt[bh][e][kb*64 + vt_pos(j)] = V[bh][kb*64 + j][e], zero for keys >= L;
 //    rows of Vt hold Lp (L rounded up to 64) entries.
 // V goes through LDS: each thread then gathers two adjacent dims of 8 keys
@@ -352,8 +370,8 @@ __device__ __forceinline__ int f16_row_exponent(float mx)
 template <int D>
 __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
     const __bf16* __restrict__ K, const __bf16* __restrict__ V, float* __restrict__ fk,
-    __bf16* __restrict__ Vt, _Float16* __restrict__ K16, int2* __restrict__ sched, int BH, int L,
-    int Lp)
+    __bf16* __restrict__ Vt, _Float16* __restrict__ K16, _Float16* __restrict__ KN16,
+    int2* __restrict__ sched, int BH, int L, int Lp)
 {
     constexpr int RS = D + 2;                  // LDS row stride (elements), odd word count
     constexpr int LPR = D / 8;                 // lanes per key row for the norms
@@ -405,8 +423,20 @@ __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
             for (int i = 0; i < 8; ++i)
                 h[i] = (_Float16)(xv[i] * sc);
             *reinterpret_cast<f16x8*>(K16 + hoff + (size_t)kg * D + sub * 8) = h;
+            const double inv = 1.0 / fmax(sqrt(ss), 1e-12);
             if (sub == 0)
-                fk[(size_t)bh * L + kg] = (float)ldexp(1.0 / fmax(sqrt(ss), 1e-12), ex);
+                fk[(size_t)bh * L + kg] = (float)ldexp(inv, ex);
+            if (KN16) {
+                // fp32 product, then f16 (a direct fp64 -> f16 conversion
+                // is a long integer sequence on this part); the fp32 step
+                // adds at most 2^-23 relative to the f16 rounding
+                const float invf = (float)inv;
+                f16x8 hn;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    hn[i] = (_Float16)(xv[i] * invf);
+                *reinterpret_cast<f16x8*>(KN16 + hoff + (size_t)kg * D + sub * 8) = hn;
+            }
         }
     }
 
@@ -545,20 +575,22 @@ __device__ __forceinline__ void load_row_stats(const double* ST, size_t row, C& 
 // d = 64; 64-key tiles there allowed one buffer only (two need 66 KB and
 // halve the occupancy), which left every tile load exposed.
 //
-// Scores.  The prep kernel's K16 rows are exact (k_j scaled by 2^-e_j) and
-// fk_j = 2^e_j / |k_j|.  The query operand is either
-//  * fast: f16(lambda_i q_i / |q_i|), the row factor folded in and rounded
-//    to f16 once (2^-12 relative per element), so that t = acc * fk_j: one
-//    multiply per pair instead of two in each pass; or
-//  * exact: q_i 2^-e_i, exact in f16, with t = acc * (fk_j * lambda_i'),
-//    the scores of the raw inputs with fp32 accumulation.
+// Scores.  The prep kernel's K16 rows are exact (k_j scaled by 2^-e_j),
+// fk_j = 2^e_j / |k_j|, and its KN16 rows the normalised keys rounded to
+// f16.  The operands are either
+//  * fast: f16(lambda_i q_i / |q_i|) against KN16, both factors folded in
+//    and each operand rounded to f16 once, so that t = acc: no multiply per
+//    pair (two before the factors were folded in); or
+//  * exact: q_i 2^-e_i against K16, both exact in f16, with
+//    t = acc * (fk_j * lambda_i'), the scores of the raw inputs with fp32
+//    accumulation.
 // The deep-row redo and the training forward (EXACT: its row statistics
 // feed the backward) take the exact operand; the plain forward the fast one.
 template <int D, int P, int PHI, bool RW, bool EXACT>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const _Float16* __restrict__ K16,
-    const __bf16* __restrict__ VT, __bf16* __restrict__ O,
+    const _Float16* __restrict__ KN16, const __bf16* __restrict__ VT, __bf16* __restrict__ O,
     const float* __restrict__ FK, const int2* __restrict__ sched, int L, int Lp,
     double lam_scale, float eps, int p_rt, double* __restrict__ ST)
 {
@@ -594,8 +626,10 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
     const __bf16* Qh = Q + hoff;
     __bf16* Oh = O + hoff;
 
-    // this head's K, V^T and key factors; buffer reads past them return zeros
+    // this head's K (exact and normalised), V^T and key factors; buffer
+    // reads past them return zeros
     const void* kbase = K16 + hoff;
+    const void* knbase = EXACT ? kbase : KN16 + hoff;
     const unsigned kbytes = (unsigned)L * D * 2u;
     const void* vbase = VT + (size_t)bh * D * Lp;
     const unsigned vbytes = (unsigned)D * Lp * 2u;
@@ -626,19 +660,20 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
     for (int c2 = 0; c2 < C2; ++c2)
         vrd[c2] = T::KBYTES + (row16 * T::VS + ((4 * c2 + grp) ^ T::vswz(row16))) * 16;
 
-    auto issue = [&](int kt, int buf, bool with_v) {
+    // fast: the normalised keys and no key factors
+    auto issue = [&](int kt, int buf, bool with_v, bool fast) {
         unsigned char* base = smem(buf);
 #pragma unroll
         for (int n = 0; n < T::KLOADS; ++n)
-            load16_to_lds(kbase, kbytes, base + (wave * T::KLOADS + n) * 1024, kld[n],
-                            kt * BK * D * 2);
+            load16_to_lds(fast ? knbase : kbase, kbytes, base + (wave * T::KLOADS + n) * 1024,
+                          kld[n], kt * BK * D * 2);
         if (with_v) {
 #pragma unroll
             for (int n = 0; n < T::VLOADS; ++n)
                 load16_to_lds(vbase, vbytes, base + T::KBYTES + (wave * T::VLOADS + n) * 1024,
                                 vld[n], kt * BK * 2);
         }
-        if (wave == 0)
+        if (wave == 0 && !fast)
             load4_to_lds(fbase, fbytes, base + T::KBYTES + T::VBYTES, lane * 4, kt * BK * 4);
     };
 
@@ -718,16 +753,17 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
             }
             return acc;
         };
-        // t = acc * f_key (fast) or acc * lam * f_key (exact); masked
-        // (t = -inf) on diagonal tiles
+        // t = acc (fast) or acc * lam * f_key (exact); masked (t = -inf) on
+        // diagonal tiles
         auto scale_block = [&](int kt, const unsigned char* base, int ks, f32x4 acc, bool diag) {
-            const f32x4 f4 = *reinterpret_cast<const f32x4*>(
-                base + T::KBYTES + T::VBYTES + (16 * ks + 4 * grp) * 4);
             f32x4 t;
-            if constexpr (FAST)
-                t = acc * f4;
-            else
+            if constexpr (FAST) {
+                t = acc;
+            } else {
+                const f32x4 f4 = *reinterpret_cast<const f32x4*>(
+                    base + T::KBYTES + T::VBYTES + (16 * ks + 4 * grp) * 4);
                 t = acc * (f4 * lam);
+            }
             if (diag) {
                 const int k0 = kt * BK + 16 * ks + 4 * grp;
 #pragma unroll
@@ -776,8 +812,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         pos_sum += softplus2_acc(t[r]);
-                    tmax = fmaxf(fmaxf(tmax, t[0]), t[1]);
-                    tmax = fmaxf(fmaxf(tmax, t[2]), t[3]);
+                    tmax = max3_scores(tmax, t[0], t[1]);
+                    tmax = max3_scores(tmax, t[2], t[3]);
                 } else if constexpr (PHI == kPhiSoftplus) {
                     f32x4 u;
 #pragma unroll
@@ -785,9 +821,9 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
                         u[r] = __builtin_amdgcn_exp2f(-fabsf(t[r]));
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        pos_sum += fmaxf(t[r], 0.0f);
-                    tmax = fmaxf(fmaxf(tmax, t[0]), t[1]);
-                    tmax = fmaxf(fmaxf(tmax, t[2]), t[3]);
+                        pos_sum += max_scores(t[r], 0.0f);
+                    tmax = max3_scores(tmax, t[0], t[1]);
+                    tmax = max3_scores(tmax, t[2], t[3]);
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         prod = __builtin_fmaf(prod, u[r], prod);
@@ -795,8 +831,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         pos_sum += sigmoid2(t[r]);
-                    tmax = fmaxf(fmaxf(tmax, t[0]), t[1]);
-                    tmax = fmaxf(fmaxf(tmax, t[2]), t[3]);
+                    tmax = max3_scores(tmax, t[0], t[1]);
+                    tmax = max3_scores(tmax, t[2], t[3]);
                 }
             }
             if constexpr (KIND == kPass1Sum && PHI == kPhiSoftplus)
@@ -817,12 +853,12 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();                   // tile kt landed; buf^1 free
                 if (kt + 1 < ntiles)
-                    issue(kt + 1, buf ^ 1, with_v);
+                    issue(kt + 1, buf ^ 1, with_v, FAST);
                 if (wave_active)
                     body(kt, smem(buf), diag_tag);
             };
             __syncthreads();                       // earlier readers done with the buffers
-            issue(0, 0, with_v);
+            issue(0, 0, with_v, FAST);
             for (int kt = 0; kt < kdiag; ++kt)
                 step(kt, std::false_type{});
             if constexpr (BK == kBQ16) {

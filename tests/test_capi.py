@@ -66,8 +66,8 @@ def test_library_has_no_oracle_dependency(L):
 
 def test_noalloc_host_checks(L):
     """lssar_attn_fwd_noalloc validates on the host before any HIP call: bad
-    arguments, and an input whose workspace exceeds the 64 MiB scratch."""
-    assert sfa.lssar_noalloc_scratch_bytes() == 64 << 20
+    arguments, and an input whose workspace exceeds the 96 MiB scratch."""
+    assert sfa.lssar_noalloc_scratch_bytes() == 96 << 20
     f = L.lssar_attn_fwd_noalloc
     q, k, v, o = A, A + STEP, A + 2 * STEP, A + 3 * STEP
     assert f(0, k, v, o, 1, 2, 64, 64, 3, 1e-4, 1, None) == sfa.LSSAR_EINVAL
@@ -78,7 +78,7 @@ def test_noalloc_host_checks(L):
 
 
 def test_version_and_status_strings(L):
-    assert sfa.lssar_version() == 800
+    assert sfa.lssar_version() == 900
     assert sfa.lssar_status_str(0) == "ok"
     for st in (-1, -2, -3, -4, -5, 7):
         s = sfa.lssar_status_str(st)
@@ -96,11 +96,12 @@ def test_workspace_bytes(L):
     # attention kernel's dispatch table (8 bytes per workgroup, rounded up)
     def r256(x):
         return (x + 255) // 256 * 256
-    # and the f16 copy of K
+    # and the two f16 copies of K (exact rows scaled by powers of two, and
+    # the normalised rows)
     assert sfa.lssar_workspace_bytes(1, 12, 8192, 64, sfa.LSSAR_BF16) == \
-        4 * 12 * 8192 + 2 * 12 * 64 * 8192 * 2 + r256(8 * 1536)
+        4 * 12 * 8192 + 3 * 12 * 64 * 8192 * 2 + r256(8 * 1536)
     assert sfa.lssar_workspace_bytes(2, 3, 77, 128, sfa.LSSAR_BF16) == \
-        2048 + 6 * 128 * 128 * 2 + r256(6 * 77 * 128 * 2) + \
+        2048 + 6 * 128 * 128 * 2 + 2 * r256(6 * 77 * 128 * 2) + \
         r256(8 * len(sfa.lssar_fwd_schedule(2, 3, 77)))
     assert sfa.lssar_workspace_bytes(0, 1, 1, 64, 0) == 0
     assert sfa.lssar_workspace_bytes(1, 1, 1, 96, 0) == 0

@@ -224,8 +224,8 @@ def test_prep_workspace_contents():
     """The prep step writes 1/max(|k_j|, 1e-12) per key row (fp64 for fp32
     inputs) and, for bf16: V^T with every 64-key block permuted for the
     attention kernel, zero past L; the exact f16 copy of K (rows scaled by
-    powers of two) with the key factor 2^e_j / |k_j|; and the attention
-    kernel's dispatch table."""
+    powers of two) with the key factor 2^e_j / |k_j|; the normalised keys
+    rounded to f16; and the attention kernel's dispatch table."""
     import softmax_free_attention_amd as sfa
     for dtype, d in (("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)):
         L = 77
@@ -264,10 +264,19 @@ def test_prep_workspace_contents():
             ex = np.where(mx > 0, np.frexp(mx)[1] - 15, 0)
             assert np.array_equal(k16.astype(np.float64), k * np.ldexp(1.0, -ex)[..., None])
             assert np.max(np.abs(fk / (want * np.ldexp(1.0, ex)) - 1.0)) < 1e-6
+            # KN16: k_j / max(|k_j|, 1e-12) rounded to f16 (within half an
+            # f16 ulp of the fp64 value, plus the fp32 product's 2^-23
+            # relative; zero rows stay zero)
+            knoff = koff + (2 * 3 * L * d * 2 + 255) // 256 * 256
+            kn16 = raw[knoff:knoff + 2 * 3 * L * d * 2].view(np.float16).reshape(2, 3, L, d)
+            kh = k.astype(np.float64) * want[..., None]
+            half_ulp = np.ldexp(1.0, np.maximum(np.frexp(np.abs(kh))[1] - 12, -25))
+            assert np.all(np.abs(kn16.astype(np.float64) - kh) <= half_ulp + np.abs(kh) * 2.0 ** -22)
+            assert not np.any(kn16[0, 0, 5])
             # the attention kernel's dispatch table: (head, block) per
             # workgroup, as the host-side schedule query gives it
             items = sfa.lssar_fwd_schedule(2, 3, L)
-            soff = koff + (2 * 3 * L * d * 2 + 255) // 256 * 256
+            soff = knoff + (2 * 3 * L * d * 2 + 255) // 256 * 256
             tab = raw[soff:soff + 8 * len(items)].view(np.int32).reshape(-1, 2)
             nqb = (L + 63) // 64
             want_tab = np.array([[x // nqb, x % nqb] if x >= 0 else [-1, -1] for x in items])
@@ -280,7 +289,7 @@ def test_prep_workspace_contents():
         raw = ws.cpu().numpy()
         off = (4 * B * H * L + 255) // 256 * 256 + \
             (B * H * 64 * ((L + 63) // 64 * 64) * 2 + 255) // 256 * 256 + \
-            (B * H * L * 64 * 2 + 255) // 256 * 256
+            2 * ((B * H * L * 64 * 2 + 255) // 256 * 256)
         items = sfa.lssar_fwd_schedule(B, H, L)
         tab = raw[off:off + 8 * len(items)].view(np.int32).reshape(-1, 2)
         nqb = (L + 63) // 64

@@ -199,7 +199,7 @@ def time_path(q, k, v, p, steps, warmup, eps=1e-4, settle_s=0.0, repeats=5):
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for s in range(steps):
         ev[s][0].record(stream)
-        sfa.lssar_prep(k, v, ws, stream=stream)
+        sfa.lssar_prep(k, ws, stream=stream)
         ev[s][1].record(stream)
         sfa.lssar_attn_fwd_prepped(q, k, v, ws, out, p=p, eps=eps, stream=stream)
         ev[s][2].record(stream)

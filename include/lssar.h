@@ -76,8 +76,7 @@ enum {
 
 /* Workspace for every forward entry point that takes one, in bytes, each
  * part rounded up to 256: one key factor per key row (fp32 for bf16 inputs:
- * 4*B*H*L; fp64 for fp32 inputs: 8*B*H*L); for bf16 inputs also a
- * transposed copy of V (B*H*d*Lp bf16, Lp = L rounded up to 64), two f16
+ * 4*B*H*L; fp64 for fp32 inputs: 8*B*H*L); for bf16 inputs also two f16
  * copies of K (B*H*L*d f16 each: exact rows scaled by powers of two, and
  * the normalised rows) and the attention kernel's dispatch table (8 bytes
  * per workgroup, lssar_fwd_schedule).  Returns 0 for invalid sizes. */
@@ -103,7 +102,7 @@ int lssar_attn_fwd(const void* q, const void* k, const void* v, void* out,
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * lssar_attn_fwd with no allocation and no workspace argument.  Its
  * workspace is a static device array of the library, one per GPU, of
- * lssar_noalloc_scratch_bytes() = 96 MiB, held from the library's first use
+ * lssar_noalloc_scratch_bytes() = 64 MiB, held from the library's first use
  * on that GPU until the process ends (bf16 at d = 64 fits up to about 250 K
  * query rows B*H*L, e.g. B1 H12 L16384).
  *  - Arguments, layout and output as for lssar_attn_fwd_ws on the CURRENT
@@ -122,21 +121,21 @@ int lssar_attn_fwd_noalloc(const void* q, const void* k, const void* v,
 /* Size of lssar_attn_fwd_noalloc's per-GPU scratch, in bytes. */
 size_t lssar_noalloc_scratch_bytes(void);
 
-/* The prep step alone (the prep kernels).  Writes into the workspace the
- * key factors (Key design 1's K_j <- K_j / |K_j|_2, kept as a factor of the
- * score): for fp32 inputs fk[bh*L + j] = 1 / max(|k_j|_2, 1e-12) in fp64;
- * for bf16 inputs, with e_j the power of two that brings row j's largest
- * magnitude into [2^14, 2^15), the exact f16 row k_j 2^-e_j and
- * fk[bh*L + j] = 2^e_j / max(|k_j|_2, 1e-12) in fp32, the normalised row
- * k_j / max(|k_j|_2, 1e-12) rounded to f16, V transposed per head, and the
+/* The prep step alone (the prep kernel; it reads K only).  Writes into the
+ * workspace the key factors (Key design 1's K_j <- K_j / |K_j|_2, kept as a
+ * factor of the score): for fp32 inputs fk[bh*L + j] = 1 / max(|k_j|_2,
+ * 1e-12) in fp64; for bf16 inputs, with e_j the power of two that brings
+ * row j's largest magnitude into [2^14, 2^15), the exact f16 row
+ * k_j 2^-e_j and fk[bh*L + j] = 2^e_j / max(|k_j|_2, 1e-12) in fp32, the
+ * normalised row k_j / max(|k_j|_2, 1e-12) rounded to f16, and the
  * attention kernel's dispatch table.  Workspace rules as for
- * lssar_attn_fwd_ws; a bad workspace is LSSAR_EWORKSPACE. */
-int lssar_prep(const void* k, const void* v, void* workspace,
-               size_t workspace_bytes, int B, int H, int L, int d, int dtype,
-               void* stream);
+ * lssar_attn_fwd_ws (it must not overlap k); a bad workspace is
+ * LSSAR_EWORKSPACE. */
+int lssar_prep(const void* k, void* workspace, size_t workspace_bytes, int B,
+               int H, int L, int d, int dtype, void* stream);
 
 /* The attention kernel alone (fused, two passes), reading the workspace
- * that lssar_prep filled for these k and v (stream-ordered after it). */
+ * that lssar_prep filled for this k (stream-ordered after it). */
 int lssar_attn_fwd_prepped(const void* q, const void* k, const void* v,
                            void* workspace, size_t workspace_bytes, void* out,
                            int B, int H, int L, int d, int p, float eps,

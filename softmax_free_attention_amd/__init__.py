@@ -66,7 +66,7 @@ def lib():
         L.lssar_attn_fwd_ws.restype = i
         L.lssar_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
         L.lssar_attn_fwd.restype = i
-        L.lssar_prep.argtypes = [vp, vp, vp, sz, i, i, i, i, i, vp]
+        L.lssar_prep.argtypes = [vp, vp, sz, i, i, i, i, i, vp]
         L.lssar_prep.restype = i
         L.lssar_attn_fwd_prepped.argtypes = [vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, i, vp]
         L.lssar_attn_fwd_prepped.restype = i
@@ -229,12 +229,13 @@ def _ws_args(workspace):
     return _ptr(workspace), workspace.numel() * workspace.element_size()
 
 
-def lssar_prep(k, v, workspace, *, stream=None):
-    """The prep step (prep kernels): key-row inverse norms and, for bf16, V^T, into
-    the workspace."""
-    B, H, L, d, dt = _check_qkv(k, k, v)
+def lssar_prep(k, workspace, *, stream=None):
+    """The prep step (prep kernel, K only): key-row inverse norms and, for bf16,
+    the exact and the normalised f16 keys and the dispatch table, into the
+    workspace."""
+    B, H, L, d, dt = _check_qkv(k, k, k)
     wp, wn = _ws_args(workspace)
-    st = lib().lssar_prep(_ptr(k), _ptr(v), wp, wn, B, H, L, d, dt, _stream_ptr(stream))
+    st = lib().lssar_prep(_ptr(k), wp, wn, B, H, L, d, dt, _stream_ptr(stream))
     _raise(st, "lssar_prep")
     return workspace
 
@@ -242,7 +243,7 @@ def lssar_prep(k, v, workspace, *, stream=None):
 def lssar_attn_fwd_prepped(q, k, v, workspace, out, *, p: int, eps: float = DEFAULT_EPS,
                            stream=None):
     """The attention kernel alone (fused), given a workspace filled by
-    lssar_prep for these k and v."""
+    lssar_prep for this k."""
     B, H, L, d, dt = _check_qkv(q, k, v, out)
     wp, wn = _ws_args(workspace)
     st = lib().lssar_attn_fwd_prepped(_ptr(q), _ptr(k), _ptr(v), wp, wn, _ptr(out), B, H, L, d,

@@ -47,14 +47,14 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout: [fk: key factor per key row, fp32 for bf16 inputs and
-// fp64 for fp32 inputs][Vt: bf16 V^T, bf16 inputs only][K16: f16 copy of K,
-// rows scaled by powers of two, bf16 inputs only][KN16: the normalised keys
-// in f16, bf16 inputs only][sched: the attention kernel's (head, block) per
-// workgroup, int2, bf16 inputs only]
+// fp64 for fp32 inputs][K16: f16 copy of K, rows scaled by powers of two,
+// bf16 inputs only][KN16: the normalised keys in f16, bf16 inputs only]
+// [sched: the attention kernel's (head, block) per workgroup, int2, bf16
+// inputs only]
 struct Layout {
-    size_t fk_bytes, vt_bytes, k16_bytes, kn16_bytes, sched_bytes;
+    size_t fk_bytes, k16_bytes, kn16_bytes, sched_bytes;
     int Lp;
-    size_t total() const { return fk_bytes + vt_bytes + k16_bytes + kn16_bytes + sched_bytes; }
+    size_t total() const { return fk_bytes + k16_bytes + kn16_bytes + sched_bytes; }
 };
 
 Layout layout(long long B, long long H, long long L, int d, int dtype)
@@ -62,7 +62,6 @@ Layout layout(long long B, long long H, long long L, int d, int dtype)
     Layout w;
     w.Lp = (int)((L + lssar::kBK - 1) / lssar::kBK * lssar::kBK);
     w.fk_bytes = round256((size_t)((dtype == LSSAR_F32 ? 8 : 4) * B * H * L));
-    w.vt_bytes = dtype == LSSAR_BF16 ? round256((size_t)(B * H * d) * (size_t)w.Lp * 2) : 0;
     w.k16_bytes = dtype == LSSAR_BF16 ? round256((size_t)(B * H * d) * (size_t)L * 2) : 0;
     w.kn16_bytes = w.k16_bytes;
     w.sched_bytes = 0;
@@ -139,20 +138,20 @@ void launch_knorm_f32(const void* k, double* fk, long nrows, hipStream_t s)
 }
 
 template <int D>
-void launch_prep_bf16(const void* k, const void* v, float* fk, void* vt, void* k16, void* kn16,
-                      int2* sched, int BH, int L, int Lp, hipStream_t s)
+void launch_prep_bf16(const void* k, float* fk, void* k16, void* kn16, int2* sched, int BH, int L,
+                      int Lp, hipStream_t s)
 {
+    const int per_xcd =
+        (int)(lssar::FwdSched(BH, Lp / lssar::kBK).grid() / lssar::kSchedXcds);
     hipLaunchKernelGGL((lssar::lssar_prep_bf16_kernel<D>), dim3(Lp / lssar::kBK, BH),
-                       dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(k),
-                       static_cast<const __bf16*>(v), fk, static_cast<__bf16*>(vt),
+                       dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(k), fk,
                        static_cast<_Float16*>(k16), static_cast<_Float16*>(kn16), sched, BH, L,
-                       Lp);
+                       Lp, per_xcd);
 }
 
 // Where the bf16 workspace parts start.
 struct WsParts {
     float* fk;
-    __bf16* vt;
     _Float16* k16;
     _Float16* kn16;
     int2* sched;
@@ -160,15 +159,15 @@ struct WsParts {
 WsParts ws_parts(void* ws, const Layout& w)
 {
     unsigned char* b = static_cast<unsigned char*>(ws);
-    const size_t o_k16 = w.fk_bytes + w.vt_bytes, o_kn16 = o_k16 + w.k16_bytes;
-    return {reinterpret_cast<float*>(b), reinterpret_cast<__bf16*>(b + w.fk_bytes),
-            reinterpret_cast<_Float16*>(b + o_k16), reinterpret_cast<_Float16*>(b + o_kn16),
+    const size_t o_k16 = w.fk_bytes, o_kn16 = o_k16 + w.k16_bytes;
+    return {reinterpret_cast<float*>(b), reinterpret_cast<_Float16*>(b + o_k16),
+            reinterpret_cast<_Float16*>(b + o_kn16),
             reinterpret_cast<int2*>(b + o_kn16 + w.kn16_bytes)};
 }
 
 // fast_keys: also write the normalised f16 keys, which every bf16 attention
 // kernel but the training forward's (exact scores throughout) reads
-int run_prep(const void* k, const void* v, void* ws, int B, int H, int L, int d, int dtype,
+int run_prep(const void* k, void* ws, int B, int H, int L, int d, int dtype,
              hipStream_t s, bool fast_keys = true)
 {
     const Layout w = layout(B, H, L, d, dtype);
@@ -177,10 +176,9 @@ int run_prep(const void* k, const void* v, void* ws, int B, int H, int L, int d,
         const WsParts pt = ws_parts(ws, w);
         void* kn16 = fast_keys ? pt.kn16 : nullptr;
         if (d == 64)
-            launch_prep_bf16<64>(k, v, pt.fk, pt.vt, pt.k16, kn16, pt.sched, B * H, L, w.Lp, s);
+            launch_prep_bf16<64>(k, pt.fk, pt.k16, kn16, pt.sched, B * H, L, w.Lp, s);
         else
-            launch_prep_bf16<128>(k, v, pt.fk, pt.vt, pt.k16, kn16, pt.sched, B * H, L, w.Lp,
-                                  s);
+            launch_prep_bf16<128>(k, pt.fk, pt.k16, kn16, pt.sched, B * H, L, w.Lp, s);
     } else {
         double* fk = static_cast<double*>(ws);
         if (d == 64)
@@ -208,15 +206,16 @@ void launch_fwd(const void* q, const void* k, const void* v, void* ws, void* out
             if (stats) {
                 hipLaunchKernelGGL((lssar::lssar_fwd_bf16_kernel<D, P, PHI, RW, true>), grid,
                                    dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(q),
-                                   pt.k16, nullptr, pt.vt, static_cast<__bf16*>(out), pt.fk,
-                                   pt.sched, L, w.Lp, lam_scale, eps, p, stats);
+                                   pt.k16, nullptr, static_cast<const __bf16*>(v),
+                                   static_cast<__bf16*>(out), pt.fk, pt.sched, L, lam_scale, eps,
+                                   p, stats);
                 return;
             }
         }
         hipLaunchKernelGGL((lssar::lssar_fwd_bf16_kernel<D, P, PHI, RW, false>), grid,
                            dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(q), pt.k16,
-                           pt.kn16, pt.vt, static_cast<__bf16*>(out), pt.fk, pt.sched, L, w.Lp,
-                           lam_scale, eps, p, nullptr);
+                           pt.kn16, static_cast<const __bf16*>(v), static_cast<__bf16*>(out),
+                           pt.fk, pt.sched, L, lam_scale, eps, p, nullptr);
     } else {
         const int nqb = (L + lssar::kBQ32 - 1) / lssar::kBQ32;
         hipLaunchKernelGGL((lssar::lssar_fwd_f32_kernel<D, P, PHI, RW>),
@@ -326,7 +325,7 @@ int fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H,
     hipStream_t s = static_cast<hipStream_t>(stream);
     // the training forward (exact scores) does not read the normalised keys
     const bool training = stats && var.phi == LSSAR_PHI_SOFTPLUS && var.reweight;
-    st = run_prep(k, v, workspace, B, H, L, d, dtype, s, !training);
+    st = run_prep(k, workspace, B, H, L, d, dtype, s, !training);
     if (st != LSSAR_OK)
         return st;
     return run_fwd(q, k, v, workspace, out, B, H, L, d, p, eps, dtype, s, var, stats);
@@ -580,7 +579,7 @@ int lssar_attn_fwd(const void* q, const void* k, const void* v, void* out, int B
     hipError_t e = hipMallocAsync(&ws, bytes, s);
     if (e != hipSuccess)
         return hip_fail(e);
-    st = run_prep(k, v, ws, B, H, L, d, dtype, s);
+    st = run_prep(k, ws, B, H, L, d, dtype, s);
     if (st == LSSAR_OK)
         st = run_fwd(q, k, v, ws, out, B, H, L, d, p, eps, dtype, s);
     e = hipFreeAsync(ws, s);
@@ -594,7 +593,7 @@ int lssar_attn_fwd(const void* q, const void* k, const void* v, void* out, int B
 // uses its name as an address (on the host it is only a stand-in): each
 // device's address comes from hipGetSymbolAddress, taken once per device
 // with that device current, and is what the kernels receive.
-constexpr size_t kScratchBytes = (size_t)96 << 20;
+constexpr size_t kScratchBytes = (size_t)64 << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
@@ -635,7 +634,7 @@ int lssar_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* ou
     if (st != LSSAR_OK)
         return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = run_prep(k, v, ws, B, H, L, d, dtype, s);
+    st = run_prep(k, ws, B, H, L, d, dtype, s);
     if (st != LSSAR_OK)
         return st;
     return run_fwd(q, k, v, ws, out, B, H, L, d, p, eps, dtype, s);
@@ -643,22 +642,22 @@ int lssar_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* ou
 
 size_t lssar_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
-int lssar_prep(const void* k, const void* v, void* workspace, size_t workspace_bytes, int B,
-               int H, int L, int d, int dtype, void* stream)
+int lssar_prep(const void* k, void* workspace, size_t workspace_bytes, int B, int H, int L,
+               int d, int dtype, void* stream)
 {
-    if (!k || !v)
+    if (!k)
         return LSSAR_EINVAL;
     int st = validate_shape(B, H, L, d, dtype);
     if (st != LSSAR_OK)
         return st;
-    if (!aligned16(k) || !aligned16(v))
+    if (!aligned16(k))
         return LSSAR_EINVAL;
     const size_t tbytes = (size_t)B * H * L * d * elem_bytes(dtype);
-    st = validate_ws(workspace, workspace_bytes, layout(B, H, L, d, dtype), tbytes, k, v,
+    st = validate_ws(workspace, workspace_bytes, layout(B, H, L, d, dtype), tbytes, k, nullptr,
                      nullptr, nullptr);
     if (st != LSSAR_OK)
         return st;
-    return run_prep(k, v, workspace, B, H, L, d, dtype, static_cast<hipStream_t>(stream));
+    return run_prep(k, workspace, B, H, L, d, dtype, static_cast<hipStream_t>(stream));
 }
 
 int lssar_attn_fwd_prepped(const void* q, const void* k, const void* v, void* workspace,

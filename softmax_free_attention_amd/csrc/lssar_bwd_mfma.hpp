@@ -45,7 +45,6 @@
 
 namespace lssar {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Softplus2(t) (exact for every t, as softplus2_acc) and its derivative
 // sigma(t ln 2) = e / (1 + e), e = 2^t, from one exp2.
@@ -69,15 +68,6 @@ __device__ __forceinline__ void sp_sig_plain(float t, float& sp, float& sig)
     const float ope = 1.0f + e;
     sp = __builtin_amdgcn_logf(ope);
     sig = e * __builtin_amdgcn_rcpf(ope);
-}
-
-// Four 16-bit elements by the LDS transpose read (ds_read_b64_tr_b16): see
-// the key-side kernel for the lane layout.
-__device__ __forceinline__ bf16x4 lds_read_tr16(const unsigned char* p)
-{
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-    return __builtin_bit_cast(bf16x4, v);
 }
 
 // Four fp32 values as the bf16 operand of the 16x16x16 MFMA (round to

@@ -326,19 +326,6 @@ __global__ __launch_bounds__(kThreads) void lssar_knorm_f32_kernel(const float* 
         fk[row] = 1.0 / fmax(sqrt(ss), 1e-12);
 }
 
-// Position of key `key` (0..63 of a 64-key block) inside a row of V^T.  With
-// key = 32 c + 16 h + 4 g + r the position is 32 c + 8 g + 4 h + r, so the 8
-// keys that lane group g feeds to one 32-key MFMA step (taken from two
-// 16-key score blocks) sit in one 16-byte word.
-__device__ __forceinline__ int vt_pos(int key)
-{
-    return (key & 32) + (((key >> 2) & 3) << 3) + (((key >> 4) & 1) << 2) + (key & 3);
-}
-__device__ __forceinline__ int vt_key(int pos)
-{
-    return (pos & 32) + (((pos >> 2) & 1) << 4) + (((pos >> 3) & 3) << 2) + (pos & 3);
-}
-
 // Exponent e that brings a row whose largest magnitude is mx into
 // [2^14, 2^15) when scaled by 2^-e (0 for a zero row): every bf16 value of
 // the row is then an f16 value (no overflow; a value below 2^-29 mx goes
@@ -359,34 +346,31 @@ __device__ __forceinline__ int f16_row_exponent(float mx)
 //  * KN16[bh][j] = f16(k_j / max(|k_j|_2, 1e-12)) (unless KN16 is null): the
 //    normalised key rounded to f16, the fast path's operand, whose scores
 //    need no per-pair key factor;
-//  * Vt[bh][e][kb*64 + vt_pos(j)] = V[bh][kb*64 + j][e], zero for keys >= L;
-//    rows of Vt hold Lp (L rounded up to 64) entries.
-// V goes through LDS: each thread then gathers two adjacent dims of 8 keys
-// with 4-byte LDS reads and writes two 16-byte pieces of V^T.
 //  * sched[w] = (bh, qb) for the attention kernel's workgroup w
 //    (lssar_sched.hpp): each workgroup enters the query block qb = kb of
-//    its head (the blocks and the 64-key blocks coincide), and the first
-//    workgroup also marks the empty indices (-1, -1).
+//    its head (the blocks and the 64-key blocks coincide), and the
+//    workgroups (kb, 0) also mark the empty indices (-1, -1) of XCDs
+//    kb, kb + nkb, ... up to per_xcd, the grid's indices per XCD (from the
+//    host).  (One thread that counted all eight slices and wrote every
+//    empty index set the end of the kernel.)
 template <int D>
 __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
-    const __bf16* __restrict__ K, const __bf16* __restrict__ V, float* __restrict__ fk,
-    __bf16* __restrict__ Vt, _Float16* __restrict__ K16, _Float16* __restrict__ KN16,
-    int2* __restrict__ sched, int BH, int L, int Lp)
+    const __bf16* __restrict__ K, float* __restrict__ fk, _Float16* __restrict__ K16,
+    _Float16* __restrict__ KN16, int2* __restrict__ sched, int BH, int L, int Lp, int per_xcd)
 {
-    constexpr int RS = D + 2;                  // LDS row stride (elements), odd word count
     constexpr int LPR = D / 8;                 // lanes per key row for the norms
-    __shared__ __attribute__((aligned(16))) uint32_t tile[64 * RS / 2];
     const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
     const size_t hoff = (size_t)bh * L * D;
 
     if (tid == 0) {
         const FwdSched sc(BH, Lp / kBK);
         sched[sc.index_of(bh, kb)] = make_int2(bh, kb);
-        if (kb == 0 && bh == 0) {
-            const int m = (int)(sc.grid() / kSchedXcds);
-            for (int x = 0; x < kSchedXcds; ++x)
-                for (int l = sc.count(x); l < m; ++l)
-                    sched[l * kSchedXcds + x] = make_int2(-1, -1);
+    }
+    if (bh == 0 && tid < 64) {
+        for (int x = kb; x < kSchedXcds; x += (int)gridDim.x) {
+            const int n = FwdSched(BH, Lp / kBK).count(x);
+            for (int l = n + tid; l < per_xcd; l += 64)
+                sched[l * kSchedXcds + x] = make_int2(-1, -1);
         }
     }
 
@@ -439,40 +423,6 @@ __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
             }
         }
     }
-
-    // V block -> LDS (row stride RS elements: 4-byte aligned rows)
-#pragma unroll
-    for (int n = 0; n < 64 * D / 8 / kThreads; ++n) {
-        const int c = tid + n * kThreads;
-        const int key = c / (D / 8), col8 = c % (D / 8);
-        const int kg = kb * 64 + key;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (kg < L)
-            w = *reinterpret_cast<const u32x4*>(V + hoff + (size_t)kg * D + col8 * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            tile[(key * RS + col8 * 8) / 2 + e] = w[e];
-    }
-    __syncthreads();
-    // V^T: thread -> dims (2m, 2m+1), positions 8 p8 .. 8 p8 + 7
-    __bf16* Vth = Vt + (size_t)bh * D * Lp;
-#pragma unroll
-    for (int n = 0; n < (D / 2) * 8 / kThreads; ++n) {
-        const int c = tid + n * kThreads;
-        const int m = c / 8, p8 = c % 8;
-        uint32_t wv[8];
-#pragma unroll
-        for (int h = 0; h < 8; ++h)
-            wv[h] = tile[(vt_key(8 * p8 + h) * RS) / 2 + m];     // (v[key][2m], v[key][2m+1])
-        u32x4 lo, hi;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            lo[h] = __builtin_amdgcn_perm(wv[2 * h + 1], wv[2 * h], 0x05040100u);
-            hi[h] = __builtin_amdgcn_perm(wv[2 * h + 1], wv[2 * h], 0x07060302u);
-        }
-        *reinterpret_cast<u32x4*>(Vth + (size_t)(2 * m) * Lp + kb * 64 + 8 * p8) = lo;
-        *reinterpret_cast<u32x4*>(Vth + (size_t)(2 * m + 1) * Lp + kb * 64 + 8 * p8) = hi;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -501,28 +451,44 @@ __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
 // t = -inf, which adds exactly 0 to every sum in both passes (2^-inf = 0,
 // max(-inf, 0) = 0; in pass 2 Softplus2 = 0 gives y = clamp(-tau c) = 0).
 
-// One tile of BK keys: K (BK rows of D), V^T (D rows of BK keys) and the BK
+// One tile of BK keys: K and V (BK rows of D each, row-major) and the BK
 // key factors (the area holds 64; the loader writes 64).
 template <int D, int BK>
 struct Bf16Tile {
-    static constexpr int R = D / 8;                       // 16-byte slots per K row
-    static constexpr int VS = BK / 8;                     // 16-byte slots per V^T row
+    static constexpr int R = D / 8;                       // 16-byte slots per row
     static constexpr int KBYTES = BK * D * 2;             // K tile
-    static constexpr int VBYTES = D * BK * 2;             // V^T tile
+    static constexpr int VBYTES = BK * D * 2;             // V tile
     static constexpr int FBYTES = 64 * 4;                 // key factors
     static constexpr int BYTES = KBYTES + VBYTES + FBYTES;
     static constexpr int KLOADS = KBYTES / 1024 / kWaves; // 1 KB wave-loads per wave
     static constexpr int VLOADS = VBYTES / 1024 / kWaves;
     // XOR swizzle of a K row's slots (key & 15 is all that matters)
     __device__ static int kswz(int key) { return R == 8 ? ((key >> 1) & 7) : (key & 15); }
-    // XOR swizzle of a V^T row's VS slots, so that the lanes reading one MFMA
-    // operand (rows e..e+15, one slot each) meet no bank twice; chosen by
-    // timing the read patterns on the hardware ((e >> 2) & 3 for 4-slot rows
-    // was 1.6x slower)
-    __device__ static int vswz(int e) { return VS == 8 ? ((e >> 1) & 7) : ((e >> 1) & 3); }
+    // XOR swizzle of a V row's slots.  V is read only by the LDS transpose
+    // read (the A operand of O^T = V^T P^T: four consecutive keys of one
+    // dim per lane); these are the swizzles an in-bounds microbenchmark
+    // timed fastest for that read at 8 and 16 slots per row.
+    __device__ static int vswz(int key)
+    {
+        return R == 8 ? (key & 7) : ((((key & 3) << 2) | ((key >> 2) & 3)) ^ ((key >> 1) & 2));
+    }
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Four 16-bit elements by the LDS transpose read (ds_read_b64_tr_b16).  In
+// each group of 16 lanes, lane j names 8 bytes (four consecutive elements
+// of one row), and lane 4 q + e receives element e of the 8 bytes named by
+// lanes q, q + 4, q + 8 and q + 12: with lane j naming row r0 + j / 4,
+// columns c0 + 4 (j % 4) .. + 3, lane 4 q + e gets column c0 + 4 q + e of
+// rows r0 .. r0 + 3.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const unsigned char* p)
+{
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    return __builtin_bit_cast(bf16x4, v);
+}
 
 // Buffer loads of base[voffset + soffset] written straight to LDS at
 // lds + size * lane, 16 or 4 bytes per lane (reads at or past `nbytes`
@@ -590,9 +556,9 @@ template <int D, int P, int PHI, bool RW, bool EXACT>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const _Float16* __restrict__ K16,
-    const _Float16* __restrict__ KN16, const __bf16* __restrict__ VT, __bf16* __restrict__ O,
-    const float* __restrict__ FK, const int2* __restrict__ sched, int L, int Lp,
-    double lam_scale, float eps, int p_rt, double* __restrict__ ST)
+    const _Float16* __restrict__ KN16, const __bf16* __restrict__ V, __bf16* __restrict__ O,
+    const float* __restrict__ FK, const int2* __restrict__ sched, int L, double lam_scale,
+    float eps, int p_rt, double* __restrict__ ST)
 {
     static_assert(D == 64 || D == 128, "head dim");
     constexpr int BK = D == 64 ? 64 : 32;      // keys per tile
@@ -626,13 +592,12 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
     const __bf16* Qh = Q + hoff;
     __bf16* Oh = O + hoff;
 
-    // this head's K (exact and normalised), V^T and key factors; buffer
-    // reads past them return zeros
+    // this head's K (exact and normalised), V and key factors; buffer reads
+    // past them return zeros
     const void* kbase = K16 + hoff;
     const void* knbase = EXACT ? kbase : KN16 + hoff;
     const unsigned kbytes = (unsigned)L * D * 2u;
-    const void* vbase = VT + (size_t)bh * D * Lp;
-    const unsigned vbytes = (unsigned)D * Lp * 2u;
+    const void* vbase = V + hoff;
     const void* fbase = FK + (size_t)bh * L;
     const unsigned fbytes = (unsigned)L * 4u;
 
@@ -647,18 +612,26 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
 #pragma unroll
     for (int n = 0; n < T::VLOADS; ++n) {
         const int slot = (wave * T::VLOADS + n) * 64 + lane;
-        const int e = slot / T::VS, c = (slot % T::VS) ^ T::vswz(e);
-        vld[n] = (e * Lp + c * 8) * 2;
+        const int key = slot / T::R, c = (slot % T::R) ^ T::vswz(key);
+        vld[n] = (key * D + c * 8) * 2;
     }
-    // per-lane LDS byte offsets of the MFMA operand slots (16 ks / 16 ds rows
+    // per-lane LDS byte offsets of the MFMA operand slots (16 ks key rows
     // further on are constant offsets)
-    int krd[DC], vrd[C2];
+    int krd[DC], vrd[DS];
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
         krd[dc] = (row16 * T::R + ((4 * dc + grp) ^ T::kswz(row16))) * 16;
+    // V by the transpose read: lane j of group grp names key 4 grp + j / 4
+    // (plus 16 h + 32 c2) and dims 16 ds + 4 (j % 4) .. + 3, and receives
+    // keys 4 grp .. 4 grp + 3 of dim 16 ds + j; the swizzle depends on the
+    // key mod 16 only
+    {
+        const int x = 4 * grp + (row16 >> 2);
+        const int X = ((row16 >> 1) & 1) ^ T::vswz(x);
 #pragma unroll
-    for (int c2 = 0; c2 < C2; ++c2)
-        vrd[c2] = T::KBYTES + (row16 * T::VS + ((4 * c2 + grp) ^ T::vswz(row16))) * 16;
+        for (int ds = 0; ds < DS; ++ds)
+            vrd[ds] = T::KBYTES + (x * T::R + ((2 * ds) ^ X)) * 16 + (row16 & 1) * 8;
+    }
 
     // fast: the normalised keys and no key factors
     auto issue = [&](int kt, int buf, bool with_v, bool fast) {
@@ -670,8 +643,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
         if (with_v) {
 #pragma unroll
             for (int n = 0; n < T::VLOADS; ++n)
-                load16_to_lds(vbase, vbytes, base + T::KBYTES + (wave * T::VLOADS + n) * 1024,
-                                vld[n], kt * BK * 2);
+                load16_to_lds(vbase, kbytes, base + T::KBYTES + (wave * T::VLOADS + n) * 1024,
+                              vld[n], kt * BK * D * 2);
         }
         if (wave == 0 && !fast)
             load4_to_lds(fbase, fbytes, base + T::KBYTES + T::VBYTES, lane * 4, kt * BK * 4);
@@ -958,8 +931,11 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
                 const bf16x8 bfr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
                 for (int ds = 0; ds < DS; ++ds) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + vrd[c2] +
-                                                                      ds * 16 * T::VS * 16);
+                    // keys 32 c2 + 4 grp + 0..3, then 32 c2 + 16 + 4 grp + 0..3
+                    // of dim 16 ds + row16: the order of bfr
+                    const unsigned char* vp = base + vrd[ds] + 32 * c2 * T::R * 16;
+                    const bf16x4 v0 = lds_read_tr16(vp), v1 = lds_read_tr16(vp + 16 * T::R * 16);
+                    const bf16x8 a = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
                     oacc[ds] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfr, oacc[ds], 0, 0, 0);
                 }
                 dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bfr, dacc, 0, 0, 0);

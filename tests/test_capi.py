@@ -66,8 +66,8 @@ def test_library_has_no_oracle_dependency(L):
 
 def test_noalloc_host_checks(L):
     """lssar_attn_fwd_noalloc validates on the host before any HIP call: bad
-    arguments, and an input whose workspace exceeds the 96 MiB scratch."""
-    assert sfa.lssar_noalloc_scratch_bytes() == 96 << 20
+    arguments, and an input whose workspace exceeds the 64 MiB scratch."""
+    assert sfa.lssar_noalloc_scratch_bytes() == 64 << 20
     f = L.lssar_attn_fwd_noalloc
     q, k, v, o = A, A + STEP, A + 2 * STEP, A + 3 * STEP
     assert f(0, k, v, o, 1, 2, 64, 64, 3, 1e-4, 1, None) == sfa.LSSAR_EINVAL
@@ -92,16 +92,15 @@ def test_workspace_bytes(L):
     assert sfa.lssar_workspace_bytes(2, 3, 5, 128, sfa.LSSAR_F32) == 256
     assert sfa.lssar_workspace_bytes(1, 1, 100, 64, sfa.LSSAR_F32) == 1024
     assert sfa.lssar_workspace_bytes(1, 1, 32, 64, sfa.LSSAR_F32) == 256
-    # bf16: plus V^T with rows padded to a multiple of 64 keys, plus the
-    # attention kernel's dispatch table (8 bytes per workgroup, rounded up)
+    # bf16: plus two f16 copies of K (exact rows scaled by powers of two,
+    # and the normalised rows) and the attention kernel's dispatch table (8
+    # bytes per workgroup), each rounded up
     def r256(x):
         return (x + 255) // 256 * 256
-    # and the two f16 copies of K (exact rows scaled by powers of two, and
-    # the normalised rows)
     assert sfa.lssar_workspace_bytes(1, 12, 8192, 64, sfa.LSSAR_BF16) == \
-        4 * 12 * 8192 + 3 * 12 * 64 * 8192 * 2 + r256(8 * 1536)
+        4 * 12 * 8192 + 2 * 12 * 64 * 8192 * 2 + r256(8 * 1536)
     assert sfa.lssar_workspace_bytes(2, 3, 77, 128, sfa.LSSAR_BF16) == \
-        2048 + 6 * 128 * 128 * 2 + 2 * r256(6 * 77 * 128 * 2) + \
+        2048 + 2 * r256(6 * 77 * 128 * 2) + \
         r256(8 * len(sfa.lssar_fwd_schedule(2, 3, 77)))
     assert sfa.lssar_workspace_bytes(0, 1, 1, 64, 0) == 0
     assert sfa.lssar_workspace_bytes(1, 1, 1, 96, 0) == 0
@@ -154,14 +153,15 @@ def test_allocating_entry_validates(L):
 
 def test_stage_entries_validate(L):
     k, v, ws = A, A + STEP, A + 4 * STEP
-    # prep: null k/v, bad d, bad workspace (null, misaligned, small, overlapping)
-    assert L.lssar_prep(0, v, ws, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EINVAL
-    assert L.lssar_prep(k, 0, ws, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EINVAL
-    assert L.lssar_prep(k, v, ws, 1 << 20, 1, 1, 8, 72, 1, None) == sfa.LSSAR_EUNSUPPORTED
-    assert L.lssar_prep(k, v, 0, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
-    assert L.lssar_prep(k, v, ws + 16, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
-    assert L.lssar_prep(k, v, ws, 64, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
-    assert L.lssar_prep(k, v, v - 256, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
+    # prep (K only): null or misaligned k, bad d, bad workspace (null,
+    # misaligned, small, overlapping k)
+    assert L.lssar_prep(0, ws, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EINVAL
+    assert L.lssar_prep(k + 8, ws, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EINVAL
+    assert L.lssar_prep(k, ws, 1 << 20, 1, 1, 8, 72, 1, None) == sfa.LSSAR_EUNSUPPORTED
+    assert L.lssar_prep(k, 0, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
+    assert L.lssar_prep(k, ws + 16, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
+    assert L.lssar_prep(k, ws, 64, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
+    assert L.lssar_prep(k, k - 256, 1 << 20, 1, 1, 8, 64, 1, None) == sfa.LSSAR_EWORKSPACE
     # prepped: the fused-call checks plus the workspace
     q, o = A + 2 * STEP, A + 3 * STEP
     assert L.lssar_attn_fwd_prepped(q, k, v, 0, 1 << 20, o, 1, 1, 8, 64, 3, 1e-4, 1,

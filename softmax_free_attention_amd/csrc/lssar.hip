@@ -165,8 +165,8 @@ WsParts ws_parts(void* ws, const Layout& w)
             reinterpret_cast<int2*>(b + o_kn16 + w.kn16_bytes)};
 }
 
-// fast_keys: also write the normalised f16 keys, which every bf16 attention
-// kernel but the training forward's (exact scores throughout) reads
+// fast_keys: also write the normalised f16 keys, which the bf16 Softplus
+// kernels read, except the training forward's (exact scores throughout)
 int run_prep(const void* k, void* ws, int B, int H, int L, int d, int dtype,
              hipStream_t s, bool fast_keys = true)
 {
@@ -323,9 +323,10 @@ int fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H,
     if (st != LSSAR_OK)
         return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // the training forward (exact scores) does not read the normalised keys
+    // the training forward and the Sigmoid map (exact scores) do not read
+    // the normalised keys
     const bool training = stats && var.phi == LSSAR_PHI_SOFTPLUS && var.reweight;
-    st = run_prep(k, workspace, B, H, L, d, dtype, s, !training);
+    st = run_prep(k, workspace, B, H, L, d, dtype, s, var.phi == LSSAR_PHI_SOFTPLUS && !training);
     if (st != LSSAR_OK)
         return st;
     return run_fwd(q, k, v, workspace, out, B, H, L, d, p, eps, dtype, s, var, stats);

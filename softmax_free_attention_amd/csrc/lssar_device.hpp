@@ -551,7 +551,11 @@ __device__ __forceinline__ void load_row_stats(const double* ST, size_t row, C& 
 //    t = acc * (fk_j * lambda_i'), the scores of the raw inputs with fp32
 //    accumulation.
 // The deep-row redo and the training forward (EXACT: its row statistics
-// feed the backward) take the exact operand; the plain forward the fast one.
+// feed the backward) take the exact operands; the plain Softplus forward the
+// fast ones.  The Sigmoid map takes the exact operands throughout: with a
+// map bounded by 1 the gap sigma_max - tau is below 1, so nearly every row
+// of a long sequence has kappa_i = p lambda_i / gap_i far above kCondMax
+// (about 1600 at L = 8192, d = 64, p = 15) and would be computed twice.
 template <int D, int P, int PHI, bool RW, bool EXACT>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel(
@@ -662,7 +666,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
     // and for Softplus with softplus2_acc (deep or ill-conditioned rows).
     auto block_body = [&](auto redo_tag) {
         constexpr bool REDO = decltype(redo_tag)::value;
-        constexpr bool FAST = !REDO && !EXACT;     // query operand (see above)
+        // operands (see above)
+        constexpr bool FAST = !REDO && !EXACT && PHI == kPhiSoftplus;
         const int q0 = qb * kBQ16;
         const int qw0 = q0 + wave * kMQ16;         // first query row of this wave
         const int qwl = min(qw0 + kMQ16 - 1, L - 1);  // last valid query row
@@ -960,7 +965,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
     };
 
     block_body(std::false_type{});
-    if constexpr (PHI == kPhiSoftplus || (RW && !EXACT)) {
+    if constexpr (PHI == kPhiSoftplus) {
         __syncthreads();                           // every lane's flag store is done
         if (flags[0])
             block_body(std::true_type{});

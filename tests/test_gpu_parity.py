@@ -300,6 +300,38 @@ def test_causality_and_scale_invariance():
     assert torch.equal(o3.view(torch.int16), base.view(torch.int16))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_row_scaling_over_a_wide_range(d):
+    """Every factor of the scores is scale-free: scaling each row of Q and K
+    by its own power of two in [2^-30, 2^30] changes neither the output of
+    the plain forward (normalised f16 operands, and the exact operands of
+    redone blocks) nor that of the training forward and its statistics,
+    bitwise.  (Rows stay above the 1e-12 norm clamp and their squares in
+    range.)"""
+    import softmax_free_attention_amd as sfa
+    inp = gen.make_inputs("x8_planted", B=1, H=2, L=700, d=d, p=15, seed=41)
+    q, k, v = (to_device(a, "bf16") for a in (inp.q, inp.k, inp.v))
+    r = np.random.default_rng(43)
+    sq = torch.from_numpy(np.ldexp(1.0, r.integers(-30, 31, size=(1, 2, 700, 1)))).cuda()
+    sk = torch.from_numpy(np.ldexp(1.0, r.integers(-30, 31, size=(1, 2, 700, 1)))).cuda()
+    q2 = (q.double() * sq).to(torch.bfloat16)
+    k2 = (k.double() * sk).to(torch.bfloat16)
+    # the scaled rows are exact
+    assert torch.equal((q2.double() / sq).to(torch.bfloat16).view(torch.int16), q.view(torch.int16))
+    assert torch.equal((k2.double() / sk).to(torch.bfloat16).view(torch.int16), k.view(torch.int16))
+    base, got = run_ws(q, k, v, 15), run_ws(q2, k2, v, 15)
+    torch.cuda.synchronize()
+    assert torch.equal(base.view(torch.int16), got.view(torch.int16))
+    outs = []
+    for a, b in ((q, k), (q2, k2)):
+        out, st = torch.empty_like(a), sfa.stats_for(a)
+        sfa.lssar_attn_fwd_stats_ws(a, b, v, out, st, sfa.workspace_for(a), p=15)
+        outs.append((out, st))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[1][1])
+
+
 def test_linearity_in_v():
     inp = gen.make_inputs("gpt2s", B=1, H=2, L=300, d=128, dtype="f32", p=3, seed=31)
     q, k, v = (to_device(a, "f32") for a in (inp.q, inp.k, inp.v))

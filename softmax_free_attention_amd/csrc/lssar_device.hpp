@@ -661,6 +661,11 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
     // the block
     if (tid == 0)
         flags[0] = 0;
+    // this lane's row asked for the redo: a redone block stores only such
+    // rows, so that a row's output depends on its own keys alone (rows that
+    // did not ask keep the first pass's results; which rows of a block ask
+    // depends on later keys, and the two passes round differently)
+    bool redo_me = false;
 
     // The query block; REDO: computed again from the exact query operand,
     // and for Softplus with softplus2_acc (deep or ill-conditioned rows).
@@ -866,18 +871,23 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
             } else {
                 rc = row_constants<PHI>(qi + 1, s1r, trow, eps);
                 if constexpr (PHI == kPhiSoftplus && !REDO)
-                    if (qi < L && trow < kDeep)
+                    if (qi < L && trow < kDeep) {
                         flags[0] = 1;
+                        redo_me = true;
+                    }
             }
             // kappa_i = p lambda_i c_i
             if constexpr (FAST) {
                 const float pf = (float)(P > 0 ? P : p_rt);
-                if (qi < L && pf * lam_row * rc.c > kCondMax)
+                if (qi < L && pf * lam_row * rc.c > kCondMax) {
                     flags[0] = 1;
+                    redo_me = true;
+                }
             }
-            // a redone block stores again, after its first store
+            // a redone block stores its asking rows again, after their
+            // first store
             if constexpr (PHI == kPhiSoftplus)
-                if (ST && qi < L && grp == 0)
+                if (ST && qi < L && grp == 0 && (!REDO || redo_me))
                     save_row_stats(ST, (size_t)bh * L + qi, s1r, trow);
         }
 
@@ -949,11 +959,13 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
 
         tile_loop(true, pass2_tile);
         if constexpr (!RW && PHI == kPhiSoftplus && !REDO)
-            if (qi < L && dacc[0] < (float)(qi + 1) * kDeepMean)
+            if (qi < L && dacc[0] < (float)(qi + 1) * kDeepMean) {
                 flags[0] = 1;
+                redo_me = true;
+            }
 
         // ---------------- finalize: out_i = U_i / D_i (0 if degenerate) ----------------
-        if (qi < L) {
+        if (qi < L && (!REDO || redo_me)) {
             const float inv = rc.degen ? 0.0f : 1.0f / dacc[0];
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds) {

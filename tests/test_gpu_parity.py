@@ -285,17 +285,27 @@ def test_prep_workspace_contents():
 
 
 def test_causality_and_scale_invariance():
-    """Future keys/values never reach a row (bitwise); scaling Q and K rows
-    by powers of two changes nothing (bitwise: every factor is exact)."""
+    """Future keys/values never reach a row (bitwise), also when they make
+    other rows of the row's 64-row block ask for the exact redo (a redone
+    block stores only the rows that asked); scaling Q and K rows by powers
+    of two changes nothing (bitwise: every factor is exact)."""
     inp = gen.make_inputs("gpt2s", B=1, H=2, L=400, d=64, p=15, seed=21)
     q, k, v = (to_device(a, "bf16") for a in (inp.q, inp.k, inp.v))
     base = run_ws(q, k, v, 15)
-    for cut in (0, 3, 63, 64, 200):
-        k2, v2 = k.clone(), v.clone()
-        k2[:, :, cut + 1:] = torch.randn_like(k2[:, :, cut + 1:])
-        v2[:, :, cut + 1:] = torch.randn_like(v2[:, :, cut + 1:]) * 100
-        o2 = run_ws(q, k2, v2, 15)
-        assert torch.equal(o2[:, :, :cut + 1].view(torch.int16), base[:, :, :cut + 1].view(torch.int16))
+    g = torch.Generator(device="cuda").manual_seed(123)
+    for trial in range(4):
+        for cut in (0, 3, 63, 64, 65, 127, 200):
+            k2, v2 = k.clone(), v.clone()
+            n = k2[:, :, cut + 1:].shape
+            k2[:, :, cut + 1:] = torch.randn(n, generator=g, device="cuda").to(k.dtype)
+            v2[:, :, cut + 1:] = (torch.randn(n, generator=g, device="cuda") * 100).to(v.dtype)
+            if trial == 3:
+                # future keys that make every later row of the block nearly tied
+                k2[:, :, cut + 1:] = k2[:, :, cut:cut + 1]
+            o2 = run_ws(q, k2, v2, 15)
+            same = torch.equal(o2[:, :, :cut + 1].view(torch.int16),
+                               base[:, :, :cut + 1].view(torch.int16))
+            assert same, (trial, cut)
     o3 = run_ws(q * 4.0, k * 0.25, v, 15)
     assert torch.equal(o3.view(torch.int16), base.view(torch.int16))
 

@@ -345,7 +345,7 @@ def test_row_scaling_over_a_wide_range(d):
 def test_linearity_in_v():
     inp = gen.make_inputs("gpt2s", B=1, H=2, L=300, d=128, dtype="f32", p=3, seed=31)
     q, k, v = (to_device(a, "f32") for a in (inp.q, inp.k, inp.v))
-    v2 = torch.randn_like(v)
+    v2 = torch.randn(v.shape, generator=torch.Generator(device="cuda").manual_seed(32), device="cuda")
     a, b, c = run_ws(q, k, v, 3), run_ws(q, k, v2, 3), run_ws(q, k, 2 * v - 3 * v2, 3)
     assert float((c - (2 * a - 3 * b)).abs().max()) < 1e-4
 

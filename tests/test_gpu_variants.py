@@ -166,12 +166,14 @@ def test_zero_queries():
 def test_causality_bitwise():
     inp = gen.make_inputs("gpt2s", B=1, H=2, L=300, d=64, p=15, seed=71)
     q, k, v = (to_device(a, "bf16") for a in (inp.q, inp.k, inp.v))
+    g = torch.Generator(device="cuda").manual_seed(72)
     for variant in ("sigmoid", "lssa"):
         base = run_variant(q, k, v, variant, 15)
-        for cut in (0, 4, 64, 200):
+        for cut in (0, 4, 64, 65, 200):
             k2, v2 = k.clone(), v.clone()
-            k2[:, :, cut + 1:] = torch.randn_like(k2[:, :, cut + 1:])
-            v2[:, :, cut + 1:] = torch.randn_like(v2[:, :, cut + 1:]) * 100
+            n = k2[:, :, cut + 1:].shape
+            k2[:, :, cut + 1:] = torch.randn(n, generator=g, device="cuda").to(k.dtype)
+            v2[:, :, cut + 1:] = (torch.randn(n, generator=g, device="cuda") * 100).to(v.dtype)
             o2 = run_variant(q, k2, v2, variant, 15)
             assert torch.equal(o2[:, :, :cut + 1].view(torch.int16),
                                base[:, :, :cut + 1].view(torch.int16))

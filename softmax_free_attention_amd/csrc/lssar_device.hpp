@@ -708,14 +708,19 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             // log2(e) ln d ln i / max(|q_i|, 1e-12)  (Key design 1: log d . log N)
-            const double lamd = query_factor(lam_scale, qi + 1, (double)ss);
-            lam_row = (float)(lam_scale * log((double)(qi + 1)));
+            // in fp32: a few ulp of lambda_i against the fp32 scores' (d + 3)
+            // ulp of ln d ln i; the fp64 log and divide cost a block about
+            // 100 double-precision instructions per wave, noticeable on rows
+            // of a few tiles
+            constexpr float kLn2 = 0.693147180559945309f;
+            lam_row = (float)lam_scale * (__builtin_amdgcn_logf((float)(qi + 1)) * kLn2);
+            const float lamf = lam_row / fmaxf(sqrtf(ss), 1e-12f);
             // fast: lambda_i q^_i rounded to f16; exact: q_i 2^-e_i and the
             // factor lambda_i 2^e_i / |q_i| applied to the accumulator
             const int ex = f16_row_exponent(mx);
-            const float sc = FAST ? (float)lamd : ldexpf(1.0f, -ex);
+            const float sc = FAST ? lamf : ldexpf(1.0f, -ex);
             if constexpr (!FAST)
-                lam = (float)ldexp(lamd, ex);
+                lam = ldexpf(lamf, ex);
 #pragma unroll
             for (int dc = 0; dc < DC; ++dc)
 #pragma unroll

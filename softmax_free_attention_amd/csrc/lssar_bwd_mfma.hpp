@@ -305,8 +305,11 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             gf[dc] = __builtin_bit_cast(bf16x8, x);
         }
         const float rqi = qvalid ? rq[(size_t)bh * L + qi] : 0.0f;
-        // log2(e) ln d ln i / |q_i|  (Key design 1: log d . log N)
-        const float lam = (float)(lam_scale * log((double)(qi + 1))) * rqi;
+        // log2(e) ln d ln i / |q_i|  (Key design 1: log d . log N), in fp32
+        // as in the forward (a few ulp against the scores' fp32 error)
+        constexpr float kLn2 = 0.693147180559945309f;
+        const float lam_i = (float)lam_scale * (__builtin_amdgcn_logf((float)(qi + 1)) * kLn2);
+        const float lam = lam_i * rqi;
 
         // (init: the accumulator's starting value)
         auto mm_block = [&](const unsigned char* base, int off, const bf16x8 (&b)[DC], int ks,
@@ -376,7 +379,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
             const float alpha = (float)p_rt * s1 / (gap * Y);
             const float epsr = alpha / s1 * Pd;
             // ln d ln i / (S ln 2), S in base 2: lam_scale ln i / S
-            const float kappa = (float)(lam_scale * log((double)(qi + 1))) / s1;
+            const float kappa = lam_i / s1;
             // A and E carry 1 / |q_i|: dk^ sums (dc_ij / |q_i|) q_i, and dq
             // = (dq^ - (dq^ . q^) q^) / |q_i| takes the factor from them
             const float a_ = degen ? 0.0f : kappa * alpha * rqi;

@@ -32,9 +32,13 @@
  *    asynchronous with respect to the host and ordered on the stream.
  *  - Square causal self-attention: query i sees keys 1..i; one K/V head per
  *    Q head; q and k are the vectors after any positional rotation.
- *  - Arithmetic, bf16 inputs: scores contract the raw inputs on bf16 MFMA
- *    with fp32 accumulation; norms, Softplus, row sums and the re-weighting
- *    run in fp32; bf16 weights feed the P.V contraction (fp32 accumulation).
+ *  - Arithmetic, bf16 inputs: the Softplus forward's scores contract
+ *    lambda_i q^_i against k^_j, each rounded to f16, on f16 MFMA; a query
+ *    block with an ill-conditioned or deep row is computed again, and every
+ *    other entry point's scores computed, from the raw inputs on bf16 MFMA;
+ *    fp32 accumulation throughout.  Norms, Softplus, row sums and the
+ *    re-weighting run in fp32; bf16 weights feed the P.V contraction (fp32
+ *    accumulation).
  *    fp32 inputs: scores on fp64 MFMA, norms and the score -> Softplus ->
  *    re-weighting chain in fp64, fp32 weights and P.V on fp32 MFMA.  The
  *    output is rounded to the input dtype (nearest-even).
@@ -76,10 +80,10 @@ enum {
 
 /* Workspace for every forward entry point that takes one, in bytes, each
  * part rounded up to 256: one key factor per key row (fp32 for bf16 inputs:
- * 4*B*H*L; fp64 for fp32 inputs: 8*B*H*L); for bf16 inputs also two f16
- * copies of K (B*H*L*d f16 each: exact rows scaled by powers of two, and
- * the normalised rows) and the attention kernel's dispatch table (8 bytes
- * per workgroup, lssar_fwd_schedule).  Returns 0 for invalid sizes. */
+ * 4*B*H*L; fp64 for fp32 inputs: 8*B*H*L); for bf16 inputs also the
+ * normalised rows of K in f16 (B*H*L*d f16) and the attention kernel's
+ * dispatch table (8 bytes per workgroup, lssar_fwd_schedule).  Returns 0
+ * for invalid sizes. */
 size_t lssar_workspace_bytes(int B, int H, int L, int d, int dtype);
 
 /* LSSAR causal attention forward (Key designs 1-3 above) with a
@@ -103,8 +107,8 @@ int lssar_attn_fwd(const void* q, const void* k, const void* v, void* out,
  * lssar_attn_fwd with no allocation and no workspace argument.  Its
  * workspace is a static device array of the library, one per GPU, of
  * lssar_noalloc_scratch_bytes() = 64 MiB, held from the library's first use
- * on that GPU until the process ends (bf16 at d = 64 fits up to about 250 K
- * query rows B*H*L, e.g. B1 H12 L16384).
+ * on that GPU until the process ends (bf16 at d = 64 fits up to about 500 K
+ * query rows B*H*L, e.g. B1 H12 L32768).
  *  - Arguments, layout and output as for lssar_attn_fwd_ws on the CURRENT
  *    device; `stream` must belong to it.
  *  - LSSAR_ESCRATCH (checked on the host, before any HIP call) if
@@ -124,11 +128,10 @@ size_t lssar_noalloc_scratch_bytes(void);
 /* The prep step alone (the prep kernel; it reads K only).  Writes into the
  * workspace the key factors (Key design 1's K_j <- K_j / |K_j|_2, kept as a
  * factor of the score): for fp32 inputs fk[bh*L + j] = 1 / max(|k_j|_2,
- * 1e-12) in fp64; for bf16 inputs, with e_j the power of two that brings
- * row j's largest magnitude into [2^14, 2^15), the exact f16 row
- * k_j 2^-e_j and fk[bh*L + j] = 2^e_j / max(|k_j|_2, 1e-12) in fp32, the
- * normalised row k_j / max(|k_j|_2, 1e-12) rounded to f16, and the
- * attention kernel's dispatch table.  Workspace rules as for
+ * 1e-12) in fp64; for bf16 inputs fk[bh*L + j] = 1 / max(|k_j|_2, 1e-12)
+ * (fp64, rounded to fp32), the normalised row k_j / max(|k_j|_2, 1e-12)
+ * rounded to f16, and the attention kernel's dispatch table.  Workspace
+ * rules as for
  * lssar_attn_fwd_ws (it must not overlap k); a bad workspace is
  * LSSAR_EWORKSPACE. */
 int lssar_prep(const void* k, void* workspace, size_t workspace_bytes, int B,
@@ -229,8 +232,8 @@ int lssar_attn_bwd_ws(const void* q, const void* k, const void* v,
  *    q^_i . k^_j (natural logarithms).  Rows r are (b, h, i - 1) row-major.
  *  - Values come from the kernels' arithmetic (fp32 for bf16 inputs, fp64
  *    for fp32 inputs), rounded to fp64.
- *  - For bf16 inputs the scores come from the exact query rows (q_i scaled
- *    by a power of two, exact in f16) with the fp32 factors applied to the
+ *  - For bf16 inputs the scores come from the raw query and key rows (bf16
+ *    products, exact in fp32) with the fp32 factors applied to the
  *    accumulator; lssar_attn_fwd_ws folds the row factor into the query
  *    operand and rounds it to f16, so the two outputs agree to the bf16
  *    parity bar, not bitwise.  fp32 inputs: bitwise the same output.

@@ -47,14 +47,13 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout: [fk: key factor per key row, fp32 for bf16 inputs and
-// fp64 for fp32 inputs][K16: f16 copy of K, rows scaled by powers of two,
-// bf16 inputs only][KN16: the normalised keys in f16, bf16 inputs only]
+// fp64 for fp32 inputs][KN16: the normalised keys in f16, bf16 inputs only]
 // [sched: the attention kernel's (head, block) per workgroup, int2, bf16
 // inputs only]
 struct Layout {
-    size_t fk_bytes, k16_bytes, kn16_bytes, sched_bytes;
+    size_t fk_bytes, kn16_bytes, sched_bytes;
     int Lp;
-    size_t total() const { return fk_bytes + k16_bytes + kn16_bytes + sched_bytes; }
+    size_t total() const { return fk_bytes + kn16_bytes + sched_bytes; }
 };
 
 Layout layout(long long B, long long H, long long L, int d, int dtype)
@@ -62,8 +61,7 @@ Layout layout(long long B, long long H, long long L, int d, int dtype)
     Layout w;
     w.Lp = (int)((L + lssar::kBK - 1) / lssar::kBK * lssar::kBK);
     w.fk_bytes = round256((size_t)((dtype == LSSAR_F32 ? 8 : 4) * B * H * L));
-    w.k16_bytes = dtype == LSSAR_BF16 ? round256((size_t)(B * H * d) * (size_t)L * 2) : 0;
-    w.kn16_bytes = w.k16_bytes;
+    w.kn16_bytes = dtype == LSSAR_BF16 ? round256((size_t)(B * H * d) * (size_t)L * 2) : 0;
     w.sched_bytes = 0;
     if (dtype == LSSAR_BF16) {
         const int nqb = (int)((L + lssar::kBQ16 - 1) / lssar::kBQ16);
@@ -138,30 +136,27 @@ void launch_knorm_f32(const void* k, double* fk, long nrows, hipStream_t s)
 }
 
 template <int D>
-void launch_prep_bf16(const void* k, float* fk, void* k16, void* kn16, int2* sched, int BH, int L,
-                      int Lp, hipStream_t s)
+void launch_prep_bf16(const void* k, float* fk, void* kn16, int2* sched, int BH, int L, int Lp,
+                      hipStream_t s)
 {
     const int per_xcd =
         (int)(lssar::FwdSched(BH, Lp / lssar::kBK).grid() / lssar::kSchedXcds);
     hipLaunchKernelGGL((lssar::lssar_prep_bf16_kernel<D>), dim3(Lp / lssar::kBK, BH),
                        dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(k), fk,
-                       static_cast<_Float16*>(k16), static_cast<_Float16*>(kn16), sched, BH, L,
-                       Lp, per_xcd);
+                       static_cast<_Float16*>(kn16), sched, BH, L, Lp, per_xcd);
 }
 
 // Where the bf16 workspace parts start.
 struct WsParts {
     float* fk;
-    _Float16* k16;
     _Float16* kn16;
     int2* sched;
 };
 WsParts ws_parts(void* ws, const Layout& w)
 {
     unsigned char* b = static_cast<unsigned char*>(ws);
-    const size_t o_k16 = w.fk_bytes, o_kn16 = o_k16 + w.k16_bytes;
-    return {reinterpret_cast<float*>(b), reinterpret_cast<_Float16*>(b + o_k16),
-            reinterpret_cast<_Float16*>(b + o_kn16),
+    const size_t o_kn16 = w.fk_bytes;
+    return {reinterpret_cast<float*>(b), reinterpret_cast<_Float16*>(b + o_kn16),
             reinterpret_cast<int2*>(b + o_kn16 + w.kn16_bytes)};
 }
 
@@ -176,9 +171,9 @@ int run_prep(const void* k, void* ws, int B, int H, int L, int d, int dtype,
         const WsParts pt = ws_parts(ws, w);
         void* kn16 = fast_keys ? pt.kn16 : nullptr;
         if (d == 64)
-            launch_prep_bf16<64>(k, pt.fk, pt.k16, kn16, pt.sched, B * H, L, w.Lp, s);
+            launch_prep_bf16<64>(k, pt.fk, kn16, pt.sched, B * H, L, w.Lp, s);
         else
-            launch_prep_bf16<128>(k, pt.fk, pt.k16, kn16, pt.sched, B * H, L, w.Lp, s);
+            launch_prep_bf16<128>(k, pt.fk, kn16, pt.sched, B * H, L, w.Lp, s);
     } else {
         double* fk = static_cast<double*>(ws);
         if (d == 64)
@@ -206,15 +201,17 @@ void launch_fwd(const void* q, const void* k, const void* v, void* ws, void* out
             if (stats) {
                 hipLaunchKernelGGL((lssar::lssar_fwd_bf16_kernel<D, P, PHI, RW, true>), grid,
                                    dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(q),
-                                   pt.k16, nullptr, static_cast<const __bf16*>(v),
+                                   static_cast<const __bf16*>(k), nullptr,
+                                   static_cast<const __bf16*>(v),
                                    static_cast<__bf16*>(out), pt.fk, pt.sched, L, lam_scale, eps,
                                    p, stats);
                 return;
             }
         }
         hipLaunchKernelGGL((lssar::lssar_fwd_bf16_kernel<D, P, PHI, RW, false>), grid,
-                           dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(q), pt.k16,
-                           pt.kn16, static_cast<const __bf16*>(v), static_cast<__bf16*>(out),
+                           dim3(lssar::kThreads), 0, s, static_cast<const __bf16*>(q),
+                           static_cast<const __bf16*>(k), pt.kn16, static_cast<const __bf16*>(v),
+                           static_cast<__bf16*>(out),
                            pt.fk, pt.sched, L, lam_scale, eps, p, nullptr);
     } else {
         const int nqb = (L + lssar::kBQ32 - 1) / lssar::kBQ32;
@@ -859,7 +856,7 @@ const char* lssar_status_str(int status)
 
 int lssar_last_hip_error(void) { return g_last_hip_error; }
 
-int lssar_version(void) { return 900; }
+int lssar_version(void) { return 910; }
 
 long long lssar_fwd_schedule(int B, int H, int L, int* items, long long capacity)
 {

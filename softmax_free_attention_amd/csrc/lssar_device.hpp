@@ -326,23 +326,9 @@ __global__ __launch_bounds__(kThreads) void lssar_knorm_f32_kernel(const float* 
         fk[row] = 1.0 / fmax(sqrt(ss), 1e-12);
 }
 
-// Exponent e that brings a row whose largest magnitude is mx into
-// [2^14, 2^15) when scaled by 2^-e (0 for a zero row): every bf16 value of
-// the row is then an f16 value (no overflow; a value below 2^-29 mx goes
-// subnormal, an error under 2^-24 of the row's largest product).
-__device__ __forceinline__ int f16_row_exponent(float mx)
-{
-    int ex;
-    frexpf(mx, &ex);
-    return mx > 0.0f ? ex - 15 : 0;
-}
-
 // Prep for the bf16 kernel, one workgroup per (64-key block kb, head bh):
-//  * K16[bh][j] = k_j 2^-e_j in f16, exact (e_j from f16_row_exponent): the
-//    attention kernel's MFMA operand for K;
-//  * fk[bh*L + j] = 2^e_j / max(|k_j|_2, 1e-12) for the block's keys (fp64
-//    sum of squares, one rounding to fp32), so that fk_j (q . K16_j) =
-//    (q . k_j) / |k_j|;
+//  * fk[bh*L + j] = 1 / max(|k_j|_2, 1e-12) for the block's keys (fp64 sum
+//    of squares, one rounding to fp32): the exact scores' key factor;
 //  * KN16[bh][j] = f16(k_j / max(|k_j|_2, 1e-12)) (unless KN16 is null): the
 //    normalised key rounded to f16, the fast path's operand, whose scores
 //    need no per-pair key factor;
@@ -353,10 +339,11 @@ __device__ __forceinline__ int f16_row_exponent(float mx)
 //    kb, kb + nkb, ... up to per_xcd, the grid's indices per XCD (from the
 //    host).  (One thread that counted all eight slices and wrote every
 //    empty index set the end of the kernel.)
+// The exact scores read K itself (bf16 products are exact in fp32).
 template <int D>
 __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
-    const __bf16* __restrict__ K, float* __restrict__ fk, _Float16* __restrict__ K16,
-    _Float16* __restrict__ KN16, int2* __restrict__ sched, int BH, int L, int Lp, int per_xcd)
+    const __bf16* __restrict__ K, float* __restrict__ fk, _Float16* __restrict__ KN16,
+    int2* __restrict__ sched, int BH, int L, int Lp, int per_xcd)
 {
     constexpr int LPR = D / 8;                 // lanes per key row for the norms
     const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
@@ -381,7 +368,6 @@ __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
         const int key = c / LPR, sub = c % LPR;
         const int kg = kb * 64 + key;
         double ss = 0.0;
-        float mx = 0.0f;
         float xv[8];
         u32x4 w = {0u, 0u, 0u, 0u};
         if (kg < L)
@@ -392,24 +378,14 @@ __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
             xv[2 * e + 1] = bf16hi(w[e]);
             ss = fma((double)xv[2 * e], (double)xv[2 * e], ss);
             ss = fma((double)xv[2 * e + 1], (double)xv[2 * e + 1], ss);
-            mx = fmaxf(mx, fmaxf(fabsf(xv[2 * e]), fabsf(xv[2 * e + 1])));
         }
 #pragma unroll
-        for (int m = LPR / 2; m >= 1; m >>= 1) {
+        for (int m = LPR / 2; m >= 1; m >>= 1)
             ss += __shfl_xor(ss, m, LPR);
-            mx = fmaxf(mx, __shfl_xor(mx, m, LPR));
-        }
-        const int ex = f16_row_exponent(mx);
         if (kg < L) {
-            const float sc = ldexpf(1.0f, -ex);
-            f16x8 h;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                h[i] = (_Float16)(xv[i] * sc);
-            *reinterpret_cast<f16x8*>(K16 + hoff + (size_t)kg * D + sub * 8) = h;
             const double inv = 1.0 / fmax(sqrt(ss), 1e-12);
             if (sub == 0)
-                fk[(size_t)bh * L + kg] = (float)ldexp(inv, ex);
+                fk[(size_t)bh * L + kg] = (float)inv;
             if (KN16) {
                 // fp32 product, then f16 (a direct fp64 -> f16 conversion
                 // is a long integer sequence on this part); the fp32 step
@@ -541,15 +517,15 @@ __device__ __forceinline__ void load_row_stats(const double* ST, size_t row, C& 
 // d = 64; 64-key tiles there allowed one buffer only (two need 66 KB and
 // halve the occupancy), which left every tile load exposed.
 //
-// Scores.  The prep kernel's K16 rows are exact (k_j scaled by 2^-e_j),
-// fk_j = 2^e_j / |k_j|, and its KN16 rows the normalised keys rounded to
-// f16.  The operands are either
-//  * fast: f16(lambda_i q_i / |q_i|) against KN16, both factors folded in
-//    and each operand rounded to f16 once, so that t = acc: no multiply per
-//    pair (two before the factors were folded in); or
-//  * exact: q_i 2^-e_i against K16, both exact in f16, with
-//    t = acc * (fk_j * lambda_i'), the scores of the raw inputs with fp32
-//    accumulation.
+// Scores.  The prep kernel writes fk_j = 1 / |k_j| and the KN16 rows, the
+// normalised keys rounded to f16.  The operands are either
+//  * fast: f16(lambda_i q_i / |q_i|) against KN16 on the f16 MFMA, both
+//    factors folded in and each operand rounded to f16 once, so that
+//    t = acc: no multiply per pair (two before the factors were folded in);
+//    or
+//  * exact: q_i against k_j, the raw bf16 rows, on the bf16 MFMA (the
+//    products are exact in fp32), with t = acc * (fk_j * lambda_i / |q_i|):
+//    the scores of the raw inputs with fp32 accumulation.
 // The deep-row redo and the training forward (EXACT: its row statistics
 // feed the backward) take the exact operands; the plain Softplus forward the
 // fast ones.  The Sigmoid map takes the exact operands throughout: with a
@@ -559,7 +535,7 @@ __device__ __forceinline__ void load_row_stats(const double* ST, size_t row, C& 
 template <int D, int P, int PHI, bool RW, bool EXACT>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel(
-    const __bf16* __restrict__ Q, const _Float16* __restrict__ K16,
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const _Float16* __restrict__ KN16, const __bf16* __restrict__ V, __bf16* __restrict__ O,
     const float* __restrict__ FK, const int2* __restrict__ sched, int L, double lam_scale,
     float eps, int p_rt, double* __restrict__ ST)
@@ -596,9 +572,9 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
     const __bf16* Qh = Q + hoff;
     __bf16* Oh = O + hoff;
 
-    // this head's K (exact and normalised), V and key factors; buffer reads
+    // this head's K (raw and normalised), V and key factors; buffer reads
     // past them return zeros
-    const void* kbase = K16 + hoff;
+    const void* kbase = K + hoff;
     const void* knbase = EXACT ? kbase : KN16 + hoff;
     const unsigned kbytes = (unsigned)L * D * 2u;
     const void* vbase = V + hoff;
@@ -684,11 +660,11 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
         const int qi = qw0 + row16;                // this lane's query row (0-based)
 
         // ---- query rows: B operand of S^T = K Q^T, and the row factor ----
-        f16x8 qf[DC];
+        std::conditional_t<FAST, f16x8, bf16x8> qf[DC];
         float lam = 0.0f;
         float lam_row;                             // lambda_i = log2(e) ln d ln i
         {
-            float ss = 0.0f, mx = 0.0f;
+            float ss = 0.0f;
             u32x4 w[DC];
 #pragma unroll
             for (int dc = 0; dc < DC; ++dc) {
@@ -700,13 +676,10 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
                     float a = bf16lo(w[dc][e]), b = bf16hi(w[dc][e]);
                     ss = __builtin_fmaf(a, a, ss);
                     ss = __builtin_fmaf(b, b, ss);
-                    mx = fmaxf(mx, fmaxf(fabsf(a), fabsf(b)));
                 }
             }
             ss += __shfl_xor(ss, 16);
             ss += __shfl_xor(ss, 32);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
             // log2(e) ln d ln i / max(|q_i|, 1e-12)  (Key design 1: log d . log N)
             // in fp32: a few ulp of lambda_i against the fp32 scores' (d + 3)
             // ulp of ln d ln i; the fp64 log and divide cost a block about
@@ -715,19 +688,22 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
             constexpr float kLn2 = 0.693147180559945309f;
             lam_row = (float)lam_scale * (__builtin_amdgcn_logf((float)(qi + 1)) * kLn2);
             const float lamf = lam_row / fmaxf(sqrtf(ss), 1e-12f);
-            // fast: lambda_i q^_i rounded to f16; exact: q_i 2^-e_i and the
-            // factor lambda_i 2^e_i / |q_i| applied to the accumulator
-            const int ex = f16_row_exponent(mx);
-            const float sc = FAST ? lamf : ldexpf(1.0f, -ex);
-            if constexpr (!FAST)
-                lam = ldexpf(lamf, ex);
+            // fast: lambda_i q^_i rounded to f16; exact: q_i itself and the
+            // factor lambda_i / |q_i| applied to the accumulator
+            if constexpr (FAST) {
 #pragma unroll
-            for (int dc = 0; dc < DC; ++dc)
+                for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    qf[dc][2 * e] = (_Float16)(bf16lo(w[dc][e]) * sc);
-                    qf[dc][2 * e + 1] = (_Float16)(bf16hi(w[dc][e]) * sc);
-                }
+                    for (int e = 0; e < 4; ++e) {
+                        qf[dc][2 * e] = (_Float16)(bf16lo(w[dc][e]) * lamf);
+                        qf[dc][2 * e + 1] = (_Float16)(bf16hi(w[dc][e]) * lamf);
+                    }
+            } else {
+                lam = lamf;
+#pragma unroll
+                for (int dc = 0; dc < DC; ++dc)
+                    qf[dc] = __builtin_bit_cast(bf16x8, w[dc]);
+            }
         }
 
         // scores of 16-key block ks: acc[r] = k_(16ks+4grp+r) . q_(row16)
@@ -735,9 +711,13 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int dc = 0; dc < DC; ++dc) {
-                const f16x8 a =
-                    *reinterpret_cast<const f16x8*>(base + krd[dc] + ks * 16 * T::R * 16);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[dc], acc, 0, 0, 0);
+                const unsigned char* a = base + krd[dc] + ks * 16 * T::R * 16;
+                if constexpr (FAST)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        *reinterpret_cast<const f16x8*>(a), qf[dc], acc, 0, 0, 0);
+                else
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        *reinterpret_cast<const bf16x8*>(a), qf[dc], acc, 0, 0, 0);
             }
             return acc;
         };

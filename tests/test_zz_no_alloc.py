@@ -66,7 +66,7 @@ def test_noalloc_matches_ws(case):
 
 def test_noalloc_refuses_input_beyond_scratch():
     import softmax_free_attention_amd as sfa
-    shape = (1, 16, 8192, 128)
+    shape = (1, 32, 8192, 128)
     assert sfa.lssar_workspace_bytes(*shape, sfa.LSSAR_BF16) > sfa.lssar_noalloc_scratch_bytes()
     q = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
     out = torch.empty_like(q)

@@ -815,9 +815,14 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
         // diagonal tiles follow it: with both bodies inside the loop, their
         // accumulators were copied back at every iteration (20 moves per
         // tile in pass 2).
+        // Tile kt goes to buffer (kt + kdiag) & 1, so that the (first)
+        // diagonal tile lands in buffer 0, and the loop runs two tiles per
+        // iteration: every buffer index is then a constant, and the LDS
+        // reads take the buffer's offset as an immediate (with the index
+        // kt & 1 each tile paid a vector add per operand address).
         auto tile_loop = [&](bool with_v, auto body) {
-            auto step = [&](int kt, auto diag_tag) {
-                const int buf = kt & 1;
+            auto step = [&](int kt, auto buf_tag, auto diag_tag) {
+                constexpr int buf = decltype(buf_tag)::value;
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();                   // tile kt landed; buf^1 free
                 if (kt + 1 < ntiles)
@@ -825,15 +830,25 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
                 if (wave_active)
                     body(kt, smem(buf), diag_tag);
             };
+            using B0 = std::integral_constant<int, 0>;
+            using B1 = std::integral_constant<int, 1>;
             __syncthreads();                       // earlier readers done with the buffers
-            issue(0, 0, with_v, FAST);
-            for (int kt = 0; kt < kdiag; ++kt)
-                step(kt, std::false_type{});
-            if constexpr (BK == kBQ16) {
-                step(kdiag, std::true_type{});     // the one diagonal tile
-            } else {
-                for (int kt = kdiag; kt < ntiles; ++kt)
-                    step(kt, std::true_type{});
+            const bool odd = (kdiag & 1) != 0;
+            issue(0, odd ? 1 : 0, with_v, FAST);
+            int kt = 0;
+            if (odd) {
+                step(0, B1{}, std::false_type{});
+                kt = 1;
+            }
+            for (; kt < kdiag; kt += 2) {          // kdiag - kt is even here
+                step(kt, B0{}, std::false_type{});
+                step(kt + 1, B1{}, std::false_type{});
+            }
+            step(kdiag, B0{}, std::true_type{});   // the diagonal tile(s)
+            if constexpr (BK != kBQ16) {
+                // 32-key tiles: the block's 64 rows span at most two
+                if (kdiag + 1 < ntiles)
+                    step(kdiag + 1, B1{}, std::true_type{});
             }
         };
         auto run_pass1 = [&](auto kind_tag) {

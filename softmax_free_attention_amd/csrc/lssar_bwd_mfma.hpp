@@ -1029,11 +1029,15 @@ __attribute__((amdgpu_waves_per_eu(3))) void lssar_bwd_kside_kernel(
             exact = *deep_flag != 0;
         }
         // the first query tile (qt = kb) holds the diagonal, the later ones
-        // lie wholly after every key of the block: it is peeled off the loop
+        // lie wholly after every key of the block: it is peeled off the loop.
+        // Double-buffered, tile n sits in buffer n & 1 and the loop runs two
+        // tiles per iteration, so that every buffer index is a constant and
+        // the LDS reads take the buffer's offset as an immediate (a runtime
+        // index cost a vector add per operand address and tile).
         auto tile_loop = [&](auto exact_tag) {
-            auto step = [&](int n, auto diag_tag) {
+            auto step = [&](int n, auto buf_tag, auto diag_tag) {
                 if constexpr (NB == 2) {
-                    const int buf = n & 1;
+                    constexpr int buf = decltype(buf_tag)::value;
                     __builtin_amdgcn_s_waitcnt(0);
                     __syncthreads();               // tile n landed; buffer buf ^ 1 free
                     if (n + 1 < ntiles)
@@ -1049,13 +1053,18 @@ __attribute__((amdgpu_waves_per_eu(3))) void lssar_bwd_kside_kernel(
                         tile(qt0 + n, lds, diag_tag, exact_tag);
                 }
             };
+            using B0 = std::integral_constant<int, 0>;
+            using B1 = std::integral_constant<int, 1>;
             if constexpr (NB == 2) {
                 __syncthreads();                   // earlier readers done with both buffers
                 issue(qt0, 0);
             }
-            step(0, std::true_type{});
-            for (int n = 1; n < ntiles; ++n)
-                step(n, std::false_type{});
+            step(0, B0{}, std::true_type{});
+            for (int n = 1; n < ntiles; n += 2) {
+                step(n, B1{}, std::false_type{});
+                if (n + 1 < ntiles)
+                    step(n + 1, B0{}, std::false_type{});
+            }
         };
         if (exact)
             tile_loop(std::true_type{});

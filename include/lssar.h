@@ -188,7 +188,11 @@ size_t lssar_decode_workspace_bytes(int B, int H, int Lmax, int d, int dtype);
  *    Values are clamped to [0, Lmax]; a sequence of length 0 gets zeros.
  *  - p, eps, dtype, errors: as for lssar_attn_fwd_ws.  d in {64, 128}.
  *  - workspace: lssar_decode_workspace_bytes(), 256-byte aligned, overlapping
- *    no argument.  Allocates nothing; three kernel launches on `stream`. */
+ *    no argument.  Allocates nothing; three kernel launches on `stream`
+ *    (bf16 with B*H >= 176: one launch, one workgroup per head, which uses
+ *    only the per-row part of the workspace).  Either way the output is
+ *    deterministic; the two schedules sum in different orders and agree to
+ *    rounding. */
 int lssar_decode_ws(const void* q, const void* k_cache, const void* v_cache,
                     const int* lens, void* out, int B, int H, int Lmax, int d,
                     int p, float eps, int dtype, void* workspace,

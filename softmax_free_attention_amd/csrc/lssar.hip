@@ -366,6 +366,16 @@ int validate_decode_shape(int B, int H, int Lmax, int d, int dtype)
     return LSSAR_OK;
 }
 
+// Heads from which the bf16 decode step runs as one launch with one
+// workgroup per head (lssar_decode_fused_kernel).  One such workgroup reads
+// about 37 GB/s, the split path about 6.6 TB/s in all, so below about 180
+// heads the split path is faster: with 192 heads (B16 H12, 8192 rows,
+// d = 64) the one-launch path took 63.2 us against 68.0 us, with 128 heads
+// (B4 H32, 4096 rows, d = 128) 46.7 us against 43.8 us.  (Lmax <= 2^22
+// keeps a head's cache, at most 2^30 bytes, within the 32-bit byte offsets
+// of its buffer loads.)
+constexpr int kDecFusedMinHeads = 176;
+
 template <typename T, int D, int P>
 void launch_decode(const void* q, const void* kc, const void* vc, const int* lens, void* out,
                    void* ws, int B, int H, int Lmax, int p, float eps, double lam_scale,
@@ -379,6 +389,17 @@ void launch_decode(const void* q, const void* kc, const void* vc, const int* len
     C* part1 = reinterpret_cast<C*>(base + w.scores_bytes);
     C* part2 = reinterpret_cast<C*>(base + w.scores_bytes + w.part1_bytes);
     const int BH = B * H;
+    // bf16 with enough heads to fill the part: one workgroup per head, one
+    // launch (the Softplus values go to the scores area)
+    if constexpr (std::is_same<T, __bf16>::value) {
+        if (BH >= kDecFusedMinHeads) {
+            hipLaunchKernelGGL((lssar::lssar_decode_fused_kernel<D, P>), dim3((unsigned)BH),
+                               dim3(lssar::kDecFusedThreads), 0, s, static_cast<const T*>(q),
+                               static_cast<const T*>(kc), static_cast<const T*>(vc), lens,
+                               scores, static_cast<T*>(out), H, Lmax, lam_scale, eps, p);
+            return;
+        }
+    }
     const unsigned grid = (unsigned)((long long)BH * w.nsplit);
     hipLaunchKernelGGL((lssar::lssar_decode_scores_kernel<T, D>), dim3(grid),
                        dim3(lssar::kDecThreads), 0, s, static_cast<const T*>(q),

@@ -491,6 +491,190 @@ __global__ __launch_bounds__(kDecThreads) void lssar_decode_pv_kernel(
         out2[e] = (accs[0][e] + accs[1][e]) + (accs[2][e] + accs[3][e]);
 }
 
+// The whole decode step in one launch, one workgroup per (batch, head), for
+// bf16 caches with many heads.  Phase A reads the head's K rows, stores
+// each key's Softplus value (base 2) in the scores area of the workspace and
+// reduces S1 and the largest score over the workgroup; phase B reads the V
+// rows, forms each key's weight from its stored value and accumulates
+// U = sum w v and D = sum w, and the workgroup writes out = U / D.  No
+// partials leave the workgroup, so the chunk partials, the combine kernel
+// and two kernel boundaries of the split path are gone.  With 192 heads,
+// 192 workgroups of 512 threads with 8 loads in flight per lane read a
+// cache at 7.1 TB/s in an in-bounds probe, against 6.6 TB/s for 12,288
+// workgroups of 32 KB each; the split path is kept for fewer heads.
+// Lanes: as in the split kernels, LPK lanes share a key and a wave-load
+// reads KPW consecutive keys (1 KB); load n of wave w in a round covers
+// keys (n NW + w) KPW + 0 .. KPW - 1.  Each round's loads are issued before
+// the previous round is consumed.
+constexpr int kDecFusedThreads = 512;
+
+template <int D, int P>
+__global__ __launch_bounds__(kDecFusedThreads) void lssar_decode_fused_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc, const __bf16* __restrict__ Vc,
+    const int* __restrict__ lens, float* __restrict__ sps, __bf16* __restrict__ out, int H,
+    int Lmax, double lam_scale, float eps, int p_rt)
+{
+    constexpr int EPL = 8;                     // bf16 values per 16-byte load
+    constexpr int LPK = D / EPL;               // lanes per key
+    constexpr int KPW = 64 / LPK;              // keys per wave-load
+    constexpr int NW = kDecFusedThreads / 64;  // waves
+    constexpr int NLD = 8;                     // loads per lane and round
+    constexpr int KPR = NW * KPW * NLD;        // keys per round
+    constexpr unsigned RB = D * 2;             // bytes per cache row
+    static_assert(LPK == 8 || LPK == 16, "decode lane layout");
+    __shared__ float red[NW][2];
+    __shared__ float accs[NW][D + 1];
+
+    const int bh = (int)blockIdx.x;
+    const int len = dec_len(lens, bh / H, Lmax);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane % LPK, ksl = lane / LPK;
+    __bf16* orow = out + (size_t)bh * D;
+    if (len == 0) {                            // uniform: an empty cache gives 0
+        for (int e = (int)threadIdx.x; e < D; e += kDecFusedThreads)
+            orow[e] = (__bf16)0.0f;
+        return;
+    }
+    const __bf16* kbase = Kc + (size_t)bh * Lmax * D;
+    const __bf16* vbase = Vc + (size_t)bh * Lmax * D;
+    const unsigned nbytes = (unsigned)len * RB;  // rows past len read as zeros
+    float* sh = sps + (size_t)bh * Lmax;
+    const unsigned sbytes = (unsigned)len * 4u;
+    // the lane's own key of load n (one key per lane: load sub mod NLD;
+    // at d = 128 the upper half of each key's lanes repeats the lower)
+    const int nown = sub & (NLD - 1);
+    auto key_of = [&](int k0, int n) { return k0 + (n * NW + wave) * KPW + ksl; };
+    auto load_round = [&](const __bf16* base, int k0, u32x4 (&raw)[NLD]) {
+#pragma unroll
+        for (int n = 0; n < NLD; ++n)
+            raw[n] = buf_load16(base, nbytes, (unsigned)key_of(k0, n) * RB + sub * 16u);
+    };
+
+    // the query and log2(e) ln d ln i / max(|q|, 1e-12), i = len (Key
+    // design 1: log d . log N), as in the split scores kernel
+    const bf16x8 q8 = __builtin_bit_cast(bf16x8, load_raw(Q + (size_t)bh * D + sub * EPL));
+    const float qss = lane_group_sum<LPK>(dot8_bf16(q8, q8, 0.0f));
+    const float lam = (float)lam_scale * (__builtin_amdgcn_logf((float)len) * 0.69314718055994531f) *
+                      __builtin_amdgcn_rsqf(fmaxf(qss, 1e-24f));
+
+    // ---- phase A: scores, their Softplus values, S1 and the largest score ----
+    float s1 = 0.0f, tmax = -INFINITY;
+    u32x4 cur[NLD], nxt[NLD];
+    load_round(kbase, 0, nxt);
+    for (int k0 = 0; k0 < len; k0 += KPR) {
+#pragma unroll
+        for (int n = 0; n < NLD; ++n)
+            cur[n] = nxt[n];
+        if (k0 + KPR < len)
+            load_round(kbase, k0 + KPR, nxt);
+        float dot = 0.0f, ss = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NLD; ++n) {
+            const bf16x8 k8 = __builtin_bit_cast(bf16x8, cur[n]);
+            const float dn = lane_group_sum<LPK>(dot8_bf16(q8, k8, 0.0f));
+            const float sn = lane_group_sum<LPK>(dot8_bf16(k8, k8, 0.0f));
+            dot = n == nown ? dn : dot;
+            ss = n == nown ? sn : ss;
+        }
+        const int key = key_of(k0, nown);
+        if (key < len && sub < NLD) {
+            // 1 / max(|k|, 1e-12) = rsqrt(max(|k|^2, 1e-24)), v_rsq_f32
+            const float t = dot * lam * __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
+            const float sp = softplus_dec(t);
+            sh[key] = sp;
+            s1 += sp;
+            tmax = dmax(tmax, t);
+        }
+    }
+    // phase B's first round in flight across the reduction
+    load_round(vbase, 0, nxt);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        s1 += __shfl_xor(s1, o);
+        tmax = dmax(tmax, __shfl_xor(tmax, o));
+    }
+    if (lane == 0) {
+        red[wave][0] = s1;
+        red[wave][1] = tmax;
+    }
+    __syncthreads();                           // also: every Softplus value stored
+    float S = 0.0f, m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {             // a fixed order
+        S += red[w][0];
+        m = dmax(m, red[w][1]);
+    }
+    // row constants of the re-weighting (Key design 2)
+    const float spmax = softplus_dec(m);
+    const float o = len <= 3 ? 0.0f : 1.0f;
+    const float tau = o * S / (float)len;
+    const float gap = spmax - tau;
+    const float mrow = (float)len * gap / S;   // max_j (i A_j - o_i)
+    if (!(mrow > eps)) {                       // uniform: a degenerate row is 0
+        for (int e = (int)threadIdx.x; e < D; e += kDecFusedThreads)
+            orow[e] = (__bf16)0.0f;
+        return;
+    }
+    const float c = 1.0f / gap, tc = tau * c;
+
+    // ---- phase B: weights, U = sum w v and D = sum w ----
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+        acc[e] = 0.0f;
+    float dsum = 0.0f;
+    for (int k0 = 0; k0 < len; k0 += KPR) {
+#pragma unroll
+        for (int n = 0; n < NLD; ++n)
+            cur[n] = nxt[n];
+        // the lane's own key's Softplus value (0 past len)
+        const int key = key_of(k0, nown);
+        const float sp = buf_load_c(sh, sbytes, (unsigned)key * 4u);
+        if (k0 + KPR < len)
+            load_round(vbase, k0 + KPR, nxt);
+        const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(sp, c, -tc), 0.0f, 1.0f);
+        const float wown = key < len ? pow_chain<P>(y, p_rt) : 0.0f;
+        dsum += sub < NLD ? wown : 0.0f;       // each key once
+#pragma unroll
+        for (int n = 0; n < NLD; ++n) {
+            const float w = group_lane<LPK>(wown, n);
+            float vv[EPL];
+            unpack(cur[n], vv);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+                acc[e] = __builtin_fmaf(w, vv[e], acc[e]);
+        }
+    }
+    // lanes with the same sub hold the same dims: sum over the key slots,
+    // then over the waves in a fixed order
+#pragma unroll
+    for (int o2 = LPK; o2 < 64; o2 <<= 1) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            acc[e] += __shfl_xor(acc[e], o2);
+    }
+#pragma unroll
+    for (int o2 = 1; o2 < 64; o2 <<= 1)
+        dsum += __shfl_xor(dsum, o2);
+    if (ksl == 0) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            accs[wave][sub * EPL + e] = acc[e];
+    }
+    if (lane == 0)
+        accs[wave][D] = dsum;
+    __syncthreads();
+    for (int e = (int)threadIdx.x; e < D; e += kDecFusedThreads) {
+        float u = 0.0f, den = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            u += accs[w][e];
+            den += accs[w][D];
+        }
+        orow[e] = (__bf16)(den > 0.0f ? u / den : 0.0f);
+    }
+}
+
 // out = U / D over the chunks of each head (0 when D = 0: degenerate rows
 // and empty caches).  One workgroup per head: thread (g, e) sums chunks
 // g, g + G, ... of element e (G = 256 / (D + 1) rounded down, the element D

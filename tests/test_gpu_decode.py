@@ -163,6 +163,76 @@ def test_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+# From this many (batch, head) pairs on, bf16 decode runs as one launch with
+# one workgroup per head; below it, as three launches over cache chunks.
+FUSED_MIN_HEADS = 176
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("p", [3, 15, 7])
+def test_one_launch_path_parity(d, p):
+    """bf16 with B*H >= 176 (one workgroup per head): every head against the
+    oracle, at lengths 0..4, one round of keys and the next (512 keys per
+    round at d = 64, 256 at d = 128) and their ragged tails, a length above
+    Lmax (clamped) and the full cache."""
+    B, H = 16, -(-FUSED_MIN_HEADS // 16)
+    for Lmax in (5, 513, 1100):
+        inp = gen.make_decode_inputs("x8_decode", B=B, H=H, Lmax=Lmax, d=d, dtype="bf16", p=p,
+                                     seed=Lmax + d)
+        lens = np.array([0, 1, 2, 3, 4, 255, 256, 257, 511, 512, 513, 1000, 1023, 1100,
+                         Lmax + 50, Lmax], np.int32)
+        q, k, v = (to_device(a, "bf16") for a in (inp.q, inp.k, inp.v))
+        got = to_host(run_decode(q, k, v, lens, p))
+        eff = np.minimum(lens, Lmax)
+        assert np.all(got[0] == 0.0)
+        want = oracle_decode(inp.q, inp.k, inp.v, eff, p)
+        worst = _compare(got, want, BF16_TOL, f"one launch d={d} p={p} Lmax={Lmax}")
+        print(f"one-launch decode d={d} p={p} Lmax={Lmax}: max-abs {worst:.3e}", flush=True)
+
+
+def test_one_launch_path_matches_split_path():
+    """The same heads through both paths (B*H = 192 runs as one launch, the
+    first two sequences alone, B*H = 24, as three): the outputs agree to the
+    bf16 bar, and the one-launch path is deterministic."""
+    for d in (64, 128):
+        inp = gen.make_decode_inputs("x8_decode_ragged", B=16, H=12, Lmax=900, d=d, dtype="bf16",
+                                     seed=d)
+        q, k, v = (to_device(a, "bf16") for a in (inp.q, inp.k, inp.v))
+        one = run_decode(q, k, v, inp.lens, 15)
+        again = run_decode(q, k, v, inp.lens, 15)
+        assert torch.equal(one.view(torch.int16), again.view(torch.int16))
+        split = run_decode(q[:2].contiguous(), k[:2].contiguous(), v[:2].contiguous(),
+                           inp.lens[:2], 15)
+        diff = float((one[:2].float() - split.float()).abs().max())
+        print(f"d={d}: one launch vs split max-abs {diff:.3e}", flush=True)
+        assert diff <= BF16_TOL
+
+
+def test_one_launch_path_edges():
+    """B*H >= 176: rows past each length hold NaN and are never read (bitwise
+    the same output); a zero query makes every score 0, so rows from 4 on are
+    degenerate (0) and rows 1..3 the mean of their values."""
+    B, H, Lmax = 16, 12, 600
+    inp = gen.make_decode_inputs("x8_decode_ragged", B=B, H=H, Lmax=Lmax, dtype="bf16", seed=4)
+    q, k, v = (to_device(a, "bf16") for a in (inp.q, inp.k, inp.v))
+    base = run_decode(q, k, v, inp.lens, 15)
+    k2, v2 = k.clone(), v.clone()
+    for b, n in enumerate(inp.lens):
+        k2[b, :, n:] = float("nan")
+        v2[b, :, n:] = float("nan")
+    o2 = run_decode(q, k2, v2, inp.lens, 15)
+    assert torch.equal(o2.view(torch.int16), base.view(torch.int16))
+    assert bool(torch.isfinite(o2.float()).all())
+    qz = np.zeros_like(inp.q)
+    lens = np.array([1, 2, 3, 4, 5, 600] + [300] * (B - 6), np.int32)
+    got = to_host(run_decode(to_device(qz, "bf16"), k, v, lens, 3))
+    assert np.all(got[3:] == 0.0)
+    for b in range(3):
+        n = int(lens[b])
+        mean = inp.v[b, :, :n].astype(np.float64).mean(axis=1)
+        assert np.max(np.abs(got[b] - mean)) <= BF16_TOL
+
+
 @pytest.mark.parametrize("name", ["x8_decode", "x8_decode_ragged", "wide_decode"])
 def test_full_decode_workload_sampled(name):
     """The bench's decode workloads at full size, sampled heads vs the oracle."""

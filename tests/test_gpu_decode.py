@@ -190,6 +190,17 @@ def test_one_launch_path_parity(d, p):
         print(f"one-launch decode d={d} p={p} Lmax={Lmax}: max-abs {worst:.3e}", flush=True)
 
 
+def test_one_launch_path_without_lens():
+    """B*H >= 176 with lens = NULL: every head uses all Lmax rows."""
+    B, H, Lmax = 16, 12, 700
+    inp = gen.make_decode_inputs("x8_decode", B=B, H=H, Lmax=Lmax, d=64, dtype="bf16", seed=11)
+    q, k, v = (to_device(a, "bf16") for a in (inp.q, inp.k, inp.v))
+    got = to_host(run_decode(q, k, v, None, 15))
+    want = oracle_decode(inp.q, inp.k, inp.v, np.full(B, Lmax, np.int32), 15)
+    worst = _compare(got, want, BF16_TOL, "one launch, lens NULL")
+    print(f"one-launch decode, lens NULL: max-abs {worst:.3e}", flush=True)
+
+
 def test_one_launch_path_matches_split_path():
     """The same heads through both paths (B*H = 192 runs as one launch, the
     first two sequences alone, B*H = 24, as three): the outputs agree to the

@@ -104,9 +104,11 @@ def test_training_pair_in_a_graph():
     _replays(g, [q, k, v, dout], fresh, [out, st, dq, dk, dv], eager)
 
 
-def test_decode_in_a_graph():
+@pytest.mark.parametrize("B,H", [(4, 3), (16, 12)])
+def test_decode_in_a_graph(B, H):
+    """B*H = 12 runs the three split kernels, B*H = 192 the one-launch kernel."""
     import softmax_free_attention_amd as sfa
-    inp = gen.make_decode_inputs("x8_decode_ragged", B=4, H=3, Lmax=900)
+    inp = gen.make_decode_inputs("x8_decode_ragged", B=B, H=H, Lmax=900)
     q, kc, vc = (to_device(a, "bf16") for a in (inp.q, inp.k, inp.v))
     lens = torch.from_numpy(np.ascontiguousarray(inp.lens, np.int32)).cuda()
     ws, out = sfa.decode_workspace_for(kc), torch.empty_like(q)
@@ -125,7 +127,7 @@ def test_decode_in_a_graph():
         return [ref]
 
     def fresh(n):
-        d = gen.make_decode_inputs("x8_decode_ragged", B=4, H=3, Lmax=900, seed=40 + n)
+        d = gen.make_decode_inputs("x8_decode_ragged", B=B, H=H, Lmax=900, seed=40 + n)
         new_lens = np.minimum(np.asarray(d.lens, np.int32) - 50 * n, 900).clip(1)
         return [to_device(d.q, "bf16"), to_device(d.k, "bf16"), to_device(d.v, "bf16"),
                 torch.from_numpy(np.ascontiguousarray(new_lens, np.int32)).cuda()]

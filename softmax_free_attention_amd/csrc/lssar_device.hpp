@@ -158,9 +158,15 @@ __device__ __forceinline__ float max3_scores(float a, float b, float c)
 
 // What a run of pass 1 accumulates: S1 (in product form) and the row max,
 // S1 from softplus2_acc and the row max (blocks computed again), or the row
-// max alone.
+// max alone; or S1 as the product of the factors 1 + 2^t themselves and the
+// row max (kPass1Prod: scores at most kProdMaxT).
 constexpr int kPass1Sum = 0;
 constexpr int kPass1Acc = 1;
+constexpr int kPass1Prod = 2;
+// Largest base-2 score for which two factors 1 + 2^t times a mantissa below
+// 1 stay finite in fp32 (2^121 < 2^128), with room for the f16 operands'
+// rounding of lambda_i q^_i . k^_j above lambda_i.
+constexpr float kProdMaxT = 60.0f;
 
 // y^P for y in [0, 1] by a fixed multiplication chain (P = 0: runtime p).
 template <int P, typename F>
@@ -760,6 +766,10 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
         // ---------------- pass 1: S1 and the row max of the scores ----------------
         float s1 = 0.0f;
         float tmax = -INFINITY;
+        // kPass1Prod: the running product of the factors 1 + 2^t as a
+        // mantissa pm in [0.5, 1) and an exponent pe
+        float pm = 1.0f;
+        int pe = 0;
         auto pass1_tile = [&](int kt, const unsigned char* base, auto diag_tag, auto kind_tag) {
             constexpr bool DIAG = decltype(diag_tag)::value;
             constexpr int KIND = decltype(kind_tag)::value;
@@ -780,6 +790,22 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         pos_sum += softplus2_acc(t[r]);
+                    tmax = max3_scores(tmax, t[0], t[1]);
+                    tmax = max3_scores(tmax, t[2], t[3]);
+                } else if constexpr (KIND == kPass1Prod) {
+                    // log2(1 + 2^t) summed as log2 of the product of the
+                    // factors, renormalised after every two of them (each
+                    // at most 2^kProdMaxT + 1): one exp2 and one fma per
+                    // pair, no max and add for the positive part
+#pragma unroll
+                    for (int r = 0; r < 4; r += 2) {
+                        const float u0 = __builtin_amdgcn_exp2f(t[r]);
+                        const float u1 = __builtin_amdgcn_exp2f(t[r + 1]);
+                        pm = __builtin_fmaf(pm, u0, pm);
+                        pm = __builtin_fmaf(pm, u1, pm);
+                        pe += __builtin_amdgcn_frexp_expf(pm);
+                        pm = __builtin_amdgcn_frexp_mantf(pm);
+                    }
                     tmax = max3_scores(tmax, t[0], t[1]);
                     tmax = max3_scores(tmax, t[2], t[3]);
                 } else if constexpr (PHI == kPhiSoftplus) {
@@ -860,10 +886,24 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
         constexpr bool ACC = REDO && PHI == kPhiSoftplus;   // softplus2_acc
         RowConst rc = {0.0f, 0.0f, false};
         if constexpr (RW) {
-            if constexpr (ACC)
+            if constexpr (ACC) {
                 run_pass1(std::integral_constant<int, kPass1Acc>{});
-            else
+            } else if constexpr (FAST) {
+                // every score of the block is at most about lambda of its
+                // last row (|q^ . k^| <= 1): the product form when that
+                // stays within kProdMaxT (wave-uniform)
+                constexpr float kLn2 = 0.693147180559945309f;
+                const float lam_last = (float)lam_scale *
+                    (__builtin_amdgcn_logf((float)min(L, q0 + kBQ16)) * kLn2);
+                if (__builtin_amdgcn_readfirstlane((int)(lam_last <= kProdMaxT))) {
+                    run_pass1(std::integral_constant<int, kPass1Prod>{});
+                    s1 = __builtin_amdgcn_logf(pm) + (float)pe;
+                } else {
+                    run_pass1(std::integral_constant<int, kPass1Sum>{});
+                }
+            } else {
                 run_pass1(std::integral_constant<int, kPass1Sum>{});
+            }
             const float trow = row_max(tmax);
             const float s1r = row_sum(s1);
             if constexpr (ACC) {

@@ -39,6 +39,25 @@ def test_long_sequence_sampled_rows(L, d, p):
     assert err <= BF16_TOL and np.all(np.isfinite(got))
 
 
+@pytest.mark.parametrize("L,d,lo", [(5400, 128, 5120), (22200, 64, 21888)])
+def test_pass1_forms_meet(L, d, lo):
+    """The plain forward sums a block's Softplus values as the product of the
+    factors 1 + 2^t (base 2) while every score is at most 60, that is while
+    log2(e) ln d ln(last row) <= 60, and as max(t, 0) plus log2 of the
+    factors 1 + 2^-|t| after that: rows 5276 on at d = 128, 22027 on at
+    d = 64.  Every row of the four 64-row blocks around the switch against
+    the oracle."""
+    inp = gen.make_inputs("x16", B=1, H=1, L=L, d=d, p=15, seed=L + d)
+    q, k, v = (to_device(a, "bf16") for a in (inp.q, inp.k, inp.v))
+    got = to_host(run_ws(q, k, v, 15))
+    rows = list(range(lo, lo + 256))
+    want = oracle.lssar_rows(inp.q[0, 0], inp.k[0, 0], inp.v[0, 0], rows, 15)
+    err = np.max(np.abs(got[0, 0, rows] - want), axis=1)
+    print(f"L={L} d={d}: rows {lo}..{lo + 255} max-abs {err.max():.3e} (row {lo + int(err.argmax())})",
+          flush=True)
+    assert float(err.max()) <= BF16_TOL and np.all(np.isfinite(got))
+
+
 @pytest.mark.parametrize("L", [3, 65])
 def test_many_short_heads(L):
     B, H = 128, 16

@@ -888,10 +888,12 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 1 : 4))) void lssar_fwd_bf16_kernel
         if constexpr (RW) {
             if constexpr (ACC) {
                 run_pass1(std::integral_constant<int, kPass1Acc>{});
-            } else if constexpr (FAST) {
+            } else if constexpr (PHI == kPhiSoftplus && (FAST || D == 64)) {
                 // every score of the block is at most about lambda of its
                 // last row (|q^ . k^| <= 1): the product form when that
-                // stays within kProdMaxT (wave-uniform)
+                // stays within kProdMaxT (wave-uniform).  (The training
+                // forward at d = 128 keeps the other form: with both, its
+                // kernel spills 12 bytes per lane at 128 VGPRs.)
                 constexpr float kLn2 = 0.693147180559945309f;
                 const float lam_last = (float)lam_scale *
                     (__builtin_amdgcn_logf((float)min(L, q0 + kBQ16)) * kLn2);

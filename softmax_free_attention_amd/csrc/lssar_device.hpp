@@ -156,10 +156,11 @@ __device__ __forceinline__ float max3_scores(float a, float b, float c)
     return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
-// What a run of pass 1 accumulates: S1 (in product form) and the row max,
-// S1 from softplus2_acc and the row max (blocks computed again), or the row
-// max alone; or S1 as the product of the factors 1 + 2^t themselves and the
-// row max (kPass1Prod: scores at most kProdMaxT).
+// What a run of pass 1 accumulates besides the row max.  kPass1Sum: S1 as
+// max(t, 0) plus log2 of the product of the factors 1 + 2^-|t| (Softplus),
+// or as a plain sum (Sigmoid); kPass1Acc: S1 from softplus2_acc (blocks
+// computed again); kPass1Prod: S1 as log2 of the product of the factors
+// 1 + 2^t themselves (scores at most kProdMaxT).
 constexpr int kPass1Sum = 0;
 constexpr int kPass1Acc = 1;
 constexpr int kPass1Prod = 2;
@@ -425,13 +426,19 @@ __global__ __launch_bounds__(kThreads) void lssar_prep_bf16_kernel(
 // banks.  Lane group grp = lane >> 4 holds keys 16 ks + 4 grp + r (r = 0..3)
 // of every 16-key block ks of a tile.
 //
-// Pass 1 keeps, per lane and query row, the partial sums of
-//   Softplus2(t) = max(t, 0) + log2(1 + 2^-|t|)
-// as sum_j max(t_j, 0) plus log2 of the product of the factors
-// (1 + 2^-|t_j|), each in (1, 2]: one exp2 per pair and one log2 per tile for
-// its 16 factors (their product stays below 2^16).  Masked pairs get
-// t = -inf, which adds exactly 0 to every sum in both passes (2^-inf = 0,
-// max(-inf, 0) = 0; in pass 2 Softplus2 = 0 gives y = clamp(-tau c) = 0).
+// Pass 1 keeps, per lane and query row, the sum of Softplus2(t) =
+// log2(1 + 2^t) in one of two product forms:
+//  * while every score of the block is at most kProdMaxT: log2 of the
+//    product of the factors 1 + 2^t_j, held as a mantissa in [0.5, 1) and
+//    an exponent and renormalised after every two factors (one exp2 and
+//    one fma per pair, one log2 per row);
+//  * otherwise (long rows), as Softplus2(t) = max(t, 0) + log2(1 + 2^-|t|):
+//    sum_j max(t_j, 0) plus log2 of the product of the factors
+//    (1 + 2^-|t_j|), each in (1, 2] (one exp2 per pair and one log2 per
+//    tile for its 16 factors, whose product stays below 2^16).
+// Masked pairs get t = -inf, which adds exactly 0 to every sum in both
+// passes (2^-inf = 0 and a factor 1, max(-inf, 0) = 0; in pass 2
+// Softplus2 = 0 gives y = clamp(-tau c) = 0).
 
 // One tile of BK keys: K and V (BK rows of D each, row-major) and the BK
 // key factors (the area holds 64; the loader writes 64).

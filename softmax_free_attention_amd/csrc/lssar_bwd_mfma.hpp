@@ -484,10 +484,17 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 // pass 1 as in the forward: sum max(t, 0) plus log2 of the
                 // product of the factors 1 + 2^-|t| (one exp2 per pair), and
                 // for a block with a deep row the exact Softplus (softplus2_acc)
-                auto pass1 = [&](auto acc_tag) {
+                // PROD: log2 of the product of the factors 1 + 2^t, a
+                // mantissa and an exponent renormalised after every two, as
+                // in the forward while the block's scores stay within
+                // kProdMaxT
+                auto pass1 = [&](auto acc_tag, auto prod_tag) {
                     constexpr bool ACC = decltype(acc_tag)::value;
+                    constexpr bool PROD = decltype(prod_tag)::value;
                     s1 = 0.0f;
                     tmax = -INFINITY;
+                    float pm = 1.0f;
+                    int pe = 0;
                     tile_loop(false, [&](int kt, const unsigned char* base, auto diag_tag) {
                         constexpr bool DIAG = decltype(diag_tag)::value;
                         const int nks = DIAG ? min(4, (qwl - kt * 64) / 16 + 1) : 4;
@@ -499,11 +506,20 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                             f32x4 f4;
                             const f32x4 t =
                                 scores(kt, base, ks, mm_block(base, KOFF, qf, ks), DIAG, f4);
+                            if constexpr (PROD) {
+#pragma unroll
+                                for (int r = 0; r < 4; r += 2) {
+                                    pm = __builtin_fmaf(pm, __builtin_amdgcn_exp2f(t[r]), pm);
+                                    pm = __builtin_fmaf(pm, __builtin_amdgcn_exp2f(t[r + 1]), pm);
+                                    pe += __builtin_amdgcn_frexp_expf(pm);
+                                    pm = __builtin_amdgcn_frexp_mantf(pm);
+                                }
+                            }
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
                                 if constexpr (ACC) {
                                     pos += softplus2_acc(t[r]);
-                                } else {
+                                } else if constexpr (!PROD) {
                                     pos += fmaxf(t[r], 0.0f);
                                     prod = __builtin_fmaf(prod, __builtin_amdgcn_exp2f(-fabsf(t[r])),
                                                           prod);
@@ -513,9 +529,11 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                         }
                         if constexpr (ACC)
                             s1 += pos;
-                        else
+                        else if constexpr (!PROD)
                             s1 += pos + __builtin_amdgcn_logf(prod);
                     });
+                    if constexpr (PROD)
+                        s1 = __builtin_amdgcn_logf(pm) + (float)pe;
                     s1 += __shfl_xor(s1, 16);
                     s1 += __shfl_xor(s1, 32);
                     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
@@ -525,12 +543,19 @@ __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1))) void lssar_bwd_qside_ker
                 // set by lanes of deep rows, read after one more barrier
                 if (tid == 0)
                     *deep_flag = 0;
-                pass1(std::false_type{});
+                // every score of the block is at most about lambda of its
+                // last row (wave-uniform)
+                const float lam_last = (float)lam_scale *
+                    (__builtin_amdgcn_logf((float)min(L, qb * 64 + 64)) * kLn2);
+                if (__builtin_amdgcn_readfirstlane((int)(lam_last <= kProdMaxT)))
+                    pass1(std::false_type{}, std::true_type{});
+                else
+                    pass1(std::false_type{}, std::false_type{});
                 if (qvalid && tmax < kDeep)
                     *deep_flag = 1;
                 __syncthreads();
                 if (*deep_flag)
-                    pass1(std::true_type{});
+                    pass1(std::true_type{}, std::false_type{});
             }
             store_tmax();
             row_consts();
